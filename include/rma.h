@@ -1,0 +1,204 @@
+/*
+ * rma.h -- C ABI of librma.so: Top-K+phi residual-mass-accounting decode on
+ * AMD MI355X (gfx950).
+ *
+ * Method: "Residual-Mass Accounting for Partial-KV Decoding" (arXiv
+ * 2604.05438).  §1 summarises it: at prefill, fixed-size positive-feature
+ * summaries (S, u) are built over the non-anchor mid-region of each kv head;
+ * at decode, exact unnormalised terms are computed over the sink/tail anchors
+ * and the retrieved tokens, the retrieved tokens' feature contributions are
+ * subtracted from the summaries, the residual numerator/denominator estimate
+ * phi(q)^T S_res, phi(q)^T u_res is added in the unnormalised domain, and a
+ * single normalisation follows (§4.3, Eq. 10).  The KV cache format is left
+ * unchanged (the v1 abstract: the module keeps backbone weights and the
+ * KV-cache format unchanged), so every call reads the caller's cache in place.
+ *
+ * Conventions shared by every call
+ *  - All pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *    every buffer, including the workspace.  The library never allocates or
+ *    frees memory and never synchronises: each call validates its arguments on
+ *    the host, then enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *    null stream) and returns.  Device-side faults surface at the caller's
+ *    next synchronisation.
+ *  - A "unit" is one (request, layer, kv head).  Units are numbered
+ *    u = 0..n_units-1; parameter set p = u % n_param_sets serves unit u.
+ *  - KV cache view (rma_kv): element (u, t, j) of K (or V) lives at
+ *    k[u*unit_stride + t*d + j], rows t = 0..t_cap-1, d = head dim.  K and V
+ *    share dtype, strides and shape.  Positions [0, L) are the prefill
+ *    segment; [L, L + n_gen) are generated tokens.
+ *  - Span (rma_span): anchors A = [0, n_sink) u [L - n_tail, L), mid-region
+ *    M = [n_sink, L - n_tail) of size L_mid = L - n_sink - n_tail (page §3,
+ *    Eq. 2), generated tokens [L, L + n_gen) (exact, never in the residual,
+ *    page §3 before Eq. 5 and Eq. 11).
+ *  - Query q: fp32 [n_units][G][d]; query head g of unit u is the g-th of the G
+ *    query heads that share the kv head (GQA).
+ *  - Supported now: d in {64, 128}; m in {64, 128}; G in 1..8; K/V dtype
+ *    RMA_F32 or RMA_BF16; phi_k storage RMA_F32 or RMA_BF16.  Anything else
+ *    returns RMA_ERR_UNSUPPORTED.
+ *  - Alignment: every device pointer must be 16-byte aligned, and unit_stride
+ *    a multiple of 8 elements; otherwise RMA_ERR_INVALID_ARG.
+ *  - Errors: validation happens before anything is enqueued; on an error
+ *    nothing is launched and the outputs are untouched.  rma_last_error()
+ *    gives a message for the calling thread's last failed call.
+ *  - Workspace: calls that need scratch take (workspace, workspace_bytes);
+ *    rma_workspace_bytes() gives the size.  The first 4096 bytes of a
+ *    workspace hold completion counters that must be zero before the first
+ *    use (e.g. allocate it zero-filled); every call leaves them zero again.
+ *    Calls that may run concurrently need distinct workspaces.
+ *  - NaN/Inf inputs are not checked; outputs are then unspecified (no fault).
+ */
+#ifndef RMA_H_
+#define RMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMA_ABI_VERSION 1
+
+typedef enum {
+  RMA_OK = 0,
+  RMA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misalignment, K > L_mid, ... */
+  RMA_ERR_UNSUPPORTED = -2,  /* d, m, G or dtype outside the supported set */
+  RMA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  RMA_ERR_HIP = -4           /* a kernel launch failed */
+} rma_status;
+
+typedef enum { RMA_F32 = 0, RMA_BF16 = 1 } rma_dtype;
+
+/* Read-only view of one KV cache (K and V of n_units units). */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t dtype;        /* rma_dtype of K and V */
+  int32_t n_units;
+  int64_t t_cap;        /* rows per unit */
+  int64_t unit_stride;  /* elements between consecutive units (>= t_cap*d) */
+  int32_t d;            /* head dim (d_h = d_v) */
+  int32_t reserved;
+} rma_kv;
+
+/* Prefill segment and generated tokens, identical for every unit. */
+typedef struct {
+  int64_t L;            /* prefill length */
+  int32_t n_sink;
+  int32_t n_tail;
+  int64_t n_gen;        /* generated tokens visible to this decode step */
+} rma_span;
+
+/* Operation ids for rma_workspace_bytes(). */
+#define RMA_OP_BUILD_SUMMARIES 1
+#define RMA_OP_DECODE_TOPK 2
+#define RMA_OP_DECODE_MERGE 3
+
+/* rma_decode_merge() flags (page §5.2 Table 1 and §7.1 Table 3 variants). */
+#define RMA_MERGE_SUB 0u           /* Top-K+phi: subtract retrieved tokens (default) */
+#define RMA_MERGE_NO_RESIDUAL 1u   /* selection-only Top-K: drop the residual */
+#define RMA_MERGE_NO_SUBTRACT 2u   /* NoSub: add the whole-mid estimate, no subtraction */
+
+/*
+ * rma_phi_features -- positive feature map (page App. C.1 "Why positivity
+ * matters"; the elu+1 form of the workloads):
+ *     phi[u][r][:] = elu(W[p] x[u][r] + b[p]) + 1,   p = u % n_param_sets.
+ * x:   [n_units][rows][d] of x_dtype, unit stride x_unit_stride elements, row
+ *      stride d.
+ * W:   fp32 [n_param_sets][m][d] row-major;  b: fp32 [n_param_sets][m].
+ * phi: [n_units][rows][m] of phi_dtype, dense.
+ * Used at decode for f = phi_q(q) (rows = G).  Arithmetic is fp32.
+ */
+rma_status rma_phi_features(const void* x, int32_t x_dtype, int32_t n_units, int64_t rows,
+                            int64_t x_unit_stride, int32_t d, const float* W, const float* b,
+                            int32_t m, int32_t n_param_sets, void* phi, int32_t phi_dtype,
+                            void* stream);
+
+/*
+ * rma_build_summaries -- prefill summaries over the mid-region (page §1 and
+ * §4.1; Eq. 6):
+ *     Phi_K[u][i][:] = phi_k(k[u][n_sink + i]),  i = 0..L_mid-1
+ *     S[u]   = sum_i Phi_K[u][i] v[u][n_sink+i]^T     fp32 [m][d]
+ *     u_[u]  = sum_i Phi_K[u][i]                       fp32 [m]
+ *     kappa[u] >= max_i ||k[u][n_sink+i]||_2           fp32 (an upper bound)
+ * If Wk != NULL, phi_k rows are computed (elu(Wk[p] k + bk[p]) + 1), rounded
+ * to phi_dtype and written to phi_k; S and u are formed from the rounded rows
+ * so that the rows later subtracted at decode are exactly those summed here.
+ * If Wk == NULL (bk ignored), phi_k is an INPUT holding the rows (any positive
+ * features, e.g. for an ideal-factorisation check) and is only read.
+ * phi_k: [n_units][L_mid][m] of phi_dtype, dense.  S, u_, kappa overwritten.
+ * Needs L_mid >= 0 (L_mid == 0 gives S = u = 0, kappa = 0).
+ * Workspace: rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ...).
+ */
+rma_status rma_build_summaries(const rma_kv* kv, const rma_span* span, const float* Wk,
+                               const float* bk, int32_t m, int32_t n_param_sets, void* phi_k,
+                               int32_t phi_dtype, float* S, float* u_, float* kappa,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rma_decode_topk -- exhaustive Top-K over the mid-region (page §1: exhaustive
+ * Top-K is the control selector that fixes the exact support; §3 Eq. 3: K(q)
+ * is a subset of M of size K).  For every query head it ranks all mid tokens
+ * by the exact real value of q.k_i (scaling by 1/sqrt(d) does not change the
+ * order), ties to the lower position, and returns the K winners.
+ * q:       fp32 [n_units][G][d].
+ * kappa:   fp32 [n_units], from rma_build_summaries (bounds the fp32 scoring
+ *          error; selection is exact for any inputs).
+ * idx:     int32 [n_units][G][K]: absolute positions in [n_sink, L - n_tail),
+ *          ascending.
+ * sel_scores: fp32 [n_units][G][K]: s_i = fl32(q.k_i) / sqrt(d) of idx[...],
+ *          consumed by rma_decode_merge.
+ * 0 <= K <= L_mid.  K == 0 writes nothing.
+ * Workspace: rma_workspace_bytes(RMA_OP_DECODE_TOPK, ...) (depends on G, K).
+ */
+rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rma_span* span,
+                           const float* kappa, int32_t K, int32_t* idx, float* sel_scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rma_decode_merge -- exact branch, retrieved-token subtraction, residual
+ * estimate and single normalisation (page §3 Eq. 3-4 and 11, §4.2 Eq. 9,
+ * §4.3 Eq. 10):
+ *   E = A u K(q) u Gen, s_i = q.k_i/sqrt(d), m* = max_{i in E} s_i,
+ *   N_E = sum_E e^{s_i - m*} v_i,  Z_E = sum_E e^{s_i - m*},
+ *   w_i = f.Phi_K[i] (i in K(q)),  f = phi_q[u][g],
+ *   nu_R = S^T f - sum_{K(q)} w_i v_i,  Z_R = max(u^T f - sum_{K(q)} w_i, 0)
+ *   (both exactly 0 when K == L_mid; the clamp is the page's App. C.1 guard
+ *   against subtraction artifacts),
+ *   y = (N_E + e^{-m*} nu_R) / (Z_E + e^{-m*} Z_R).
+ * q: fp32 [n_units][G][d];  phi_q: fp32 [n_units][G][m] (any positive
+ * features; rma_phi_features gives phi_q).  idx, sel_scores as written by
+ * rma_decode_topk (K per head).  phi_k, S, u_ as written/used by
+ * rma_build_summaries.
+ * flags: RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL (selection-only Top-K) or
+ *        RMA_MERGE_NO_SUBTRACT (NoSub).
+ * y: fp32 [n_units][G][d].  stats: NULL or fp32 [n_units][G][4] =
+ *    (m*, Z_E, Z_R (unshifted, after the clamp), sum_{K(q)} w_i).
+ * Requires n_sink + n_tail + n_gen + K > 0.
+ * Workspace: rma_workspace_bytes(RMA_OP_DECODE_MERGE, ...).
+ */
+rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
+                            const rma_span* span, const int32_t* idx, const float* sel_scores,
+                            int32_t K, const void* phi_k, int32_t phi_dtype, int32_t m,
+                            const float* S, const float* u_, uint32_t flags, float* y,
+                            float* stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for `op` (one of RMA_OP_*); 0 on invalid arguments.  G and K
+ * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK. */
+size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* span, int32_t G,
+                           int32_t K, int32_t m);
+
+/* Static text for a status code; never NULL. */
+const char* rma_status_string(int32_t status);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* rma_last_error(void);
+
+/* RMA_ABI_VERSION of the loaded library. */
+int32_t rma_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMA_H_ */

@@ -1,0 +1,295 @@
+// C ABI entry points of librma: argument validation, planning, workspace sizing.
+// Validation runs entirely on the host before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "rma_internal.hpp"
+
+namespace rma {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rma_status fail(rma_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == RMA_F32 || dt == RMA_BF16; }
+size_t dtype_size(int dt) { return dt == RMA_F32 ? 4 : 2; }
+
+#define RMA_CHECK(cond, status, ...)              \
+  do {                                            \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+rma_status check_kv_span(const rma_kv* kv, const rma_span* sp, bool need_v) {
+  RMA_CHECK(kv != nullptr && sp != nullptr, RMA_ERR_INVALID_ARG, "kv or span is NULL");
+  RMA_CHECK(dtype_ok(kv->dtype), RMA_ERR_UNSUPPORTED, "unsupported K/V dtype %d", kv->dtype);
+  RMA_CHECK(kv->d == 64 || kv->d == 128, RMA_ERR_UNSUPPORTED, "head dim %d not in {64,128}", kv->d);
+  RMA_CHECK(kv->n_units >= 1 && kv->n_units <= 65535, RMA_ERR_INVALID_ARG,
+            "n_units must be in [1, 65535]");
+  RMA_CHECK(kv->k != nullptr, RMA_ERR_INVALID_ARG, "kv->k is NULL");
+  RMA_CHECK(!need_v || kv->v != nullptr, RMA_ERR_INVALID_ARG, "kv->v is NULL");
+  RMA_CHECK(aligned16(kv->k) && (!need_v || aligned16(kv->v)), RMA_ERR_INVALID_ARG,
+            "K/V pointers must be 16-byte aligned");
+  RMA_CHECK(kv->unit_stride % 8 == 0, RMA_ERR_INVALID_ARG, "unit_stride must be a multiple of 8");
+  RMA_CHECK(sp->L >= 0 && sp->n_sink >= 0 && sp->n_tail >= 0 && sp->n_gen >= 0,
+            RMA_ERR_INVALID_ARG, "negative span field");
+  RMA_CHECK((int64_t)sp->n_sink + sp->n_tail <= sp->L, RMA_ERR_INVALID_ARG,
+            "n_sink + n_tail (%d + %d) exceeds L (%lld)", sp->n_sink, sp->n_tail,
+            (long long)sp->L);
+  RMA_CHECK(sp->L <= INT32_MAX / 2 && sp->n_gen <= INT32_MAX / 2, RMA_ERR_INVALID_ARG,
+            "L or n_gen too large");
+  RMA_CHECK(kv->t_cap >= sp->L + sp->n_gen, RMA_ERR_INVALID_ARG,
+            "t_cap (%lld) < L + n_gen (%lld)", (long long)kv->t_cap,
+            (long long)(sp->L + sp->n_gen));
+  RMA_CHECK(kv->unit_stride >= kv->t_cap * kv->d, RMA_ERR_INVALID_ARG,
+            "unit_stride < t_cap * d");
+  return RMA_OK;
+}
+
+int64_t l_mid(const rma_span& sp) { return sp.L - sp.n_sink - sp.n_tail; }
+
+}  // namespace
+
+// ------------------------------------------------------------- plans
+BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_phi,
+                     int phi_dtype) {
+  BuildPlan p{};
+  const int64_t Lm = l_mid(sp);
+  const int64_t U = kv.n_units;
+  p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
+  const int tile = p.mfma ? 64 : 32;
+  if (Lm > 0) {
+    int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(2048, U)));
+    int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
+    p.ch = (int)ch;
+    p.n_chunks = (int)ceil_div(Lm, ch);
+  }
+  const int64_t per_unit = (int64_t)m * kv.d + m + 1;
+  p.red_slices = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(512, U), ceil_div(per_unit, 256)));
+  size_t off = counter_bytes(U);
+  const size_t nc = (size_t)std::max(p.n_chunks, 1);
+  p.off_S = off;
+  off = align_up(off + (size_t)U * nc * m * kv.d * 4);
+  p.off_u = off;
+  off = align_up(off + (size_t)U * nc * m * 4);
+  p.off_kap = off;
+  off = align_up(off + (size_t)U * nc * 4);
+  p.total = off;
+  return p;
+}
+
+TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
+  TopkPlan p{};
+  const int64_t Lm = l_mid(sp);
+  const int64_t U = kv.n_units;
+  const int tile = (kv.d == 64) ? 64 : 32;  // tokens per scan block pass
+  const int64_t ch_max = std::max<int64_t>(tile, (kScanScoreSlots / G) / tile * tile);
+  if (Lm > 0) {
+    int64_t lo = ceil_div(Lm, ch_max);
+    int64_t hi = std::min<int64_t>(kSelMaxChunks, ceil_div(Lm, tile));
+    int64_t nc = std::max<int64_t>(lo, std::min<int64_t>(ceil_div(1024, U), hi));
+    int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
+    p.ch = (int)ch;
+    p.n_chunks = (int)ceil_div(Lm, ch);
+    if (K >= Lm) {
+      p.r_min = p.r_cap = p.ch;
+    } else {
+      int64_t rmin = std::max<int64_t>(64, 2 * ceil_div(K, p.n_chunks) + 32);
+      p.r_min = (int)std::min<int64_t>(ch, rmin);
+      p.r_cap = (int)std::min<int64_t>(ch, p.r_min + 128);
+    }
+    p.e_max = (int)std::min<int64_t>(kSelMaxEntries, (int64_t)p.n_chunks * p.r_cap);
+  }
+  size_t off = counter_bytes(U);
+  p.off_ent = off;
+  off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * std::max(p.r_cap, 1) * 8);
+  p.off_meta = off;
+  off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * 8);
+  p.total = off;
+  p.sel_lds = align_up((size_t)p.e_max * 9 + 16, 16);
+  return p;
+}
+
+MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) {
+  (void)m;
+  MergePlan p{};
+  const int64_t U = kv.n_units;
+  const int64_t T = (int64_t)sp.n_sink + sp.n_tail + sp.n_gen + K;
+  int64_t ns = std::max<int64_t>(1, std::min<int64_t>(ceil_div(1024, U), ceil_div(T, 16)));
+  ns = std::max<int64_t>(ns, ceil_div(T, 1024));
+  p.sl = (int)ceil_div(T, ns);
+  p.n_slices = (int)ceil_div(T, p.sl);
+  p.part_floats = 4 + 2 * kv.d;
+  size_t off = counter_bytes(U);
+  p.off_part = off;
+  off = align_up(off + (size_t)U * p.n_slices * G * p.part_floats * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace rma
+
+using namespace rma;
+
+extern "C" {
+
+const char* rma_status_string(int32_t s) {
+  switch (s) {
+    case RMA_OK: return "RMA_OK";
+    case RMA_ERR_INVALID_ARG: return "RMA_ERR_INVALID_ARG";
+    case RMA_ERR_UNSUPPORTED: return "RMA_ERR_UNSUPPORTED";
+    case RMA_ERR_WORKSPACE: return "RMA_ERR_WORKSPACE";
+    case RMA_ERR_HIP: return "RMA_ERR_HIP";
+    default: return "RMA_ERR_UNKNOWN";
+  }
+}
+
+const char* rma_last_error(void) { return g_last_error; }
+
+int32_t rma_abi_version(void) { return RMA_ABI_VERSION; }
+
+size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int32_t G, int32_t K,
+                           int32_t m) {
+  if (kv == nullptr || sp == nullptr || kv->n_units < 1 || (kv->d != 64 && kv->d != 128))
+    return 0;
+  if (sp->L < 0 || sp->n_sink < 0 || sp->n_tail < 0 || (int64_t)sp->n_sink + sp->n_tail > sp->L)
+    return 0;
+  switch (op) {
+    case RMA_OP_BUILD_SUMMARIES:
+      if (m != 64 && m != 128) return 0;
+      // the larger of the two builder layouts (MFMA tiles are coarser)
+      return std::max(plan_build(*kv, *sp, m, true, RMA_BF16).total,
+                      plan_build(*kv, *sp, m, false, RMA_F32).total);
+    case RMA_OP_DECODE_TOPK:
+      if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp)) return 0;
+      return plan_topk(*kv, *sp, G, K).total;
+    case RMA_OP_DECODE_MERGE:
+      if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp)) return 0;
+      return plan_merge(*kv, *sp, G, K, m).total;
+    default:
+      return 0;
+  }
+}
+
+rma_status rma_phi_features(const void* x, int32_t x_dtype, int32_t n_units, int64_t rows,
+                            int64_t x_unit_stride, int32_t d, const float* W, const float* b,
+                            int32_t m, int32_t P, void* phi, int32_t phi_dtype, void* stream) {
+  g_last_error[0] = 0;
+  RMA_CHECK(x && W && b && phi, RMA_ERR_INVALID_ARG, "NULL pointer argument");
+  RMA_CHECK(dtype_ok(x_dtype) && dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported dtype");
+  RMA_CHECK(d == 64 || d == 128, RMA_ERR_UNSUPPORTED, "d %d not in {64,128}", d);
+  RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
+  RMA_CHECK(n_units >= 1 && n_units <= 65535 && rows >= 0 && P >= 1, RMA_ERR_INVALID_ARG,
+            "bad sizes");
+  RMA_CHECK(rows <= INT32_MAX / 2, RMA_ERR_INVALID_ARG, "rows too large");
+  RMA_CHECK(x_unit_stride >= rows * d && x_unit_stride % 8 == 0, RMA_ERR_INVALID_ARG,
+            "x_unit_stride must be >= rows*d and a multiple of 8");
+  RMA_CHECK(aligned16(x) && aligned16(W) && aligned16(b) && aligned16(phi), RMA_ERR_INVALID_ARG,
+            "pointers must be 16-byte aligned");
+  if (rows == 0) return RMA_OK;
+  hipError_t e = launch_phi(x, x_dtype, n_units, rows, x_unit_stride, d, W, b, m, P, phi,
+                            phi_dtype, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float* Wk,
+                               const float* bk, int32_t m, int32_t P, void* phi_k,
+                               int32_t phi_dtype, float* S, float* u, float* kappa,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, true);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
+  RMA_CHECK(dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported phi dtype");
+  RMA_CHECK(P >= 1, RMA_ERR_INVALID_ARG, "n_param_sets must be >= 1");
+  RMA_CHECK(Wk == nullptr || bk != nullptr, RMA_ERR_INVALID_ARG, "bk is NULL");
+  RMA_CHECK(S && u && kappa, RMA_ERR_INVALID_ARG, "NULL output pointer");
+  RMA_CHECK(phi_k != nullptr || l_mid(*sp) == 0, RMA_ERR_INVALID_ARG, "phi_k is NULL");
+  RMA_CHECK(aligned16(S) && aligned16(u) && aligned16(kappa) && aligned16(phi_k) &&
+                aligned16(Wk) && aligned16(bk),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  BuildPlan pl = plan_build(*kv, *sp, m, Wk != nullptr, phi_dtype);
+  RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
+            "workspace is NULL or misaligned");
+  RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
+            workspace_bytes, pl.total);
+  hipError_t e = launch_build(pl, *kv, *sp, Wk, bk, m, P, phi_k, phi_dtype, S, u, kappa,
+                              (uint8_t*)workspace, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rma_span* sp,
+                           const float* kappa, int32_t K, int32_t* idx, float* sel_scores,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, false);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(G >= 1 && G <= 8, RMA_ERR_UNSUPPORTED, "G %d not in 1..8", G);
+  RMA_CHECK(K >= 0 && K <= l_mid(*sp), RMA_ERR_INVALID_ARG, "K %d outside [0, L_mid=%lld]", K,
+            (long long)l_mid(*sp));
+  if (K == 0) return RMA_OK;
+  RMA_CHECK(q && kappa && idx && sel_scores, RMA_ERR_INVALID_ARG, "NULL pointer argument");
+  RMA_CHECK(aligned16(q) && aligned16(kappa) && aligned16(idx) && aligned16(sel_scores),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  TopkPlan pl = plan_topk(*kv, *sp, G, K);
+  RMA_CHECK(pl.n_chunks <= kSelMaxChunks, RMA_ERR_UNSUPPORTED, "mid-region too long for G=%d", G);
+  RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
+            "workspace is NULL or misaligned");
+  RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
+            workspace_bytes, pl.total);
+  hipError_t e = launch_topk(pl, q, G, *kv, *sp, kappa, K, idx, sel_scores, (uint8_t*)workspace,
+                             (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
+                            const rma_span* sp, const int32_t* idx, const float* sel, int32_t K,
+                            const void* phi_k, int32_t phi_dtype, int32_t m, const float* S,
+                            const float* u, uint32_t flags, float* y, float* stats,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, true);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(G >= 1 && G <= 8, RMA_ERR_UNSUPPORTED, "G %d not in 1..8", G);
+  RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
+  RMA_CHECK(dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported phi dtype");
+  RMA_CHECK(flags == RMA_MERGE_SUB || flags == RMA_MERGE_NO_RESIDUAL ||
+                flags == RMA_MERGE_NO_SUBTRACT,
+            RMA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  RMA_CHECK(K >= 0 && K <= l_mid(*sp), RMA_ERR_INVALID_ARG, "K %d outside [0, L_mid]", K);
+  RMA_CHECK((int64_t)sp->n_sink + sp->n_tail + sp->n_gen + K > 0, RMA_ERR_INVALID_ARG,
+            "empty exact support (no anchors, generated or retrieved tokens)");
+  const bool need_res = flags != RMA_MERGE_NO_RESIDUAL;
+  RMA_CHECK(q && y, RMA_ERR_INVALID_ARG, "NULL q or y");
+  RMA_CHECK(K == 0 || (idx && sel), RMA_ERR_INVALID_ARG, "NULL idx or sel_scores");
+  RMA_CHECK(!need_res || (phi_q && S && u), RMA_ERR_INVALID_ARG, "NULL phi_q, S or u");
+  RMA_CHECK(!need_res || K == 0 || phi_k, RMA_ERR_INVALID_ARG, "NULL phi_k");
+  RMA_CHECK(aligned16(q) && aligned16(phi_q) && aligned16(idx) && aligned16(sel) &&
+                aligned16(phi_k) && aligned16(S) && aligned16(u) && aligned16(y) &&
+                aligned16(stats),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  MergePlan pl = plan_merge(*kv, *sp, G, K, m);
+  RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
+            "workspace is NULL or misaligned");
+  RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
+            workspace_bytes, pl.total);
+  hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype, m, S, u,
+                              flags, y, stats, (uint8_t*)workspace, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,437 @@
+// Prefill summary builder and the phi feature kernel ("Residual-Mass Accounting
+// for Partial-KV Decoding": §1 and §4.1, summaries S = sum phi_k(k_i) v_i^T and
+// u = sum phi_k(k_i) over the mid-region; App. C.1 for the positive map).
+//
+// build_mfma  (bf16 K/V, bf16 phi rows, computed phi)  grid (chunks, units),
+//   256 threads, 64-token tiles through LDS:
+//     Z = K_tile W^T        v_mfma_f32_16x16x32_bf16; W is split into bf16
+//                           hi + lo parts (K is exactly bf16), so Z carries
+//                           ~2^-17 relative error instead of bf16's 2^-9
+//     Phi = elu(Z + b) + 1  rounded once to bf16; the rounded rows are both
+//                           stored and summed, so decode subtracts exactly
+//                           what the summaries contain
+//     S += Phi^T V_tile     v_mfma_f32_16x16x32_bf16 with the token index as
+//                           the contraction; A comes straight from the step-1
+//                           accumulators, B is gathered from the V tile in LDS
+//                           with the same token permutation
+//     u += column sums of the rounded Phi;  kappa = max ||k_i||_2 (rounded up)
+// build_valu  (every other dtype combination, or phi given as an input)
+// build_reduce  sums the per-chunk partials in chunk order (deterministic).
+#include "rma_device.hpp"
+#include "rma_internal.hpp"
+
+#include <math.h>
+
+namespace rma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// upper bound of sqrt(x) for a sum of squares computed in fp32 over <= 128 terms
+__device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) * (1.0f + 1e-5f); }
+
+// ====================================================================== MFMA builder
+template <int D, int M>
+__global__ void __launch_bounds__(256)
+build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
+                  int n_sink, int L_mid, int ch, int n_chunks, const float* __restrict__ W,
+                  const float* __restrict__ bias, int P, uint16_t* __restrict__ phik,
+                  float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
+  constexpr int TT = 64;              // tokens per tile
+  constexpr int KS = D / 32;          // k-steps of step 1
+  constexpr int FT = M / 16;          // feature tiles
+  constexpr int FTW = FT / 4;         // feature tiles per wave
+  constexpr int CT = D / 16;          // column tiles of step 2
+  constexpr int KROW = D + 8;         // Ks row stride (bf16 elements): 16 B pad -> 4-bank shift
+  constexpr int VROW = D + 4;         // Vs row stride: 8 B pad -> 2-bank shift
+  constexpr int PROW = M + 8;         // Phi staging row stride
+  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+  constexpr int LCH = TT * CPR / 256; // 16-byte chunks per thread per tile (K or V)
+  static_assert(FTW >= 1, "M >= 64");
+
+  __shared__ __align__(16) uint16_t Ks[TT * KROW];
+  __shared__ __align__(16) uint16_t Vs[TT * VROW];
+  __shared__ __align__(16) uint16_t Ps[TT * PROW];
+  __shared__ float s_b[M];
+  __shared__ float s_kap[4];
+
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int p = u % P;
+  const int t0 = c * ch;
+  const int n = min(ch, L_mid - t0);
+  const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
+  const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
+  uint16_t* php = phik + ((size_t)u * L_mid + t0) * M;
+
+  for (int i = tid; i < M; i += 256) s_b[i] = bias[(size_t)p * M + i];
+
+  // W (fp32) -> bf16 hi + lo B-operands for this wave's feature tiles
+  bf16x8_t Whi[FTW][KS], Wlo[FTW][KS];
+#pragma unroll
+  for (int i = 0; i < FTW; ++i) {
+    const int f = (wave * FTW + i) * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float* wr = W + ((size_t)p * M + f) * D + 32 * ks + 8 * g4;
+      u16x8_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = wr[e];
+        const uint32_t hb = f32_to_bf16_bits(w);
+        hi[e] = (unsigned short)hb;
+        lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
+      }
+      Whi[i][ks] = as_bf16x8(hi);
+      Wlo[i][ks] = as_bf16x8(lo);
+    }
+  }
+
+  f32x4 Sacc[FTW][CT];
+#pragma unroll
+  for (int i = 0; i < FTW; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) Sacc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float uacc[FTW];
+#pragma unroll
+  for (int i = 0; i < FTW; ++i) uacc[i] = 0.f;
+  float kapmax = 0.f;
+
+  // prefetch the first tile
+  uint4 kreg[LCH], vreg[LCH];
+  auto load_tile = [&](int tok0) {
+#pragma unroll
+    for (int j = 0; j < LCH; ++j) {
+      const int chunk = tid + 256 * j;
+      const int row = chunk / CPR, cc = chunk % CPR;
+      if (tok0 + row < n) {
+        kreg[j] = ld_stream16(reinterpret_cast<const uint4*>(kp + (size_t)(tok0 + row) * D) + cc);
+        vreg[j] = ld_stream16(reinterpret_cast<const uint4*>(vp + (size_t)(tok0 + row) * D) + cc);
+      } else {
+        kreg[j] = make_uint4(0, 0, 0, 0);
+        vreg[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_tile(0);
+  __syncthreads();
+
+  for (int tok0 = 0; tok0 < n; tok0 += TT) {
+    // stage the tile
+#pragma unroll
+    for (int j = 0; j < LCH; ++j) {
+      const int chunk = tid + 256 * j;
+      const int row = chunk / CPR, cc = chunk % CPR;
+      *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kreg[j];
+      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8) = make_uint2(vreg[j].x, vreg[j].y);
+      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8 + 4) = make_uint2(vreg[j].z, vreg[j].w);
+    }
+    __syncthreads();
+    if (tok0 + TT < n) load_tile(tok0 + TT);
+
+    // kappa: 4 threads per token row
+    {
+      const int row = tid >> 2, qd = tid & 3;
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 4; e += 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(Ks + row * KROW + qd * (D / 4) + e);
+        const float a = bf16lo(w), b2 = bf16hi(w);
+        ss = __fmaf_rn(a, a, ss);
+        ss = __fmaf_rn(b2, b2, ss);
+      }
+      ss = dpp_add_quad_xor1(ss);
+      ss = dpp_add_quad_xor2(ss);
+      if (tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
+    }
+
+    // step 1: Z = K W^T, epilogue phi, keep bf16 bits as step-2 A operands
+    uint32_t phv[FTW][4][2];  // [feature tile][token tile][packed pair of r]
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      bf16x8_t A[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        A[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Ks + (tt * 16 + l16) * KROW + 32 * ks + 8 * g4));
+#pragma unroll
+      for (int i = 0; i < FTW; ++i) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Whi[i][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Wlo[i][ks], acc, 0, 0, 0);
+        }
+        const int f = (wave * FTW + i) * 16 + l16;
+        const float bf = s_b[f];
+        uint32_t bits[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = tt * 16 + 4 * g4 + r;
+          uint32_t hb = f32_to_bf16_bits(phi_elu1(acc[r] + bf));
+          if (tok0 + row >= n) hb = 0u;  // padding tokens contribute nothing
+          bits[r] = hb;
+          uacc[i] += __uint_as_float(hb << 16);
+          Ps[row * PROW + f] = (uint16_t)hb;
+        }
+        phv[i][tt][0] = bits[0] | (bits[1] << 16);
+        phv[i][tt][1] = bits[2] | (bits[3] << 16);
+      }
+    }
+
+    // step 2: S += Phi^T V, contraction over 32-token blocks.  Hardware k-slot
+    // e of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or 32*kb + 16 + 4*g4
+    // + (e - 4) (e >= 4): exactly where step 1 left the Phi values.
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        u16x8_t bv;
+        const int col = ct * 16 + l16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 32 * kb2 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
+          bv[e] = Vs[tok * VROW + col];
+        }
+        const bf16x8_t Bv = as_bf16x8(bv);
+#pragma unroll
+        for (int i = 0; i < FTW; ++i) {
+          u16x8_t av;
+          const uint32_t w0 = phv[i][2 * kb2][0], w1 = phv[i][2 * kb2][1];
+          const uint32_t w2 = phv[i][2 * kb2 + 1][0], w3 = phv[i][2 * kb2 + 1][1];
+          av[0] = (unsigned short)w0; av[1] = (unsigned short)(w0 >> 16);
+          av[2] = (unsigned short)w1; av[3] = (unsigned short)(w1 >> 16);
+          av[4] = (unsigned short)w2; av[5] = (unsigned short)(w2 >> 16);
+          av[6] = (unsigned short)w3; av[7] = (unsigned short)(w3 >> 16);
+          Sacc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), Bv, Sacc[i][ct], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    // store the Phi tile rows (16-byte pieces, coalesced)
+    constexpr int PCR = M / 8;
+#pragma unroll
+    for (int j = 0; j < TT * PCR / 256; ++j) {
+      const int chunk = tid + 256 * j;
+      const int row = chunk / PCR, cc = chunk % PCR;
+      if (tok0 + row < n)
+        *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) =
+            *reinterpret_cast<const uint4*>(Ps + row * PROW + cc * 8);
+    }
+  }
+
+  // ---- partials of this chunk
+  float* Sp = pS + ((size_t)u * n_chunks + c) * M * D;
+#pragma unroll
+  for (int i = 0; i < FTW; ++i) {
+    const int fb = (wave * FTW + i) * 16;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sp[(size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16] = Sacc[i][ct][r];
+    float us = uacc[i];
+    us += __shfl_xor(us, 16, kWave);
+    us += __shfl_xor(us, 32, kWave);
+    if (g4 == 0) pu[((size_t)u * n_chunks + c) * M + fb + l16] = us;
+  }
+  kapmax = wave_max(kapmax);
+  if (lane == 0) s_kap[wave] = kapmax;
+  __syncthreads();
+  if (tid == 0) pk[(size_t)u * n_chunks + c] = fmaxf(fmaxf(s_kap[0], s_kap[1]), fmaxf(s_kap[2], s_kap[3]));
+}
+
+// ====================================================================== VALU builder
+template <typename KT, typename PT, int D, int M>
+__global__ void __launch_bounds__(256)
+build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int n_sink,
+                  int L_mid, int ch, int n_chunks, const float* __restrict__ W,
+                  const float* __restrict__ bias, int P, PT* __restrict__ phik,
+                  float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
+  constexpr int TT = 32;
+  __shared__ float Kt[TT][D + 1];
+  __shared__ float Vt[TT][D + 1];
+  __shared__ float Pt[TT][129];
+  __shared__ float s_kap[256];
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int p = u % P;
+  const int t0 = c * ch;
+  const int n = min(ch, L_mid - t0);
+  const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
+  const KT* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
+  PT* php = phik + ((size_t)u * L_mid + t0) * M;
+  // thread -> (feature, column range) for S: M*D/256 accumulators
+  constexpr int cols_per = (M * D) / 256;       // 16, 32 or 64
+  const int f_s = tid / (D / cols_per);          // feature of this thread's S slice
+  const int c_s = (tid % (D / cols_per)) * cols_per;
+  float acc[cols_per];
+#pragma unroll
+  for (int i = 0; i < cols_per; ++i) acc[i] = 0.f;
+  float uacc = 0.f, kap = 0.f;
+
+  for (int tok0 = 0; tok0 < n; tok0 += TT) {
+    for (int i = tid; i < TT * D; i += 256) {
+      const int r = i / D, j = i % D;
+      const bool ok = tok0 + r < n;
+      Kt[r][j] = ok ? ld_f32(kp, (size_t)(tok0 + r) * D + j) : 0.f;
+      Vt[r][j] = ok ? ld_f32(vp, (size_t)(tok0 + r) * D + j) : 0.f;
+    }
+    __syncthreads();
+    if (tid < TT && tok0 + tid < n) {
+      float ss = 0.f;
+      for (int j = 0; j < D; ++j) ss = __fmaf_rn(Kt[tid][j], Kt[tid][j], ss);
+      kap = fmaxf(kap, sqrtf(ss) * (1.0f + 1e-5f));
+    }
+    for (int i = tid; i < TT * M; i += 256) {
+      const int r = i / M, f = i % M;
+      float ph = 0.f;
+      if (tok0 + r < n) {
+        if (W != nullptr) {
+          float z = bias[(size_t)p * M + f];
+          const float* wr = W + ((size_t)p * M + f) * D;
+          for (int j = 0; j < D; ++j) z = __fmaf_rn(wr[j], Kt[r][j], z);
+          ph = st_round<PT>(phi_elu1(z));
+          st_elem(php, (size_t)(tok0 + r) * M + f, ph);
+        } else {
+          ph = ld_f32(php, (size_t)(tok0 + r) * M + f);
+        }
+      }
+      Pt[r][f] = ph;
+    }
+    __syncthreads();
+    for (int r = 0; r < TT; ++r) {
+      const float ph = Pt[r][f_s];
+#pragma unroll
+      for (int i = 0; i < cols_per; ++i) acc[i] = __fmaf_rn(ph, Vt[r][c_s + i], acc[i]);
+      if (c_s == 0) uacc += ph;
+    }
+    __syncthreads();
+  }
+  float* Sp = pS + ((size_t)u * n_chunks + c) * M * D;
+#pragma unroll
+  for (int i = 0; i < cols_per; ++i) Sp[(size_t)f_s * D + c_s + i] = acc[i];
+  if (c_s == 0) pu[((size_t)u * n_chunks + c) * M + f_s] = uacc;
+  s_kap[tid] = kap;
+  __syncthreads();
+  if (tid == 0) {
+    float mx = 0.f;
+    for (int i = 0; i < TT; ++i) mx = fmaxf(mx, s_kap[i]);
+    pk[(size_t)u * n_chunks + c] = mx;
+  }
+}
+
+// ====================================================================== reduce
+__global__ void __launch_bounds__(256)
+build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
+                    const float* __restrict__ pk, int n_chunks, int M, int D, int slices,
+                    float* __restrict__ S, float* __restrict__ u_, float* __restrict__ kappa) {
+  const int u = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
+  const int per_unit = M * D + M + 1;
+  const int per_slice = (per_unit + slices - 1) / slices;
+  const int e0 = sl * per_slice, e1 = min(per_unit, e0 + per_slice);
+  for (int e = e0 + tid; e < e1; e += 256) {
+    float v = 0.f;
+    if (e < M * D) {
+      for (int c = 0; c < n_chunks; ++c) v += pS[((size_t)u * n_chunks + c) * M * D + e];
+      S[(size_t)u * M * D + e] = v;
+    } else if (e < M * D + M) {
+      const int f = e - M * D;
+      for (int c = 0; c < n_chunks; ++c) v += pu[((size_t)u * n_chunks + c) * M + f];
+      u_[(size_t)u * M + f] = v;
+    } else {
+      for (int c = 0; c < n_chunks; ++c) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
+      kappa[u] = v;
+    }
+  }
+}
+
+// ====================================================================== phi features
+template <typename XT, typename PT>
+__global__ void __launch_bounds__(256)
+phi_kernel(const XT* __restrict__ x, int64_t xstride, int rows, int D, const float* __restrict__ W,
+           const float* __restrict__ bias, int M, int P, PT* __restrict__ phi) {
+  constexpr int RB = 8;  // rows per block
+  __shared__ float xs[RB][129];
+  const int u = blockIdx.y, r0 = blockIdx.x * RB, tid = threadIdx.x;
+  const int p = u % P;
+  const int nr = min(RB, rows - r0);
+  for (int i = tid; i < nr * D; i += 256) xs[i / D][i % D] = ld_f32(x, (size_t)u * xstride + (size_t)(r0 + i / D) * D + i % D);
+  __syncthreads();
+  for (int i = tid; i < nr * M; i += 256) {
+    const int r = i / M, f = i % M;
+    float z = bias[(size_t)p * M + f];
+    const float* wr = W + ((size_t)p * M + f) * D;
+    for (int j = 0; j < D; ++j) z = __fmaf_rn(wr[j], xs[r][j], z);
+    st_elem(phi, ((size_t)u * rows + r0 + r) * M + f, st_round<PT>(phi_elu1(z)));
+  }
+}
+
+// ====================================================================== launch
+hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, const float* W,
+                        const float* b, int m, int P, void* phi_k, int phi_dtype, float* S,
+                        float* u, float* kappa, uint8_t* ws, hipStream_t st) {
+  const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
+  float* pS = reinterpret_cast<float*>(ws + pl.off_S);
+  float* pu = reinterpret_cast<float*>(ws + pl.off_u);
+  float* pk = reinterpret_cast<float*>(ws + pl.off_kap);
+  if (pl.n_chunks > 0) {
+    const dim3 grid(pl.n_chunks, kv.n_units);
+    if (pl.mfma) {
+      const uint16_t* kk = static_cast<const uint16_t*>(kv.k);
+      const uint16_t* vv = static_cast<const uint16_t*>(kv.v);
+      uint16_t* ph = static_cast<uint16_t*>(phi_k);
+#define RMA_BM(DD, MM)                                                                          \
+  hipLaunchKernelGGL((build_mfma_kernel<DD, MM>), grid, dim3(256), 0, st, kk, vv, kv.unit_stride, \
+                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph, pS, pu, pk)
+      if (kv.d == 64 && m == 64) RMA_BM(64, 64);
+      else if (kv.d == 64) RMA_BM(64, 128);
+      else if (m == 64) RMA_BM(128, 64);
+      else RMA_BM(128, 128);
+#undef RMA_BM
+    } else {
+#define RMA_BV1(KT, PT, DD, MM)                                                                   \
+  hipLaunchKernelGGL((build_valu_kernel<KT, PT, DD, MM>), grid, dim3(256), 0, st,                  \
+                     static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,   \
+                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, static_cast<PT*>(phi_k), pS, \
+                     pu, pk)
+#define RMA_BV(KT, PT)                                                 \
+  do {                                                                 \
+    if (kv.d == 64 && m == 64) RMA_BV1(KT, PT, 64, 64);                \
+    else if (kv.d == 64) RMA_BV1(KT, PT, 64, 128);                     \
+    else if (m == 64) RMA_BV1(KT, PT, 128, 64);                        \
+    else RMA_BV1(KT, PT, 128, 128);                                    \
+  } while (0)
+      if (kv.dtype == RMA_BF16) {
+        if (phi_dtype == RMA_BF16) RMA_BV(uint16_t, uint16_t); else RMA_BV(uint16_t, float);
+      } else {
+        if (phi_dtype == RMA_BF16) RMA_BV(float, uint16_t); else RMA_BV(float, float);
+      }
+#undef RMA_BV1
+#undef RMA_BV
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(build_reduce_kernel, dim3(pl.red_slices, kv.n_units), dim3(256), 0, st, pS, pu,
+                     pk, pl.n_chunks, m, kv.d, pl.red_slices, S, u, kappa);
+  return hipGetLastError();
+}
+
+hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride, int d,
+                      const float* W, const float* b, int m, int P, void* phi, int phi_dtype,
+                      hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(rows, 8), n_units);
+#define RMA_PHI(XT, PT)                                                                          \
+  hipLaunchKernelGGL((phi_kernel<XT, PT>), grid, dim3(256), 0, st, static_cast<const XT*>(x),   \
+                     xstride, (int)rows, d, W, b, m, P, static_cast<PT*>(phi))
+  if (x_dtype == RMA_F32) {
+    if (phi_dtype == RMA_F32) RMA_PHI(float, float); else RMA_PHI(float, uint16_t);
+  } else {
+    if (phi_dtype == RMA_F32) RMA_PHI(uint16_t, float); else RMA_PHI(uint16_t, uint16_t);
+  }
+#undef RMA_PHI
+  return hipGetLastError();
+}
+
+}  // namespace rma

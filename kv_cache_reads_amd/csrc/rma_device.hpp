@@ -1,0 +1,210 @@
+// Device helpers shared by the librma kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rma {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float round_bf16(float x) {
+  return __uint_as_float(f32_to_bf16_bits(x) << 16);
+}
+
+// Load `n` consecutive elements (16-byte aligned) of a K/V row as fp32.
+template <typename T, int N>
+__device__ __forceinline__ void load_row_f32(const T* p, float (&out)[N]);
+
+template <int N>
+__device__ __forceinline__ void load_row_f32(const uint16_t* p, float (&out)[N]) {
+  static_assert(N % 8 == 0, "bf16 rows load in 16-byte pieces");
+  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    uint4 w = p4[i];
+    out[8 * i + 0] = bf16lo(w.x); out[8 * i + 1] = bf16hi(w.x);
+    out[8 * i + 2] = bf16lo(w.y); out[8 * i + 3] = bf16hi(w.y);
+    out[8 * i + 4] = bf16lo(w.z); out[8 * i + 5] = bf16hi(w.z);
+    out[8 * i + 6] = bf16lo(w.w); out[8 * i + 7] = bf16hi(w.w);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_row_f32(const float* p, float (&out)[N]) {
+  static_assert(N % 4 == 0, "fp32 rows load in 16-byte pieces");
+  const float4* p4 = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    float4 w = p4[i];
+    out[4 * i + 0] = w.x; out[4 * i + 1] = w.y; out[4 * i + 2] = w.z; out[4 * i + 3] = w.w;
+  }
+}
+
+// Streaming 16-byte load (nontemporal hint: read-once data).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Raw 16-byte pieces of a row (for double buffering of loads).
+template <typename T> struct RowPieces;
+template <> struct RowPieces<uint16_t> { static constexpr int kElemsPerPiece = 8; };
+template <> struct RowPieces<float> { static constexpr int kElemsPerPiece = 4; };
+
+__device__ __forceinline__ void unpack_piece(const uint4& w, const uint16_t*, float* out) {
+  out[0] = bf16lo(w.x); out[1] = bf16hi(w.x); out[2] = bf16lo(w.y); out[3] = bf16hi(w.y);
+  out[4] = bf16lo(w.z); out[5] = bf16hi(w.z); out[6] = bf16lo(w.w); out[7] = bf16hi(w.w);
+}
+__device__ __forceinline__ void unpack_piece(const uint4& w, const float*, float* out) {
+  out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
+  out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
+}
+
+// ---------------------------------------------------------------- DPP sums
+// Butterfly sums inside groups of 2/4/8/16 lanes with DPP row permutations.
+// After lane_group_sum<N>, every lane of an aligned N-lane group holds the sum.
+__device__ __forceinline__ float dpp_add_quad_xor1(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_add_quad_xor2(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_add_half_mirror(float v) {  // lane i <-> 7-i within 8
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_add_row_mirror(float v) {  // lane i <-> 15-i within 16
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) v = dpp_add_quad_xor1(v);
+  if constexpr (N >= 4) v = dpp_add_quad_xor2(v);
+  if constexpr (N >= 8) v = dpp_add_half_mirror(v);
+  if constexpr (N >= 16) v = dpp_add_row_mirror(v);
+  return v;
+}
+
+// Full-wave reductions (ds_swizzle/bpermute based; used off the hot loops).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum over the wave (lane 0 first).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- keys
+// Monotone map fp32 -> uint32 (a < b  =>  key(a) <= key(b); -0 < +0).
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t ord_f64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// ---------------------------------------------------------------- exact-ish dot
+// Double-double dot product of an fp32 query with a stored key row.  Every
+// product q_j*k_j is exact in fp64 (24x8 or 24x24 significand bits); TwoSum
+// keeps the rounding error of each addition, so (hi, lo) carries the sum with
+// error of order d * 2^-106 * sum|q_j k_j|.  Distinct exact scores further apart
+// than that are ordered correctly; identical keys give bitwise identical pairs.
+struct DD { double hi, lo; };
+
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+template <typename T, int D>
+__device__ DD dd_dot(const float* q, const T* krow) {
+  double s = 0.0, c = 0.0;
+#pragma unroll 4
+  for (int j0 = 0; j0 < D; j0 += 8) {
+    float kv[8];
+    if constexpr (sizeof(T) == 2) {
+      uint4 w = *reinterpret_cast<const uint4*>(krow + j0);
+      unpack_piece(w, (const uint16_t*)nullptr, kv);
+    } else {
+      float4 a = *reinterpret_cast<const float4*>(krow + j0);
+      float4 b = *reinterpret_cast<const float4*>(krow + j0 + 4);
+      kv[0] = a.x; kv[1] = a.y; kv[2] = a.z; kv[3] = a.w;
+      kv[4] = b.x; kv[5] = b.y; kv[6] = b.z; kv[7] = b.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double p = (double)q[j0 + e] * (double)kv[e];
+      double t, err;
+      two_sum(s, p, t, err);
+      s = t;
+      c += err;
+    }
+  }
+  DD r;
+  two_sum(s, c, r.hi, r.lo);
+  if (r.hi == 0.0) r.hi = 0.0;  // canonical +0
+  if (r.lo == 0.0) r.lo = 0.0;
+  return r;
+}
+
+// a > b in the (exact score desc, position asc) order
+__device__ __forceinline__ bool dd_key_greater(DD a, int ia, DD b, int ib) {
+  if (a.hi != b.hi) return a.hi > b.hi;
+  if (a.lo != b.lo) return a.lo > b.lo;
+  return ia < ib;
+}
+
+// Scalar element access for fp32 or bf16 storage.
+__device__ __forceinline__ float ld_f32(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f32(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+template <typename T> __device__ __forceinline__ float st_round(float x);
+template <> __device__ __forceinline__ float st_round<float>(float x) { return x; }
+template <> __device__ __forceinline__ float st_round<uint16_t>(float x) { return round_bf16(x); }
+__device__ __forceinline__ void st_elem(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_elem(uint16_t* p, size_t i, float v) {
+  p[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// ---------------------------------------------------------------- misc
+__device__ __forceinline__ float phi_elu1(float z) { return z > 0.f ? z + 1.f : __expf(z); }
+
+}  // namespace rma

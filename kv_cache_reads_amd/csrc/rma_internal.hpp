@@ -1,0 +1,73 @@
+// Host-side planning shared by the C ABI entry points and the kernel launchers.
+// A plan fixes the tiling of one call; the workspace size and every launch are
+// derived from the same plan, so they cannot disagree.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rma.h"
+
+namespace rma {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Completion counters (one uint32 per unit) lead every workspace.
+inline size_t counter_bytes(int64_t n_units) { return align_up((size_t)n_units * 4, 4096); }
+
+// ------------------------------------------------------------- build
+struct BuildPlan {
+  bool mfma;         // bf16 K/V, bf16 phi, computed phi -> MFMA builder
+  int n_chunks;      // token chunks per unit
+  int ch;            // tokens per chunk (multiple of the tile)
+  int red_slices;    // reduce kernel: blocks per unit
+  size_t off_S, off_u, off_kap, total;
+};
+BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_phi, int phi_dtype);
+
+// ------------------------------------------------------------- top-k
+constexpr int kScanThreads = 256;
+constexpr int kScanBins = 512;          // linear score bins per head in the scan
+constexpr int kScanScoreSlots = 8192;   // fp32 LDS score slots per scan block (G * ch <= this)
+constexpr int kSelMaxChunks = 256;
+constexpr int kSelBandMax = 512;        // band members resolved in LDS
+constexpr int kSelMaxEntries = 11264;   // union entries held in LDS by a select block
+
+struct TopkPlan {
+  int n_chunks, ch, r_min, r_cap;
+  int e_max;                 // entries the select block can hold
+  size_t off_ent, off_meta, total;
+  size_t sel_lds;            // dynamic LDS bytes of the select kernel
+};
+TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K);
+
+// ------------------------------------------------------------- merge
+struct MergePlan {
+  int n_slices, sl;          // slices of the per-head entry list, entries per slice
+  int part_floats;           // floats per (slice, head) partial
+  size_t off_part, total;
+};
+MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t x_unit_stride,
+                      int d, const float* W, const float* b, int m, int P, void* phi,
+                      int phi_dtype, hipStream_t st);
+
+hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, const float* W,
+                        const float* b, int m, int P, void* phi_k, int phi_dtype, float* S,
+                        float* u, float* kappa, uint8_t* ws, hipStream_t st);
+
+hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
+                       const rma_span& sp, const float* kappa, int K, int32_t* idx,
+                       float* sel_scores, uint8_t* ws, hipStream_t st);
+
+hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,
+                        const rma_kv& kv, const rma_span& sp, const int32_t* idx,
+                        const float* sel, int K, const void* phi_k, int phi_dtype, int m,
+                        const float* S, const float* u, uint32_t flags, float* y, float* stats,
+                        uint8_t* ws, hipStream_t st);
+
+}  // namespace rma

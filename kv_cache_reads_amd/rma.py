@@ -1,0 +1,236 @@
+"""ctypes binding of librma.so (include/rma.h).
+
+Argument marshalling only: every step of the method runs in the library's HIP
+kernels.  Tensors must live on the current HIP device; work is enqueued on
+torch's current stream.  The functions keep the C names; output tensors are
+allocated with torch when not supplied.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librma.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "rma.h")
+
+RMA_OK, RMA_ERR_INVALID_ARG, RMA_ERR_UNSUPPORTED, RMA_ERR_WORKSPACE, RMA_ERR_HIP = 0, -1, -2, -3, -4
+RMA_F32, RMA_BF16 = 0, 1
+RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE = 1, 2, 3
+RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
+
+
+class RmaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("n_units", ctypes.c_int32), ("t_cap", ctypes.c_int64),
+                ("unit_stride", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class _Span(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int64), ("n_sink", ctypes.c_int32), ("n_tail", ctypes.c_int32),
+                ("n_gen", ctypes.c_int64)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Span:
+    """Prefill length, anchors and generated tokens (identical for all units)."""
+    L: int
+    n_sink: int
+    n_tail: int
+    n_gen: int = 0
+
+    @property
+    def L_mid(self) -> int:
+        return self.L - self.n_sink - self.n_tail
+
+    def _c(self) -> _Span:
+        return _Span(self.L, self.n_sink, self.n_tail, self.n_gen)
+
+
+_lib = None
+_VP, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
+
+
+def lib():
+    """Load librma.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_reads_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    P_KV, P_SP = ctypes.POINTER(_KV), ctypes.POINTER(_Span)
+    L.rma_phi_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP]
+    L.rma_build_summaries.argtypes = [P_KV, P_SP, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_merge.argtypes = [_VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP,
+                                   _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_workspace_bytes.argtypes = [_I32, P_KV, P_SP, _I32, _I32, _I32]
+    L.rma_workspace_bytes.restype = _SZ
+    L.rma_status_string.argtypes = [_I32]
+    L.rma_status_string.restype = ctypes.c_char_p
+    L.rma_last_error.argtypes = []
+    L.rma_last_error.restype = ctypes.c_char_p
+    L.rma_abi_version.restype = _I32
+    for f in ("rma_phi_features", "rma_build_summaries", "rma_decode_topk", "rma_decode_merge"):
+        getattr(L, f).restype = _I32
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions include/rma.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(rma_\w+)\s*\(", text, flags=re.M)))
+
+
+def _check(status: int):
+    if status != RMA_OK:
+        L = lib()
+        raise RmaError(status, f"{L.rma_status_string(status).decode()}: {L.rma_last_error().decode()}")
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return RMA_F32
+    if t == torch.bfloat16:
+        return RMA_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _kv(k: torch.Tensor, v: Optional[torch.Tensor]) -> _KV:
+    assert k.dim() == 3 and k.stride(2) == 1 and k.stride(1) == k.shape[2], "K must be [U, T, d] with dense rows"
+    if v is not None:
+        assert v.shape == k.shape and v.stride() == k.stride() and v.dtype == k.dtype
+    return _KV(k.data_ptr(), 0 if v is None else v.data_ptr(), _dt(k.dtype), k.shape[0], k.shape[1],
+               k.stride(0), k.shape[2], 0)
+
+
+class Workspace:
+    """A zero-initialised device buffer reused across calls on one stream (the
+    library leaves its counters zeroed after every call)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8,
+                                   device=self.device or torch.device("cuda"))
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _ws(ws: Optional[Workspace], nbytes: int) -> torch.Tensor:
+    if ws is None:
+        dev = torch.cuda.current_device()
+        ws = _default_ws.setdefault(dev, Workspace(torch.device("cuda", dev)))
+    return ws.get(nbytes)
+
+
+def rma_workspace_bytes(op: int, k: torch.Tensor, span: Span, G: int = 1, K: int = 0, m: int = 128) -> int:
+    kv = _kv(k, None)
+    sp = span._c()
+    return int(lib().rma_workspace_bytes(op, ctypes.byref(kv), ctypes.byref(sp), G, K, m))
+
+
+def rma_phi_features(x: torch.Tensor, W: torch.Tensor, b: torch.Tensor,
+                     phi_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+    """phi[u, r] = elu(W[u % P] x[u, r] + b[u % P]) + 1;  x: [U, rows, d]."""
+    U, rows, d = x.shape
+    P, m, _ = W.shape
+    if out is None:
+        out = torch.empty(U, rows, m, dtype=phi_dtype, device=x.device)
+    assert x.stride(2) == 1 and x.stride(1) == d
+    _check(lib().rma_phi_features(_p(x), _dt(x.dtype), U, rows, x.stride(0), d, _p(W), _p(b), m, P,
+                                  _p(out), _dt(out.dtype), _stream()))
+    return out
+
+
+def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Optional[torch.Tensor],
+                        bk: Optional[torch.Tensor], m: Optional[int] = None,
+                        phi_k: Optional[torch.Tensor] = None, phi_dtype: torch.dtype = torch.bfloat16,
+                        n_param_sets: Optional[int] = None, ws: Optional[Workspace] = None):
+    """Returns (phi_k [U, L_mid, m], S [U, m, d], u [U, m], kappa [U])."""
+    U, _, d = k.shape
+    if m is None:
+        m = Wk.shape[1] if Wk is not None else phi_k.shape[2]
+    P = n_param_sets or (Wk.shape[0] if Wk is not None else 1)
+    if phi_k is None:
+        assert Wk is not None, "phi_k must be given when Wk is None"
+        phi_k = torch.empty(U, span.L_mid, m, dtype=phi_dtype, device=k.device)
+    S = torch.empty(U, m, d, dtype=torch.float32, device=k.device)
+    u = torch.empty(U, m, dtype=torch.float32, device=k.device)
+    kappa = torch.empty(U, dtype=torch.float32, device=k.device)
+    kv, sp = _kv(k, v), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ctypes.byref(kv), ctypes.byref(sp), 1, 0, m))
+    w = _ws(ws, nb)
+    _check(lib().rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), _p(Wk), _p(bk), m, P, _p(phi_k),
+                                     _dt(phi_k.dtype), _p(S), _p(u), _p(kappa), _p(w), w.numel(), _stream()))
+    return phi_k, S, u, kappa
+
+
+def rma_decode_topk(q: torch.Tensor, k: torch.Tensor, span: Span, kappa: torch.Tensor, K: int,
+                    ws: Optional[Workspace] = None, idx: Optional[torch.Tensor] = None,
+                    sel_scores: Optional[torch.Tensor] = None):
+    """q: [U, G, d] fp32.  Returns (idx [U, G, K] int32 ascending, sel_scores [U, G, K])."""
+    U, G, d = q.shape
+    if idx is None:
+        idx = torch.empty(U, G, K, dtype=torch.int32, device=q.device)
+    if sel_scores is None:
+        sel_scores = torch.empty(U, G, K, dtype=torch.float32, device=q.device)
+    kv, sp = _kv(k, None), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(sp), G, K, 0))
+    w = _ws(ws, nb)
+    _check(lib().rma_decode_topk(_p(q), G, ctypes.byref(kv), ctypes.byref(sp), _p(kappa), K, _p(idx),
+                                 _p(sel_scores), _p(w), w.numel(), _stream()))
+    return idx, sel_scores
+
+
+def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                     span: Span, idx: Optional[torch.Tensor], sel_scores: Optional[torch.Tensor], K: int,
+                     phi_k: Optional[torch.Tensor], S: Optional[torch.Tensor], u: Optional[torch.Tensor],
+                     flags: int = RMA_MERGE_SUB, m: Optional[int] = None, want_stats: bool = False,
+                     ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None):
+    """Returns y [U, G, d] (and stats [U, G, 4] = (m*, Z_E, Z_R, retrieved phi mass))."""
+    U, G, d = q.shape
+    if m is None:
+        m = S.shape[1] if S is not None else 128
+    if y is None:
+        y = torch.empty(U, G, d, dtype=torch.float32, device=q.device)
+    stats = torch.empty(U, G, 4, dtype=torch.float32, device=q.device) if want_stats else None
+    kv, sp = _kv(k, v), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE_MERGE, ctypes.byref(kv), ctypes.byref(sp), G, K, m))
+    w = _ws(ws, nb)
+    pdt = _dt(phi_k.dtype) if phi_k is not None else RMA_BF16
+    _check(lib().rma_decode_merge(_p(q), _p(phi_q), G, ctypes.byref(kv), ctypes.byref(sp), _p(idx),
+                                  _p(sel_scores), K, _p(phi_k), pdt, m, _p(S), _p(u), flags, _p(y),
+                                  _p(stats), _p(w), w.numel(), _stream()))
+    return (y, stats) if want_stats else y
+
+
+def rma_abi_version() -> int:
+    return int(lib().rma_abi_version())

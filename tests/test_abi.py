@@ -1,0 +1,101 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function that
+include/rma.h declares, and rejects bad arguments on the host before any HIP
+call (so these calls never touch a device)."""
+import ctypes
+
+import pytest
+
+from kv_cache_reads_amd import rma as R
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(R.LIB_PATH),
+                                reason="librma.so not built")
+
+
+def test_exports_every_declared_symbol():
+    names = R.header_functions()
+    assert set(names) >= {"rma_phi_features", "rma_build_summaries", "rma_decode_topk",
+                          "rma_decode_merge", "rma_workspace_bytes", "rma_status_string",
+                          "rma_last_error", "rma_abi_version"}
+    L = R.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.rma_abi_version() == 1
+    assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
+    assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
+
+
+def _kv(d=64, U=2, T=1024, dtype=R.RMA_BF16, ptr=0x10000):
+    return R._KV(ptr, ptr + 0x100000, dtype, U, T, T * d, d, 0)
+
+
+def _sp(L=1024, ns=4, nt=32, ng=0):
+    return R._Span(L, ns, nt, ng)
+
+
+def _topk(kv, sp, G=2, K=10, q=0x2000, kappa=0x3000, idx=0x4000, sel=0x5000, ws=0x6000, wsb=1 << 30):
+    return R.lib().rma_decode_topk(q, G, ctypes.byref(kv), ctypes.byref(sp), kappa, K, idx, sel, ws, wsb, None)
+
+
+def test_topk_validation_errors():
+    L = R.lib()
+    assert _topk(_kv(), _sp(), K=2000) == R.RMA_ERR_INVALID_ARG            # K > L_mid
+    assert b"K 2000" in L.rma_last_error()
+    assert _topk(_kv(), _sp(ns=600, nt=600)) == R.RMA_ERR_INVALID_ARG      # anchors exceed L
+    assert _topk(_kv(d=96), _sp()) == R.RMA_ERR_UNSUPPORTED                # head dim
+    assert _topk(_kv(), _sp(), G=9) == R.RMA_ERR_UNSUPPORTED               # group size
+    assert _topk(_kv(dtype=5), _sp()) == R.RMA_ERR_UNSUPPORTED             # dtype
+    assert _topk(_kv(), _sp(), q=0) == R.RMA_ERR_INVALID_ARG               # null q
+    assert _topk(_kv(), _sp(), idx=0x4004) == R.RMA_ERR_INVALID_ARG        # misaligned
+    assert _topk(_kv(ptr=0x10008), _sp()) == R.RMA_ERR_INVALID_ARG         # misaligned K
+    assert _topk(_kv(T=1000), _sp(L=1024)) == R.RMA_ERR_INVALID_ARG        # t_cap < L
+    assert _topk(_kv(), _sp(ng=5)) == R.RMA_ERR_INVALID_ARG                # t_cap < L + n_gen
+    assert _topk(_kv(), _sp(), ws=0) == R.RMA_ERR_WORKSPACE
+    assert _topk(_kv(), _sp(), wsb=16) == R.RMA_ERR_WORKSPACE
+    assert _topk(_kv(), _sp(), K=0) == R.RMA_OK                            # nothing to do, nothing launched
+
+
+def test_build_and_merge_validation_errors():
+    L = R.lib()
+    kv, sp = _kv(), _sp()
+    P = ctypes.c_void_p
+    st = L.rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), 0x1000, 0x1100, 96, 1, 0x2000,
+                               R.RMA_BF16, 0x3000, 0x4000, 0x5000, 0x6000, 1 << 30, None)
+    assert st == R.RMA_ERR_UNSUPPORTED                                     # m
+    st = L.rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), 0x1000, 0, 128, 1, 0x2000,
+                               R.RMA_BF16, 0x3000, 0x4000, 0x5000, 0x6000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG                                     # bk NULL
+    st = L.rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), 0x1000, 0x1100, 128, 1, 0x2000,
+                               R.RMA_BF16, 0x3000, 0x4000, 0x5000, 0x6000, 8, None)
+    assert st == R.RMA_ERR_WORKSPACE
+    # merge: empty exact support, unknown flags, NULL phi_q with residual
+    sp0 = _sp(L=1024, ns=0, nt=0)
+    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kv), ctypes.byref(sp0), 0x2000, 0x2100, 0,
+                            0x3000, R.RMA_BF16, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG
+    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+                            0x3000, R.RMA_BF16, 128, 0x4000, 0x5000, 7, 0x6000, None, 0x7000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG
+    st = L.rma_decode_merge(0x1000, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+                            0x3000, R.RMA_BF16, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG
+    st = L.rma_phi_features(0x1000, R.RMA_F32, 1, 4, 4 * 64, 64, 0x2000, 0x3000, 100, 1, 0x4000,
+                            R.RMA_F32, None)
+    assert st == R.RMA_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_are_monotone_in_K_and_units():
+    L = R.lib()
+    sp = _sp(L=32768, ns=4, nt=64)
+    sizes = []
+    for U in (1, 8, 64):
+        kv = _kv(U=U, T=32768)
+        s = [L.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(sp), 4, K, 0)
+             for K in (1, 328, 3000)]
+        assert all(x > 0 for x in s) and s == sorted(s)
+        sizes.append(s[1])
+        assert L.rma_workspace_bytes(R.RMA_OP_BUILD_SUMMARIES, ctypes.byref(kv), ctypes.byref(sp), 1, 0, 128) > 0
+        assert L.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, ctypes.byref(kv), ctypes.byref(sp), 4, 328, 128) > 0
+    assert sizes == sorted(sizes)
+    kv = _kv()
+    assert L.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(_sp()), 2, 5000, 0) == 0
+    assert L.rma_workspace_bytes(99, ctypes.byref(kv), ctypes.byref(_sp()), 2, 10, 128) == 0

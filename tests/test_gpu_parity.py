@@ -1,0 +1,259 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Top-K indices must match bit for bit; outputs within 2e-3 abs / 1e-2 rel.
+Inputs are seeded synthetic workloads (kv_cache_reads_amd.workload).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity_util import (R, W, check_prefill, check_summaries, check_y, hip_decode, hip_prefill,
+                         host_unit, log, oracle_decode, oracle_prefill, prefill_span, decode_span)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SMALL = {
+    "c0": W.CONFIGS["c0"],
+    # ragged mid-regions (not a multiple of any tile), several units and heads
+    "c1_small": W.CONFIGS["c1"].with_(L=4096 + 37, K=(41,)),
+    "c2_small": W.CONFIGS["c2"].with_(L=6000 + 3, K=(29, 59, 118, 236)),
+    "c3_small": W.CONFIGS["c3"].with_(batch=2, layers=2, L=3000, K=(29,), steps=3),
+    "c4_small": W.CONFIGS["c4"].with_(batch=1, layers=2, L=5003, K=(50,), steps=2),
+}
+
+
+def _gen(cfg):
+    torch.manual_seed(0)
+    return W.generate(cfg, device=DEV)
+
+
+def _run_case(cfg, units, Ks=None, steps=None, check_pre=True):
+    inp = _gen(cfg)
+    pre = hip_prefill(inp)
+    torch.cuda.synchronize()
+    steps = range(cfg.steps) if steps is None else steps
+    Ks = cfg.K if Ks is None else Ks
+    gpu = {}
+    for K in Ks:
+        for st in steps:
+            out = hip_decode(inp, pre, K, st)
+            gpu[(K, st)] = {k: v.cpu() for k, v in out.items()}
+    torch.cuda.synchronize()
+    worst = (0.0, 0.0)
+    for u in units:
+        hu = host_unit(inp, u)
+        ref_pre = oracle_prefill(cfg, hu)
+        if check_pre:
+            check_prefill(cfg, pre, u, ref_pre)
+            _, M, _ = O.partition(cfg.L, cfg.n_sink, cfg.n_tail)
+            check_summaries(cfg, pre, u, ref_pre, hu["v"][M])
+        for (K, st), out in gpu.items():
+            for g in range(cfg.G):
+                y_ref, idx_ref, _ = oracle_decode(cfg, hu, ref_pre, K, st, g)
+                idx = out["idx"][u, g].numpy().astype(np.int64)
+                assert np.array_equal(idx, idx_ref), f"{cfg.name} unit {u} head {g} K={K} step {st}: top-K differs"
+                a, r = check_y(out["y"][u, g].numpy(), y_ref, f"{cfg.name} u{u} g{g} K{K} s{st}")
+                worst = (max(worst[0], a), max(worst[1], r))
+    log(f"{cfg.name}: units {len(list(units))} worst abs {worst[0]:.2e} rel {worst[1]:.2e}")
+    return inp, pre
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs_match_oracle(name):
+    cfg = SMALL[name]
+    log(f"case {name}: {cfg}")
+    _run_case(cfg, range(cfg.U))
+
+
+def test_c0_exact_ties_and_outputs():
+    cfg = W.CONFIGS["c0"]
+    inp, pre = _run_case(cfg, [0])
+    # the three planted keys (identical vectors) are all retrieved by head 0
+    out = hip_decode(inp, pre, cfg.K[0], 0)
+    sel = set(out["idx"][0, 0].cpu().tolist())
+    assert set(inp.needle_pos[0]) <= sel
+
+
+def test_c1_full():
+    cfg = W.CONFIGS["c1"]
+    _run_case(cfg, range(cfg.U))
+
+
+def test_c2_full_budget_sweep():
+    cfg = W.CONFIGS["c2"]
+    _run_case(cfg, range(cfg.U))
+
+
+def test_c3_full_sampled_units():
+    cfg = W.CONFIGS["c3"]
+    # units spread over requests, layers and kv heads
+    units = [0, 7, 129, 517, 1030, 1555, 2047]
+    _run_case(cfg, units, check_pre=True)
+
+
+@pytest.mark.slow
+def test_c4_full_sampled_units():
+    cfg = W.CONFIGS["c4"]
+    units = [0, 9, 230, 455, 895]   # both entropy regimes (even / odd layers)
+    _run_case(cfg, units, steps=[0, 7], check_pre=True)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+def _manual_unit(L=2048, ns=4, nt=32, d=64, G=2, seed=0, ngen=0, kv_dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    T = L + ngen
+    k = torch.randn(1, T, d, generator=g).to(kv_dtype)
+    v = torch.randn(1, T, d, generator=g).to(kv_dtype)
+    q = (1.5 * torch.randn(1, G, d, generator=g)).float()
+    return k, v, q
+
+
+def test_ideal_factorisation_recovers_full_attention():
+    # keys from a 64-word codebook, phi_k = onehot(code), phi_q_c = e^{q.c/sqrt d}
+    L, ns, nt, d, m, G = 3000, 4, 32, 64, 64, 2
+    gen = torch.Generator().manual_seed(5)
+    book = (0.5 * torch.randn(m, d, generator=gen)).bfloat16().float()
+    codes = torch.randint(0, m, (L,), generator=gen)
+    k = book[codes][None].bfloat16()
+    v = torch.randn(1, L, d, generator=gen).bfloat16()
+    q = torch.randn(1, G, d, generator=gen).float()
+    M = torch.arange(ns, L - nt)
+    phi_k = torch.nn.functional.one_hot(codes[M], m).bfloat16()[None]
+    f = torch.exp(q.double() @ book.double().T / math.sqrt(d)).float()          # [1, G, m]
+    span = R.Span(L, ns, nt, 0)
+    kd, vd = k.to(DEV), v.to(DEV)
+    phi_d, S, u, kappa = R.rma_build_summaries(kd, vd, span, None, None, m=m, phi_k=phi_k.to(DEV))
+    kf, vf = k[0].double().numpy(), v[0].double().numpy()
+    for K in (0, 1, 77, 1500, L - ns - nt - 1, L - ns - nt):
+        idx, sel = (R.rma_decode_topk(q.to(DEV), kd, span, kappa, K) if K > 0 else (None, None))
+        y = R.rma_decode_merge(q.to(DEV), f.to(DEV), kd, vd, span, idx, sel, K, phi_d, S, u).cpu()
+        for g in range(G):
+            y_full = O.full_attention(q[0, g].numpy(), kf, vf, L)
+            check_y(y[0, g].numpy(), y_full, f"codebook K={K} g={g}")
+
+
+def test_zero_features_give_selection_only_topk():
+    k, v, q = _manual_unit(L=4000, G=3, ngen=2)
+    cfgW = torch.randn(1, 128, 64) / 8
+    cfgb = torch.randn(1, 128) / 8
+    L, ns, nt, K = 4000, 4, 32, 40
+    kd, vd = k.to(DEV), v.to(DEV)
+    pre = R.rma_build_summaries(kd, vd, R.Span(L, ns, nt, 0), cfgW.to(DEV), cfgb.to(DEV))
+    sp = R.Span(L, ns, nt, 2)
+    idx, sel = R.rma_decode_topk(q.to(DEV), kd, sp, pre[3], K)
+    zero = torch.zeros(1, 3, 128, device=DEV)
+    y0 = R.rma_decode_merge(q.to(DEV), zero, kd, vd, sp, idx, sel, K, pre[0], pre[1], pre[2]).cpu()
+    y1 = R.rma_decode_merge(q.to(DEV), None, kd, vd, sp, idx, sel, K, None, None, None,
+                            flags=R.RMA_MERGE_NO_RESIDUAL, m=128).cpu()
+    kf, vf = k[0].double().numpy(), v[0].double().numpy()
+    for g in range(3):
+        sel_ref = O.topk_indices(q[0, g].numpy(), kf[ns:L - nt], K, first_index=ns)
+        assert np.array_equal(idx[0, g].cpu().numpy(), sel_ref)
+        E = np.concatenate([np.arange(ns), sel_ref, np.arange(L - nt, L), [L, L + 1]])
+        s = kf[E] @ q[0, g].double().numpy() / 8.0
+        p = np.exp(s - s.max())
+        y_ref = (p @ vf[E]) / p.sum()
+        check_y(y0[0, g].numpy(), y_ref, "f=0")
+        check_y(y1[0, g].numpy(), y_ref, "NO_RESIDUAL")
+
+
+def test_merge_variants_match_oracle():
+    cfg = SMALL["c1_small"]
+    inp = _gen(cfg)
+    pre = hip_prefill(inp)
+    K = cfg.K[0]
+    for flags, variant in ((R.RMA_MERGE_NO_RESIDUAL, "topk"), (R.RMA_MERGE_NO_SUBTRACT, "nosub")):
+        out = hip_decode(inp, pre, K, 0, flags=flags)
+        for u in (0, cfg.U - 1):
+            hu = host_unit(inp, u)
+            rp = oracle_prefill(cfg, hu)
+            for g in range(cfg.G):
+                y_ref, _, _ = oracle_decode(cfg, hu, rp, K, 0, g, variant=variant)
+                check_y(out["y"][u, g].cpu().numpy(), y_ref, f"{variant} u{u} g{g}")
+
+
+def test_determinism_and_gqa_equivalence():
+    cfg = SMALL["c1_small"]
+    inp = _gen(cfg)
+    pre = hip_prefill(inp)
+    pre2 = hip_prefill(inp)
+    for a, b in zip(pre, pre2):
+        assert torch.equal(a, b)
+    K = cfg.K[0]
+    o1 = hip_decode(inp, pre, K, 0)
+    o2 = hip_decode(inp, pre, K, 0)
+    for key in ("idx", "sel", "y"):
+        assert torch.equal(o1[key], o2[key]), key
+    # each query head alone (G = 1, the kv head replicated per query head)
+    U, G = cfg.U, cfg.G
+    q = inp.q[0]                                      # [U, G, d]
+    k1 = inp.k.repeat_interleave(G, dim=0)
+    v1 = inp.v.repeat_interleave(G, dim=0)
+    sp = R.Span(cfg.L, cfg.n_sink, cfg.n_tail, 0)
+    kap1 = pre[3].repeat_interleave(G)
+    idx1, sel1 = R.rma_decode_topk(q.reshape(U * G, 1, -1).contiguous(), k1, sp, kap1, K)
+    assert torch.equal(idx1.view(U, G, K), o1["idx"])
+
+
+# ------------------------------------------------------------------ adversarial selection
+def _topk_case(k, q, L, ns, nt, K):
+    kd = k.to(DEV)
+    v = torch.zeros_like(k)
+    pre = R.rma_build_summaries(kd, v.to(DEV), R.Span(L, ns, nt, 0), torch.randn(1, 64, 64, device=DEV) / 8,
+                                torch.zeros(1, 64, device=DEV))
+    idx, sel = R.rma_decode_topk(q.to(DEV), kd, R.Span(L, ns, nt, 0), pre[3], K)
+    kf = k[0].float().double().numpy()
+    for g in range(q.shape[1]):
+        ref = O.topk_indices(q[0, g].numpy(), kf[ns:L - nt], K, first_index=ns)
+        got = idx[0, g].cpu().numpy()
+        assert np.array_equal(got, ref), f"K={K} head {g}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
+        # selected scores are the fp32 scores of the selected tokens
+        s_ref = kf[got] @ q[0, g].double().numpy() / 8.0
+        assert np.allclose(sel[0, g].cpu().numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
+    return idx
+
+
+@pytest.mark.parametrize("K", [1, 7, 300, 1999, 2000 - 36 - 1, 2000 - 36])
+def test_topk_all_equal_keys(K):
+    L, ns, nt = 2000, 4, 32
+    k = torch.ones(1, L, 64).bfloat16()
+    q = torch.randn(1, 2, 64)
+    if K <= L - ns - nt:
+        _topk_case(k, q, L, ns, nt, K)
+
+
+def test_topk_planted_ties_and_near_ties_at_the_boundary():
+    L, ns, nt, K = 6000, 4, 64, 50
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn(1, L, 64, generator=g)
+    q = torch.randn(1, 4, 64, generator=g)
+    qh = q[0, 0] / q[0, 0].norm()
+    # 60 copies of one key straddle the K-th boundary (exact ties -> lower index)
+    pos = torch.randperm(L - ns - nt, generator=g)[:60] + ns
+    k[0, pos] = (3.0 * qh).bfloat16().float()
+    # near-ties: keys one bf16 ulp apart in one component
+    base = (2.5 * qh).bfloat16()
+    pos2 = torch.randperm(L - ns - nt, generator=g)[:40] + ns
+    for i, p in enumerate(pos2.tolist()):
+        kk = base.clone()
+        bits = kk.view(torch.int16)
+        bits[i % 64] += (i % 3) - 1
+        k[0, p] = kk.float()
+    _topk_case(k.bfloat16(), q, L, ns, nt, K)
+    _topk_case(k.bfloat16(), q, L, ns, nt, 75)
+
+
+def test_topk_sorted_keys_force_fallback():
+    # scores increase with position: every chunk holds only top tokens at its end;
+    # the per-chunk reports cannot certify completeness and the exact path runs
+    L, ns, nt = 3000, 4, 32
+    q = torch.zeros(1, 1, 64)
+    q[0, 0, 0] = 1.0
+    k = torch.zeros(1, L, 64)
+    k[0, :, 0] = torch.linspace(-2, 2, L)
+    _topk_case(k.bfloat16(), q, L, ns, nt, 500)
+    _topk_case(k.bfloat16(), q, L, ns, nt, 5)
