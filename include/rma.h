@@ -41,10 +41,11 @@
  *    nothing is launched and the outputs are untouched.  rma_last_error()
  *    gives a message for the calling thread's last failed call.
  *  - Workspace: calls that need scratch take (workspace, workspace_bytes);
- *    rma_workspace_bytes() gives the size.  The first 4096 bytes of a
- *    workspace hold completion counters that must be zero before the first
- *    use (e.g. allocate it zero-filled); every call leaves them zero again.
- *    Calls that may run concurrently need distinct workspaces.
+ *    rma_workspace_bytes() gives the size.  The first RMA_WORKSPACE_COUNTER_BYTES
+ *    bytes of every workspace hold completion counters that must be zero
+ *    before the first use (e.g. allocate it zero-filled); every call leaves
+ *    them zero again, so one workspace can serve any sequence of calls on one
+ *    stream.  Calls that may run concurrently need distinct workspaces.
  *  - NaN/Inf inputs are not checked; outputs are then unspecified (no fault).
  */
 #ifndef RMA_H_
@@ -58,6 +59,9 @@ extern "C" {
 #endif
 
 #define RMA_ABI_VERSION 1
+
+/* Leading bytes of every workspace that hold completion counters. */
+#define RMA_WORKSPACE_COUNTER_BYTES 262144
 
 typedef enum {
   RMA_OK = 0,

@@ -9,6 +9,7 @@
 #include "rma_internal.hpp"
 
 namespace rma {
+static_assert(kCounterBytes == RMA_WORKSPACE_COUNTER_BYTES, "counter region size");
 namespace {
 
 thread_local char g_last_error[512] = "";

@@ -14,8 +14,11 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Completion counters (one uint32 per unit) lead every workspace.
-inline size_t counter_bytes(int64_t n_units) { return align_up((size_t)n_units * 4, 4096); }
+// Completion counters (one uint32 per unit, up to the 65535-unit limit) lead
+// every workspace at a fixed size, so that scratch written by one call never
+// lands on counters another call (with a different unit count) relies on.
+constexpr size_t kCounterBytes = 65536 * 4;
+inline size_t counter_bytes(int64_t /*n_units*/) { return kCounterBytes; }
 
 // ------------------------------------------------------------- build
 struct BuildPlan {

@@ -23,6 +23,7 @@ RMA_OK, RMA_ERR_INVALID_ARG, RMA_ERR_UNSUPPORTED, RMA_ERR_WORKSPACE, RMA_ERR_HIP
 RMA_F32, RMA_BF16 = 0, 1
 RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE = 1, 2, 3
 RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
+RMA_WORKSPACE_COUNTER_BYTES = 262144
 
 
 class RmaError(RuntimeError):
@@ -173,8 +174,10 @@ def rma_phi_features(x: torch.Tensor, W: torch.Tensor, b: torch.Tensor,
 def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Optional[torch.Tensor],
                         bk: Optional[torch.Tensor], m: Optional[int] = None,
                         phi_k: Optional[torch.Tensor] = None, phi_dtype: torch.dtype = torch.bfloat16,
-                        n_param_sets: Optional[int] = None, ws: Optional[Workspace] = None):
-    """Returns (phi_k [U, L_mid, m], S [U, m, d], u [U, m], kappa [U])."""
+                        n_param_sets: Optional[int] = None, ws: Optional[Workspace] = None,
+                        out: Optional[tuple] = None):
+    """Returns (phi_k [U, L_mid, m], S [U, m, d], u [U, m], kappa [U]).  `out` may
+    supply preallocated (S, u, kappa)."""
     U, _, d = k.shape
     if m is None:
         m = Wk.shape[1] if Wk is not None else phi_k.shape[2]
@@ -182,9 +185,12 @@ def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Option
     if phi_k is None:
         assert Wk is not None, "phi_k must be given when Wk is None"
         phi_k = torch.empty(U, span.L_mid, m, dtype=phi_dtype, device=k.device)
-    S = torch.empty(U, m, d, dtype=torch.float32, device=k.device)
-    u = torch.empty(U, m, dtype=torch.float32, device=k.device)
-    kappa = torch.empty(U, dtype=torch.float32, device=k.device)
+    if out is not None:
+        S, u, kappa = out
+    else:
+        S = torch.empty(U, m, d, dtype=torch.float32, device=k.device)
+        u = torch.empty(U, m, dtype=torch.float32, device=k.device)
+        kappa = torch.empty(U, dtype=torch.float32, device=k.device)
     kv, sp = _kv(k, v), span._c()
     nb = int(lib().rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ctypes.byref(kv), ctypes.byref(sp), 1, 0, m))
     w = _ws(ws, nb)

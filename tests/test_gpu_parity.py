@@ -199,6 +199,25 @@ def test_determinism_and_gqa_equivalence():
     assert torch.equal(idx1.view(U, G, K), o1["idx"])
 
 
+def test_workspace_reuse_across_unit_counts():
+    # scratch beyond the counter region holds garbage from earlier calls; the
+    # counters of every unit (here > 1024 units) must still be clean
+    cfg = W.CONFIGS["c3"].with_(batch=9, layers=16, L=600, K=(6,), steps=1)   # 1152 units
+    inp = _gen(cfg)
+    ws = R.Workspace()
+    buf = ws.get(64 << 20)
+    buf[R.RMA_WORKSPACE_COUNTER_BYTES:] = 255
+    pre = hip_prefill(inp, ws=ws)
+    out = hip_decode(inp, pre, cfg.K[0], 0, ws=ws)
+    for u in (0, 1030, cfg.U - 1):
+        hu = host_unit(inp, u)
+        rp = oracle_prefill(cfg, hu)
+        for g in range(cfg.G):
+            y_ref, idx_ref, _ = oracle_decode(cfg, hu, rp, cfg.K[0], 0, g)
+            assert np.array_equal(out["idx"][u, g].cpu().numpy(), idx_ref)
+            check_y(out["y"][u, g].cpu().numpy(), y_ref, f"ws reuse u{u} g{g}")
+
+
 # ------------------------------------------------------------------ adversarial selection
 def _topk_case(k, q, L, ns, nt, K):
     kd = k.to(DEV)
