@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the Top-K+phi residual-mass-accounting path on one MI355X.
+
+One step = one pass of the whole path over one batch of the workload:
+prefill summaries (phi_k rows, S, u; rma_build_summaries), then for every
+decode step of the workload phi_q (rma_phi_features), the exhaustive Top-K
+(rma_decode_topk) and the exact branch + subtraction + residual + single
+normalisation (rma_decode_merge).  Default workload: the 1B-shaped GQA layer at
+32K context with a 1 % budget (8 kv heads x 4 query heads, d=64, K=328).
+
+Inputs are resident in HBM before timing starts.  Steps rotate over copies of
+the inputs whose total exceeds 1 GB so that no step is served from the 256 MB
+last-level cache.  Each step is replayed from a HIP graph (compared against an
+eager run first).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config c1]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+METRIC = "decode queries/s + achieved HBM GB/s (% peak), 1B-shape GQA, 32K ctx, 1% budget"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--K", type=int, default=None, help="override the retrieved-token count")
+    ap.add_argument("--rotate-bytes", type=float, default=1.2e9)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ byte model
+def call_bytes(cfg, K, n_gen):
+    """Algorithmic HBM bytes of each call for one batch (inputs read once,
+    outputs written once; workspace scratch excluded)."""
+    U, G, d, m, P = cfg.U, cfg.G, cfg.d, cfg.m, cfg.P
+    Lm, na = cfg.L_mid, cfg.n_anchor
+    e = 4 if cfg.kv_dtype == "f32" else 2
+    ep = 4 if cfg.phi_dtype == "f32" else 2
+    params = P * (m * d * 4 + m * 4)
+    build = U * (2 * Lm * d * e + Lm * m * ep + m * d * 4 + m * 4 + 4) + params
+    phi = U * G * (d * 4 + m * 4) + params
+    topk = U * (Lm * d * e + 4) + U * G * (d * 4 + K * 8)
+    merge = U * G * (K * (d * e + m * ep + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4) \
+        + U * (m * d * 4 + m * 4)
+    return dict(build=build, phi=phi, topk=topk, merge=merge)
+
+
+# ------------------------------------------------------------------ runner
+class PathRunner:
+    """Prepared C-ABI calls for one copy of the inputs (no per-call allocation)."""
+
+    def __init__(self, R, cfg, inp, K, ws, torch):
+        self.R, self.cfg, self.K, self.t = R, cfg, K, torch
+        L = R.lib()
+        self.L = L
+        dev = inp.k.device
+        U, G, d, m = cfg.U, cfg.G, cfg.d, cfg.m
+        self.k, self.v, self.q, self.W, self.b = inp.k, inp.v, inp.q, inp.W, inp.b
+        self.phi_k = torch.empty(U, cfg.L_mid, m, dtype=cfg.torch_phi_dtype(), device=dev)
+        self.S = torch.empty(U, m, d, dtype=torch.float32, device=dev)
+        self.u = torch.empty(U, m, dtype=torch.float32, device=dev)
+        self.kappa = torch.empty(U, dtype=torch.float32, device=dev)
+        self.f = torch.empty(cfg.steps, U, G, m, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(cfg.steps, U, G, max(K, 1), dtype=torch.int32, device=dev)
+        self.sel = torch.empty(cfg.steps, U, G, max(K, 1), dtype=torch.float32, device=dev)
+        self.y = torch.empty(cfg.steps, U, G, d, dtype=torch.float32, device=dev)
+        self.kv = R._kv(inp.k, inp.v)
+        self.sp_pre = R.Span(cfg.L, cfg.n_sink, cfg.n_tail, 0)._c()
+        self.sp_dec = [R.Span(cfg.L, cfg.n_sink, cfg.n_tail, cfg.n_gen(s))._c() for s in range(cfg.steps)]
+        self.ws = ws
+        P = ctypes.c_void_p
+        self.p = lambda t: P(t.data_ptr())
+        self.kdt = R._dt(inp.k.dtype)
+        self.pdt = R._dt(self.phi_k.dtype)
+
+    def build(self, st):
+        cfg, p = self.cfg, self.p
+        r = self.L.rma_build_summaries(ctypes.byref(self.kv), ctypes.byref(self.sp_pre), p(self.W), p(self.b),
+                                       cfg.m, cfg.P, p(self.phi_k), self.pdt, p(self.S), p(self.u),
+                                       p(self.kappa), p(self.ws), self.ws.numel(), st)
+        assert r == 0, r
+
+    def phi(self, s, st):
+        cfg, p = self.cfg, self.p
+        q = self.q[s]
+        r = self.L.rma_phi_features(p(q), 0, cfg.U, cfg.G, q.stride(0), cfg.d, p(self.W), p(self.b), cfg.m,
+                                    cfg.P, p(self.f[s]), 0, st)
+        assert r == 0, r
+
+    def topk(self, s, st):
+        cfg, p = self.cfg, self.p
+        r = self.L.rma_decode_topk(p(self.q[s]), cfg.G, ctypes.byref(self.kv), ctypes.byref(self.sp_dec[s]),
+                                   p(self.kappa), self.K, p(self.idx[s]), p(self.sel[s]), p(self.ws),
+                                   self.ws.numel(), st)
+        assert r == 0, r
+
+    def merge(self, s, st):
+        cfg, p = self.cfg, self.p
+        r = self.L.rma_decode_merge(p(self.q[s]), p(self.f[s]), cfg.G, ctypes.byref(self.kv),
+                                    ctypes.byref(self.sp_dec[s]), p(self.idx[s]), p(self.sel[s]), self.K,
+                                    p(self.phi_k), self.pdt, cfg.m, p(self.S), p(self.u), 0, p(self.y[s]),
+                                    None, p(self.ws), self.ws.numel(), st)
+        assert r == 0, r
+
+    def step(self, st, ev=None):
+        """The whole path; `ev` = list of events recorded between the calls."""
+        t = self.t
+        if ev is not None:
+            ev[0].record()
+        self.build(st)
+        if ev is not None:
+            ev[1].record()
+        for s in range(self.cfg.steps):
+            self.phi(s, st)
+            if ev is not None and s == 0:
+                ev[2].record()
+            self.topk(s, st)
+            if ev is not None and s == 0:
+                ev[3].record()
+            self.merge(s, st)
+            if ev is not None and s == 0:
+                ev[4].record()
+
+
+def cpu_baseline(cfg, inp, K, seconds):
+    """The oracle (numpy fp64) on host cores: prefill + decode of whole units."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import oracle as O
+    ncpu = len(os.sched_getaffinity(0))
+
+    def host(u):
+        p = u % cfg.P
+        return dict(k=inp.k[u].float().cpu().numpy().astype(np.float64),
+                    v=inp.v[u].float().cpu().numpy().astype(np.float64),
+                    q=inp.q[:, u].cpu().numpy(), W=inp.W[p].cpu().numpy(), b=inp.b[p].cpu().numpy())
+
+    _, M, _ = O.partition(cfg.L, cfg.n_sink, cfg.n_tail)
+    with threadpool_limits(limits=ncpu):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        nq, units, dt = 0, 0, 0.0
+        done = False
+        while not done:
+            for uidx in range(cfg.U):
+                hu = host(uidx)                      # host copy, not timed
+                t1 = time.perf_counter()
+                P, S, uu = O.prefill_unit(hu["k"][M], hu["v"][M], hu["W"], hu["b"])
+                for s in range(cfg.steps):
+                    for g in range(cfg.G):
+                        q = hu["q"][s, g]
+                        f = O.phi_features(q[None], hu["W"], hu["b"])[0]
+                        O.decode_query(q, f, hu["k"], hu["v"], P, S, uu, cfg.L, cfg.n_sink, cfg.n_tail,
+                                       cfg.n_gen(s), K)
+                        nq += 1
+                dt += time.perf_counter() - t1
+                units += 1
+                if dt >= seconds:
+                    done = True
+                    break
+    return dict(value=nq / dt, unit="queries/s", cores=int(threads), kind="oracle",
+                sample=f"{units} units of the same workload (prefill summaries + all {cfg.steps} decode "
+                       f"step(s) x {cfg.G} query heads per unit), {dt:.1f} s, numpy fp64 with "
+                       f"{threads} BLAS threads on {ncpu} visible cores")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: --gpus must be 1 "
+                                   "(the units of a batch shard across GPUs with no communication)"}))
+        sys.exit(2)
+    import torch
+    from kv_cache_reads_amd import rma as R
+    from kv_cache_reads_amd import workload as Wl
+
+    torch.cuda.set_device(0)
+    cfg = Wl.CONFIGS[args.config]
+    K = args.K if args.K is not None else cfg.K[0]
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] workload {cfg.name}: {cfg.desc}; K={K}")
+    t0 = time.time()
+    inp = Wl.generate(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+
+    per_copy = (inp.k.numel() + inp.v.numel()) * inp.k.element_size() + \
+        cfg.U * cfg.L_mid * cfg.m * (4 if cfg.phi_dtype == "f32" else 2)
+    n_copies = max(1, math.ceil(args.rotate_bytes / per_copy))
+    free = torch.cuda.mem_get_info()[0]
+    n_copies = max(1, min(n_copies, int(0.6 * free // max(per_copy, 1))))
+    copies = [inp]
+    for _ in range(n_copies - 1):
+        copies.append(Wl.Inputs(cfg, inp.k.clone(), inp.v.clone(), inp.q.clone(), inp.W.clone(),
+                                inp.b.clone(), inp.needle_pos))
+    sp = R.Span(cfg.L, cfg.n_sink, cfg.n_tail, cfg.n_gen(cfg.steps - 1))
+    wsb = max(R.rma_workspace_bytes(R.RMA_OP_BUILD_SUMMARIES, inp.k, sp, 1, 0, cfg.m),
+              R.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, inp.k, sp, cfg.G, K, cfg.m),
+              R.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, inp.k, sp, cfg.G, K, cfg.m))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    runners = [PathRunner(R, cfg, c, K, ws, torch) for c in copies]
+    log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
+
+    stream = torch.cuda.Stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    # eager reference outputs (copy 0) for the graph check
+    with torch.cuda.stream(stream):
+        runners[0].step(st)
+    stream.synchronize()
+    y_eager = runners[0].y.clone()
+    idx_eager = runners[0].idx.clone()
+
+    graphs = None
+    if not args.eager:
+        try:
+            graphs = []
+            for r in runners:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    r.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                graphs.append(g)
+            # replay checks against the eager result, with eager work in between
+            for rep in range(3):
+                runners[0].y.zero_()
+                graphs[0].replay()
+                torch.cuda.synchronize()
+                assert torch.equal(runners[0].y, y_eager) and torch.equal(runners[0].idx, idx_eager), \
+                    "graph replay differs from eager"
+                with torch.cuda.stream(stream):
+                    runners[0].step(st)
+                stream.synchronize()
+            log("[bench] HIP graph replays match the eager run")
+        except Exception as ex:  # fall back to eager launches
+            log(f"[bench] graph capture unavailable ({ex}); timing eager launches")
+            graphs = None
+
+    def run_step(i):
+        if graphs is not None:
+            graphs[i % n_copies].replay()
+        else:
+            runners[i % n_copies].step(st)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run_step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record()
+        for i in range(args.steps):
+            run_step(args.warmup + i)
+        e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    queries = cfg.U * cfg.G * cfg.steps
+    value = queries / (ms_per_step / 1e3)
+
+    # ---- per-call durations: events between the calls, eager launches queued ahead
+    n_t = int(max(5, min(200, args.steps, 2.0 / max(ms_per_step / 1e3, 1e-6))))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_t)]
+    with torch.cuda.stream(stream):
+        for i in range(n_t):
+            runners[i % n_copies].step(st, evs[i])
+    torch.cuda.synchronize()
+    names = ["build", "phi", "topk", "merge"]
+    dur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / n_t for j, n in enumerate(names)}
+    nb = call_bytes(cfg, K, cfg.n_gen(0))
+    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s))[c] for s in range(cfg.steps)
+                                   for c in ("phi", "topk", "merge"))
+    kernels = {"build": "build_mfma_kernel + build_reduce_kernel (rma_build_summaries)",
+               "phi": "phi_kernel (rma_phi_features)",
+               "topk": "topk_scan_kernel + topk_select_kernel (rma_decode_topk)",
+               "merge": "merge_kernel (rma_decode_merge)"}
+    dom = max(names, key=lambda n: dur[n])
+    achieved = nb[dom] / (dur[dom] / 1e3) / 1e9
+    gbs = {n: nb[n] / (dur[n] / 1e3) / 1e9 for n in names}
+    for n in names:
+        log(f"[bench] {n:6s} {dur[n] * 1e3:9.2f} us  {nb[n] / 1e6:8.2f} MB  {gbs[n]:8.1f} GB/s")
+    log(f"[bench] step {ms_per_step * 1e3:.2f} us, {step_bytes / 1e6:.1f} MB algorithmic "
+        f"-> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; {value / 1e6:.3f} M queries/s")
+    decode_us = sum(dur[n] for n in ("phi", "topk", "merge")) * 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.desc}",
+            "units": cfg.U, "query_heads_per_unit": cfg.G, "head_dim": cfg.d, "context": cfg.L,
+            "anchors": [cfg.n_sink, cfg.n_tail], "K": K, "phi_features": cfg.m,
+            "decode_steps": cfg.steps, "queries_per_step": queries,
+            "step": "prefill summaries + phi_q + top-K + merge",
+            "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
+            "rotating_copies": n_copies, "launch": "hip_graph" if graphs is not None else "eager",
+            "step_algorithmic_MB": round(step_bytes / 1e6, 3),
+            "step_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "per_call_us": {n: round(dur[n] * 1e3, 2) for n in names},
+            "per_call_GBps": {n: round(gbs[n], 1) for n in names},
+            "decode_only_queries_per_s": round(cfg.U * cfg.G / (decode_us / 1e6), 1),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": kernels[dom],
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(dur[dom] * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, K, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "rma_internal.hpp"
 
@@ -68,9 +69,10 @@ BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_
   const int64_t Lm = l_mid(sp);
   const int64_t U = kv.n_units;
   p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
-  const int tile = p.mfma ? 64 : 32;
+  const int tile = (p.mfma && kv.d == 64) ? 64 : 32;
   if (Lm > 0) {
-    int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(2048, U)));
+    // enough blocks to cover the chip (~2 per CU) with as few per-chunk partials as possible
+    int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(512, U)));
     int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);
@@ -98,16 +100,20 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   if (Lm > 0) {
     int64_t lo = ceil_div(Lm, ch_max);
     int64_t hi = std::min<int64_t>(kSelMaxChunks, ceil_div(Lm, tile));
-    int64_t nc = std::max<int64_t>(lo, std::min<int64_t>(ceil_div(1024, U), hi));
+    int64_t nc = std::max<int64_t>(lo, std::min<int64_t>(ceil_div(512, U), hi));
     int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);
     if (K >= Lm) {
       p.r_min = p.r_cap = p.ch;
     } else {
-      int64_t rmin = std::max<int64_t>(64, 2 * ceil_div(K, p.n_chunks) + 32);
+      // a chunk holds ~Binomial(ch, K/L_mid) of the K winners (mean mu); reporting
+      // mu + 5 sqrt(mu) + 8 makes an incomplete report (-> exact fallback) rare
+      const double mu = (double)K / p.n_chunks;
+      int64_t rmin = (int64_t)std::ceil(mu + 5.0 * std::sqrt(mu) + 8.0);
+      rmin = std::max<int64_t>(16, (rmin + 7) / 8 * 8);
       p.r_min = (int)std::min<int64_t>(ch, rmin);
-      p.r_cap = (int)std::min<int64_t>(ch, p.r_min + 128);
+      p.r_cap = (int)std::min<int64_t>(ch, 2 * p.r_min + 32);
     }
     p.e_max = (int)std::min<int64_t>(kSelMaxEntries, (int64_t)p.n_chunks * p.r_cap);
   }
@@ -116,8 +122,10 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * std::max(p.r_cap, 1) * 8);
   p.off_meta = off;
   off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * 8);
+  p.off_hp = off;
+  off = align_up(off + (size_t)U * G * 16);
   p.total = off;
-  p.sel_lds = align_up((size_t)p.e_max * 9 + 16, 16);
+  p.sel_lds = align_up((size_t)p.e_max * 8 + 16, 16);
   return p;
 }
 
@@ -126,15 +134,13 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) 
   MergePlan p{};
   const int64_t U = kv.n_units;
   const int64_t T = (int64_t)sp.n_sink + sp.n_tail + sp.n_gen + K;
-  int64_t ns = std::max<int64_t>(1, std::min<int64_t>(ceil_div(1024, U), ceil_div(T, 16)));
-  ns = std::max<int64_t>(ns, ceil_div(T, 1024));
-  p.sl = (int)ceil_div(T, ns);
-  p.n_slices = (int)ceil_div(T, p.sl);
-  p.part_floats = 4 + 2 * kv.d;
-  size_t off = counter_bytes(U);
-  p.off_part = off;
-  off = align_up(off + (size_t)U * p.n_slices * G * p.part_floats * 4);
-  p.total = off;
+  (void)G;
+  // one block per (unit, head): no scratch beyond the (unused) counter region
+  p.sl = (int)T;
+  p.n_slices = 1;
+  p.part_floats = 0;
+  p.off_part = counter_bytes(U);
+  p.total = counter_bytes(U);
   return p;
 }
 

@@ -34,23 +34,32 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_
 __device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) * (1.0f + 1e-5f); }
 
 // ====================================================================== MFMA builder
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 template <int D, int M>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * M <= 64 * 128 ? 2 : 1)))
 build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
                   int n_sink, int L_mid, int ch, int n_chunks, const float* __restrict__ W,
                   const float* __restrict__ bias, int P, uint16_t* __restrict__ phik,
                   float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
-  constexpr int TT = 64;              // tokens per tile
-  constexpr int KS = D / 32;          // k-steps of step 1
-  constexpr int FT = M / 16;          // feature tiles
-  constexpr int FTW = FT / 4;         // feature tiles per wave
-  constexpr int CT = D / 16;          // column tiles of step 2
-  constexpr int KROW = D + 8;         // Ks row stride (bf16 elements): 16 B pad -> 4-bank shift
-  constexpr int VROW = D + 4;         // Vs row stride: 8 B pad -> 2-bank shift
-  constexpr int PROW = M + 8;         // Phi staging row stride
-  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int LCH = TT * CPR / 256; // 16-byte chunks per thread per tile (K or V)
-  static_assert(FTW >= 1, "M >= 64");
+  constexpr int TT = D == 64 ? 64 : 32;  // tokens per tile
+  constexpr int NTT = TT / 16;            // 16-token MFMA tiles per tile
+  constexpr int KB = TT / 32;             // 32-token contraction blocks per tile
+  constexpr int KS = D / 32;              // k-steps of step 1
+  constexpr int FT = M / 16;              // feature tiles
+  constexpr int FTW = FT / 4;             // feature tiles per wave
+  constexpr int CT = D / 16;              // column tiles of step 2
+  constexpr int KROW = D + 8;             // Ks row stride (bf16 elements): 16 B pad -> 4-bank shift
+  constexpr int VROW = D + 4;             // Vs row stride: 8 B pad -> 2-bank shift
+  constexpr int PROW = M + 8;             // Phi staging row stride
+  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int LCH = TT * CPR / 256;     // 16-byte chunks per thread per tile (K or V)
+  static_assert(FTW >= 1 && LCH >= 1, "tile shape");
 
   __shared__ __align__(16) uint16_t Ks[TT * KROW];
   __shared__ __align__(16) uint16_t Vs[TT * VROW];
@@ -89,69 +98,64 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       Wlo[i][ks] = as_bf16x8(lo);
     }
   }
-
-  f32x4 Sacc[FTW][CT];
+  u16x8_t ones_v;
 #pragma unroll
-  for (int i = 0; i < FTW; ++i)
+  for (int e = 0; e < 8; ++e) ones_v[e] = 0x3F80;  // bf16 1.0: u = Phi^T 1 on the MFMA
+  const bf16x8_t Bones = as_bf16x8(ones_v);
+
+  f32x4 Sacc[FTW][CT], Uacc[FTW];
+#pragma unroll
+  for (int i = 0; i < FTW; ++i) {
+    Uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) Sacc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float uacc[FTW];
-#pragma unroll
-  for (int i = 0; i < FTW; ++i) uacc[i] = 0.f;
+  }
   float kapmax = 0.f;
 
-  // prefetch the first tile
-  uint4 kreg[LCH], vreg[LCH];
-  auto load_tile = [&](int tok0) {
+  auto load_tile = [&](uint4 (&kr)[LCH], uint4 (&vr)[LCH], int tok0) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + 256 * j;
       const int row = chunk / CPR, cc = chunk % CPR;
       if (tok0 + row < n) {
-        kreg[j] = ld_stream16(reinterpret_cast<const uint4*>(kp + (size_t)(tok0 + row) * D) + cc);
-        vreg[j] = ld_stream16(reinterpret_cast<const uint4*>(vp + (size_t)(tok0 + row) * D) + cc);
+        kr[j] = ld_stream16(reinterpret_cast<const uint4*>(kp + (size_t)(tok0 + row) * D) + cc);
+        vr[j] = ld_stream16(reinterpret_cast<const uint4*>(vp + (size_t)(tok0 + row) * D) + cc);
       } else {
-        kreg[j] = make_uint4(0, 0, 0, 0);
-        vreg[j] = make_uint4(0, 0, 0, 0);
+        kr[j] = make_uint4(0, 0, 0, 0);
+        vr[j] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  load_tile(0);
-  __syncthreads();
-
-  for (int tok0 = 0; tok0 < n; tok0 += TT) {
-    // stage the tile
+  auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH]) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + 256 * j;
       const int row = chunk / CPR, cc = chunk % CPR;
-      *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kreg[j];
-      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8) = make_uint2(vreg[j].x, vreg[j].y);
-      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8 + 4) = make_uint2(vreg[j].z, vreg[j].w);
+      *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kr[j];
+      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8) = make_uint2(vr[j].x, vr[j].y);
+      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8 + 4) = make_uint2(vr[j].z, vr[j].w);
     }
-    __syncthreads();
-    if (tok0 + TT < n) load_tile(tok0 + TT);
-
-    // kappa: 4 threads per token row
+  };
+  auto compute_tile = [&](int tok0) {
+    // kappa: 256/TT threads per token row
     {
-      const int row = tid >> 2, qd = tid & 3;
+      constexpr int TPR = 256 / TT, EPT = D / TPR;
+      const int row = tid / TPR, qd = tid % TPR;
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 4; e += 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(Ks + row * KROW + qd * (D / 4) + e);
+      for (int e = 0; e < EPT; e += 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(Ks + row * KROW + qd * EPT + e);
         const float a = bf16lo(w), b2 = bf16hi(w);
         ss = __fmaf_rn(a, a, ss);
         ss = __fmaf_rn(b2, b2, ss);
       }
-      ss = dpp_add_quad_xor1(ss);
-      ss = dpp_add_quad_xor2(ss);
+      ss = lane_group_sum<TPR>(ss);
       if (tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
     }
-
-    // step 1: Z = K W^T, epilogue phi, keep bf16 bits as step-2 A operands
-    uint32_t phv[FTW][4][2];  // [feature tile][token tile][packed pair of r]
+    // step 1: Z = K W^T, epilogue phi, keep bf16 pairs as step-2 A operands
+    uint32_t phv[FTW][NTT][2];  // [feature tile][token tile][packed (r0,r1), (r2,r3)]
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
       bf16x8_t A[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -166,26 +170,40 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         }
         const int f = (wave * FTW + i) * 16 + l16;
         const float bf = s_b[f];
-        uint32_t bits[4];
+        float ph[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = tt * 16 + 4 * g4 + r;
-          uint32_t hb = f32_to_bf16_bits(phi_elu1(acc[r] + bf));
-          if (tok0 + row >= n) hb = 0u;  // padding tokens contribute nothing
-          bits[r] = hb;
-          uacc[i] += __uint_as_float(hb << 16);
-          Ps[row * PROW + f] = (uint16_t)hb;
+          ph[r] = (tok0 + row < n) ? phi_elu1(acc[r] + bf) : 0.f;  // padding rows add nothing
         }
-        phv[i][tt][0] = bits[0] | (bits[1] << 16);
-        phv[i][tt][1] = bits[2] | (bits[3] << 16);
+        const uint32_t p01 = pack_bf16x2(ph[0], ph[1]), p23 = pack_bf16x2(ph[2], ph[3]);
+        phv[i][tt][0] = p01;
+        phv[i][tt][1] = p23;
+        const int row0 = tt * 16 + 4 * g4;
+        Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
+        Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
+        Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
+        Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
       }
     }
-
-    // step 2: S += Phi^T V, contraction over 32-token blocks.  Hardware k-slot
-    // e of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or 32*kb + 16 + 4*g4
-    // + (e - 4) (e >= 4): exactly where step 1 left the Phi values.
+    // step 2: S += Phi^T V, u += Phi^T 1; contraction over 32-token blocks.
+    // Hardware k-slot e of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or
+    // 32*kb + 16 + 4*g4 + (e - 4) (e >= 4): exactly where step 1 left Phi.
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < KB; ++kb2) {
+      bf16x8_t Aph[FTW];
+#pragma unroll
+      for (int i = 0; i < FTW; ++i) {
+        u16x8_t av;
+        const uint32_t w0 = phv[i][2 * kb2][0], w1 = phv[i][2 * kb2][1];
+        const uint32_t w2 = phv[i][2 * kb2 + 1][0], w3 = phv[i][2 * kb2 + 1][1];
+        av[0] = (unsigned short)w0; av[1] = (unsigned short)(w0 >> 16);
+        av[2] = (unsigned short)w1; av[3] = (unsigned short)(w1 >> 16);
+        av[4] = (unsigned short)w2; av[5] = (unsigned short)(w2 >> 16);
+        av[6] = (unsigned short)w3; av[7] = (unsigned short)(w3 >> 16);
+        Aph[i] = as_bf16x8(av);
+        Uacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph[i], Bones, Uacc[i], 0, 0, 0);
+      }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         u16x8_t bv;
@@ -197,29 +215,39 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         }
         const bf16x8_t Bv = as_bf16x8(bv);
 #pragma unroll
-        for (int i = 0; i < FTW; ++i) {
-          u16x8_t av;
-          const uint32_t w0 = phv[i][2 * kb2][0], w1 = phv[i][2 * kb2][1];
-          const uint32_t w2 = phv[i][2 * kb2 + 1][0], w3 = phv[i][2 * kb2 + 1][1];
-          av[0] = (unsigned short)w0; av[1] = (unsigned short)(w0 >> 16);
-          av[2] = (unsigned short)w1; av[3] = (unsigned short)(w1 >> 16);
-          av[4] = (unsigned short)w2; av[5] = (unsigned short)(w2 >> 16);
-          av[6] = (unsigned short)w3; av[7] = (unsigned short)(w3 >> 16);
-          Sacc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), Bv, Sacc[i][ct], 0, 0, 0);
-        }
+        for (int i = 0; i < FTW; ++i)
+          Sacc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph[i], Bv, Sacc[i][ct], 0, 0, 0);
       }
     }
     __syncthreads();
     // store the Phi tile rows (16-byte pieces, coalesced)
     constexpr int PCR = M / 8;
 #pragma unroll
-    for (int j = 0; j < TT * PCR / 256; ++j) {
+    for (int j = 0; j < (TT * PCR + 255) / 256; ++j) {
       const int chunk = tid + 256 * j;
       const int row = chunk / PCR, cc = chunk % PCR;
-      if (tok0 + row < n)
+      if (chunk < TT * PCR && tok0 + row < n)
         *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) =
             *reinterpret_cast<const uint4*>(Ps + row * PROW + cc * 8);
     }
+  };
+
+  // two register stages in turn: tile t+2 loads while tile t is computed
+  uint4 kA[LCH], vA[LCH], kB[LCH], vB[LCH];
+  load_tile(kA, vA, 0);
+  if (TT < n) load_tile(kB, vB, TT);
+  for (int tok0 = 0; tok0 < n; tok0 += 2 * TT) {
+    __syncthreads();
+    stage_tile(kA, vA);
+    __syncthreads();
+    if (tok0 + 2 * TT < n) load_tile(kA, vA, tok0 + 2 * TT);
+    compute_tile(tok0);
+    if (tok0 + TT >= n) break;
+    __syncthreads();
+    stage_tile(kB, vB);
+    __syncthreads();
+    if (tok0 + 3 * TT < n) load_tile(kB, vB, tok0 + 3 * TT);
+    compute_tile(tok0 + TT);
   }
 
   // ---- partials of this chunk
@@ -231,10 +259,10 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) Sp[(size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16] = Sacc[i][ct][r];
-    float us = uacc[i];
-    us += __shfl_xor(us, 16, kWave);
-    us += __shfl_xor(us, 32, kWave);
-    if (g4 == 0) pu[((size_t)u * n_chunks + c) * M + fb + l16] = us;
+    if (l16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pu[((size_t)u * n_chunks + c) * M + fb + 4 * g4 + r] = Uacc[i][r];
+    }
   }
   kapmax = wave_max(kapmax);
   if (lane == 0) s_kap[wave] = kapmax;
@@ -333,10 +361,12 @@ build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
   for (int e = e0 + tid; e < e1; e += 256) {
     float v = 0.f;
     if (e < M * D) {
+#pragma unroll 16
       for (int c = 0; c < n_chunks; ++c) v += pS[((size_t)u * n_chunks + c) * M * D + e];
       S[(size_t)u * M * D + e] = v;
     } else if (e < M * D + M) {
       const int f = e - M * D;
+#pragma unroll 16
       for (int c = 0; c < n_chunks; ++c) v += pu[((size_t)u * n_chunks + c) * M + f];
       u_[(size_t)u * M + f] = v;
     } else {

@@ -99,6 +99,56 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ---------------------------------------------------------------- DPP wave ops
+// Wave-wide reductions and scans on DPP row permutations and row broadcasts
+// (row_bcast:15 / row_bcast:31 exist on GFX9-family parts such as gfx950).
+// They must be called by all 64 lanes of the wave.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// max within each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row_max16(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_min_dpp(float v) { return -wave_max_dpp(-v); }
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = lane_group_sum<16>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+// inclusive prefix sum over the wave (lane 0 first)
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_i<0x111>(v);        // row_shr:1
+  v += dpp_i<0x112>(v);        // row_shr:2
+  v += dpp_i<0x114>(v);        // row_shr:4
+  v += dpp_i<0x118>(v);        // row_shr:8
+  v += dpp_i<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// number of set bits of `mask` below this lane
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Full-wave reductions (ds_swizzle/bpermute based; used off the hot loops).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -36,17 +36,21 @@ constexpr int kScanBins = 512;          // linear score bins per head in the sca
 constexpr int kScanScoreSlots = 8192;   // fp32 LDS score slots per scan block (G * ch <= this)
 constexpr int kSelMaxChunks = 256;
 constexpr int kSelBandMax = 512;        // band members resolved in LDS
-constexpr int kSelMaxEntries = 11264;   // union entries held in LDS by a select block
+constexpr int kSelMaxEntries = 16384;   // union entries held in LDS by a select block
+constexpr int kSelBins = 1024;          // linear bins over the union's score range
 
 struct TopkPlan {
   int n_chunks, ch, r_min, r_cap;
   int e_max;                 // entries the select block can hold
-  size_t off_ent, off_meta, total;
+  size_t off_ent, off_meta, off_hp, total;
   size_t sel_lds;            // dynamic LDS bytes of the select kernel
 };
 TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K);
 
 // ------------------------------------------------------------- merge
+constexpr int kMergeThreads = 512;    // one block per (unit, query head)
+constexpr int kMergeChunk = 2048;     // exact-support entries staged in LDS at a time
+
 struct MergePlan {
   int n_slices, sl;          // slices of the per-head entry list, entries per slice
   int part_floats;           // floats per (slice, head) partial

@@ -35,11 +35,13 @@ struct HeadParams {
   float eps;    // bound on the fp32 scoring error of any mid token
 };
 
-// Identical in every kernel: a fixed sequential order and explicit roundings,
-// so the scan and the select bin a score identically.
-__device__ __forceinline__ HeadParams head_params(const float* qg, int D, float kappa) {
+// Computed by one wave with a fixed reduction order (every scan block of a unit
+// gets identical bits); the select reads the copy the scan stores, so a score
+// is binned identically by both kernels.
+__device__ __forceinline__ HeadParams head_params_wave(const float* qg, int D, float kappa) {
   float n2 = 0.f;
-  for (int j = 0; j < D; ++j) n2 = __fmaf_rn(qg[j], qg[j], n2);
+  for (int j = lane_id(); j < D; j += kWave) n2 = __fmaf_rn(qg[j], qg[j], n2);
+  n2 = wave_sum_dpp(n2);
   const float qn = __fsqrt_rn(n2);
   const float kap = (kappa > 0.f && kappa < 3.0e38f) ? kappa : 0.f;
   HeadParams h;
@@ -55,28 +57,18 @@ __device__ __forceinline__ int lin_bin(float x, const HeadParams& h) {
   return (t >= 0.f) ? (int)fminf(t, (float)(kScanBins - 1)) : 0;  // monotone in x; NaN -> 0
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads); returns the
-// exclusive prefix, `total` receives the sum.  Uses `buf` (>= 256 ints).
+// Block-wide exclusive scan of one int per thread (256 threads = 4 waves);
+// returns the exclusive prefix, `total` receives the sum.  Uses buf[0..3].
 __device__ __forceinline__ int block_excl_scan256(int v, int* buf, int& total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan_dpp(v);
+  if (lane == kWave - 1) buf[wave] = incl;
   __syncthreads();
-  if (tid < kWave) {
-    int a0 = buf[4 * tid], a1 = buf[4 * tid + 1], a2 = buf[4 * tid + 2], a3 = buf[4 * tid + 3];
-    int ls = a0 + a1 + a2 + a3;
-    int incl = wave_incl_scan(ls);
-    int ex = incl - ls;
-    buf[4 * tid] = ex;
-    buf[4 * tid + 1] = ex + a0;
-    buf[4 * tid + 2] = ex + a0 + a1;
-    buf[4 * tid + 3] = ex + a0 + a1 + a2;
-    if (tid == kWave - 1) buf[256] = incl;
-  }
+  const int w0 = buf[0], w1 = buf[1], w2 = buf[2], w3 = buf[3];
+  const int base = (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
+  total = w0 + w1 + w2 + w3;
   __syncthreads();
-  int r = buf[tid];
-  total = buf[256];
-  __syncthreads();
-  return r;
+  return base + incl - v;
 }
 
 // ====================================================================== scan
@@ -85,7 +77,7 @@ __global__ void __launch_bounds__(kScanThreads)
 topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t ustride,
                  int n_sink, int L_mid, int ch, int n_chunks, int r_min, int r_cap,
                  const float* __restrict__ kappa, float2* __restrict__ ent,
-                 int2* __restrict__ meta) {
+                 int2* __restrict__ meta, float4* __restrict__ hpw) {
   constexpr int E = 16;              // key elements per lane
   constexpr int LPT = D / E;         // lanes per token (4 or 8)
   constexpr int TPW = kWave / LPT;   // tokens per wave pass
@@ -118,11 +110,14 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       qr[g][4 * i] = v.x; qr[g][4 * i + 1] = v.y; qr[g][4 * i + 2] = v.z; qr[g][4 * i + 3] = v.w;
     }
   }
-  if (tid < G) s_hp[tid] = head_params(q + ((size_t)u * G + tid) * D, D, kappa[u]);
+  for (int g = wave; g < G; g += 4) {
+    const HeadParams h = head_params_wave(q + ((size_t)u * G + g) * D, D, kappa[u]);
+    if (lane == 0) s_hp[g] = h;
+  }
 
   const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D + part * E;
-  for (int p0 = 0; p0 < n; p0 += TPP * UNR) {
-    uint4 raw[UNR][PIECES];
+  constexpr int STEP = TPP * UNR;
+  auto load = [&](uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       const int t = p0 + i * TPP + wave * TPW + slot;
@@ -135,6 +130,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
         for (int pc = 0; pc < PIECES; ++pc) raw[i][pc] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto score = [&](const uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       const int t = p0 + i * TPP + wave * TPW + slot;
@@ -150,6 +147,16 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
         if (t < n && (g % LPT) == part) sc[g * CHMAX + t] = a;
       }
     }
+  };
+  // two register buffers in turn: the next step's rows load while this one is scored
+  uint4 ra[UNR][PIECES], rb[UNR][PIECES];
+  load(ra, 0);
+  for (int p0 = 0; p0 < n; p0 += 2 * STEP) {
+    if (p0 + STEP < n) load(rb, p0 + STEP);
+    score(ra, p0);
+    if (p0 + STEP >= n) break;
+    if (p0 + 2 * STEP < n) load(ra, p0 + 2 * STEP);
+    score(rb, p0 + STEP);
   }
   __syncthreads();
 
@@ -169,8 +176,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
     int ls = 0;
 #pragma unroll
     for (int j = 0; j < NB / kWave; ++j) ls += (int)h[lane * (NB / kWave) + j];
-    const int incl = wave_incl_scan(ls);
-    const int total = __shfl(incl, kWave - 1, kWave);
+    const int incl = wave_incl_scan_dpp(ls);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
     const int suf = total - incl + ls;  // tokens in this lane's bins and above
     const unsigned long long ball = __ballot(suf >= target);
     const int lstar = 63 - __clzll((long long)ball);
@@ -183,8 +190,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
         if (run >= target) { bc = lane * (NB / kWave) + j; break; }
       }
     }
-    bc = __shfl(bc, lstar, kWave);
-    run = __shfl(run, lstar, kWave);
+    bc = __builtin_amdgcn_readlane(bc, lstar);
+    run = __builtin_amdgcn_readlane(run, lstar);
     // lower the threshold to just above the highest non-empty bin below it: the
     // same tokens pass, and the select's completeness test is least strict
     int hb = -1;
@@ -193,8 +200,7 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       const int bin = lane * (NB / kWave) + j;
       if (bin < bc && h[bin] != 0u) hb = bin;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) hb = max(hb, __shfl_xor(hb, o, kWave));
+    hb = (int)wave_max_dpp((float)hb);
     if (lane == 0) { s_bc[g] = hb + 1; s_nrep[g] = run; }
   }
   __syncthreads();
@@ -219,7 +225,10 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       }
     }
   }
-  if (tid < G) meta[(size_t)(u * G + tid) * n_chunks + c] = make_int2(s_bc[tid], s_nrep[tid]);
+  if (tid < G) {
+    meta[(size_t)(u * G + tid) * n_chunks + c] = make_int2(s_bc[tid], s_nrep[tid]);
+    if (c == 0) hpw[u * G + tid] = make_float4(s_hp[tid].rg, s_hp[tid].inv_w, s_hp[tid].eps, 0.f);
+  }
 }
 
 // ====================================================================== select
@@ -257,7 +266,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int krem, int* 
     int c[4], ls = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { c[j] = (int)hist[255 - 4 * tid - j]; ls += c[j]; }
-    const int incl = wave_incl_scan(ls);
+    const int incl = wave_incl_scan_dpp(ls);
     const unsigned long long ball = __ballot(incl >= krem);
     const int lstar = __ffsll((long long)ball) - 1;
     if (tid == lstar) {
@@ -323,23 +332,27 @@ template <typename KT, int D>
 __global__ void __launch_bounds__(256)
 topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb, int64_t ustride,
                    int n_sink, int L_mid, int ch, int n_chunks, int r_cap, int K, int e_max,
-                   const float* __restrict__ kappa, const float2* __restrict__ ent,
+                   const float4* __restrict__ hpw, const float2* __restrict__ ent,
                    const int2* __restrict__ meta, int32_t* __restrict__ idx_out,
                    float* __restrict__ sc_out, float inv_sqrt_d) {
-  extern __shared__ __align__(16) float es[];  // e_max fp32 scores of the union
+  constexpr int NBS = kSelBins;
+  constexpr int SELF = 1 << 30;                // "selected" mark on a band member's position
+  extern __shared__ __align__(16) float dyn[];
+  float* es = dyn;                             // union scores (fp32, unscaled)
+  int* ep = reinterpret_cast<int*>(dyn + e_max);  // union mid positions
   __shared__ int s_off[kSelMaxChunks + 1];
   __shared__ int s_bcs[kSelMaxChunks];
   __shared__ int s_nrep[kSelMaxChunks];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[NBS];
   __shared__ int s_buf[257];
   __shared__ int s_misc[8];
+  __shared__ float s_fl[8];
   __shared__ DD s_bdd[kSelBandMax];
-  __shared__ int s_bpos[kSelBandMax];
-  __shared__ int s_bmid[kSelBandMax];
+  __shared__ int s_bidx[kSelBandMax];
   __shared__ float s_qf[128];
-  __shared__ HeadParams s_hp;
 
   const int ug = blockIdx.x, u = ug / G, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
   const float* qg = q + (size_t)ug * D;
   const int2* mt = meta + (size_t)ug * n_chunks;
   const float2* en = ent + (size_t)ug * n_chunks * r_cap;
@@ -347,67 +360,114 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   float* so = sc_out + (size_t)ug * K;
   const KT* kunit = kb + (size_t)u * ustride;
 
-  if (tid == 0) s_hp = head_params(qg, D, kappa[u]);
+  const float4 hp4 = hpw[ug];  // written by the scan: identical binning and error bound
+  const HeadParams hp{hp4.x, hp4.y, hp4.z};
   if (tid < D) s_qf[tid] = qg[tid];
-  if (tid == 0) {
-    int off = 0, trunc = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const int2 mm = mt[c];
-      if (mm.y > r_cap) trunc = 1;
-      s_off[c] = off;
-      s_bcs[c] = mm.x;
-      s_nrep[c] = mm.y;
-      off += min(mm.y, r_cap);
-    }
-    s_off[n_chunks] = off;
-    s_misc[7] = trunc;
+  // chunk reports: one thread per chunk (n_chunks <= 256), offsets by a block scan
+  int w_c = 0, trunc = 0;
+  if (tid < n_chunks) {
+    const int2 mm = mt[tid];
+    trunc = mm.y > r_cap;
+    w_c = min(mm.y, r_cap);
+    s_bcs[tid] = mm.x;
+    s_nrep[tid] = mm.y;
   }
+  int nE;
+  const int off_c = block_excl_scan256(w_c, s_buf, nE);
+  if (tid < n_chunks) s_off[tid] = off_c;
+  if (tid == 0) s_off[n_chunks] = nE;
+  trunc = __syncthreads_or(trunc);
+  int wmax = (int)wave_max_dpp((float)w_c);
+  if (lane == 0) s_buf[8 + wave] = wmax;
   __syncthreads();
-  const int nE = s_off[n_chunks];
+  wmax = max(max(s_buf[8], s_buf[9]), max(s_buf[10], s_buf[11]));
 
   if (K == L_mid) {  // every mid token is selected; the chunks reported all of them in order
-    for (int c = 0; c < n_chunks; ++c) {
-      const int o = s_off[c], w = s_off[c + 1] - o;
-      for (int j = tid; j < w; j += 256) {
+    for (int i = tid; i < n_chunks * wmax; i += 256) {
+      const int c = i / wmax, j = i - c * wmax;
+      if (j < s_off[c + 1] - s_off[c]) {
         const float2 e = en[(size_t)c * r_cap + j];
-        io[o + j] = n_sink + __float_as_int(e.y);
-        so[o + j] = e.x * inv_sqrt_d;
+        io[s_off[c] + j] = n_sink + __float_as_int(e.y);
+        so[s_off[c] + j] = e.x * inv_sqrt_d;
       }
     }
     return;
   }
 
-  bool fallback = s_misc[7] != 0 || nE > e_max || nE < K;
+  bool fallback = trunc != 0 || nE > e_max || nE < K;
   float th_lo = 0.f, th_hi = 0.f;
+  int n_band = 0, kp = 0;
   if (!fallback) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int o = s_off[c], w = s_off[c + 1] - o;
-      for (int j = tid; j < w; j += 256) es[o + j] = en[(size_t)c * r_cap + j].x;
+    __syncthreads();
+    // gather the union: slot (chunk c, j < wmax) of the padded report layout;
+    // eight loads per thread are issued before any is consumed
+    const int nslots = n_chunks * wmax;
+    for (int i0 = 0; i0 < nslots; i0 += 8 * 256) {
+      float2 e[8];
+      int dst[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 256 + tid;
+        const int c = i / wmax, j = i - c * wmax;
+        dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
+        if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (dst[k] >= 0) {
+          es[dst[k]] = e[k].x;
+          ep[dst[k]] = __float_as_int(e[k].y);
+        }
+      }
     }
     __syncthreads();
-    // radix select of the K-th largest score (ordered 32-bit key, 8-bit digits)
-    uint32_t prefix = 0u, mask = 0u;
-    int krem = K;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0u;
-      __syncthreads();
-      for (int i = tid; i < nE; i += 256) {
-        const uint32_t k = ord_f32(es[i]);
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    // range of the union, then a linear histogram over it
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = tid; i < nE; i += 256) { lo = fminf(lo, es[i]); hi = fmaxf(hi, es[i]); }
+    lo = wave_min_dpp(lo);
+    hi = wave_max_dpp(hi);
+    if (lane == 0) { s_fl[wave] = lo; s_fl[4 + wave] = hi; }
+    for (int b = tid; b < NBS; b += 256) hist[b] = 0u;
+    __syncthreads();
+    lo = fminf(fminf(s_fl[0], s_fl[1]), fminf(s_fl[2], s_fl[3]));
+    hi = fmaxf(fmaxf(s_fl[4], s_fl[5]), fmaxf(s_fl[6], s_fl[7]));
+    const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
+    auto ubin = [&](float x) {
+      const float t = __fmul_rn(__fsub_rn(x, lo), inv);
+      return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
+    };
+    for (int i = tid; i < nE; i += 256) atomicAdd(&hist[ubin(es[i])], 1u);
+    __syncthreads();
+    // bin of the K-th largest score: thread t owns bins NBS-4t-1 .. NBS-4t-4 (descending)
+    {
+      int c4[4], ls = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c4[j] = (int)hist[NBS - 4 * tid - 1 - j]; ls += c4[j]; }
+      int tot;
+      const int ex = block_excl_scan256(ls, s_buf, tot);
+      if (ex < K && ex + ls >= K) {
+        int run = ex;
+        for (int j = 0; j < 4; ++j) {
+          if (run + c4[j] >= K) { s_misc[0] = NBS - 4 * tid - 1 - j; break; }
+          run += c4[j];
+        }
       }
-      __syncthreads();
-      find_digit(hist, krem, s_misc);
-      __syncthreads();
-      krem -= s_misc[1];
-      prefix |= (uint32_t)s_misc[0] << shift;
-      mask |= 255u << shift;
-      __syncthreads();
     }
-    const float tt = unord_f32(prefix);
-    const HeadParams hp = s_hp;
-    th_lo = tt - 2.5f * hp.eps;
-    th_hi = tt + 2.5f * hp.eps;
+    __syncthreads();
+    const int bK = s_misc[0];
+    // exact extent of that bin: the K-th largest score t lies in [xlo, xhi]
+    float xlo = INFINITY, xhi = -INFINITY;
+    for (int i = tid; i < nE; i += 256)
+      if (ubin(es[i]) == bK) { xlo = fminf(xlo, es[i]); xhi = fmaxf(xhi, es[i]); }
+    xlo = wave_min_dpp(xlo);
+    xhi = wave_max_dpp(xhi);
+    __syncthreads();
+    if (lane == 0) { s_fl[wave] = xlo; s_fl[4 + wave] = xhi; }
+    __syncthreads();
+    xlo = fminf(fminf(s_fl[0], s_fl[1]), fminf(s_fl[2], s_fl[3]));
+    xhi = fmaxf(fmaxf(s_fl[4], s_fl[5]), fmaxf(s_fl[6], s_fl[7]));
+    th_lo = xlo - 2.5f * hp.eps;
+    th_hi = xhi + 2.5f * hp.eps;
     // every chunk must have reported all of its tokens scoring >= th_lo
     const int blo = lin_bin(th_lo, hp);
     int bad = 0;
@@ -415,81 +475,70 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
       const int n_c = min(ch, L_mid - c * ch);
       if (s_nrep[c] != n_c && s_bcs[c] > blo) bad = 1;
     }
+    if (tid == 0) { s_misc[3] = 0; s_misc[4] = 0; }
     fallback = __syncthreads_or(bad) != 0;
+    if (!fallback) {
+      int nin = 0;
+      for (int i0 = 0; i0 < nE; i0 += 256) {
+        const int i = i0 + tid;
+        const float sc = i < nE ? es[i] : -INFINITY;
+        nin += __popcll(__ballot(sc > th_hi));
+        const bool in_band = i < nE && sc <= th_hi && sc >= th_lo;
+        const uint64_t bm = __ballot(in_band);
+        int base = 0;
+        if (lane == 0 && bm != 0ull) base = atomicAdd(&s_misc[4], (int)__popcll(bm));
+        base = __builtin_amdgcn_readlane(base, 0);
+        const int b = base + lanes_below(bm);
+        if (in_band && b < kSelBandMax) s_bidx[b] = i;
+      }
+      if (lane == 0) atomicAdd(&s_misc[3], nin);
+      __syncthreads();
+      n_band = s_misc[4];
+      kp = K - s_misc[3];
+      fallback = n_band > kSelBandMax || kp < 1 || n_band < kp;
+    }
   }
   if (!fallback) {
-    if (tid == 0) { s_misc[3] = 0; s_misc[4] = 0; }
-    __syncthreads();
-    int nin = 0;
-    for (int i = tid; i < nE; i += 256) {
-      const float s = es[i];
-      if (s > th_hi) {
-        ++nin;
-      } else if (s >= th_lo) {
-        const int b = atomicAdd(&s_misc[4], 1);
-        if (b < kSelBandMax) s_bpos[b] = i;
-      }
+    // band: exact double-double scores when it must be split
+    for (int b = tid; b < n_band; b += 256) {
+      const int i = s_bidx[b];
+      s_bdd[b] = (n_band > kp) ? dd_dot<KT, D>(s_qf, kunit + (size_t)(n_sink + ep[i]) * D) : DD{0.0, 0.0};
     }
-    atomicAdd(&s_misc[3], nin);
     __syncthreads();
-    const int n_in = s_misc[3], n_band = s_misc[4];
-    const int kp = K - n_in;
-    if (n_band > kSelBandMax || kp < 1 || n_band < kp) {
-      fallback = true;
+    // rank by (exact score desc, position asc); mark the winners' positions
+    for (int b = tid; b < n_band; b += 256) {
+      const int i = s_bidx[b];
+      bool take = true;
+      if (n_band > kp) {
+        int rank = 0;
+        const DD mine = s_bdd[b];
+        const int mp = ep[i];
+        for (int b2 = 0; b2 < n_band; ++b2) rank += dd_key_greater(s_bdd[b2], ep[s_bidx[b2]], mine, mp);
+        take = rank < kp;
+      }
+      hist[b] = take ? 1u : 0u;  // the histogram is no longer needed
+    }
+    __syncthreads();
+    for (int b = tid; b < n_band; b += 256)
+      if (hist[b] != 0u) ep[s_bidx[b]] |= SELF;
+    __syncthreads();
+    // ordered compaction of the selected entries in position order
+    const int per = (nE + 255) / 256;
+    const int i0 = min(nE, tid * per), i1 = min(nE, i0 + per);
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) cnt += (es[i] > th_hi) || (ep[i] & SELF);
+    int total;
+    int pos = block_excl_scan256(cnt, s_buf, total);
+    if (total != K) {
+      fallback = true;  // uniform: every thread sees the same total
     } else {
-      // band members: mid position and (if the band must be split) exact score
-      for (int b = tid; b < n_band; b += 256) {
-        const int i = s_bpos[b];
-        int lo = 0, hi = n_chunks - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        const int pos = __float_as_int(en[(size_t)lo * r_cap + (i - s_off[lo])].y);
-        s_bmid[b] = pos;
-        if (n_band > kp) s_bdd[b] = dd_dot<KT, D>(s_qf, kunit + (size_t)(n_sink + pos) * D);
-      }
-      __syncthreads();
-      // rank within the band by (exact score desc, position asc); mark in es
-      for (int b = tid; b < n_band; b += 256) {
-        bool take = true;
-        if (n_band > kp) {
-          int rank = 0;
-          const DD mine = s_bdd[b];
-          const int mp = s_bmid[b];
-          for (int b2 = 0; b2 < n_band; ++b2) rank += dd_key_greater(s_bdd[b2], s_bmid[b2], mine, mp);
-          take = rank < kp;
-        }
-        es[s_bpos[b]] = take ? __int_as_float(0x7f800000) : __int_as_float(0xff800000);
-      }
-      __syncthreads();
-      // ordered compaction of the selected entries (es > th_hi) in position order
-      const int per = (nE + 255) / 256;
-      const int i0 = min(nE, tid * per), i1 = min(nE, i0 + per);
-      int cnt = 0;
-      for (int i = i0; i < i1; ++i) cnt += es[i] > th_hi;
-      int total;
-      int pos = block_excl_scan256(cnt, s_buf, total);
-      if (total != K) {
-        fallback = true;  // uniform: every thread sees the same total
-      } else if (i0 < i1) {
-        int c = 0;
-        {
-          int lo = 0, hi = n_chunks - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= i0) lo = mid; else hi = mid - 1;
+      for (int i = i0; i < i1; ++i) {
+        if ((es[i] > th_hi) || (ep[i] & SELF)) {
+          if (pos < K) {
+            io[pos] = n_sink + (ep[i] & ~SELF);
+            so[pos] = es[i] * inv_sqrt_d;
           }
-          c = lo;
-        }
-        for (int i = i0; i < i1; ++i) {
-          while (s_off[c + 1] <= i) ++c;
-          if (es[i] > th_hi) {
-            const float2 e = en[(size_t)c * r_cap + (i - s_off[c])];
-            io[pos] = n_sink + __float_as_int(e.y);
-            so[pos] = e.x * inv_sqrt_d;
-            ++pos;
-          }
+          ++pos;
         }
       }
     }
@@ -508,12 +557,12 @@ size_t g_lds_limit = 0;
 template <typename KT, int D>
 hipError_t launch_scan_g(int G, dim3 grid, hipStream_t st, const float* q, const KT* kb,
                          int64_t ustride, int n_sink, int L_mid, const TopkPlan& pl,
-                         const float* kappa, float2* ent, int2* meta) {
+                         const float* kappa, float2* ent, int2* meta, float4* hpw) {
 #define RMA_SCAN_CASE(GG)                                                                     \
   case GG:                                                                                    \
     hipLaunchKernelGGL((topk_scan_kernel<KT, D, GG>), grid, dim3(kScanThreads), 0, st, q, kb, \
                        ustride, n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_min, pl.r_cap, kappa, \
-                       ent, meta);                                                            \
+                       ent, meta, hpw);                                                       \
     break;
   switch (G) {
     RMA_SCAN_CASE(1) RMA_SCAN_CASE(2) RMA_SCAN_CASE(3) RMA_SCAN_CASE(4)
@@ -532,17 +581,18 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
   const KT* kb = static_cast<const KT*>(kv.k);
   float2* ent = reinterpret_cast<float2*>(ws + pl.off_ent);
   int2* meta = reinterpret_cast<int2*>(ws + pl.off_meta);
+  float4* hpw = reinterpret_cast<float4*>(ws + pl.off_hp);
   hipError_t e = launch_scan_g<KT, D>(G, dim3(pl.n_chunks, kv.n_units), st, q, kb, kv.unit_stride,
-                                      sp.n_sink, L_mid, pl, kappa, ent, meta);
+                                      sp.n_sink, L_mid, pl, kappa, ent, meta, hpw);
   if (e != hipSuccess) return e;
-  // dynamic LDS: the union scores, within what the device allows per block
-  const size_t static_lds = 16 * 1024;
+  // dynamic LDS: the union (score, position) pairs, within the per-block limit
+  const size_t static_lds = 24 * 1024;
   int e_max = pl.e_max;
-  if (g_lds_limit > static_lds) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - static_lds) / 4);
-  const size_t lds = (size_t)std::max(e_max, 1) * 4;
+  if (g_lds_limit > static_lds) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - static_lds) / 8);
+  const size_t lds = (size_t)std::max(e_max, 1) * 8;
   hipLaunchKernelGGL((topk_select_kernel<KT, D>), dim3(kv.n_units * G), dim3(256), lds, st, q, G,
                      kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
-                     kappa, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
+                     hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 
