@@ -69,7 +69,7 @@ BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_
   const int64_t Lm = l_mid(sp);
   const int64_t U = kv.n_units;
   p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
-  const int tile = (p.mfma && kv.d == 64) ? 64 : 32;
+  const int tile = p.mfma ? 64 : 32;
   if (Lm > 0) {
     // enough blocks to cover the chip (~2 per CU) with as few per-chunk partials as possible
     int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(512, U)));

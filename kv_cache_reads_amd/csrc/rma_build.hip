@@ -42,30 +42,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int D, int M>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * M <= 64 * 128 ? 2 : 1)))
+__global__ void __launch_bounds__(M * 4) 
 build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
                   int n_sink, int L_mid, int ch, int n_chunks, const float* __restrict__ W,
                   const float* __restrict__ bias, int P, uint16_t* __restrict__ phik,
                   float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
-  constexpr int TT = D == 64 ? 64 : 32;  // tokens per tile
+  constexpr int NW = M / 16;              // one 16-feature tile per wave
+  constexpr int NT = NW * 64;
+  constexpr int TT = 64;                  // tokens per tile
   constexpr int NTT = TT / 16;            // 16-token MFMA tiles per tile
   constexpr int KB = TT / 32;             // 32-token contraction blocks per tile
   constexpr int KS = D / 32;              // k-steps of step 1
-  constexpr int FT = M / 16;              // feature tiles
-  constexpr int FTW = FT / 4;             // feature tiles per wave
   constexpr int CT = D / 16;              // column tiles of step 2
-  constexpr int KROW = D + 8;             // Ks row stride (bf16 elements): 16 B pad -> 4-bank shift
-  constexpr int VROW = D + 4;             // Vs row stride: 8 B pad -> 2-bank shift
-  constexpr int PROW = M + 8;             // Phi staging row stride
+  constexpr int KROW = D + 8;             // Ks row stride (bf16): 16 B pad -> 4-bank shift per row
+  constexpr int VTROW = TT + 4;           // Vt row stride (one row per d column): 8 B pad
+  constexpr int PROW = M + 4;             // Phi staging row stride: 8 B pad -> the 4 lane groups
+                                          // of a step-1 tile land 8 banks apart
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int LCH = TT * CPR / 256;     // 16-byte chunks per thread per tile (K or V)
-  static_assert(FTW >= 1 && LCH >= 1, "tile shape");
+  constexpr int LCH = TT * CPR / NT;      // 16-byte chunks per thread per tile (K or V)
+  static_assert(LCH >= 1 && TT * CPR % NT == 0, "tile shape");
 
   __shared__ __align__(16) uint16_t Ks[TT * KROW];
-  __shared__ __align__(16) uint16_t Vs[TT * VROW];
+  __shared__ __align__(16) uint16_t Vt[D * VTROW];
   __shared__ __align__(16) uint16_t Ps[TT * PROW];
-  __shared__ float s_b[M];
-  __shared__ float s_kap[4];
+  __shared__ float s_kap[NW];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
@@ -75,47 +75,39 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   uint16_t* php = phik + ((size_t)u * L_mid + t0) * M;
+  const int f = wave * 16 + l16;          // this lane's feature in step 1
+  const float bf = bias[(size_t)p * M + f];
 
-  for (int i = tid; i < M; i += 256) s_b[i] = bias[(size_t)p * M + i];
-
-  // W (fp32) -> bf16 hi + lo B-operands for this wave's feature tiles
-  bf16x8_t Whi[FTW][KS], Wlo[FTW][KS];
+  // W (fp32) -> bf16 hi + lo B-operands of this wave's feature tile
+  bf16x8_t Whi[KS], Wlo[KS];
 #pragma unroll
-  for (int i = 0; i < FTW; ++i) {
-    const int f = (wave * FTW + i) * 16 + l16;
+  for (int ks = 0; ks < KS; ++ks) {
+    const float* wr = W + ((size_t)p * M + f) * D + 32 * ks + 8 * g4;
+    u16x8_t hi, lo;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float* wr = W + ((size_t)p * M + f) * D + 32 * ks + 8 * g4;
-      u16x8_t hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = wr[e];
-        const uint32_t hb = f32_to_bf16_bits(w);
-        hi[e] = (unsigned short)hb;
-        lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
-      }
-      Whi[i][ks] = as_bf16x8(hi);
-      Wlo[i][ks] = as_bf16x8(lo);
+    for (int e = 0; e < 8; ++e) {
+      const float w = wr[e];
+      const uint32_t hb = f32_to_bf16_bits(w);
+      hi[e] = (unsigned short)hb;
+      lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
     }
+    Whi[ks] = as_bf16x8(hi);
+    Wlo[ks] = as_bf16x8(lo);
   }
   u16x8_t ones_v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones_v[e] = 0x3F80;  // bf16 1.0: u = Phi^T 1 on the MFMA
   const bf16x8_t Bones = as_bf16x8(ones_v);
 
-  f32x4 Sacc[FTW][CT], Uacc[FTW];
+  f32x4 Sacc[CT], Uacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < FTW; ++i) {
-    Uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) Sacc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int ct = 0; ct < CT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float kapmax = 0.f;
 
   auto load_tile = [&](uint4 (&kr)[LCH], uint4 (&vr)[LCH], int tok0) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
-      const int chunk = tid + 256 * j;
+      const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
       if (tok0 + row < n) {
         kr[j] = ld_stream16(reinterpret_cast<const uint4*>(kp + (size_t)(tok0 + row) * D) + cc);
@@ -126,20 +118,30 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       }
     }
   };
+  // K rows as they are; V transposed to Vt[d][token] so that a step-2 B operand
+  // (eight tokens of one d column) is two 8-byte reads.  The token index is
+  // XOR-swizzled in groups of four by the column's 8-column group, which spreads
+  // the transposing 2-byte writes of one row over the banks and keeps every
+  // 4-token group contiguous.
+  auto vt = [&](int col, int tok) { return col * VTROW + (tok ^ ((col >> 3) << 2)); };
   auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH]) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
-      const int chunk = tid + 256 * j;
+      const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
       *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kr[j];
-      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8) = make_uint2(vr[j].x, vr[j].y);
-      *reinterpret_cast<uint2*>(Vs + row * VROW + cc * 8 + 4) = make_uint2(vr[j].z, vr[j].w);
+      const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[vt(cc * 8 + 2 * e, row)] = (uint16_t)w[e];
+        Vt[vt(cc * 8 + 2 * e + 1, row)] = (uint16_t)(w[e] >> 16);
+      }
     }
   };
   auto compute_tile = [&](int tok0) {
-    // kappa: 256/TT threads per token row
+    // kappa: NT/TT threads per token row
     {
-      constexpr int TPR = 256 / TT, EPT = D / TPR;
+      constexpr int TPR = NT / TT, EPT = D / TPR;
       const int row = tid / TPR, qd = tid % TPR;
       float ss = 0.f;
 #pragma unroll
@@ -152,83 +154,62 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       ss = lane_group_sum<TPR>(ss);
       if (tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
     }
-    // step 1: Z = K W^T, epilogue phi, keep bf16 pairs as step-2 A operands
-    uint32_t phv[FTW][NTT][2];  // [feature tile][token tile][packed (r0,r1), (r2,r3)]
+    // step 1: Z = K W^T for this wave's features, epilogue phi, bf16 pairs kept
+    uint32_t phv[NTT][2];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      bf16x8_t A[KS];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        A[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Ks + (tt * 16 + l16) * KROW + 32 * ks + 8 * g4));
-#pragma unroll
-      for (int i = 0; i < FTW; ++i) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Whi[i][ks], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Wlo[i][ks], acc, 0, 0, 0);
-        }
-        const int f = (wave * FTW + i) * 16 + l16;
-        const float bf = s_b[f];
-        float ph[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = tt * 16 + 4 * g4 + r;
-          ph[r] = (tok0 + row < n) ? phi_elu1(acc[r] + bf) : 0.f;  // padding rows add nothing
-        }
-        const uint32_t p01 = pack_bf16x2(ph[0], ph[1]), p23 = pack_bf16x2(ph[2], ph[3]);
-        phv[i][tt][0] = p01;
-        phv[i][tt][1] = p23;
-        const int row0 = tt * 16 + 4 * g4;
-        Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
-        Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
-        Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
-        Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t A = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Ks + (tt * 16 + l16) * KROW + 32 * ks + 8 * g4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Whi[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Wlo[ks], acc, 0, 0, 0);
       }
+      float ph[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = tt * 16 + 4 * g4 + r;
+        ph[r] = (tok0 + row < n) ? phi_elu1(acc[r] + bf) : 0.f;  // padding rows add nothing
+      }
+      const uint32_t p01 = pack_bf16x2(ph[0], ph[1]), p23 = pack_bf16x2(ph[2], ph[3]);
+      phv[tt][0] = p01;
+      phv[tt][1] = p23;
+      const int row0 = tt * 16 + 4 * g4;
+      Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
+      Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
+      Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
+      Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
     }
-    // step 2: S += Phi^T V, u += Phi^T 1; contraction over 32-token blocks.
-    // Hardware k-slot e of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or
-    // 32*kb + 16 + 4*g4 + (e - 4) (e >= 4): exactly where step 1 left Phi.
+    // step 2: S += Phi^T V, u += Phi^T 1 over 32-token blocks.  Hardware k-slot e
+    // of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or 32*kb + 16 + 4*g4 +
+    // (e - 4) (e >= 4): exactly where step 1 left the Phi values.
 #pragma unroll
     for (int kb2 = 0; kb2 < KB; ++kb2) {
-      bf16x8_t Aph[FTW];
-#pragma unroll
-      for (int i = 0; i < FTW; ++i) {
-        u16x8_t av;
-        const uint32_t w0 = phv[i][2 * kb2][0], w1 = phv[i][2 * kb2][1];
-        const uint32_t w2 = phv[i][2 * kb2 + 1][0], w3 = phv[i][2 * kb2 + 1][1];
-        av[0] = (unsigned short)w0; av[1] = (unsigned short)(w0 >> 16);
-        av[2] = (unsigned short)w1; av[3] = (unsigned short)(w1 >> 16);
-        av[4] = (unsigned short)w2; av[5] = (unsigned short)(w2 >> 16);
-        av[6] = (unsigned short)w3; av[7] = (unsigned short)(w3 >> 16);
-        Aph[i] = as_bf16x8(av);
-        Uacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph[i], Bones, Uacc[i], 0, 0, 0);
-      }
+      // the packed pairs already are the operand: element e of lane group g4
+      const bf16x8_t Aph = __builtin_bit_cast(
+          bf16x8_t, make_uint4(phv[2 * kb2][0], phv[2 * kb2][1], phv[2 * kb2 + 1][0], phv[2 * kb2 + 1][1]));
+      Uacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bones, Uacc, 0, 0, 0);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        u16x8_t bv;
         const int col = ct * 16 + l16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = 32 * kb2 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
-          bv[e] = Vs[tok * VROW + col];
-        }
-        const bf16x8_t Bv = as_bf16x8(bv);
-#pragma unroll
-        for (int i = 0; i < FTW; ++i)
-          Sacc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph[i], Bv, Sacc[i][ct], 0, 0, 0);
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(Vt + vt(col, 32 * kb2 + 4 * g4));
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(Vt + vt(col, 32 * kb2 + 16 + 4 * g4));
+        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+        Sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bv, Sacc[ct], 0, 0, 0);
       }
     }
     __syncthreads();
-    // store the Phi tile rows (16-byte pieces, coalesced)
+    // store the Phi tile rows (16-byte pieces, coalesced; rows are 8-byte aligned in LDS)
     constexpr int PCR = M / 8;
 #pragma unroll
-    for (int j = 0; j < (TT * PCR + 255) / 256; ++j) {
-      const int chunk = tid + 256 * j;
+    for (int j = 0; j < (TT * PCR + NT - 1) / NT; ++j) {
+      const int chunk = tid + NT * j;
       const int row = chunk / PCR, cc = chunk % PCR;
-      if (chunk < TT * PCR && tok0 + row < n)
-        *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) =
-            *reinterpret_cast<const uint4*>(Ps + row * PROW + cc * 8);
+      if (chunk < TT * PCR && tok0 + row < n) {
+        const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
+        const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
+        *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) = make_uint4(a.x, a.y, b.x, b.y);
+      }
     }
   };
 
@@ -252,22 +233,24 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
 
   // ---- partials of this chunk
   float* Sp = pS + ((size_t)u * n_chunks + c) * M * D;
+  const int fb = wave * 16;
 #pragma unroll
-  for (int i = 0; i < FTW; ++i) {
-    const int fb = (wave * FTW + i) * 16;
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int r = 0; r < 4; ++r) Sp[(size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16] = Sacc[ct][r];
+  if (l16 == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sp[(size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16] = Sacc[i][ct][r];
-    if (l16 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pu[((size_t)u * n_chunks + c) * M + fb + 4 * g4 + r] = Uacc[i][r];
-    }
+    for (int r = 0; r < 4; ++r) pu[((size_t)u * n_chunks + c) * M + fb + 4 * g4 + r] = Uacc[r];
   }
-  kapmax = wave_max(kapmax);
+  kapmax = wave_max_dpp(kapmax);
   if (lane == 0) s_kap[wave] = kapmax;
   __syncthreads();
-  if (tid == 0) pk[(size_t)u * n_chunks + c] = fmaxf(fmaxf(s_kap[0], s_kap[1]), fmaxf(s_kap[2], s_kap[3]));
+  if (tid == 0) {
+    float mx = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_kap[w]);
+    pk[(size_t)u * n_chunks + c] = mx;
+  }
 }
 
 // ====================================================================== VALU builder
@@ -411,9 +394,9 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
       const uint16_t* kk = static_cast<const uint16_t*>(kv.k);
       const uint16_t* vv = static_cast<const uint16_t*>(kv.v);
       uint16_t* ph = static_cast<uint16_t*>(phi_k);
-#define RMA_BM(DD, MM)                                                                          \
-  hipLaunchKernelGGL((build_mfma_kernel<DD, MM>), grid, dim3(256), 0, st, kk, vv, kv.unit_stride, \
-                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph, pS, pu, pk)
+#define RMA_BM(DD, MM)                                                                        \
+  hipLaunchKernelGGL((build_mfma_kernel<DD, MM>), grid, dim3(MM * 4), 0, st, kk, vv,            \
+                     kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph, pS, pu, pk)
       if (kv.d == 64 && m == 64) RMA_BM(64, 64);
       else if (kv.d == 64) RMA_BM(64, 128);
       else if (m == 64) RMA_BM(128, 64);
