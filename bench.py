@@ -17,6 +17,7 @@ eager run first).  Prints one JSON line.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -41,24 +42,71 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=float, default=0.0,
+                    help="first run a plain fp32 copy-like kernel (neg) of this size, for calibrating "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------------ measured HBM traffic
+# Bytes per launch from rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch) of this script, each scaled by what the same counter reads for a plain
+# copy of known size.  A record holds only for the kernel sources it was taken on.
+TRAFFIC = {
+    # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
+    ("build_mfma_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=69251335, write_bytes=84025379),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=33732954, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=5956311, write_bytes=8192),
+}
+
+
+def csrc_digest():
+    d = os.path.join(ROOT, "kv_cache_reads_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, K):
+    rec = TRAFFIC.get((kernel, workload, K))
+    if rec is None or rec["csrc"] != csrc_digest():
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
 # ------------------------------------------------------------------ byte model
 def call_bytes(cfg, K, n_gen):
     """Algorithmic HBM bytes of each call for one batch (inputs read once,
     outputs written once; workspace scratch excluded)."""
+    kb = kernel_bytes(cfg, K, n_gen)
+    return dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
+                topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"])
+
+
+def kernel_bytes(cfg, K, n_gen):
+    """Algorithmic HBM bytes of each kernel for one batch.  The builder reads the
+    mid-region K and V rows once and writes phi_k once (its per-chunk partial sums
+    are scratch); the reduce writes S, u, kappa; the scan reads the mid-region K
+    rows once (score bins and candidate lists are scratch); the select writes the
+    indices and their scores; the merge reads what one query's exact support and
+    residual need."""
     U, G, d, m, P = cfg.U, cfg.G, cfg.d, cfg.m, cfg.P
     Lm, na = cfg.L_mid, cfg.n_anchor
     e = 4 if cfg.kv_dtype == "f32" else 2
     ep = 4 if cfg.phi_dtype == "f32" else 2
     params = P * (m * d * 4 + m * 4)
-    build = U * (2 * Lm * d * e + Lm * m * ep + m * d * 4 + m * 4 + 4) + params
-    phi = U * G * (d * 4 + m * 4) + params
-    topk = U * (Lm * d * e + 4) + U * G * (d * 4 + K * 8)
-    merge = U * G * (K * (d * e + m * ep + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4) \
-        + U * (m * d * 4 + m * 4)
-    return dict(build=build, phi=phi, topk=topk, merge=merge)
+    return {
+        "build_mfma_kernel": U * (2 * Lm * d * e + Lm * m * ep) + params,
+        "build_reduce_kernel": U * (m * d * 4 + m * 4 + 4),
+        "phi_kernel": U * G * (d * 4 + m * 4) + params,
+        "topk_scan_kernel": U * (Lm * d * e + 4) + U * G * d * 4,
+        "topk_select_kernel": U * G * K * 8,
+        "merge_kernel": U * G * (K * (d * e + m * ep + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
+        + U * (m * d * 4 + m * 4),
+    }
 
 
 # ------------------------------------------------------------------ runner
@@ -118,24 +166,34 @@ class PathRunner:
                                     None, p(self.ws), self.ws.numel(), st)
         assert r == 0, r
 
-    def step(self, st, ev=None):
-        """The whole path; `ev` = list of events recorded between the calls."""
-        t = self.t
-        if ev is not None:
-            ev[0].record()
+    def step(self, st):
+        """The whole path: prefill summaries, then every decode step."""
         self.build(st)
-        if ev is not None:
-            ev[1].record()
         for s in range(self.cfg.steps):
             self.phi(s, st)
-            if ev is not None and s == 0:
-                ev[2].record()
             self.topk(s, st)
-            if ev is not None and s == 0:
-                ev[3].record()
             self.merge(s, st)
-            if ev is not None and s == 0:
-                ev[4].record()
+
+    def traced_step(self, st, R):
+        """The whole path, eager, with every kernel bracketed by HIP events that
+        the library records on `st` (rma_trace_arm).  Returns one record per
+        call: (call name, [(kernel name, start event, end event), ...])."""
+        t = self.t
+        out = []
+
+        def traced(name, fn):
+            evs = [t.cuda.Event(enable_timing=True) for _ in range(3)]
+            R.rma_trace_arm(evs)
+            fn()
+            names = R.rma_trace_kernels()
+            out.append((name, [(n, evs[j], evs[j + 1]) for j, n in enumerate(names)]))
+
+        traced("build", lambda: self.build(st))
+        for s in range(self.cfg.steps):
+            traced("phi", lambda: self.phi(s, st))
+            traced("topk", lambda: self.topk(s, st))
+            traced("merge", lambda: self.merge(s, st))
+        return out
 
 
 def cpu_baseline(cfg, inp, K, seconds):
@@ -194,6 +252,15 @@ def main():
     K = args.K if args.K is not None else cfg.K[0]
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     log(f"[bench] workload {cfg.name}: {cfg.desc}; K={K}")
+    if args.copy_probe_mb > 0:
+        n = int(args.copy_probe_mb * 1e6) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: neg over {n * 4} bytes read + {n * 4} bytes written, 3 launches")
+        del a, b
     t0 = time.time()
     inp = Wl.generate(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -274,30 +341,43 @@ def main():
     queries = cfg.U * cfg.G * cfg.steps
     value = queries / (ms_per_step / 1e3)
 
-    # ---- per-call durations: events between the calls, eager launches queued ahead
+    # ---- per-kernel durations: HIP events recorded by the library around each
+    # kernel on the stream it launches on (eager launches, queued ahead)
     n_t = int(max(5, min(200, args.steps, 2.0 / max(ms_per_step / 1e3, 1e-6))))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_t)]
+    recs = []
     with torch.cuda.stream(stream):
         for i in range(n_t):
-            runners[i % n_copies].step(st, evs[i])
+            recs.append(runners[i % n_copies].traced_step(st, R))
     torch.cuda.synchronize()
     names = ["build", "phi", "topk", "merge"]
-    dur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / n_t for j, n in enumerate(names)}
+    call_ms = {n: 0.0 for n in names}
+    kern_ms, kern_n = {}, {}
+    for rec in recs:
+        for call, ks in rec:
+            call_ms[call] += ks[0][1].elapsed_time(ks[-1][2])
+            for kname, a, b in ks:
+                kern_ms[kname] = kern_ms.get(kname, 0.0) + a.elapsed_time(b)
+                kern_n[kname] = kern_n.get(kname, 0) + 1
+    dur = {n: call_ms[n] / n_t for n in names}                       # ms per step
+    kavg = {k: kern_ms[k] / kern_n[k] for k in kern_ms}               # ms per launch
+    launches = {k: kern_n[k] / n_t for k in kern_n}                  # launches per step
     nb = call_bytes(cfg, K, cfg.n_gen(0))
+    kb = kernel_bytes(cfg, K, cfg.n_gen(0))
     step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s))[c] for s in range(cfg.steps)
                                    for c in ("phi", "topk", "merge"))
-    kernels = {"build": "build_mfma_kernel + build_reduce_kernel (rma_build_summaries)",
-               "phi": "phi_kernel (rma_phi_features)",
-               "topk": "topk_scan_kernel + topk_select_kernel (rma_decode_topk)",
-               "merge": "merge_kernel (rma_decode_merge)"}
-    dom = max(names, key=lambda n: dur[n])
-    achieved = nb[dom] / (dur[dom] / 1e3) / 1e9
-    gbs = {n: nb[n] / (dur[n] / 1e3) / 1e9 for n in names}
+    gbs = {n: nb[n] * (1 if n == "build" else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
+    kgbs = {k: kb[k] / (kavg[k] / 1e3) / 1e9 for k in kavg}
     for n in names:
-        log(f"[bench] {n:6s} {dur[n] * 1e3:9.2f} us  {nb[n] / 1e6:8.2f} MB  {gbs[n]:8.1f} GB/s")
+        log(f"[bench] {n:6s} {dur[n] * 1e3:9.2f} us/step  {gbs[n]:8.1f} GB/s")
+    for k in kavg:
+        log(f"[bench]   {k:22s} {kavg[k] * 1e3:9.2f} us/launch x{launches[k]:.0f}  "
+            f"{kb[k] / 1e6:8.2f} MB  {kgbs[k]:8.1f} GB/s")
     log(f"[bench] step {ms_per_step * 1e3:.2f} us, {step_bytes / 1e6:.1f} MB algorithmic "
         f"-> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; {value / 1e6:.3f} M queries/s")
     decode_us = sum(dur[n] for n in ("phi", "topk", "merge")) * 1e3
+    dom = max(kavg, key=lambda k: kavg[k] * launches[k])     # most time per step
+    achieved = kgbs[dom]
+    traffic = measured_traffic(dom, cfg.name, K)
 
     out = {
         "metric": METRIC,
@@ -324,13 +404,16 @@ def main():
             "step_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "per_call_us": {n: round(dur[n] * 1e3, 2) for n in names},
             "per_call_GBps": {n: round(gbs[n], 1) for n in names},
-            "decode_only_queries_per_s": round(cfg.U * cfg.G / (decode_us / 1e6), 1),
+            "per_kernel_us": {k: round(kavg[k] * 1e3, 2) for k in kavg},
+            "per_kernel_GBps": {k: round(kgbs[k], 1) for k in kavg},
+            "decode_only_queries_per_s": round(queries / (decode_us / 1e6), 1),
         },
         "roofline": {
-            "bound": "hbm", "kernel": kernels[dom],
+            "bound": "hbm", "kernel": dom,
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-            "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(dur[dom] * 1e3, 3),
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(kavg[dom] * 1e3, 3),
+            "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md",
         },
     }
     if not args.no_cpu_baseline:

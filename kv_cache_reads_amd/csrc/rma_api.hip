@@ -11,7 +11,33 @@
 
 namespace rma {
 static_assert(kCounterBytes == RMA_WORKSPACE_COUNTER_BYTES, "counter region size");
+static_assert(kTraceMax == RMA_TRACE_MAX_EVENTS, "trace size");
+
+KernelTrace& trace() {
+  static thread_local KernelTrace t;
+  return t;
+}
+
 namespace {
+
+// Brackets the kernels of one entry point when a trace is armed; disarms it on exit.
+struct TraceScope {
+  explicit TraceScope(hipStream_t st) {
+    KernelTrace& t = trace();
+    if (t.n_events > 0) {
+      hipEventRecord(t.ev[0], st);
+      t.used = 1;
+    }
+  }
+  ~TraceScope() {
+    KernelTrace& t = trace();
+    if (t.n_events > 0 && t.used > 0) {
+      t.count = t.used - 1;
+      t.n_events = 0;
+      t.used = 0;
+    }
+  }
+};
 
 thread_local char g_last_error[512] = "";
 
@@ -165,6 +191,33 @@ const char* rma_last_error(void) { return g_last_error; }
 
 int32_t rma_abi_version(void) { return RMA_ABI_VERSION; }
 
+rma_status rma_trace_arm(void* const* events, int32_t n_events) {
+  g_last_error[0] = 0;
+  KernelTrace& t = trace();
+  if (n_events == 0) {
+    t.n_events = 0;
+    t.used = 0;
+    return RMA_OK;
+  }
+  RMA_CHECK(events != nullptr && n_events >= 2 && n_events <= kTraceMax, RMA_ERR_INVALID_ARG,
+            "n_events must be 0 or in 2..%d", kTraceMax);
+  for (int i = 0; i < n_events; ++i) {
+    RMA_CHECK(events[i] != nullptr, RMA_ERR_INVALID_ARG, "event %d is NULL", i);
+    t.ev[i] = (hipEvent_t)events[i];
+  }
+  t.n_events = n_events;
+  t.used = 0;
+  t.count = 0;
+  return RMA_OK;
+}
+
+int32_t rma_trace_count(void) { return trace().count; }
+
+const char* rma_trace_name(int32_t j) {
+  const KernelTrace& t = trace();
+  return (j >= 0 && j < t.count) ? t.name[j] : nullptr;
+}
+
 size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int32_t G, int32_t K,
                            int32_t m) {
   if (kv == nullptr || sp == nullptr || kv->n_units < 1 || (kv->d != 64 && kv->d != 128))
@@ -204,6 +257,7 @@ rma_status rma_phi_features(const void* x, int32_t x_dtype, int32_t n_units, int
   RMA_CHECK(aligned16(x) && aligned16(W) && aligned16(b) && aligned16(phi), RMA_ERR_INVALID_ARG,
             "pointers must be 16-byte aligned");
   if (rows == 0) return RMA_OK;
+  TraceScope ts((hipStream_t)stream);
   hipError_t e = launch_phi(x, x_dtype, n_units, rows, x_unit_stride, d, W, b, m, P, phi,
                             phi_dtype, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -231,6 +285,7 @@ rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float
             "workspace is NULL or misaligned");
   RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
             workspace_bytes, pl.total);
+  TraceScope ts((hipStream_t)stream);
   hipError_t e = launch_build(pl, *kv, *sp, Wk, bk, m, P, phi_k, phi_dtype, S, u, kappa,
                               (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -256,6 +311,7 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
             "workspace is NULL or misaligned");
   RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
             workspace_bytes, pl.total);
+  TraceScope ts((hipStream_t)stream);
   hipError_t e = launch_topk(pl, q, G, *kv, *sp, kappa, K, idx, sel_scores, (uint8_t*)workspace,
                              (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -293,6 +349,7 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
             "workspace is NULL or misaligned");
   RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
             workspace_bytes, pl.total);
+  TraceScope ts((hipStream_t)stream);
   hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype, m, S, u,
                               flags, y, stats, (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

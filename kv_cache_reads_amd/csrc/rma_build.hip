@@ -425,10 +425,13 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    trace_kernel(st, pl.mfma ? "build_mfma_kernel" : "build_valu_kernel");
   }
   hipLaunchKernelGGL(build_reduce_kernel, dim3(pl.red_slices, kv.n_units), dim3(256), 0, st, pS, pu,
                      pk, pl.n_chunks, m, kv.d, pl.red_slices, S, u, kappa);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) trace_kernel(st, "build_reduce_kernel");
+  return e;
 }
 
 hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride, int d,
@@ -444,7 +447,9 @@ hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int
     if (phi_dtype == RMA_F32) RMA_PHI(uint16_t, float); else RMA_PHI(uint16_t, uint16_t);
   }
 #undef RMA_PHI
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) trace_kernel(st, "phi_kernel");
+  return e;
 }
 
 }  // namespace rma

@@ -58,6 +58,27 @@ struct MergePlan {
 };
 MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
 
+// ------------------------------------------------------------- kernel timing
+// Benchmark instrumentation armed by rma_trace_arm: events recorded on the
+// call's stream before its first kernel and after each kernel.  Thread-local.
+constexpr int kTraceMax = 16;
+struct KernelTrace {
+  hipEvent_t ev[kTraceMax];
+  const char* name[kTraceMax];
+  int n_events = 0;   // armed events (0 = off)
+  int used = 0;       // events recorded by the current call
+  int count = 0;      // kernels bracketed by the last traced call
+};
+KernelTrace& trace();
+// after each kernel launch of an entry point
+inline void trace_kernel(hipStream_t st, const char* name) {
+  KernelTrace& t = trace();
+  if (t.n_events > 0 && t.used > 0 && t.used < t.n_events) {
+    t.name[t.used - 1] = name;
+    hipEventRecord(t.ev[t.used++], st);
+  }
+}
+
 // ------------------------------------------------------------- launchers
 hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t x_unit_stride,
                       int d, const float* W, const float* b, int m, int P, void* phi,

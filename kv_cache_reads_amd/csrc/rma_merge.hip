@@ -264,7 +264,9 @@ hipError_t launch_merge_t(const MergePlan& pl, const float* q, const float* phi_
                      (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx, sel, K,
                      static_cast<const PT*>(phi_k), L_mid, S, u, flags, y, stats,
                      1.0f / sqrtf((float)D));
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) trace_kernel(st, "merge_kernel");
+  return e;
 }
 
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,

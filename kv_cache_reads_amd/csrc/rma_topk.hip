@@ -570,7 +570,9 @@ hipError_t launch_scan_g(int G, dim3 grid, hipStream_t st, const float* q, const
     default: return hipErrorInvalidValue;
   }
 #undef RMA_SCAN_CASE
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) trace_kernel(st, "topk_scan_kernel");
+  return e;
 }
 
 template <typename KT, int D>
@@ -593,7 +595,9 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
   hipLaunchKernelGGL((topk_select_kernel<KT, D>), dim3(kv.n_units * G), dim3(256), lds, st, q, G,
                      kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
                      hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) trace_kernel(st, "topk_select_kernel");
+  return e;
 }
 
 }  // namespace

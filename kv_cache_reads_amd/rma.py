@@ -85,6 +85,12 @@ def lib():
     L.rma_last_error.argtypes = []
     L.rma_last_error.restype = ctypes.c_char_p
     L.rma_abi_version.restype = _I32
+    L.rma_trace_arm.argtypes = [ctypes.POINTER(_VP), _I32]
+    L.rma_trace_arm.restype = _I32
+    L.rma_trace_count.argtypes = []
+    L.rma_trace_count.restype = _I32
+    L.rma_trace_name.argtypes = [_I32]
+    L.rma_trace_name.restype = ctypes.c_char_p
     for f in ("rma_phi_features", "rma_build_summaries", "rma_decode_topk", "rma_decode_merge"):
         getattr(L, f).restype = _I32
     _lib = L
@@ -240,3 +246,23 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
 
 def rma_abi_version() -> int:
     return int(lib().rma_abi_version())
+
+
+def rma_trace_arm(events) -> None:
+    """Arm per-kernel timing for the next call on this thread (benchmark
+    instrumentation): `events` are torch.cuda.Event(enable_timing=True); the
+    call records events[0] before its first kernel and events[j] after its j-th."""
+    L = lib()
+    handles = []
+    for e in events:
+        if not e.cuda_event:          # torch creates the event lazily on first record
+            e.record()
+        handles.append(e.cuda_event)
+    arr = (_VP * max(len(handles), 1))(*handles)
+    _check(L.rma_trace_arm(arr, len(handles)))
+
+
+def rma_trace_kernels():
+    """Names of the kernels the last traced call bracketed, in launch order."""
+    L = lib()
+    return [L.rma_trace_name(j).decode() for j in range(L.rma_trace_count())]

@@ -99,3 +99,17 @@ def test_workspace_sizes_are_monotone_in_K_and_units():
     kv = _kv()
     assert L.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(_sp()), 2, 5000, 0) == 0
     assert L.rma_workspace_bytes(99, ctypes.byref(kv), ctypes.byref(_sp()), 2, 10, 128) == 0
+
+
+def test_trace_arm_validation():
+    """Kernel-timing hook: argument checks only (arming stores handles; no HIP call)."""
+    L = R.lib()
+    VP = ctypes.c_void_p
+    two = (VP * 2)(0x1000, 0x2000)
+    assert L.rma_trace_arm(two, 1) == R.RMA_ERR_INVALID_ARG              # one event brackets nothing
+    assert L.rma_trace_arm(two, 17) == R.RMA_ERR_INVALID_ARG             # more than RMA_TRACE_MAX_EVENTS
+    assert L.rma_trace_arm((VP * 2)(0x1000, None), 2) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_trace_arm(None, 2) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_trace_arm(two, 2) == R.RMA_OK
+    assert L.rma_trace_arm(None, 0) == R.RMA_OK                          # disarm
+    assert L.rma_trace_count() == 0 and L.rma_trace_name(0) is None
