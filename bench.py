@@ -54,19 +54,24 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=69251335, write_bytes=84025379),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=33732954, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="609daad7834738d0", fetch_bytes=5956311, write_bytes=8192),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="47638f3c12c048a4", fetch_bytes=69251335, write_bytes=84025379),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="47638f3c12c048a4", fetch_bytes=33732954, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="47638f3c12c048a4", fetch_bytes=5956311, write_bytes=8192),
 }
 
 
 def csrc_digest():
+    """Digest of the kernel sources' code (comments and whitespace ignored)."""
+    import re
     d = os.path.join(ROOT, "kv_cache_reads_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp")):
+            code = open(os.path.join(d, f)).read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
             h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

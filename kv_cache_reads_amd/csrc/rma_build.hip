@@ -3,7 +3,7 @@
 // u = sum phi_k(k_i) over the mid-region; App. C.1 for the positive map).
 //
 // build_mfma  (bf16 K/V, bf16 phi rows, computed phi)  grid (chunks, units),
-//   256 threads, 64-token tiles through LDS:
+//   m/16 waves (one 16-feature tile each), 64-token tiles through LDS:
 //     Z = K_tile W^T        v_mfma_f32_16x16x32_bf16; W is split into bf16
 //                           hi + lo parts (K is exactly bf16), so Z carries
 //                           ~2^-17 relative error instead of bf16's 2^-9
