@@ -103,8 +103,6 @@ BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);
   }
-  const int64_t per_unit = (int64_t)m * kv.d + m + 1;
-  p.red_slices = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(512, U), ceil_div(per_unit, 256)));
   size_t off = counter_bytes(U);
   const size_t nc = (size_t)std::max(p.n_chunks, 1);
   p.off_S = off;

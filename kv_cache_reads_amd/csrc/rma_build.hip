@@ -22,6 +22,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace rma {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -55,7 +57,9 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   constexpr int KS = D / 32;              // k-steps of step 1
   constexpr int CT = D / 16;              // column tiles of step 2
   constexpr int KROW = D + 8;             // Ks row stride (bf16): 16 B pad -> 4-bank shift per row
-  constexpr int VTROW = TT + 4;           // Vt row stride (one row per d column): 8 B pad
+  constexpr int VROW = D + 16;            // Vs row stride (bf16): rows 32 dwords + 8 (mod 64) apart,
+                                          // so the 8 rows one transposing read touches per
+                                          // half-wave cover the 64 banks once
   constexpr int PROW = M + 4;             // Phi staging row stride: 8 B pad -> the 4 lane groups
                                           // of a step-1 tile land 8 banks apart
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
@@ -63,7 +67,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   static_assert(LCH >= 1 && TT * CPR % NT == 0, "tile shape");
 
   __shared__ __align__(16) uint16_t Ks[TT * KROW];
-  __shared__ __align__(16) uint16_t Vt[D * VTROW];
+  __shared__ __align__(16) uint16_t Vs[TT * VROW];
   __shared__ __align__(16) uint16_t Ps[TT * PROW];
   __shared__ float s_kap[NW];
 
@@ -118,27 +122,31 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       }
     }
   };
-  // K rows as they are; V transposed to Vt[d][token] so that a step-2 B operand
-  // (eight tokens of one d column) is two 8-byte reads.  The token index is
-  // XOR-swizzled in groups of four by the column's 8-column group, which spreads
-  // the transposing 2-byte writes of one row over the banks and keeps every
-  // 4-token group contiguous.
-  auto vt = [&](int col, int tok) { return col * VTROW + (tok ^ ((col >> 3) << 2)); };
+  // K and V rows as they are (16-byte writes)
   auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH]) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
       *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kr[j];
-      const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[vt(cc * 8 + 2 * e, row)] = (uint16_t)w[e];
-        Vt[vt(cc * 8 + 2 * e + 1, row)] = (uint16_t)(w[e] >> 16);
-      }
+      *reinterpret_cast<uint4*>(Vs + row * VROW + cc * 8) = vr[j];
     }
   };
-  auto compute_tile = [&](int tok0) {
+  // Step-2 B operand of one 16-column tile: eight tokens of one V column per lane,
+  // gathered by two transposing LDS reads (ds_read_b64_tr_b16).  Within a 16-lane
+  // group, lane j receives element e from the 8-byte piece that lane 4e + j/4
+  // addressed, at position j%4; so lane l' points at token (l'/4) of the group's
+  // 4-token block and at columns 4*(l'%4) .. +3 of the tile, and lane j gets the
+  // four tokens of column j.
+  const int tr_row = 4 * g4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  auto ld_tr = [&](int row, int col) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(Vs + row * VROW + col));
+    return __builtin_bit_cast(uint2, r);
+  };
+  auto compute_tile = [&](int tok0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     // kappa: NT/TT threads per token row
     {
       constexpr int TPR = NT / TT, EPT = D / TPR;
@@ -152,7 +160,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         ss = __fmaf_rn(b2, b2, ss);
       }
       ss = lane_group_sum<TPR>(ss);
-      if (tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
+      if (FULL || tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
     }
     // step 1: Z = K W^T for this wave's features, epilogue phi, bf16 pairs kept
     uint32_t phv[NTT][2];
@@ -169,7 +177,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = tt * 16 + 4 * g4 + r;
-        ph[r] = (tok0 + row < n) ? phi_elu1(acc[r] + bf) : 0.f;  // padding rows add nothing
+        ph[r] = (FULL || tok0 + row < n) ? phi_elu1(acc[r] + bf) : 0.f;  // padding rows add nothing
       }
       const uint32_t p01 = pack_bf16x2(ph[0], ph[1]), p23 = pack_bf16x2(ph[2], ph[3]);
       phv[tt][0] = p01;
@@ -191,9 +199,8 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       Uacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bones, Uacc, 0, 0, 0);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const int col = ct * 16 + l16;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(Vt + vt(col, 32 * kb2 + 4 * g4));
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(Vt + vt(col, 32 * kb2 + 16 + 4 * g4));
+        const uint2 lo4 = ld_tr(32 * kb2 + tr_row, ct * 16 + tr_col);
+        const uint2 hi4 = ld_tr(32 * kb2 + 16 + tr_row, ct * 16 + tr_col);
         const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
         Sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bv, Sacc[ct], 0, 0, 0);
       }
@@ -205,7 +212,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     for (int j = 0; j < (TT * PCR + NT - 1) / NT; ++j) {
       const int chunk = tid + NT * j;
       const int row = chunk / PCR, cc = chunk % PCR;
-      if (chunk < TT * PCR && tok0 + row < n) {
+      if (chunk < TT * PCR && (FULL || tok0 + row < n)) {
         const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
         const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
         *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) = make_uint4(a.x, a.y, b.x, b.y);
@@ -222,13 +229,15 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     stage_tile(kA, vA);
     __syncthreads();
     if (tok0 + 2 * TT < n) load_tile(kA, vA, tok0 + 2 * TT);
-    compute_tile(tok0);
+    if (tok0 + TT <= n) compute_tile(tok0, std::true_type{});
+    else compute_tile(tok0, std::false_type{});
     if (tok0 + TT >= n) break;
     __syncthreads();
     stage_tile(kB, vB);
     __syncthreads();
     if (tok0 + 3 * TT < n) load_tile(kB, vB, tok0 + 3 * TT);
-    compute_tile(tok0 + TT);
+    if (tok0 + 2 * TT <= n) compute_tile(tok0 + TT, std::true_type{});
+    else compute_tile(tok0 + TT, std::false_type{});
   }
 
   // ---- partials of this chunk
@@ -333,50 +342,111 @@ build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t 
 }
 
 // ====================================================================== reduce
+// Sums the per-chunk partials of each unit.  A block covers 64 float4 outputs of
+// one unit; wave w sums chunks [w*nq, (w+1)*nq) in order (its loads issued
+// together, 16 at a time) and the four wave sums are added in wave order, so
+// the result is the same on every run.
+constexpr int kRedBatch = 16;
 __global__ void __launch_bounds__(256)
 build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
-                    const float* __restrict__ pk, int n_chunks, int M, int D, int slices,
+                    const float* __restrict__ pk, int n_chunks, int M, int D,
                     float* __restrict__ S, float* __restrict__ u_, float* __restrict__ kappa) {
-  const int u = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const int per_unit = M * D + M + 1;
-  const int per_slice = (per_unit + slices - 1) / slices;
-  const int e0 = sl * per_slice, e1 = min(per_unit, e0 + per_slice);
-  for (int e = e0 + tid; e < e1; e += 256) {
-    float v = 0.f;
-    if (e < M * D) {
-#pragma unroll 16
-      for (int c = 0; c < n_chunks; ++c) v += pS[((size_t)u * n_chunks + c) * M * D + e];
-      S[(size_t)u * M * D + e] = v;
-    } else if (e < M * D + M) {
-      const int f = e - M * D;
-#pragma unroll 16
-      for (int c = 0; c < n_chunks; ++c) v += pu[((size_t)u * n_chunks + c) * M + f];
-      u_[(size_t)u * M + f] = v;
+  __shared__ float4 part[4][64];
+  const int u = blockIdx.y, tid = threadIdx.x, o = tid & 63, w = tid >> 6;
+  const int nS4 = M * D / 4, nU4 = M / 4;
+  const int e = blockIdx.x * 64 + o;               // float4 output index within the unit
+  const bool live = e < nS4 + nU4;
+  const float4* src = nullptr;
+  size_t stride = 0;
+  if (live) {
+    if (e < nS4) {
+      src = reinterpret_cast<const float4*>(pS + (size_t)u * n_chunks * M * D) + e;
+      stride = (size_t)nS4;
     } else {
-      for (int c = 0; c < n_chunks; ++c) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
-      kappa[u] = v;
+      src = reinterpret_cast<const float4*>(pu + (size_t)u * n_chunks * M) + (e - nS4);
+      stride = (size_t)nU4;
     }
+  }
+  const int nq = (n_chunks + 3) / 4;
+  const int c0 = min(n_chunks, w * nq), c1 = min(n_chunks, c0 + nq);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    for (int cb = c0; cb < c1; cb += kRedBatch) {
+      float4 t[kRedBatch];
+#pragma unroll
+      for (int k = 0; k < kRedBatch; ++k)
+        if (cb + k < c1) t[k] = src[(size_t)(cb + k) * stride];
+#pragma unroll
+      for (int k = 0; k < kRedBatch; ++k)
+        if (cb + k < c1) {
+          acc.x += t[k].x;
+          acc.y += t[k].y;
+          acc.z += t[k].z;
+          acc.w += t[k].w;
+        }
+    }
+  }
+  part[w][o] = acc;
+  __syncthreads();
+  if (w == 0 && live) {
+    float4 r = part[0][o];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      r.x += part[k][o].x;
+      r.y += part[k][o].y;
+      r.z += part[k][o].z;
+      r.w += part[k][o].w;
+    }
+    if (e < nS4) reinterpret_cast<float4*>(S + (size_t)u * M * D)[e] = r;
+    else reinterpret_cast<float4*>(u_ + (size_t)u * M)[e - nS4] = r;
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    float v = 0.f;
+    for (int c = 0; c < n_chunks; ++c) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
+    kappa[u] = v;
   }
 }
 
 // ====================================================================== phi features
-template <typename XT, typename PT>
+// Block = (8 rows, unit, 16 features).  A 16-lane group owns one feature: its
+// lanes hold D/16 consecutive weights (coalesced 16-byte loads, issued before
+// the rows arrive) and the group sums its partial dots with DPP.
+template <typename XT, typename PT, int D>
 __global__ void __launch_bounds__(256)
-phi_kernel(const XT* __restrict__ x, int64_t xstride, int rows, int D, const float* __restrict__ W,
+phi_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const float* __restrict__ W,
            const float* __restrict__ bias, int M, int P, PT* __restrict__ phi) {
-  constexpr int RB = 8;  // rows per block
-  __shared__ float xs[RB][129];
-  const int u = blockIdx.y, r0 = blockIdx.x * RB, tid = threadIdx.x;
+  constexpr int RB = 8, EPL = D / 16;
+  __shared__ __align__(16) float xs[RB][D];
+  const int r0 = blockIdx.x * RB, u = blockIdx.y, tid = threadIdx.x;
+  const int f = blockIdx.z * 16 + (tid >> 4), j = tid & 15;
   const int p = u % P;
   const int nr = min(RB, rows - r0);
-  for (int i = tid; i < nr * D; i += 256) xs[i / D][i % D] = ld_f32(x, (size_t)u * xstride + (size_t)(r0 + i / D) * D + i % D);
+  float w[EPL];
+  const float4* wr = reinterpret_cast<const float4*>(W + ((size_t)p * M + f) * D + j * EPL);
+#pragma unroll
+  for (int e = 0; e < EPL / 4; ++e) {
+    const float4 t = wr[e];
+    w[4 * e] = t.x;
+    w[4 * e + 1] = t.y;
+    w[4 * e + 2] = t.z;
+    w[4 * e + 3] = t.w;
+  }
+  const float bf = bias[(size_t)p * M + f];
+  for (int i = tid; i < nr * D; i += 256)
+    xs[i / D][i % D] = ld_f32(x, (size_t)u * xstride + (size_t)(r0 + i / D) * D + i % D);
   __syncthreads();
-  for (int i = tid; i < nr * M; i += 256) {
-    const int r = i / M, f = i % M;
-    float z = bias[(size_t)p * M + f];
-    const float* wr = W + ((size_t)p * M + f) * D;
-    for (int j = 0; j < D; ++j) z = __fmaf_rn(wr[j], xs[r][j], z);
-    st_elem(phi, ((size_t)u * rows + r0 + r) * M + f, st_round<PT>(phi_elu1(z)));
+  for (int r = 0; r < nr; ++r) {
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[r][j * EPL + e]);
+      z = __fmaf_rn(w[e], xv.x, z);
+      z = __fmaf_rn(w[e + 1], xv.y, z);
+      z = __fmaf_rn(w[e + 2], xv.z, z);
+      z = __fmaf_rn(w[e + 3], xv.w, z);
+    }
+    z = lane_group_sum<16>(z);
+    if (j == 0) st_elem(phi, ((size_t)u * rows + r0 + r) * M + f, st_round<PT>(phi_elu1(z + bf)));
   }
 }
 
@@ -385,9 +455,11 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
                         const float* b, int m, int P, void* phi_k, int phi_dtype, float* S,
                         float* u, float* kappa, uint8_t* ws, hipStream_t st) {
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
-  float* pS = reinterpret_cast<float*>(ws + pl.off_S);
-  float* pu = reinterpret_cast<float*>(ws + pl.off_u);
-  float* pk = reinterpret_cast<float*>(ws + pl.off_kap);
+  // one chunk per unit: the builder writes S, u and kappa itself
+  const bool direct = pl.n_chunks == 1;
+  float* pS = direct ? S : reinterpret_cast<float*>(ws + pl.off_S);
+  float* pu = direct ? u : reinterpret_cast<float*>(ws + pl.off_u);
+  float* pk = direct ? kappa : reinterpret_cast<float*>(ws + pl.off_kap);
   if (pl.n_chunks > 0) {
     const dim3 grid(pl.n_chunks, kv.n_units);
     if (pl.mfma) {
@@ -427,8 +499,10 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
     if (e != hipSuccess) return e;
     trace_kernel(st, pl.mfma ? "build_mfma_kernel" : "build_valu_kernel");
   }
-  hipLaunchKernelGGL(build_reduce_kernel, dim3(pl.red_slices, kv.n_units), dim3(256), 0, st, pS, pu,
-                     pk, pl.n_chunks, m, kv.d, pl.red_slices, S, u, kappa);
+  if (direct) return hipSuccess;
+  const int blocks = (int)ceil_div((int64_t)m * kv.d / 4 + m / 4, 64);
+  hipLaunchKernelGGL(build_reduce_kernel, dim3(blocks, kv.n_units), dim3(256), 0, st, pS, pu, pk,
+                     pl.n_chunks, m, kv.d, S, u, kappa);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) trace_kernel(st, "build_reduce_kernel");
   return e;
@@ -437,15 +511,21 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
 hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride, int d,
                       const float* W, const float* b, int m, int P, void* phi, int phi_dtype,
                       hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div(rows, 8), n_units);
-#define RMA_PHI(XT, PT)                                                                          \
-  hipLaunchKernelGGL((phi_kernel<XT, PT>), grid, dim3(256), 0, st, static_cast<const XT*>(x),   \
-                     xstride, (int)rows, d, W, b, m, P, static_cast<PT*>(phi))
+  const dim3 grid((unsigned)ceil_div(rows, 8), n_units, m / 16);
+#define RMA_PHI1(XT, PT, DD)                                                                     \
+  hipLaunchKernelGGL((phi_kernel<XT, PT, DD>), grid, dim3(256), 0, st, static_cast<const XT*>(x), \
+                     xstride, (int)rows, W, b, m, P, static_cast<PT*>(phi))
+#define RMA_PHI(XT, PT)                    \
+  do {                                     \
+    if (d == 64) RMA_PHI1(XT, PT, 64);     \
+    else RMA_PHI1(XT, PT, 128);            \
+  } while (0)
   if (x_dtype == RMA_F32) {
     if (phi_dtype == RMA_F32) RMA_PHI(float, float); else RMA_PHI(float, uint16_t);
   } else {
     if (phi_dtype == RMA_F32) RMA_PHI(uint16_t, float); else RMA_PHI(uint16_t, uint16_t);
   }
+#undef RMA_PHI1
 #undef RMA_PHI
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) trace_kernel(st, "phi_kernel");

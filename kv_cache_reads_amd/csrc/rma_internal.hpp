@@ -25,7 +25,6 @@ struct BuildPlan {
   bool mfma;         // bf16 K/V, bf16 phi, computed phi -> MFMA builder
   int n_chunks;      // token chunks per unit
   int ch;            // tokens per chunk (multiple of the tile)
-  int red_slices;    // reduce kernel: blocks per unit
   size_t off_S, off_u, off_kap, total;
 };
 BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_phi, int phi_dtype);
