@@ -32,7 +32,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// upper bound of sqrt(x) for a sum of squares computed in fp32 over <= 128 terms
+// upper bound of sqrt(x) for a sum of squares computed in fp32 over <= 128 terms (its
+// rounding is below 128 * 2^-24 relative; the factor covers that and the root's)
 __device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) * (1.0f + 1e-5f); }
 
 // ====================================================================== MFMA builder
@@ -147,20 +148,24 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   };
   auto compute_tile = [&](int tok0, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    // kappa: NT/TT threads per token row
+    // kappa: the largest squared key norm (NT/TT threads per token row, bf16 pair
+    // dots; the root is taken once per chunk)
     {
       constexpr int TPR = NT / TT, EPT = D / TPR;
       const int row = tid / TPR, qd = tid % TPR;
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPT; e += 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(Ks + row * KROW + qd * EPT + e);
-        const float a = bf16lo(w), b2 = bf16hi(w);
-        ss = __fmaf_rn(a, a, ss);
-        ss = __fmaf_rn(b2, b2, ss);
+      for (int e = 0; e < EPT; e += 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(Ks + row * KROW + qd * EPT + e);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2_t h = __builtin_bit_cast(bf16x2_t, ws[i]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+        }
       }
       ss = lane_group_sum<TPR>(ss);
-      if (FULL || tok0 + row < n) kapmax = fmaxf(kapmax, norm_upper(ss));
+      if (FULL || tok0 + row < n) kapmax = fmaxf(kapmax, ss);
     }
     // step 1: Z = K W^T for this wave's features, epilogue phi, bf16 pairs kept
     uint32_t phv[NTT][2];
@@ -258,7 +263,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     float mx = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_kap[w]);
-    pk[(size_t)u * n_chunks + c] = mx;
+    pk[(size_t)u * n_chunks + c] = norm_upper(mx);
   }
 }
 
@@ -400,10 +405,11 @@ build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
     if (e < nS4) reinterpret_cast<float4*>(S + (size_t)u * M * D)[e] = r;
     else reinterpret_cast<float4*>(u_ + (size_t)u * M)[e - nS4] = r;
   }
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && w == 1) {  // kappa: the chunk maxima spread over one wave
     float v = 0.f;
-    for (int c = 0; c < n_chunks; ++c) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
-    kappa[u] = v;
+    for (int c = o; c < n_chunks; c += kWave) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
+    v = wave_max_dpp(v);
+    if (o == 0) kappa[u] = v;
   }
 }
 

@@ -37,6 +37,7 @@ constexpr int kSelMaxChunks = 256;
 constexpr int kSelBandMax = 512;        // band members resolved in LDS
 constexpr int kSelMaxEntries = 16384;   // union entries held in LDS by a select block
 constexpr int kSelBins = 1024;          // linear bins over the union's score range
+constexpr int kSelThreads = 1024;       // select block size
 
 struct TopkPlan {
   int n_chunks, ch, r_min, r_cap;

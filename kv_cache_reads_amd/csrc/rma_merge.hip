@@ -6,12 +6,16 @@
 //
 // One block per (unit, query head).  The head's exact-support entries
 //   [sinks | tail | generated | retrieved (idx)]   (n_a + n_gen + K entries)
-// are staged in LDS chunk by chunk; eight lanes share an entry (its V row, and
-// for a retrieved token its phi_k row), accumulating with a running max m*:
-//   N_E = sum e^{s_i - m*} v_i,  Z_E = sum e^{s_i - m*},
+// are staged in LDS chunk by chunk.  Eight lanes share an entry; each 8-lane
+// group takes every 64th entry, issues the row loads of four entries at once
+// (V row; K row for an anchor or generated token, whose score it computes;
+// phi_k row for a retrieved token) and keeps its own running max m:
+//   N = sum e^{s_i - m} v_i,  Z = sum e^{s_i - m},
 //   w_i = f.Phi_K[i],  nuK = sum_{K(q)} w_i v_i,  ZK = sum_{K(q)} w_i.
-// phi(q)^T S comes from fp32 MFMA (v_mfma_f32_16x16x4f32) over the unit's query
-// heads; then the subtraction, the clamp and one normalisation.
+// The group partials are combined with max rescaling (fixed order) into m*,
+// N_E, Z_E.  phi(q)^T S comes from fp32 MFMA (v_mfma_f32_16x16x4f32) over the
+// unit's query heads while the first index loads are in flight; then the
+// subtraction, the clamp and one normalisation.
 #include "rma_device.hpp"
 #include "rma_internal.hpp"
 
@@ -21,12 +25,38 @@ namespace rma {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__device__ __forceinline__ float ld_elem(const T* p, size_t i);
-template <>
-__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
-template <>
-__device__ __forceinline__ float ld_elem<float>(const float* p, size_t i) { return p[i]; }
+// N elements of type T as raw 16-byte words: loaded early, unpacked at use.
+template <typename T, int N>
+struct RawPiece {
+  static constexpr int W = N * (int)sizeof(T) / 16;
+  static_assert(W >= 1 && N * (int)sizeof(T) % 16 == 0, "pieces are whole 16-byte words");
+  uint4 w[W];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p4[i];
+  }
+  __device__ __forceinline__ void unpack(float (&out)[N]) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const uint32_t x[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          out[8 * i + 2 * k] = bf16lo(x[k]);
+          out[8 * i + 2 * k + 1] = bf16hi(x[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[4 * i + k] = __uint_as_float(x[k]);
+      }
+    }
+  }
+};
 
 template <typename KT, typename PT, int D, int M>
 __global__ void __launch_bounds__(kMergeThreads)
@@ -37,24 +67,26 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
              const float* __restrict__ S, const float* __restrict__ u_, uint32_t flags,
              float* __restrict__ y, float* __restrict__ stats, float inv_sqrt_d) {
   constexpr int NT = kMergeThreads, NW = NT / kWave;
-  constexpr int LPE = 8;            // lanes per entry in the accumulation
-  constexpr int EPW = kWave / LPE;  // entries per wave pass
+  constexpr int LPE = 8;            // lanes per entry
+  constexpr int NGR = NT / LPE;     // entry groups
   constexpr int CPL = D / LPE;      // value columns per lane
   constexpr int FPL = M / LPE;      // phi features per lane
-  constexpr int LPT = D / 16;       // lanes per anchor dot
   constexpr int CH = kMergeChunk;   // entries staged in LDS at a time
+  constexpr int SPT = CH / NT;      // staged entries per thread
+  constexpr int B = (sizeof(KT) == 2) ? 4 : 2;  // entries per group whose loads are in flight together
   const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int part = lane & (LPE - 1), slot = lane / LPE;
+  const int part = lane & (LPE - 1), grp = tid / LPE;
   const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
   const int T = n_ex + K;
   const bool sub = (flags == RMA_MERGE_SUB) && K > 0;
+  const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
+  const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
 
-  constexpr int RW = 2 * CPL + 2;  // partial floats per lane: N, NK columns, Z, ZK
   __shared__ int s_pos[CH];
   __shared__ float s_sc[CH];
-  __shared__ float s_red[NW][4][LPE][RW];
-  __shared__ float s_wm[NW];
+  __shared__ float s_wn[NW][D], s_wk[NW][D];
+  __shared__ float s_wm[NW], s_wz[NW], s_wzk[NW];
   __shared__ float s_fs[D];
   __shared__ float s_uf;
 
@@ -64,29 +96,74 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   const int32_t* ig = idx + (size_t)ug * K;
   const float* sg = sel + (size_t)ug * K;
 
-  float fr[FPL];
+  // position and score of entry j (a retrieved position is clamped into the
+  // mid-region so that a bad index cannot fault).  The index and score loads
+  // are issued for all of a thread's entries before any is used.
+  int spos[SPT];
+  float ssc[SPT];
+  auto stage_load = [&](int c0) {
+    int ri[SPT];
+    float rs[SPT];
+    if (K > 0) {
 #pragma unroll
-  for (int i = 0; i < FPL; ++i) fr[i] = sub ? phi_q[(size_t)ug * M + part * FPL + i] : 0.f;
-  float N[CPL], NK[CPL];
+      for (int r = 0; r < SPT; ++r) {
+        const int jr = min(max(c0 + tid + NT * r - n_ex, 0), K - 1);
+        ri[r] = ig[jr];
+        rs[r] = sg[jr];
+      }
+    }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) { N[c] = 0.f; NK[c] = 0.f; }
-  float Z = 0.f, ZK = 0.f, mrun = -INFINITY;
+    for (int r = 0; r < SPT; ++r) {
+      const int j = c0 + tid + NT * r;
+      const bool ret = j >= n_ex && j < T;
+      int pos = j < n_sink ? j : (j < n_a ? L - n_tail + (j - n_sink) : L + (j - n_a));
+      if (ret) pos = min(max(ri[r], n_sink), n_sink + max(L_mid, 1) - 1);
+      spos[r] = j < T ? pos : n_sink;
+      ssc[r] = ret ? rs[r] : 0.f;
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int r = 0; r < SPT; ++r) {
+      s_pos[tid + NT * r] = spos[r];
+      s_sc[tid + NT * r] = ssc[r];
+    }
+  };
+  stage_load(0);
+
+  float qr[CPL], fr[FPL];
+#pragma unroll
+  for (int i = 0; i < CPL; i += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(qg + part * CPL + i);
+    qr[i] = t.x; qr[i + 1] = t.y; qr[i + 2] = t.z; qr[i + 3] = t.w;
+  }
+  if (sub) {
+#pragma unroll
+    for (int i = 0; i < FPL; i += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(phi_q + (size_t)ug * M + part * FPL + i);
+      fr[i] = t.x; fr[i + 1] = t.y; fr[i + 2] = t.z; fr[i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FPL; ++i) fr[i] = 0.f;
+  }
 
   // ---- phi(q)^T S and u^T f for this unit's heads (fp32 MFMA 16x16x4; rows =
   //      the G query heads zero-padded to 16, k = features, columns = d)
-  const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
-  const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
   if (resid && !whole_mid) {
     const float* Su = S + (size_t)u * M * D;
     const int row = lane & 15, kq = lane >> 4;
     for (int ct = wave; ct < D / 16; ct += NW) {
       float av[M / 4], bv[M / 4];
+      const float* fq = phi_q + ((size_t)u * G + min(row, G - 1)) * M;  // rows >= G are zero
 #pragma unroll
       for (int ks = 0; ks < M / 4; ++ks) {
         const int f = 4 * ks + kq;
-        av[ks] = row < G ? phi_q[((size_t)u * G + row) * M + f] : 0.f;
+        av[ks] = fq[f];
         bv[ks] = Su[(size_t)f * D + 16 * ct + row];
       }
+#pragma unroll
+      for (int ks = 0; ks < M / 4; ++ks) av[ks] = row < G ? av[ks] : 0.f;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < M / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
@@ -103,146 +180,143 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     }
   }
 
-  // ---- exact-support entries [anchors | generated | retrieved], CH at a time
+  float N[CPL], NK[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { N[c] = 0.f; NK[c] = 0.f; }
+  float Z = 0.f, ZK = 0.f, mrun = -INFINITY;
+
+  // ---- exact-support entries, CH at a time
   for (int c0 = 0; c0 < T; c0 += CH) {
+    if (c0 > 0) {
+      __syncthreads();  // the previous chunk's entries are consumed
+      stage_load(c0);
+    }
+    stage_store();
+    __syncthreads();
     const int cnt = min(CH, T - c0);
-    __syncthreads();
-    for (int jj = tid; jj < cnt; jj += NT) {
-      const int j = c0 + jj;
-      int pos;
-      float sc = 0.f;
-      if (j < n_sink) pos = j;
-      else if (j < n_a) pos = L - n_tail + (j - n_sink);
-      else if (j < n_ex) pos = L + (j - n_a);
-      else {
-        // positions come from rma_decode_topk; clamped so a bad index cannot fault
-        pos = min(max(ig[j - n_ex], n_sink), n_sink + max(L_mid, 1) - 1);
-        sc = sg[j - n_ex];
-      }
-      s_pos[jj] = pos;
-      s_sc[jj] = sc;
-    }
-    __syncthreads();
-    const int nc = max(0, min(c0 + cnt, n_ex) - c0);  // anchors / generated in this chunk
-    if (nc > 0) {
-      const int lp = lane % LPT;
-      float qr[16];
+    for (int jb = grp; jb < cnt; jb += NGR * B) {
+      RawPiece<KT, CPL> vr[B], kr[B];
+      RawPiece<PT, FPL> pr[B];
+      float scs[B];
+      int kind[B];  // 0: none, 1: anchor or generated (scored here), 2: retrieved
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qr[e] = qg[lp * 16 + e];
-      for (int base = 0; base < nc; base += NT / LPT) {
-        const int jj = base + tid / LPT;
-        float a = 0.f;
-        if (jj < nc) {
-          float kv[16];
-          load_row_f32<16>(kunit + (size_t)s_pos[jj] * D + lp * 16, kv);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) a = __fmaf_rn(qr[e], kv[e], a);
+      for (int e = 0; e < B; ++e) {
+        const int jj = jb + e * NGR;
+        vr[e].zero();
+        kr[e].zero();
+        pr[e].zero();
+        kind[e] = 0;
+        scs[e] = 0.f;
+        if (jj < cnt) {
+          const int pos = s_pos[jj];
+          const bool ex = c0 + jj < n_ex;
+          kind[e] = ex ? 1 : 2;
+          scs[e] = s_sc[jj];
+          vr[e].load(vunit + (size_t)pos * D + part * CPL);
+          if (ex) kr[e].load(kunit + (size_t)pos * D + part * CPL);
+          else if (sub) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
         }
-        a = lane_group_sum<LPT>(a);
-        if (jj < nc && lp == 0) s_sc[jj] = a * inv_sqrt_d;
       }
-      __syncthreads();
-    }
-    // running max over the chunk
-    float mx = -INFINITY;
-    for (int jj = tid; jj < cnt; jj += NT) mx = fmaxf(mx, s_sc[jj]);
-    mx = wave_max_dpp(mx);
-    if (lane == 0) s_wm[wave] = mx;
-    __syncthreads();
-    mx = s_wm[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_wm[w]);
-    const float mnew = fmaxf(mrun, mx);
-    if (mnew > mrun) {
-      const float r = __expf(mrun - mnew);   // 0 for the first chunk
+      for (int e = 0; e < B; ++e) {
+        // both dots on every lane (zeros where unused), so the 8-lane sums
+        // never run under divergent control flow
+        float kv[CPL], ph[FPL], vv[CPL];
+        kr[e].unpack(kv);
+        pr[e].unpack(ph);
+        float a = 0.f, w = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) N[c] *= r;
-      Z *= r;
-      mrun = mnew;
-    }
-    // accumulate: 8 lanes per entry, EPW entries per wave pass
-#pragma unroll 2
-    for (int jb = wave * EPW; jb < cnt; jb += NW * EPW) {
-      const int jj = jb + slot;
-      const bool ok = jj < cnt;
-      const int pos = ok ? s_pos[jj] : n_sink;
-      float vv[CPL];
-      if (ok) {
-        load_row_f32<CPL>(vunit + (size_t)pos * D + part * CPL, vv);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) vv[c] = 0.f;
-      }
-      const float ew = ok ? __expf(s_sc[jj] - mrun) : 0.f;
-      float w = 0.f;
-      if (sub && ok && c0 + jj >= n_ex) {
-        float ph[FPL];
-        load_row_f32<FPL>(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL, ph);
+        for (int i = 0; i < CPL; ++i) a = __fmaf_rn(qr[i], kv[i], a);
 #pragma unroll
         for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
-      }
-      w = lane_group_sum<LPE>(w);
+        a = lane_group_sum<LPE>(a);
+        w = lane_group_sum<LPE>(w);
+        if (kind[e] != 0) {  // uniform within the group
+          const float s = kind[e] == 1 ? a * inv_sqrt_d : scs[e];
+          if (s > mrun) {
+            const float r = __expf(mrun - s);  // 0 while nothing is accumulated
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        N[c] = __fmaf_rn(ew, vv[c], N[c]);
-        NK[c] = __fmaf_rn(w, vv[c], NK[c]);
+            for (int c = 0; c < CPL; ++c) N[c] *= r;
+            Z *= r;
+            mrun = s;
+          }
+          const float ew = __expf(s - mrun);
+          vr[e].unpack(vv);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            N[c] = __fmaf_rn(ew, vv[c], N[c]);
+            NK[c] = __fmaf_rn(w, vv[c], NK[c]);
+          }
+          Z += ew;
+          ZK += w;
+        }
       }
-      if (part == 0) { Z += ew; ZK += w; }
     }
   }
-  // ---- sum the entry slots: slots 2r and 2r+1 share row r (DPP row_ror:8),
-  //      then the four rows of every wave through LDS
+
+  // ---- combine the eight groups of each wave (lanes l, l^8, l^16, l^32 hold the
+  //      same columns), then the waves through LDS, rescaling to the larger max
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    N[c] += dpp_f<0x128>(N[c]);
-    NK[c] += dpp_f<0x128>(NK[c]);
-  }
-  Z += dpp_f<0x128>(Z);
-  ZK += dpp_f<0x128>(ZK);
-  if ((lane & 8) == 0) {
-    float* dst = s_red[wave][lane >> 4][part];
+  for (int sh = LPE; sh < kWave; sh <<= 1) {
+    const float mo = __shfl_xor(mrun, sh, kWave);
+    const float mn = fmaxf(mrun, mo);
+    const float ra = mrun == -INFINITY ? 0.f : __expf(mrun - mn);
+    const float rb = mo == -INFINITY ? 0.f : __expf(mo - mn);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      dst[c] = N[c];
-      dst[CPL + c] = NK[c];
+      N[c] = ra * N[c] + rb * __shfl_xor(N[c], sh, kWave);
+      NK[c] += __shfl_xor(NK[c], sh, kWave);
     }
-    dst[2 * CPL] = Z;
-    dst[2 * CPL + 1] = ZK;
+    Z = ra * Z + rb * __shfl_xor(Z, sh, kWave);
+    ZK += __shfl_xor(ZK, sh, kWave);
+    mrun = mn;
+  }
+  if (lane < LPE) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      s_wn[wave][part * CPL + c] = N[c];
+      s_wk[wave][part * CPL + c] = NK[c];
+    }
+    if (lane == 0) {
+      s_wm[wave] = mrun;
+      s_wz[wave] = Z;
+      s_wzk[wave] = ZK;
+    }
   }
   __syncthreads();
+  float ms = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
+  float sw[NW];
   float ZE = 0.f, ZKt = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ZE += s_red[w][r][0][2 * CPL];
-      ZKt += s_red[w][r][0][2 * CPL + 1];
-    }
+  for (int w = 0; w < NW; ++w) {
+    sw[w] = s_wm[w] == -INFINITY ? 0.f : __expf(s_wm[w] - ms);
+    ZE += sw[w] * s_wz[w];
+    ZKt += s_wzk[w];
+  }
   float zr = 0.f;
   if (resid && !whole_mid) zr = fmaxf(s_uf - (sub ? ZKt : 0.f), 0.f);
   // y = (N_E + e^{-m*} nu) / (Z_E + e^{-m*} Z_R), scaled by e^{m* - Mx} with
   // Mx = max(m*, log Z_R) so that neither term overflows
   const float lz = zr > 0.f ? __logf(zr) : -INFINITY;
-  const float Mx = fmaxf(mrun, lz);
-  const float a = __expf(mrun - Mx);
+  const float Mx = fmaxf(ms, lz);
+  const float a = __expf(ms - Mx);
   const float bres = __expf(-Mx);
   const float den = a * ZE + bres * zr;
   for (int col = tid; col < D; col += NT) {
-    const int pp = col / CPL, c = col - pp * CPL;
     float NE = 0.f, NKc = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        NE += s_red[w][r][pp][c];
-        NKc += s_red[w][r][pp][CPL + c];
-      }
+    for (int w = 0; w < NW; ++w) {
+      NE += sw[w] * s_wn[w][col];
+      NKc += s_wk[w][col];
+    }
     float nu = 0.f;
     if (resid && !whole_mid) nu = s_fs[col] - (sub ? NKc : 0.f);
     y[(size_t)ug * D + col] = (a * NE + bres * nu) / den;
   }
   if (stats != nullptr && tid == 0) {
-    stats[(size_t)ug * 4 + 0] = mrun;
+    stats[(size_t)ug * 4 + 0] = ms;
     stats[(size_t)ug * 4 + 1] = ZE;
     stats[(size_t)ug * 4 + 2] = zr;
     stats[(size_t)ug * 4 + 3] = ZKt;

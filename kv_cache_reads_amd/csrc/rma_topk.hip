@@ -35,13 +35,11 @@ struct HeadParams {
   float eps;    // bound on the fp32 scoring error of any mid token
 };
 
-// Computed by one wave with a fixed reduction order (every scan block of a unit
-// gets identical bits); the select reads the copy the scan stores, so a score
-// is binned identically by both kernels.
-__device__ __forceinline__ HeadParams head_params_wave(const float* qg, int D, float kappa) {
-  float n2 = 0.f;
-  for (int j = lane_id(); j < D; j += kWave) n2 = __fmaf_rn(qg[j], qg[j], n2);
-  n2 = wave_sum_dpp(n2);
+// Binning parameters of one head from its squared norm n2 (computed with a fixed
+// reduction order, so every scan block of a unit gets identical bits; the
+// select reads the copy the scan stores, so a score is binned identically by
+// both kernels).
+__device__ __forceinline__ HeadParams head_params(float n2, float kappa) {
   const float qn = __fsqrt_rn(n2);
   const float kap = (kappa > 0.f && kappa < 3.0e38f) ? kappa : 0.f;
   HeadParams h;
@@ -57,18 +55,50 @@ __device__ __forceinline__ int lin_bin(float x, const HeadParams& h) {
   return (t >= 0.f) ? (int)fminf(t, (float)(kScanBins - 1)) : 0;  // monotone in x; NaN -> 0
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads = 4 waves);
-// returns the exclusive prefix, `total` receives the sum.  Uses buf[0..3].
-__device__ __forceinline__ int block_excl_scan256(int v, int* buf, int& total) {
+// Block-wide exclusive scan of one int per thread (NT threads); returns the
+// exclusive prefix, `total` receives the sum.  Uses buf[0 .. NT/64 - 1].
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* buf, int& total) {
+  constexpr int NWV = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int incl = wave_incl_scan_dpp(v);
   if (lane == kWave - 1) buf[wave] = incl;
   __syncthreads();
-  const int w0 = buf[0], w1 = buf[1], w2 = buf[2], w3 = buf[3];
-  const int base = (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
-  total = w0 + w1 + w2 + w3;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const int x = buf[w];
+    base += (w < wave) ? x : 0;
+    tot += x;
+  }
+  total = tot;
   __syncthreads();
   return base + incl - v;
+}
+__device__ __forceinline__ int block_excl_scan256(int v, int* buf, int& total) {
+  return block_excl_scan<256>(v, buf, total);
+}
+
+// The same for N independent values per thread in one pass (buf[0 .. 4N-1]):
+// v[i] becomes its exclusive prefix, total[i] the sum.
+template <int N>
+__device__ __forceinline__ void block_excl_scan256_n(int (&v)[N], int* buf, int (&total)[N]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int incl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) incl[i] = wave_incl_scan_dpp(v[i]);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) buf[4 * i + wave] = incl[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int w0 = buf[4 * i], w1 = buf[4 * i + 1], w2 = buf[4 * i + 2], w3 = buf[4 * i + 3];
+    total[i] = w0 + w1 + w2 + w3;
+    v[i] = (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0) + incl[i] - v[i];
+  }
+  __syncthreads();
 }
 
 // ====================================================================== scan
@@ -100,6 +130,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   const int t0 = c * ch;
   const int n = min(ch, L_mid - t0);
 
+  // query slices first: global loads complete in issue order, so the head
+  // parameters below only wait for these, not for the key rows
   float qr[G][E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -110,10 +142,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       qr[g][4 * i] = v.x; qr[g][4 * i + 1] = v.y; qr[g][4 * i + 2] = v.z; qr[g][4 * i + 3] = v.w;
     }
   }
-  for (int g = wave; g < G; g += 4) {
-    const HeadParams h = head_params_wave(q + ((size_t)u * G + g) * D, D, kappa[u]);
-    if (lane == 0) s_hp[g] = h;
-  }
+  // histogram bins are filled while scoring
+  for (int i = tid; i < G * NB; i += kScanThreads) hist[i] = 0u;
 
   const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D + part * E;
   constexpr int STEP = TPP * UNR;
@@ -131,6 +161,27 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       }
     }
   };
+  // two register buffers in turn, both in flight while the head parameters are derived
+  uint4 ra[UNR][PIECES], rb[UNR][PIECES];
+  load(ra, 0);
+  if (STEP < n) load(rb, STEP);
+
+  // every lane derives the same parameters from its query slices (the LPT lanes
+  // of a token hold the whole query; fixed reduction order)
+  HeadParams hp[G];
+  const float kap_u = kappa[u];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) n2 = __fmaf_rn(qr[g][e], qr[g][e], n2);
+    hp[g] = head_params(lane_group_sum<LPT>(n2), kap_u);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (tid == g) s_hp[g] = hp[g];
+  __syncthreads();  // histogram cleared
+
   auto score = [&](const uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
@@ -144,28 +195,19 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 #pragma unroll
         for (int e = 0; e < E; ++e) a = __fmaf_rn(qr[g][e], kv[e], a);
         a = lane_group_sum<LPT>(a);
-        if (t < n && (g % LPT) == part) sc[g * CHMAX + t] = a;
+        if (t < n && (g % LPT) == part) {
+          sc[g * CHMAX + t] = a;
+          atomicAdd(&hist[g * NB + lin_bin(a, hp[g])], 1u);
+        }
       }
     }
   };
-  // two register buffers in turn: the next step's rows load while this one is scored
-  uint4 ra[UNR][PIECES], rb[UNR][PIECES];
-  load(ra, 0);
   for (int p0 = 0; p0 < n; p0 += 2 * STEP) {
-    if (p0 + STEP < n) load(rb, p0 + STEP);
     score(ra, p0);
-    if (p0 + STEP >= n) break;
     if (p0 + 2 * STEP < n) load(ra, p0 + 2 * STEP);
+    if (p0 + STEP >= n) break;
     score(rb, p0 + STEP);
-  }
-  __syncthreads();
-
-  // ---- per-head linear-bin histogram of this chunk's scores
-  for (int i = tid; i < G * NB; i += kScanThreads) hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kScanThreads) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) atomicAdd(&hist[g * NB + lin_bin(sc[g * CHMAX + i], s_hp[g])], 1u);
+    if (p0 + 3 * STEP < n) load(rb, p0 + 3 * STEP);
   }
   __syncthreads();
 
@@ -205,21 +247,25 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   }
   __syncthreads();
 
-  // ---- ordered compaction of the passing tokens (position order), per head
+  // ---- ordered compaction of the passing tokens (position order), all heads
+  //      with one multi-value block scan
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-#pragma unroll 1
+  int bcs[G], cnt[G], tot[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { bcs[g] = s_bc[g]; cnt[g] = 0; }
+  for (int i = i0; i < i1; ++i) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) cnt[g] += (lin_bin(sc[g * CHMAX + i], hp[g]) >= bcs[g]);
+  }
+  block_excl_scan256_n<G>(cnt, s_buf, tot);
+#pragma unroll
   for (int g = 0; g < G; ++g) {
-    const HeadParams hp = s_hp[g];
-    const int bc = s_bc[g];
-    int cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += (lin_bin(sc[g * CHMAX + i], hp) >= bc);
-    int total;
-    int pos = block_excl_scan256(cnt, s_buf, total);
     float2* dst = ent + ((size_t)(u * G + g) * n_chunks + c) * r_cap;
+    int pos = cnt[g];
     for (int i = i0; i < i1; ++i) {
       const float s = sc[g * CHMAX + i];
-      if (lin_bin(s, hp) >= bc) {
+      if (lin_bin(s, hp[g]) >= bcs[g]) {
         if (pos < r_cap) dst[pos] = make_float2(s, __int_as_float(t0 + i));
         ++pos;
       }
@@ -279,7 +325,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int krem, int* 
   }
 }
 
-template <typename KT, int D>
+template <typename KT, int D, int NT>
 __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int L_mid, int K,
                                int32_t* io, float* so, float inv_sqrt_d, uint32_t* hist,
                                int* s_misc, int* s_buf) {
@@ -287,9 +333,9 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
   uint32_t P[5] = {0u, 0u, 0u, 0u, 0u};
   int krem = K, nd = 0;
   for (int p = 0; p < 20; ++p) {
-    hist[tid] = 0u;
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int i = tid; i < L_mid; i += 256) {
+    for (int i = tid; i < L_mid; i += NT) {
       uint32_t w[5];
       float s32;
       fb_key<KT, D>(qf, kunit, n_sink, i, w, s32);
@@ -306,7 +352,7 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
     if (cnt == krem) break;  // every key with this prefix is selected
   }
   // ordered compaction: selected iff the first nd digits are >= P
-  const int per = (L_mid + 255) / 256;
+  const int per = (L_mid + NT - 1) / NT;
   const int i0 = min(L_mid, tid * per), i1 = min(L_mid, i0 + per);
   int cnt = 0;
   for (int i = i0; i < i1; ++i) {
@@ -316,7 +362,7 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
     cnt += fb_cmp(w, P, nd) >= 0;
   }
   int total;
-  int pos = block_excl_scan256(cnt, s_buf, total);
+  int pos = block_excl_scan<NT>(cnt, s_buf, total);
   for (int i = i0; i < i1; ++i) {
     uint32_t w[5];
     float s32;
@@ -329,13 +375,15 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
 }
 
 template <typename KT, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kSelThreads)
 topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb, int64_t ustride,
                    int n_sink, int L_mid, int ch, int n_chunks, int r_cap, int K, int e_max,
                    const float4* __restrict__ hpw, const float2* __restrict__ ent,
                    const int2* __restrict__ meta, int32_t* __restrict__ idx_out,
                    float* __restrict__ sc_out, float inv_sqrt_d) {
   constexpr int NBS = kSelBins;
+  constexpr int NT = kSelThreads, NWV = NT / kWave;
+  static_assert(NBS % NT == 0, "whole bins per thread");
   constexpr int SELF = 1 << 30;                // "selected" mark on a band member's position
   extern __shared__ __align__(16) float dyn[];
   float* es = dyn;                             // union scores (fp32, unscaled)
@@ -346,7 +394,8 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   __shared__ uint32_t hist[NBS];
   __shared__ int s_buf[257];
   __shared__ int s_misc[8];
-  __shared__ float s_fl[8];
+  __shared__ float s_fl[2 * NWV];
+  __shared__ int s_wred[NWV];
   __shared__ DD s_bdd[kSelBandMax];
   __shared__ int s_bidx[kSelBandMax];
   __shared__ float s_qf[128];
@@ -373,17 +422,19 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     s_nrep[tid] = mm.y;
   }
   int nE;
-  const int off_c = block_excl_scan256(w_c, s_buf, nE);
+  const int off_c = block_excl_scan<NT>(w_c, s_buf, nE);
   if (tid < n_chunks) s_off[tid] = off_c;
   if (tid == 0) s_off[n_chunks] = nE;
   trunc = __syncthreads_or(trunc);
   int wmax = (int)wave_max_dpp((float)w_c);
-  if (lane == 0) s_buf[8 + wave] = wmax;
+  if (lane == 0) s_wred[wave] = wmax;
   __syncthreads();
-  wmax = max(max(s_buf[8], s_buf[9]), max(s_buf[10], s_buf[11]));
+  wmax = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) wmax = max(wmax, s_wred[w]);
 
   if (K == L_mid) {  // every mid token is selected; the chunks reported all of them in order
-    for (int i = tid; i < n_chunks * wmax; i += 256) {
+    for (int i = tid; i < n_chunks * wmax; i += NT) {
       const int c = i / wmax, j = i - c * wmax;
       if (j < s_off[c + 1] - s_off[c]) {
         const float2 e = en[(size_t)c * r_cap + j];
@@ -402,12 +453,12 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     // gather the union: slot (chunk c, j < wmax) of the padded report layout;
     // eight loads per thread are issued before any is consumed
     const int nslots = n_chunks * wmax;
-    for (int i0 = 0; i0 < nslots; i0 += 8 * 256) {
+    for (int i0 = 0; i0 < nslots; i0 += 8 * NT) {
       float2 e[8];
       int dst[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k * 256 + tid;
+        const int i = i0 + k * NT + tid;
         const int c = i / wmax, j = i - c * wmax;
         dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
         if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
@@ -423,33 +474,38 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     __syncthreads();
     // range of the union, then a linear histogram over it
     float lo = INFINITY, hi = -INFINITY;
-    for (int i = tid; i < nE; i += 256) { lo = fminf(lo, es[i]); hi = fmaxf(hi, es[i]); }
+    for (int i = tid; i < nE; i += NT) { lo = fminf(lo, es[i]); hi = fmaxf(hi, es[i]); }
     lo = wave_min_dpp(lo);
     hi = wave_max_dpp(hi);
-    if (lane == 0) { s_fl[wave] = lo; s_fl[4 + wave] = hi; }
-    for (int b = tid; b < NBS; b += 256) hist[b] = 0u;
+    if (lane == 0) { s_fl[wave] = lo; s_fl[NWV + wave] = hi; }
+    for (int b = tid; b < NBS; b += NT) hist[b] = 0u;
     __syncthreads();
-    lo = fminf(fminf(s_fl[0], s_fl[1]), fminf(s_fl[2], s_fl[3]));
-    hi = fmaxf(fmaxf(s_fl[4], s_fl[5]), fmaxf(s_fl[6], s_fl[7]));
+    lo = INFINITY;
+    hi = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) { lo = fminf(lo, s_fl[w]); hi = fmaxf(hi, s_fl[NWV + w]); }
     const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
     auto ubin = [&](float x) {
       const float t = __fmul_rn(__fsub_rn(x, lo), inv);
       return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
     };
-    for (int i = tid; i < nE; i += 256) atomicAdd(&hist[ubin(es[i])], 1u);
+    for (int i = tid; i < nE; i += NT) atomicAdd(&hist[ubin(es[i])], 1u);
     __syncthreads();
-    // bin of the K-th largest score: thread t owns bins NBS-4t-1 .. NBS-4t-4 (descending)
+    // bin of the K-th largest score: thread t owns bins NBS-BPT*t-1 .. NBS-BPT*(t+1)
+    // (descending)
     {
-      int c4[4], ls = 0;
+      constexpr int BPT = NBS / NT;
+      int cb[BPT], ls = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c4[j] = (int)hist[NBS - 4 * tid - 1 - j]; ls += c4[j]; }
+      for (int j = 0; j < BPT; ++j) { cb[j] = (int)hist[NBS - BPT * tid - 1 - j]; ls += cb[j]; }
       int tot;
-      const int ex = block_excl_scan256(ls, s_buf, tot);
+      const int ex = block_excl_scan<NT>(ls, s_buf, tot);
       if (ex < K && ex + ls >= K) {
         int run = ex;
-        for (int j = 0; j < 4; ++j) {
-          if (run + c4[j] >= K) { s_misc[0] = NBS - 4 * tid - 1 - j; break; }
-          run += c4[j];
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+          if (run < K && run + cb[j] >= K) s_misc[0] = NBS - BPT * tid - 1 - j;
+          run += cb[j];
         }
       }
     }
@@ -457,21 +513,23 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     const int bK = s_misc[0];
     // exact extent of that bin: the K-th largest score t lies in [xlo, xhi]
     float xlo = INFINITY, xhi = -INFINITY;
-    for (int i = tid; i < nE; i += 256)
+    for (int i = tid; i < nE; i += NT)
       if (ubin(es[i]) == bK) { xlo = fminf(xlo, es[i]); xhi = fmaxf(xhi, es[i]); }
     xlo = wave_min_dpp(xlo);
     xhi = wave_max_dpp(xhi);
     __syncthreads();
-    if (lane == 0) { s_fl[wave] = xlo; s_fl[4 + wave] = xhi; }
+    if (lane == 0) { s_fl[wave] = xlo; s_fl[NWV + wave] = xhi; }
     __syncthreads();
-    xlo = fminf(fminf(s_fl[0], s_fl[1]), fminf(s_fl[2], s_fl[3]));
-    xhi = fmaxf(fmaxf(s_fl[4], s_fl[5]), fmaxf(s_fl[6], s_fl[7]));
+    xlo = INFINITY;
+    xhi = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) { xlo = fminf(xlo, s_fl[w]); xhi = fmaxf(xhi, s_fl[NWV + w]); }
     th_lo = xlo - 2.5f * hp.eps;
     th_hi = xhi + 2.5f * hp.eps;
     // every chunk must have reported all of its tokens scoring >= th_lo
     const int blo = lin_bin(th_lo, hp);
     int bad = 0;
-    for (int c = tid; c < n_chunks; c += 256) {
+    for (int c = tid; c < n_chunks; c += NT) {
       const int n_c = min(ch, L_mid - c * ch);
       if (s_nrep[c] != n_c && s_bcs[c] > blo) bad = 1;
     }
@@ -479,7 +537,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     fallback = __syncthreads_or(bad) != 0;
     if (!fallback) {
       int nin = 0;
-      for (int i0 = 0; i0 < nE; i0 += 256) {
+      for (int i0 = 0; i0 < nE; i0 += NT) {
         const int i = i0 + tid;
         const float sc = i < nE ? es[i] : -INFINITY;
         nin += __popcll(__ballot(sc > th_hi));
@@ -500,13 +558,13 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   }
   if (!fallback) {
     // band: exact double-double scores when it must be split
-    for (int b = tid; b < n_band; b += 256) {
+    for (int b = tid; b < n_band; b += NT) {
       const int i = s_bidx[b];
       s_bdd[b] = (n_band > kp) ? dd_dot<KT, D>(s_qf, kunit + (size_t)(n_sink + ep[i]) * D) : DD{0.0, 0.0};
     }
     __syncthreads();
     // rank by (exact score desc, position asc); mark the winners' positions
-    for (int b = tid; b < n_band; b += 256) {
+    for (int b = tid; b < n_band; b += NT) {
       const int i = s_bidx[b];
       bool take = true;
       if (n_band > kp) {
@@ -519,16 +577,16 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
       hist[b] = take ? 1u : 0u;  // the histogram is no longer needed
     }
     __syncthreads();
-    for (int b = tid; b < n_band; b += 256)
+    for (int b = tid; b < n_band; b += NT)
       if (hist[b] != 0u) ep[s_bidx[b]] |= SELF;
     __syncthreads();
     // ordered compaction of the selected entries in position order
-    const int per = (nE + 255) / 256;
+    const int per = (nE + NT - 1) / NT;
     const int i0 = min(nE, tid * per), i1 = min(nE, i0 + per);
     int cnt = 0;
     for (int i = i0; i < i1; ++i) cnt += (es[i] > th_hi) || (ep[i] & SELF);
     int total;
-    int pos = block_excl_scan256(cnt, s_buf, total);
+    int pos = block_excl_scan<NT>(cnt, s_buf, total);
     if (total != K) {
       fallback = true;  // uniform: every thread sees the same total
     } else {
@@ -545,7 +603,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   }
   if (fallback) {
     __syncthreads();
-    exact_fallback<KT, D>(s_qf, kunit, n_sink, L_mid, K, io, so, inv_sqrt_d, hist, s_misc, s_buf);
+    exact_fallback<KT, D, NT>(s_qf, kunit, n_sink, L_mid, K, io, so, inv_sqrt_d, hist, s_misc, s_buf);
   }
 }
 
@@ -592,7 +650,7 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
   int e_max = pl.e_max;
   if (g_lds_limit > static_lds) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - static_lds) / 8);
   const size_t lds = (size_t)std::max(e_max, 1) * 8;
-  hipLaunchKernelGGL((topk_select_kernel<KT, D>), dim3(kv.n_units * G), dim3(256), lds, st, q, G,
+  hipLaunchKernelGGL((topk_select_kernel<KT, D>), dim3(kv.n_units * G), dim3(kSelThreads), lds, st, q, G,
                      kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
                      hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
   e = hipGetLastError();
