@@ -13,8 +13,8 @@
 //   N = sum e^{s_i - m} v_i,  Z = sum e^{s_i - m},
 //   w_i = f.Phi_K[i],  nuK = sum_{K(q)} w_i v_i,  ZK = sum_{K(q)} w_i.
 // The group partials are combined with max rescaling (fixed order) into m*,
-// N_E, Z_E.  phi(q)^T S comes from fp32 MFMA (v_mfma_f32_16x16x4f32) over the
-// unit's query heads while the first index loads are in flight; then the
+// N_E, Z_E.  phi(q)^T S is a matrix-vector product per head (fp32 VALU; its
+// loads are issued before the gathers and consumed after them); then the
 // subtraction, the clamp and one normalisation.
 #include "rma_device.hpp"
 #include "rma_internal.hpp"
@@ -22,8 +22,6 @@
 #include <math.h>
 
 namespace rma {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // N elements of type T as raw 16-byte words: loaded early, unpacked at use.
 template <typename T, int N>
@@ -73,7 +71,8 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   constexpr int FPL = M / LPE;      // phi features per lane
   constexpr int CH = kMergeChunk;   // entries staged in LDS at a time
   constexpr int SPT = CH / NT;      // staged entries per thread
-  constexpr int B = (sizeof(KT) == 2) ? 4 : 2;  // entries per group whose loads are in flight together
+  // entries per group whose loads are in flight together (bounded by registers)
+  constexpr int B = (sizeof(KT) == 4 || (sizeof(PT) == 4 && D == 128)) ? 2 : 4;
   const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
@@ -87,7 +86,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   __shared__ float s_sc[CH];
   __shared__ float s_wn[NW][D], s_wk[NW][D];
   __shared__ float s_wm[NW], s_wz[NW], s_wzk[NW];
-  __shared__ float s_fs[D];
+  __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
 
   const KT* kunit = kb + (size_t)u * ustride;
@@ -148,36 +147,36 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     for (int i = 0; i < FPL; ++i) fr[i] = 0.f;
   }
 
-  // ---- phi(q)^T S and u^T f for this unit's heads (fp32 MFMA 16x16x4; rows =
-  //      the G query heads zero-padded to 16, k = features, columns = d)
-  if (resid && !whole_mid) {
-    const float* Su = S + (size_t)u * M * D;
-    const int row = lane & 15, kq = lane >> 4;
-    for (int ct = wave; ct < D / 16; ct += NW) {
-      float av[M / 4], bv[M / 4];
-      const float* fq = phi_q + ((size_t)u * G + min(row, G - 1)) * M;  // rows >= G are zero
+  // ---- operands of phi(q)^T S and u^T f, loaded now and used after the
+  //      entries, so that their latency overlaps the gathers.  For one head
+  //      this is a matrix-vector product: thread (column col, feature block fb)
+  //      loads its FPB elements of S once (coalesced along the columns).
+  //      Without a residual the loads read q instead and are discarded.
+  const bool rs = resid && !whole_mid;
+  constexpr int FB = NT / D;          // feature blocks
+  constexpr int FPB = M / FB;         // features per block
+  const int scol = tid % D, fb = tid / D;
+  float sv[FPB], fv[FPB];
+  {
+    const float* Sp = rs ? S + (size_t)u * M * D + (size_t)fb * FPB * D + scol : qg;
+    const size_t sst = rs ? D : 0;
 #pragma unroll
-      for (int ks = 0; ks < M / 4; ++ks) {
-        const int f = 4 * ks + kq;
-        av[ks] = fq[f];
-        bv[ks] = Su[(size_t)f * D + 16 * ct + row];
-      }
+    for (int i = 0; i < FPB; ++i) sv[i] = Sp[sst * i];
+    // fb is the same for a whole wave: the f slice is a scalar (SGPR) load
+    const float* fp = rs ? phi_q + (size_t)ug * M + __builtin_amdgcn_readfirstlane(fb) * FPB : qg;
 #pragma unroll
-      for (int ks = 0; ks < M / 4; ++ks) av[ks] = row < G ? av[ks] : 0.f;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < M / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
-      // lane holds rows 4*kq + r of column 16*ct + row; keep this block's head
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * kq + r == g) s_fs[16 * ct + row] = acc[r];
+    for (int i = 0; i < FPB; i += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(fp + (rs ? i : 0));
+      fv[i] = t.x; fv[i + 1] = t.y; fv[i + 2] = t.z; fv[i + 3] = t.w;
     }
-    if (wave == NW - 1) {
-      float p = 0.f;
-      for (int f = lane; f < M; f += kWave) p = __fmaf_rn(u_[(size_t)u * M + f], phi_q[(size_t)ug * M + f], p);
-      p = wave_sum_dpp(p);
-      if (lane == 0) s_uf = p;
-    }
+  }
+  constexpr int UPL = (M + kWave - 1) / kWave;   // u^T f terms per lane (last wave)
+  float uu[UPL], uf[UPL];
+#pragma unroll
+  for (int i = 0; i < UPL; ++i) {
+    const int f = min(lane + kWave * i, M - 1);
+    uu[i] = rs ? u_[(size_t)u * M + f] : 0.f;
+    uf[i] = rs ? phi_q[(size_t)ug * M + f] : 0.f;
   }
 
   float N[CPL], NK[CPL];
@@ -254,6 +253,22 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     }
   }
 
+  // ---- phi(q)^T S (per feature block) and u^T f
+  if (rs) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < FPB; ++i) p = __fmaf_rn(fv[i], sv[i], p);
+    s_part[fb][scol] = p;
+    if (wave == NW - 1) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < UPL; ++i)
+        if (lane + kWave * i < M) t = __fmaf_rn(uu[i], uf[i], t);
+      t = wave_sum_dpp(t);
+      if (lane == 0) s_uf = t;
+    }
+  }
+
   // ---- combine the eight groups of each wave (lanes l, l^8, l^16, l^32 hold the
   //      same columns), then the waves through LDS, rescaling to the larger max
 #pragma unroll
@@ -312,7 +327,12 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
       NKc += s_wk[w][col];
     }
     float nu = 0.f;
-    if (resid && !whole_mid) nu = s_fs[col] - (sub ? NKc : 0.f);
+    if (rs) {
+      float fs = 0.f;
+#pragma unroll
+      for (int k = 0; k < FB; ++k) fs += s_part[k][col];
+      nu = fs - (sub ? NKc : 0.f);
+    }
     y[(size_t)ug * D + col] = (a * NE + bres * nu) / den;
   }
   if (stats != nullptr && tid == 0) {

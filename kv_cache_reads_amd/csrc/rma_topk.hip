@@ -147,18 +147,15 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 
   const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D + part * E;
   constexpr int STEP = TPP * UNR;
+  // rows past the chunk end re-read its last row (unconditional loads keep the
+  // load counter exact); their scores are never stored
   auto load = [&](uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
-      const int t = p0 + i * TPP + wave * TPW + slot;
-      if (t < n) {
-        const uint4* src = reinterpret_cast<const uint4*>(kp + (size_t)t * D);
+      const int t = min(p0 + i * TPP + wave * TPW + slot, n - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(kp + (size_t)t * D);
 #pragma unroll
-        for (int pc = 0; pc < PIECES; ++pc) raw[i][pc] = ld_stream16(src + pc);
-      } else {
-#pragma unroll
-        for (int pc = 0; pc < PIECES; ++pc) raw[i][pc] = make_uint4(0, 0, 0, 0);
-      }
+      for (int pc = 0; pc < PIECES; ++pc) raw[i][pc] = ld_stream16(src + pc);
     }
   };
   // two register buffers in turn, both in flight while the head parameters are derived
