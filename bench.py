@@ -2,7 +2,7 @@
 """Benchmark of the Top-K+phi residual-mass-accounting path on one MI355X.
 
 One step = one pass of the whole path over one batch of the workload:
-prefill summaries (phi_k rows, S, u; rma_build_summaries), then for every
+prefill summaries (S, u; rma_build_summaries), then for every
 decode step of the workload phi_q (rma_phi_features), the exhaustive Top-K
 (rma_decode_topk) and the exact branch + subtraction + residual + single
 normalisation (rma_decode_merge).  Default workload: the 1B-shaped GQA layer at
@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute-phi", action="store_true",
+                    help="do not store the phi_k rows at prefill; the merge recomputes the retrieved "
+                         "rows from their keys (bf16 keys; saves the rows' HBM, costs MFMA/VALU work "
+                         "at every decode step)")
     ap.add_argument("--copy-probe-mb", type=float, default=0.0,
                     help="first run a plain fp32 copy-like kernel (neg) of this size, for calibrating "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -83,18 +87,18 @@ def measured_traffic(kernel, workload, K):
 
 
 # ------------------------------------------------------------------ byte model
-def call_bytes(cfg, K, n_gen):
+def call_bytes(cfg, K, n_gen, store_phi=True):
     """Algorithmic HBM bytes of each call for one batch (inputs read once,
     outputs written once; workspace scratch excluded)."""
-    kb = kernel_bytes(cfg, K, n_gen)
+    kb = kernel_bytes(cfg, K, n_gen, store_phi)
     return dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
                 topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"])
 
 
-def kernel_bytes(cfg, K, n_gen):
+def kernel_bytes(cfg, K, n_gen, store_phi=True):
     """Algorithmic HBM bytes of each kernel for one batch.  The builder reads the
-    mid-region K and V rows once and writes phi_k once (its per-chunk partial sums
-    are scratch); the reduce writes S, u, kappa; the scan reads the mid-region K
+    mid-region K and V rows once (and writes phi_k once when the rows are stored;
+    its per-chunk partial sums are scratch); the reduce writes S, u, kappa; the scan reads the mid-region K
     rows once (score bins and candidate lists are scratch); the select writes the
     indices and their scores; the merge reads what one query's exact support and
     residual need."""
@@ -103,14 +107,18 @@ def kernel_bytes(cfg, K, n_gen):
     e = 4 if cfg.kv_dtype == "f32" else 2
     ep = 4 if cfg.phi_dtype == "f32" else 2
     params = P * (m * d * 4 + m * 4)
+    # phi_k rows are either stored by the builder and gathered by the merge
+    # (default), or not stored, the merge recomputing the retrieved ones from
+    # their key rows (which it then reads instead)
+    phi_row = m * ep if store_phi else d * e
     return {
-        "build_mfma_kernel": U * (2 * Lm * d * e + Lm * m * ep) + params,
+        "build_mfma_kernel": U * (2 * Lm * d * e + (Lm * m * ep if store_phi else 0)) + params,
         "build_reduce_kernel": U * (m * d * 4 + m * 4 + 4),
         "phi_kernel": U * G * (d * 4 + m * 4) + params,
         "topk_scan_kernel": U * (Lm * d * e + 4) + U * G * d * 4,
         "topk_select_kernel": U * G * K * 8,
-        "merge_kernel": U * G * (K * (d * e + m * ep + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
-        + U * (m * d * 4 + m * 4),
+        "merge_kernel": U * G * (K * (d * e + phi_row + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
+        + U * (m * d * 4 + m * 4) + (0 if store_phi else params),
     }
 
 
@@ -118,14 +126,15 @@ def kernel_bytes(cfg, K, n_gen):
 class PathRunner:
     """Prepared C-ABI calls for one copy of the inputs (no per-call allocation)."""
 
-    def __init__(self, R, cfg, inp, K, ws, torch):
+    def __init__(self, R, cfg, inp, K, ws, torch, store_phi):
         self.R, self.cfg, self.K, self.t = R, cfg, K, torch
         L = R.lib()
         self.L = L
         dev = inp.k.device
         U, G, d, m = cfg.U, cfg.G, cfg.d, cfg.m
         self.k, self.v, self.q, self.W, self.b = inp.k, inp.v, inp.q, inp.W, inp.b
-        self.phi_k = torch.empty(U, cfg.L_mid, m, dtype=cfg.torch_phi_dtype(), device=dev)
+        # phi_k rows: stored by the builder, or (None) recomputed by the merge
+        self.phi_k = torch.empty(U, cfg.L_mid, m, dtype=cfg.torch_phi_dtype(), device=dev) if store_phi else None
         self.S = torch.empty(U, m, d, dtype=torch.float32, device=dev)
         self.u = torch.empty(U, m, dtype=torch.float32, device=dev)
         self.kappa = torch.empty(U, dtype=torch.float32, device=dev)
@@ -138,9 +147,10 @@ class PathRunner:
         self.sp_dec = [R.Span(cfg.L, cfg.n_sink, cfg.n_tail, cfg.n_gen(s))._c() for s in range(cfg.steps)]
         self.ws = ws
         P = ctypes.c_void_p
-        self.p = lambda t: P(t.data_ptr())
+        self.p = lambda t: None if t is None else P(t.data_ptr())
         self.kdt = R._dt(inp.k.dtype)
-        self.pdt = R._dt(self.phi_k.dtype)
+        self.pdt = R._dt(cfg.torch_phi_dtype())
+        self.Wm, self.bm = (None, None) if store_phi else (inp.W, inp.b)
 
     def build(self, st):
         cfg, p = self.cfg, self.p
@@ -167,8 +177,8 @@ class PathRunner:
         cfg, p = self.cfg, self.p
         r = self.L.rma_decode_merge(p(self.q[s]), p(self.f[s]), cfg.G, ctypes.byref(self.kv),
                                     ctypes.byref(self.sp_dec[s]), p(self.idx[s]), p(self.sel[s]), self.K,
-                                    p(self.phi_k), self.pdt, cfg.m, p(self.S), p(self.u), 0, p(self.y[s]),
-                                    None, p(self.ws), self.ws.numel(), st)
+                                    p(self.phi_k), self.pdt, p(self.Wm), p(self.bm), cfg.P, cfg.m, p(self.S),
+                                    p(self.u), 0, p(self.y[s]), None, p(self.ws), self.ws.numel(), st)
         assert r == 0, r
 
     def step(self, st):
@@ -271,8 +281,9 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
 
+    store_phi = not args.recompute_phi or cfg.kv_dtype != "bf16"   # recomputed rows need bf16 keys
     per_copy = (inp.k.numel() + inp.v.numel()) * inp.k.element_size() + \
-        cfg.U * cfg.L_mid * cfg.m * (4 if cfg.phi_dtype == "f32" else 2)
+        (cfg.U * cfg.L_mid * cfg.m * (4 if cfg.phi_dtype == "f32" else 2) if store_phi else 0)
     n_copies = max(1, math.ceil(args.rotate_bytes / per_copy))
     free = torch.cuda.mem_get_info()[0]
     n_copies = max(1, min(n_copies, int(0.6 * free // max(per_copy, 1))))
@@ -285,7 +296,7 @@ def main():
               R.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, inp.k, sp, cfg.G, K, cfg.m),
               R.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, inp.k, sp, cfg.G, K, cfg.m))
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    runners = [PathRunner(R, cfg, c, K, ws, torch) for c in copies]
+    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi) for c in copies]
     log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
 
     stream = torch.cuda.Stream()
@@ -366,9 +377,9 @@ def main():
     dur = {n: call_ms[n] / n_t for n in names}                       # ms per step
     kavg = {k: kern_ms[k] / kern_n[k] for k in kern_ms}               # ms per launch
     launches = {k: kern_n[k] / n_t for k in kern_n}                  # launches per step
-    nb = call_bytes(cfg, K, cfg.n_gen(0))
-    kb = kernel_bytes(cfg, K, cfg.n_gen(0))
-    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s))[c] for s in range(cfg.steps)
+    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi)
+    kb = kernel_bytes(cfg, K, cfg.n_gen(0), store_phi)
+    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi)[c] for s in range(cfg.steps)
                                    for c in ("phi", "topk", "merge"))
     gbs = {n: nb[n] * (1 if n == "build" else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
     kgbs = {k: kb[k] / (kavg[k] / 1e3) / 1e9 for k in kavg}
@@ -403,6 +414,7 @@ def main():
             "anchors": [cfg.n_sink, cfg.n_tail], "K": K, "phi_features": cfg.m,
             "decode_steps": cfg.steps, "queries_per_step": queries,
             "step": "prefill summaries + phi_q + top-K + merge",
+            "phi_k_rows": "stored" if store_phi else "recomputed at decode (not stored)",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
             "rotating_copies": n_copies, "launch": "hip_graph" if graphs is not None else "eager",
             "step_algorithmic_MB": round(step_bytes / 1e6, 3),

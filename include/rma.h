@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 1
+#define RMA_ABI_VERSION 2
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -131,9 +131,13 @@ rma_status rma_phi_features(const void* x, int32_t x_dtype, int32_t n_units, int
  * If Wk != NULL, phi_k rows are computed (elu(Wk[p] k + bk[p]) + 1), rounded
  * to phi_dtype and written to phi_k; S and u are formed from the rounded rows
  * so that the rows later subtracted at decode are exactly those summed here.
+ * With Wk != NULL, bf16 keys/values and phi_dtype RMA_BF16, phi_k may be NULL:
+ * the rows are then not stored, and rma_decode_merge recomputes the retrieved
+ * ones bit for bit from their keys (the same projection and rounding).
  * If Wk == NULL (bk ignored), phi_k is an INPUT holding the rows (any positive
  * features, e.g. for an ideal-factorisation check) and is only read.
- * phi_k: [n_units][L_mid][m] of phi_dtype, dense.  S, u_, kappa overwritten.
+ * phi_k: NULL or [n_units][L_mid][m] of phi_dtype, dense.  S, u_, kappa
+ * overwritten.
  * Needs L_mid >= 0 (L_mid == 0 gives S = u = 0, kappa = 0).
  * Workspace: rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ...).
  */
@@ -176,7 +180,12 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
  * q: fp32 [n_units][G][d];  phi_q: fp32 [n_units][G][m] (any positive
  * features; rma_phi_features gives phi_q).  idx, sel_scores as written by
  * rma_decode_topk (K per head).  phi_k, S, u_ as written/used by
- * rma_build_summaries.
+ * rma_build_summaries.  When the subtraction needs Phi_K rows (RMA_MERGE_SUB,
+ * 0 < K < L_mid) and phi_k is NULL, they are recomputed from the retrieved
+ * keys with Wk, bk (fp32 [n_param_sets][m][d], [n_param_sets][m]; unit u uses
+ * set u % n_param_sets) exactly as rma_build_summaries computed the summed
+ * rows: bf16 keys and phi_dtype RMA_BF16 only (else RMA_ERR_UNSUPPORTED).
+ * Wk, bk are ignored when phi_k is given.
  * flags: RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL (selection-only Top-K) or
  *        RMA_MERGE_NO_SUBTRACT (NoSub).
  * y: fp32 [n_units][G][d].  stats: NULL or fp32 [n_units][G][4] =
@@ -186,9 +195,10 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
  */
 rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
                             const rma_span* span, const int32_t* idx, const float* sel_scores,
-                            int32_t K, const void* phi_k, int32_t phi_dtype, int32_t m,
-                            const float* S, const float* u_, uint32_t flags, float* y,
-                            float* stats, void* workspace, size_t workspace_bytes, void* stream);
+                            int32_t K, const void* phi_k, int32_t phi_dtype, const float* Wk,
+                            const float* bk, int32_t n_param_sets, int32_t m, const float* S,
+                            const float* u_, uint32_t flags, float* y, float* stats,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes for `op` (one of RMA_OP_*); 0 on invalid arguments.  G and K
  * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK. */

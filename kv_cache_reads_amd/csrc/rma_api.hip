@@ -274,7 +274,11 @@ rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float
   RMA_CHECK(P >= 1, RMA_ERR_INVALID_ARG, "n_param_sets must be >= 1");
   RMA_CHECK(Wk == nullptr || bk != nullptr, RMA_ERR_INVALID_ARG, "bk is NULL");
   RMA_CHECK(S && u && kappa, RMA_ERR_INVALID_ARG, "NULL output pointer");
-  RMA_CHECK(phi_k != nullptr || l_mid(*sp) == 0, RMA_ERR_INVALID_ARG, "phi_k is NULL");
+  // phi_k may be NULL only when the MFMA builder computes the features (the rows
+  // are then not stored; decode recomputes the retrieved ones)
+  RMA_CHECK(phi_k != nullptr || l_mid(*sp) == 0 ||
+                (Wk != nullptr && kv->dtype == RMA_BF16 && phi_dtype == RMA_BF16),
+            RMA_ERR_INVALID_ARG, "phi_k is NULL (allowed only for bf16 keys with Wk given)");
   RMA_CHECK(aligned16(S) && aligned16(u) && aligned16(kappa) && aligned16(phi_k) &&
                 aligned16(Wk) && aligned16(bk),
             RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
@@ -318,7 +322,8 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
 
 rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
                             const rma_span* sp, const int32_t* idx, const float* sel, int32_t K,
-                            const void* phi_k, int32_t phi_dtype, int32_t m, const float* S,
+                            const void* phi_k, int32_t phi_dtype, const float* Wk,
+                            const float* bk, int32_t P, int32_t m, const float* S,
                             const float* u, uint32_t flags, float* y, float* stats,
                             void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
@@ -337,10 +342,14 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
   RMA_CHECK(q && y, RMA_ERR_INVALID_ARG, "NULL q or y");
   RMA_CHECK(K == 0 || (idx && sel), RMA_ERR_INVALID_ARG, "NULL idx or sel_scores");
   RMA_CHECK(!need_res || (phi_q && S && u), RMA_ERR_INVALID_ARG, "NULL phi_q, S or u");
-  RMA_CHECK(!need_res || K == 0 || phi_k, RMA_ERR_INVALID_ARG, "NULL phi_k");
+  const bool need_phik = flags == RMA_MERGE_SUB && K > 0 && K < l_mid(*sp);
+  RMA_CHECK(!need_phik || phi_k != nullptr || (Wk != nullptr && bk != nullptr && P >= 1),
+            RMA_ERR_INVALID_ARG, "NULL phi_k and no Wk/bk to recompute it");
+  RMA_CHECK(!need_phik || phi_k != nullptr || (kv->dtype == RMA_BF16 && phi_dtype == RMA_BF16),
+            RMA_ERR_UNSUPPORTED, "recomputed phi_k rows need bf16 keys and bf16 phi rounding");
   RMA_CHECK(aligned16(q) && aligned16(phi_q) && aligned16(idx) && aligned16(sel) &&
-                aligned16(phi_k) && aligned16(S) && aligned16(u) && aligned16(y) &&
-                aligned16(stats),
+                aligned16(phi_k) && aligned16(Wk) && aligned16(bk) && aligned16(S) &&
+                aligned16(u) && aligned16(y) && aligned16(stats),
             RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   MergePlan pl = plan_merge(*kv, *sp, G, K, m);
   RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
@@ -348,8 +357,10 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
   RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
             workspace_bytes, pl.total);
   TraceScope ts((hipStream_t)stream);
-  hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype, m, S, u,
-                              flags, y, stats, (uint8_t*)workspace, (hipStream_t)stream);
+  // stored rows take precedence; the recompute runs only when they are absent
+  hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype,
+                              phi_k ? nullptr : Wk, bk, P, m, S, u, flags, y, stats,
+                              (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return RMA_OK;
 }

@@ -2,7 +2,9 @@
 // for Partial-KV Decoding": §1 and §4.1, summaries S = sum phi_k(k_i) v_i^T and
 // u = sum phi_k(k_i) over the mid-region; App. C.1 for the positive map).
 //
-// build_mfma  (bf16 K/V, bf16 phi rows, computed phi)  grid (chunks, units),
+// build_mfma  (bf16 K/V, bf16 phi rows, computed phi)  grid (chunks, units); with
+//   STORE false the phi rows are not written (decode recomputes the retrieved
+//   ones with this same instruction sequence),
 //   m/16 waves (one 16-feature tile each), 64-token tiles through LDS:
 //     Z = K_tile W^T        v_mfma_f32_16x16x32_bf16; W is split into bf16
 //                           hi + lo parts (K is exactly bf16), so Z carries
@@ -26,26 +28,14 @@
 
 namespace rma {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // upper bound of sqrt(x) for a sum of squares computed in fp32 over <= 128 terms (its
 // rounding is below 128 * 2^-24 relative; the factor covers that and the root's)
 __device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) * (1.0f + 1e-5f); }
 
 // ====================================================================== MFMA builder
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
-
-template <int D, int M>
-__global__ void __launch_bounds__(M * 4) 
+template <int D, int M, bool STORE>
+__global__ void __launch_bounds__(M * 4)
 build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
                   int n_sink, int L_mid, int ch, int n_chunks, const float* __restrict__ W,
                   const float* __restrict__ bias, int P, uint16_t* __restrict__ phik,
@@ -69,7 +59,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
 
   __shared__ __align__(16) uint16_t Ks[TT * KROW];
   __shared__ __align__(16) uint16_t Vs[TT * VROW];
-  __shared__ __align__(16) uint16_t Ps[TT * PROW];
+  __shared__ __align__(16) uint16_t Ps[STORE ? TT * PROW : 8];
   __shared__ float s_kap[NW];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -79,26 +69,13 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const int n = min(ch, L_mid - t0);
   const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
-  uint16_t* php = phik + ((size_t)u * L_mid + t0) * M;
+  uint16_t* php = STORE ? phik + ((size_t)u * L_mid + t0) * M : nullptr;
   const int f = wave * 16 + l16;          // this lane's feature in step 1
   const float bf = bias[(size_t)p * M + f];
 
   // W (fp32) -> bf16 hi + lo B-operands of this wave's feature tile
   bf16x8_t Whi[KS], Wlo[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const float* wr = W + ((size_t)p * M + f) * D + 32 * ks + 8 * g4;
-    u16x8_t hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float w = wr[e];
-      const uint32_t hb = f32_to_bf16_bits(w);
-      hi[e] = (unsigned short)hb;
-      lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
-    }
-    Whi[ks] = as_bf16x8(hi);
-    Wlo[ks] = as_bf16x8(lo);
-  }
+  split_w_operands<KS>(W + ((size_t)p * M + f) * D + 8 * g4, Whi, Wlo);
   u16x8_t ones_v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones_v[e] = 0x3F80;  // bf16 1.0: u = Phi^T 1 on the MFMA
@@ -171,13 +148,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     uint32_t phv[NTT][2];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t A = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Ks + (tt * 16 + l16) * KROW + 32 * ks + 8 * g4));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Whi[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Wlo[ks], acc, 0, 0, 0);
-      }
+      const f32x4 acc = proj_tile16<KS>(Ks + (tt * 16 + l16) * KROW + 8 * g4, Whi, Wlo);
       float ph[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -187,11 +158,13 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       const uint32_t p01 = pack_bf16x2(ph[0], ph[1]), p23 = pack_bf16x2(ph[2], ph[3]);
       phv[tt][0] = p01;
       phv[tt][1] = p23;
-      const int row0 = tt * 16 + 4 * g4;
-      Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
-      Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
-      Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
-      Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
+      if constexpr (STORE) {
+        const int row0 = tt * 16 + 4 * g4;
+        Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
+        Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
+        Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
+        Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
+      }
     }
     // step 2: S += Phi^T V, u += Phi^T 1 over 32-token blocks.  Hardware k-slot e
     // of lane group g4 is token 32*kb + 4*g4 + e (e < 4) or 32*kb + 16 + 4*g4 +
@@ -210,17 +183,19 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         Sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bv, Sacc[ct], 0, 0, 0);
       }
     }
-    __syncthreads();
-    // store the Phi tile rows (16-byte pieces, coalesced; rows are 8-byte aligned in LDS)
-    constexpr int PCR = M / 8;
+    if constexpr (STORE) {
+      __syncthreads();
+      // store the Phi tile rows (16-byte pieces, coalesced; rows are 8-byte aligned in LDS)
+      constexpr int PCR = M / 8;
 #pragma unroll
-    for (int j = 0; j < (TT * PCR + NT - 1) / NT; ++j) {
-      const int chunk = tid + NT * j;
-      const int row = chunk / PCR, cc = chunk % PCR;
-      if (chunk < TT * PCR && (FULL || tok0 + row < n)) {
-        const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
-        const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
-        *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) = make_uint4(a.x, a.y, b.x, b.y);
+      for (int j = 0; j < (TT * PCR + NT - 1) / NT; ++j) {
+        const int chunk = tid + NT * j;
+        const int row = chunk / PCR, cc = chunk % PCR;
+        if (chunk < TT * PCR && (FULL || tok0 + row < n)) {
+          const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
+          const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
+          *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) = make_uint4(a.x, a.y, b.x, b.y);
+        }
       }
     }
   };
@@ -472,9 +447,17 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
       const uint16_t* kk = static_cast<const uint16_t*>(kv.k);
       const uint16_t* vv = static_cast<const uint16_t*>(kv.v);
       uint16_t* ph = static_cast<uint16_t*>(phi_k);
-#define RMA_BM(DD, MM)                                                                        \
-  hipLaunchKernelGGL((build_mfma_kernel<DD, MM>), grid, dim3(MM * 4), 0, st, kk, vv,            \
-                     kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph, pS, pu, pk)
+#define RMA_BM(DD, MM)                                                                         \
+  do {                                                                                         \
+    if (ph != nullptr)                                                                         \
+      hipLaunchKernelGGL((build_mfma_kernel<DD, MM, true>), grid, dim3(MM * 4), 0, st, kk, vv, \
+                         kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph,    \
+                         pS, pu, pk);                                                          \
+    else                                                                                       \
+      hipLaunchKernelGGL((build_mfma_kernel<DD, MM, false>), grid, dim3(MM * 4), 0, st, kk,    \
+                         vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P,    \
+                         ph, pS, pu, pk);                                                      \
+  } while (0)
       if (kv.d == 64 && m == 64) RMA_BM(64, 64);
       else if (kv.d == 64) RMA_BM(64, 128);
       else if (m == 64) RMA_BM(128, 64);

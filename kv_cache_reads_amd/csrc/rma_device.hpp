@@ -257,4 +257,57 @@ __device__ __forceinline__ void st_elem(uint16_t* p, size_t i, float v) {
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float phi_elu1(float z) { return z > 0.f ? z + 1.f : __expf(z); }
 
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32); the
+// summary builder and the decode recompute of phi_k rows both round with this
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// ---- the phi projection on the MFMA, shared by the summary builder and the
+// decode recompute of retrieved phi_k rows (same operands, same instruction
+// order, so both produce the same bits)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// B operands of one 16-feature tile for lane group g4: W (fp32) split into bf16
+// hi + lo parts (w = hi + lo + O(2^-17 |w|)).  `wrow` points at W[feature][8*g4].
+template <int KS>
+__device__ __forceinline__ void split_w_operands(const float* wrow, bf16x8_t (&Whi)[KS],
+                                                 bf16x8_t (&Wlo)[KS]) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float* wr = wrow + 32 * ks;
+    u16x8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = wr[e];
+      const uint32_t hb = f32_to_bf16_bits(w);
+      hi[e] = (unsigned short)hb;
+      lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
+    }
+    Whi[ks] = as_bf16x8(hi);
+    Wlo[ks] = as_bf16x8(lo);
+  }
+}
+
+// Z = K W^T for 16 key rows x 16 features (v_mfma_f32_16x16x32_bf16).  `arow`
+// points at the lane's key row (l%16 of the tile) at column 8*g4; the result
+// holds rows 4*g4 .. 4*g4+3 of feature column l%16.
+template <int KS>
+__device__ __forceinline__ f32x4 proj_tile16(const uint16_t* arow, const bf16x8_t (&Whi)[KS],
+                                             const bf16x8_t (&Wlo)[KS]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8_t A = as_bf16x8(*reinterpret_cast<const u16x8_t*>(arow + 32 * ks));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Whi[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Wlo[ks], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 }  // namespace rma

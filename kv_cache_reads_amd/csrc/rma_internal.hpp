@@ -94,8 +94,9 @@ hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& 
 
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,
                         const rma_kv& kv, const rma_span& sp, const int32_t* idx,
-                        const float* sel, int K, const void* phi_k, int phi_dtype, int m,
-                        const float* S, const float* u, uint32_t flags, float* y, float* stats,
-                        uint8_t* ws, hipStream_t st);
+                        const float* sel, int K, const void* phi_k, int phi_dtype,
+                        const float* Wk, const float* bk, int P, int m, const float* S,
+                        const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
+                        hipStream_t st);
 
 }  // namespace rma

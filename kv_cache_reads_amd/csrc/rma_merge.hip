@@ -56,14 +56,20 @@ struct RawPiece {
   }
 };
 
-template <typename KT, typename PT, int D, int M>
+// RECOMP: phi_k rows are not stored; the retrieved tokens' rows are recomputed
+// from their keys with the summary builder's projection (same operands, same
+// MFMA order, same bf16 rounding), so the subtraction removes exactly what the
+// summaries contain.  Needs bf16 keys.
+template <typename KT, typename PT, int D, int M, bool RECOMP>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G,
              const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int L,
              int n_sink, int n_tail, int n_gen, const int32_t* __restrict__ idx,
              const float* __restrict__ sel, int K, const PT* __restrict__ phik, int L_mid,
+             const float* __restrict__ Wk, const float* __restrict__ bk, int P,
              const float* __restrict__ S, const float* __restrict__ u_, uint32_t flags,
              float* __restrict__ y, float* __restrict__ stats, float inv_sqrt_d) {
+  static_assert(!RECOMP || sizeof(KT) == 2, "recomputed phi rows need bf16 keys");
   constexpr int NT = kMergeThreads, NW = NT / kWave;
   constexpr int LPE = 8;            // lanes per entry
   constexpr int NGR = NT / LPE;     // entry groups
@@ -72,7 +78,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   constexpr int CH = kMergeChunk;   // entries staged in LDS at a time
   constexpr int SPT = CH / NT;      // staged entries per thread
   // entries per group whose loads are in flight together (bounded by registers)
-  constexpr int B = (sizeof(KT) == 4 || (sizeof(PT) == 4 && D == 128)) ? 2 : 4;
+  constexpr int B = (sizeof(KT) == 4 || (sizeof(PT) == 4 && D == 128)) ? 2 : ((RECOMP && D == 128) ? 3 : 4);
   const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
@@ -88,6 +94,14 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   __shared__ float s_wm[NW], s_wz[NW], s_wzk[NW];
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
+  // recompute: key rows of a batch of retrieved tokens, per-feature-tile partial
+  // weights, and the weights w_i = f.phi_k(k_i) of the chunk's retrieved entries
+  constexpr int TS = D == 64 ? 512 : 256;  // tokens per recompute batch (LDS bound)
+  constexpr int KROW = D + 8;       // row stride (bf16): 16 B pad
+  constexpr int NFT = M / 16;       // feature tiles
+  __shared__ __align__(16) uint16_t s_k[RECOMP ? TS * KROW : 8];
+  __shared__ float s_wp[RECOMP ? NFT : 1][RECOMP ? TS : 1];
+  __shared__ float s_w[RECOMP ? CH : 1];
 
   const KT* kunit = kb + (size_t)u * ustride;
   const KT* vunit = vb + (size_t)u * ustride;
@@ -179,6 +193,67 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     uf[i] = rs ? phi_q[(size_t)ug * M + f] : 0.f;
   }
 
+  // recompute operands of this wave's 16-feature tile (W split into bf16 hi + lo,
+  // bias, f), derived with the prologue loads in flight
+  constexpr int RKS = RECOMP ? D / 32 : 1;
+  bf16x8_t rWhi[RKS], rWlo[RKS];
+  float rbf = 0.f, rfq = 0.f;
+  if constexpr (RECOMP) {
+    if (sub) {
+      const int f = (wave % NFT) * 16 + (lane & 15), pset = u % P;
+      split_w_operands<RKS>(Wk + ((size_t)pset * M + f) * D + 8 * (lane >> 4), rWhi, rWlo);
+      rbf = bk[(size_t)pset * M + f];
+      rfq = phi_q[(size_t)ug * M + f];
+    }
+  }
+
+  // w_i of the retrieved entries [r0, cnt) of the staged chunk, into s_w
+  auto recompute_w = [&](int c0, int cnt) {
+    constexpr int CPR = D / 8;
+    constexpr int WPT = NW / NFT;                // waves per feature tile
+    const int ft = wave % NFT, th = wave / NFT;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int r0 = max(0, n_ex - c0);
+    constexpr int PPT = TS * CPR / NT;             // 16-byte row pieces per thread
+    static_assert(TS * CPR % NT == 0, "whole pieces per thread");
+    for (int sb = r0; sb < cnt; sb += TS) {
+      const int nrow = min(TS, cnt - sb);
+      // key rows into LDS (rows past the batch re-read its last row); the
+      // previous batch ended with a barrier, so the loads can all be issued
+      // before the first store
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const int i = tid + NT * j, row = i / CPR, cc = i - row * CPR;
+        const int pos = s_pos[sb + min(row, nrow - 1)];
+        *reinterpret_cast<uint4*>(s_k + row * KROW + cc * 8) =
+            *reinterpret_cast<const uint4*>(kunit + (size_t)pos * D + cc * 8);
+      }
+      __syncthreads();
+      for (int tt = th; tt < (nrow + 15) / 16; tt += WPT) {
+        const f32x4 acc = proj_tile16<RKS>(s_k + (tt * 16 + l16) * KROW + 8 * g4, rWhi, rWlo);
+        const uint32_t p01 = pack_bf16x2(phi_elu1(acc[0] + rbf), phi_elu1(acc[1] + rbf));
+        const uint32_t p23 = pack_bf16x2(phi_elu1(acc[2] + rbf), phi_elu1(acc[3] + rbf));
+        float v[4] = {rfq * bf16lo(p01), rfq * bf16hi(p01), rfq * bf16lo(p23), rfq * bf16hi(p23)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = lane_group_sum<16>(v[r]);
+        if (l16 == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s_wp[ft][tt * 16 + 4 * g4 + r] = v[r];
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < TS; i += NT) {
+        if (sb + i < cnt) {
+          float w = 0.f;
+#pragma unroll
+          for (int k = 0; k < NFT; ++k) w += s_wp[k][i];
+          s_w[sb + i] = w;
+        }
+      }
+      __syncthreads();  // s_k and s_wp are free again; after the last batch s_w is complete
+    }
+  };
+
   float N[CPL], NK[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) { N[c] = 0.f; NK[c] = 0.f; }
@@ -193,6 +268,9 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     stage_store();
     __syncthreads();
     const int cnt = min(CH, T - c0);
+    if constexpr (RECOMP) {
+      if (sub) recompute_w(c0, cnt);
+    }
     for (int jb = grp; jb < cnt; jb += NGR * B) {
       RawPiece<KT, CPL> vr[B], kr[B];
       RawPiece<PT, FPL> pr[B];
@@ -213,7 +291,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
           scs[e] = s_sc[jj];
           vr[e].load(vunit + (size_t)pos * D + part * CPL);
           if (ex) kr[e].load(kunit + (size_t)pos * D + part * CPL);
-          else if (sub) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
+          else if (sub && !RECOMP) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
         }
       }
 #pragma unroll
@@ -230,6 +308,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
         for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
         a = lane_group_sum<LPE>(a);
         w = lane_group_sum<LPE>(w);
+        if constexpr (RECOMP) w = (kind[e] == 2 && sub) ? s_w[jb + e * NGR] : 0.f;
         if (kind[e] != 0) {  // uniform within the group
           const float s = kind[e] == 1 ? a * inv_sqrt_d : scs[e];
           if (s > mrun) {
@@ -344,19 +423,21 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
 }
 
 template <typename KT, typename PT, int D>
-hipError_t launch_merge_t(const MergePlan& pl, const float* q, const float* phi_q, int G,
-                          const rma_kv& kv, const rma_span& sp, const int32_t* idx,
-                          const float* sel, int K, const void* phi_k, int m, const float* S,
-                          const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
+hipError_t launch_merge_t(const float* q, const float* phi_q, int G, const rma_kv& kv,
+                          const rma_span& sp, const int32_t* idx, const float* sel, int K,
+                          const void* phi_k, const float* Wk, const float* bk, int P, int m,
+                          const float* S, const float* u, uint32_t flags, float* y, float* stats,
                           hipStream_t st) {
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
-  auto kern = m == 64 ? merge_kernel<KT, PT, D, 64> : merge_kernel<KT, PT, D, 128>;
-  (void)pl;
-  (void)ws;
+  const bool recomp = phi_k == nullptr && Wk != nullptr;
+  auto kern = m == 64 ? merge_kernel<KT, PT, D, 64, false> : merge_kernel<KT, PT, D, 128, false>;
+  if constexpr (sizeof(KT) == 2 && sizeof(PT) == 2) {
+    if (recomp) kern = m == 64 ? merge_kernel<KT, PT, D, 64, true> : merge_kernel<KT, PT, D, 128, true>;
+  }
   hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(kMergeThreads), 0, st, q, phi_q, G,
                      static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
                      (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx, sel, K,
-                     static_cast<const PT*>(phi_k), L_mid, S, u, flags, y, stats,
+                     static_cast<const PT*>(phi_k), L_mid, Wk, bk, P, S, u, flags, y, stats,
                      1.0f / sqrtf((float)D));
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) trace_kernel(st, "merge_kernel");
@@ -365,14 +446,17 @@ hipError_t launch_merge_t(const MergePlan& pl, const float* q, const float* phi_
 
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,
                         const rma_kv& kv, const rma_span& sp, const int32_t* idx,
-                        const float* sel, int K, const void* phi_k, int phi_dtype, int m,
-                        const float* S, const float* u, uint32_t flags, float* y, float* stats,
-                        uint8_t* ws, hipStream_t st) {
-#define RMA_MERGE_DISPATCH(KT, PT)                                                             \
-  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(pl, q, phi_q, G, kv, sp, idx, sel, K, phi_k, m, \
-                                                 S, u, flags, y, stats, ws, st)                \
-                    : launch_merge_t<KT, PT, 128>(pl, q, phi_q, G, kv, sp, idx, sel, K, phi_k, \
-                                                  m, S, u, flags, y, stats, ws, st);
+                        const float* sel, int K, const void* phi_k, int phi_dtype,
+                        const float* Wk, const float* bk, int P, int m, const float* S,
+                        const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
+                        hipStream_t st) {
+  (void)pl;
+  (void)ws;
+#define RMA_MERGE_DISPATCH(KT, PT)                                                              \
+  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(q, phi_q, G, kv, sp, idx, sel, K, phi_k, Wk, bk, \
+                                                 P, m, S, u, flags, y, stats, st)                \
+                    : launch_merge_t<KT, PT, 128>(q, phi_q, G, kv, sp, idx, sel, K, phi_k, Wk,   \
+                                                  bk, P, m, S, u, flags, y, stats, st);
   if (kv.dtype == RMA_BF16) {
     if (phi_dtype == RMA_BF16) { RMA_MERGE_DISPATCH(uint16_t, uint16_t) }
     RMA_MERGE_DISPATCH(uint16_t, float)

@@ -76,8 +76,8 @@ def lib():
     L.rma_phi_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP]
     L.rma_build_summaries.argtypes = [P_KV, P_SP, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
-    L.rma_decode_merge.argtypes = [_VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP,
-                                   _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_merge.argtypes = [_VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _I32,
+                                   _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
     L.rma_workspace_bytes.argtypes = [_I32, P_KV, P_SP, _I32, _I32, _I32]
     L.rma_workspace_bytes.restype = _SZ
     L.rma_status_string.argtypes = [_I32]
@@ -181,14 +181,16 @@ def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Option
                         bk: Optional[torch.Tensor], m: Optional[int] = None,
                         phi_k: Optional[torch.Tensor] = None, phi_dtype: torch.dtype = torch.bfloat16,
                         n_param_sets: Optional[int] = None, ws: Optional[Workspace] = None,
-                        out: Optional[tuple] = None):
+                        out: Optional[tuple] = None, store_phi: bool = True):
     """Returns (phi_k [U, L_mid, m], S [U, m, d], u [U, m], kappa [U]).  `out` may
-    supply preallocated (S, u, kappa)."""
+    supply preallocated (S, u, kappa).  store_phi=False (computed features only)
+    keeps the phi_k rows out of memory: phi_k is returned as None and decode
+    recomputes the retrieved rows."""
     U, _, d = k.shape
     if m is None:
         m = Wk.shape[1] if Wk is not None else phi_k.shape[2]
     P = n_param_sets or (Wk.shape[0] if Wk is not None else 1)
-    if phi_k is None:
+    if phi_k is None and store_phi:
         assert Wk is not None, "phi_k must be given when Wk is None"
         phi_k = torch.empty(U, span.L_mid, m, dtype=phi_dtype, device=k.device)
     if out is not None:
@@ -200,8 +202,9 @@ def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Option
     kv, sp = _kv(k, v), span._c()
     nb = int(lib().rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ctypes.byref(kv), ctypes.byref(sp), 1, 0, m))
     w = _ws(ws, nb)
+    pdt = _dt(phi_k.dtype) if phi_k is not None else _dt(phi_dtype)
     _check(lib().rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), _p(Wk), _p(bk), m, P, _p(phi_k),
-                                     _dt(phi_k.dtype), _p(S), _p(u), _p(kappa), _p(w), w.numel(), _stream()))
+                                     pdt, _p(S), _p(u), _p(kappa), _p(w), w.numel(), _stream()))
     return phi_k, S, u, kappa
 
 
@@ -226,8 +229,10 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
                      span: Span, idx: Optional[torch.Tensor], sel_scores: Optional[torch.Tensor], K: int,
                      phi_k: Optional[torch.Tensor], S: Optional[torch.Tensor], u: Optional[torch.Tensor],
                      flags: int = RMA_MERGE_SUB, m: Optional[int] = None, want_stats: bool = False,
-                     ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None):
-    """Returns y [U, G, d] (and stats [U, G, 4] = (m*, Z_E, Z_R, retrieved phi mass))."""
+                     ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None,
+                     Wk: Optional[torch.Tensor] = None, bk: Optional[torch.Tensor] = None):
+    """Returns y [U, G, d] (and stats [U, G, 4] = (m*, Z_E, Z_R, retrieved phi mass)).
+    With phi_k None, the retrieved phi_k rows are recomputed from Wk, bk."""
     U, G, d = q.shape
     if m is None:
         m = S.shape[1] if S is not None else 128
@@ -238,9 +243,10 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
     nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE_MERGE, ctypes.byref(kv), ctypes.byref(sp), G, K, m))
     w = _ws(ws, nb)
     pdt = _dt(phi_k.dtype) if phi_k is not None else RMA_BF16
+    P = Wk.shape[0] if Wk is not None else 1
     _check(lib().rma_decode_merge(_p(q), _p(phi_q), G, ctypes.byref(kv), ctypes.byref(sp), _p(idx),
-                                  _p(sel_scores), K, _p(phi_k), pdt, m, _p(S), _p(u), flags, _p(y),
-                                  _p(stats), _p(w), w.numel(), _stream()))
+                                  _p(sel_scores), K, _p(phi_k), pdt, _p(Wk), _p(bk), P, m, _p(S), _p(u),
+                                  flags, _p(y), _p(stats), _p(w), w.numel(), _stream()))
     return (y, stats) if want_stats else y
 
 

@@ -41,10 +41,11 @@ def decode_span(cfg, step):
     return R.Span(cfg.L, cfg.n_sink, cfg.n_tail, cfg.n_gen(step))
 
 
-def hip_prefill(inp, ws=None):
+def hip_prefill(inp, ws=None, store_phi=True):
+    """store_phi=False: the phi_k rows are not kept; decode recomputes them."""
     cfg = inp.cfg
     return R.rma_build_summaries(inp.k, inp.v, prefill_span(cfg), inp.W, inp.b,
-                                 phi_dtype=cfg.torch_phi_dtype(), ws=ws)
+                                 phi_dtype=cfg.torch_phi_dtype(), ws=ws, store_phi=store_phi)
 
 
 def hip_decode(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None):
@@ -54,8 +55,9 @@ def hip_decode(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None):
     f = R.rma_phi_features(q, inp.W, inp.b)
     sp = decode_span(cfg, step)
     idx, sel = R.rma_decode_topk(q, inp.k, sp, kappa, K, ws=ws)
+    recompute = dict(Wk=inp.W, bk=inp.b) if phi_k is None else {}
     y, stats = R.rma_decode_merge(q, f, inp.k, inp.v, sp, idx, sel, K, phi_k, S, u, flags=flags,
-                                  want_stats=True, ws=ws)
+                                  want_stats=True, ws=ws, m=cfg.m, **recompute)
     return dict(idx=idx, sel=sel, y=y, stats=stats, f=f)
 
 
