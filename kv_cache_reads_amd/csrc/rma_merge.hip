@@ -78,7 +78,9 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   constexpr int CH = kMergeChunk;   // entries staged in LDS at a time
   constexpr int SPT = CH / NT;      // staged entries per thread
   // entries per group whose loads are in flight together (bounded by registers)
-  constexpr int B = (sizeof(KT) == 4 || (sizeof(PT) == 4 && D == 128)) ? 2 : ((RECOMP && D == 128) ? 3 : 4);
+  constexpr int B = sizeof(KT) == 4 ? 2
+                    : sizeof(PT) == 4 ? (D == 128 ? 2 : 4)
+                    : D == 128 ? (RECOMP ? 3 : 4) : 8;
   const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;

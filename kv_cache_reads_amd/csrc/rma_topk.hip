@@ -389,6 +389,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   __shared__ int s_bcs[kSelMaxChunks];
   __shared__ int s_nrep[kSelMaxChunks];
   __shared__ uint32_t hist[NBS];
+  __shared__ uint32_t bmin[NBS], bmax[NBS];   // per-bin score extent (order-preserving keys)
   __shared__ int s_buf[257];
   __shared__ int s_misc[8];
   __shared__ float s_fl[2 * NWV];
@@ -409,6 +410,16 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   const float4 hp4 = hpw[ug];  // written by the scan: identical binning and error bound
   const HeadParams hp{hp4.x, hp4.y, hp4.z};
   if (tid < D) s_qf[tid] = qg[tid];
+  // When every report slot fits SPEC per thread, all slots are loaded together
+  // with the chunk counts (one round trip; slot (c, j) is valid for j < count_c)
+  constexpr int SPEC = 8;
+  const int nslots_all = n_chunks * r_cap;
+  const bool spec = nslots_all <= SPEC * NT;
+  float2 sv[SPEC];
+  if (spec) {
+#pragma unroll
+    for (int k = 0; k < SPEC; ++k) sv[k] = en[min(tid + k * NT, nslots_all - 1)];
+  }
   // chunk reports: one thread per chunk (n_chunks <= 256), offsets by a block scan
   int w_c = 0, trunc = 0;
   if (tid < n_chunks) {
@@ -446,36 +457,53 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   float th_lo = 0.f, th_hi = 0.f;
   int n_band = 0, kp = 0;
   if (!fallback) {
-    __syncthreads();
-    // gather the union: slot (chunk c, j < wmax) of the padded report layout;
-    // eight loads per thread are issued before any is consumed
-    const int nslots = n_chunks * wmax;
-    for (int i0 = 0; i0 < nslots; i0 += 8 * NT) {
-      float2 e[8];
-      int dst[8];
+    // the union in LDS (report order = position order) and its score range
+    float lo = INFINITY, hi = -INFINITY;
+    if (spec) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k * NT + tid;
-        const int c = i / wmax, j = i - c * wmax;
-        dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
-        if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
+      for (int k = 0; k < SPEC; ++k) {
+        const int i = tid + k * NT;
+        const int c = i / r_cap, j = i - c * r_cap;
+        if (i < nslots_all && j < s_off[c + 1] - s_off[c]) {
+          es[s_off[c] + j] = sv[k].x;
+          ep[s_off[c] + j] = __float_as_int(sv[k].y);
+          lo = fminf(lo, sv[k].x);
+          hi = fmaxf(hi, sv[k].x);
+        }
       }
+    } else {
+      // slot (chunk c, j < wmax) of the padded report layout; eight loads per
+      // thread are issued before any is consumed
+      const int nslots = n_chunks * wmax;
+      for (int i0 = 0; i0 < nslots; i0 += 8 * NT) {
+        float2 e[8];
+        int dst[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (dst[k] >= 0) {
-          es[dst[k]] = e[k].x;
-          ep[dst[k]] = __float_as_int(e[k].y);
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k * NT + tid;
+          const int c = i / wmax, j = i - c * wmax;
+          dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
+          if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (dst[k] >= 0) {
+            es[dst[k]] = e[k].x;
+            ep[dst[k]] = __float_as_int(e[k].y);
+            lo = fminf(lo, e[k].x);
+            hi = fmaxf(hi, e[k].x);
+          }
         }
       }
     }
-    __syncthreads();
-    // range of the union, then a linear histogram over it
-    float lo = INFINITY, hi = -INFINITY;
-    for (int i = tid; i < nE; i += NT) { lo = fminf(lo, es[i]); hi = fmaxf(hi, es[i]); }
     lo = wave_min_dpp(lo);
     hi = wave_max_dpp(hi);
     if (lane == 0) { s_fl[wave] = lo; s_fl[NWV + wave] = hi; }
-    for (int b = tid; b < NBS; b += NT) hist[b] = 0u;
+    for (int b = tid; b < NBS; b += NT) {
+      hist[b] = 0u;
+      bmin[b] = 0xffffffffu;
+      bmax[b] = 0u;
+    }
     __syncthreads();
     lo = INFINITY;
     hi = -INFINITY;
@@ -486,7 +514,14 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
       const float t = __fmul_rn(__fsub_rn(x, lo), inv);
       return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
     };
-    for (int i = tid; i < nE; i += NT) atomicAdd(&hist[ubin(es[i])], 1u);
+    // linear histogram over the range, with each bin's exact score extent
+    for (int i = tid; i < nE; i += NT) {
+      const float x = es[i];
+      const int b = ubin(x);
+      atomicAdd(&hist[b], 1u);
+      atomicMin(&bmin[b], ord_f32(x));
+      atomicMax(&bmax[b], ord_f32(x));
+    }
     __syncthreads();
     // bin of the K-th largest score: thread t owns bins NBS-BPT*t-1 .. NBS-BPT*(t+1)
     // (descending)
@@ -509,18 +544,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     __syncthreads();
     const int bK = s_misc[0];
     // exact extent of that bin: the K-th largest score t lies in [xlo, xhi]
-    float xlo = INFINITY, xhi = -INFINITY;
-    for (int i = tid; i < nE; i += NT)
-      if (ubin(es[i]) == bK) { xlo = fminf(xlo, es[i]); xhi = fmaxf(xhi, es[i]); }
-    xlo = wave_min_dpp(xlo);
-    xhi = wave_max_dpp(xhi);
-    __syncthreads();
-    if (lane == 0) { s_fl[wave] = xlo; s_fl[NWV + wave] = xhi; }
-    __syncthreads();
-    xlo = INFINITY;
-    xhi = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) { xlo = fminf(xlo, s_fl[w]); xhi = fmaxf(xhi, s_fl[NWV + w]); }
+    const float xlo = unord_f32(bmin[bK]), xhi = unord_f32(bmax[bK]);
     th_lo = xlo - 2.5f * hp.eps;
     th_hi = xhi + 2.5f * hp.eps;
     // every chunk must have reported all of its tokens scoring >= th_lo
@@ -643,7 +667,15 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
                                       sp.n_sink, L_mid, pl, kappa, ent, meta, hpw);
   if (e != hipSuccess) return e;
   // dynamic LDS: the union (score, position) pairs, within the per-block limit
-  const size_t static_lds = 24 * 1024;
+  // left by the kernel's own (static) LDS
+  static size_t static_lds = 0;
+  if (static_lds == 0) {
+    hipFuncAttributes attr{};
+    static_lds = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&topk_select_kernel<KT, D>)) ==
+                         hipSuccess
+                     ? attr.sharedSizeBytes
+                     : 32 * 1024;
+  }
   int e_max = pl.e_max;
   if (g_lds_limit > static_lds) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - static_lds) / 8);
   const size_t lds = (size_t)std::max(e_max, 1) * 8;
