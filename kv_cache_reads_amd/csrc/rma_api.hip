@@ -99,6 +99,8 @@ BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_
   if (Lm > 0) {
     // enough blocks to cover the chip (~2 per CU) with as few per-chunk partials as possible
     int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(512, U)));
+    // chunks of at most 2^22 tokens keep the builder's 32-bit byte offsets in range
+    nc = std::max<int64_t>(nc, ceil_div(Lm, int64_t(1) << 22));
     int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);

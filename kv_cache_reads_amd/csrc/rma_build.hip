@@ -70,12 +70,26 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   uint16_t* php = STORE ? phik + ((size_t)u * L_mid + t0) * M : nullptr;
+  // range-checked views of this chunk: rows past n load as zeros, Phi stores past n drop
+  const auto rk = make_rsrc(kp, (uint32_t)n * D * 2), rv = make_rsrc(vp, (uint32_t)n * D * 2);
+  const auto rph = make_rsrc(php, STORE ? (uint32_t)n * M * 2 : 0u);
   const int f = wave * 16 + l16;          // this lane's feature in step 1
-  const float bf = bias[(size_t)p * M + f];
 
-  // W (fp32) -> bf16 hi + lo B-operands of this wave's feature tile
-  bf16x8_t Whi[KS], Wlo[KS];
-  split_w_operands<KS>(W + ((size_t)p * M + f) * D + 8 * g4, Whi, Wlo);
+  // this lane's W row piece and bias, issued ahead of the first tiles (buffer
+  // loads stay in program order relative to the tile loads and the barrier)
+  const auto rw = make_rsrc(W + (size_t)p * M * D, M * D * 4);
+  const auto rb = make_rsrc(bias + (size_t)p * M, M * 4);
+  float wv[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t wo = (f * D + 32 * ks + 8 * g4) * 4;
+    const uint4 a = buf_ld16(rw, wo), b = buf_ld16(rw, wo + 16);
+    const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[ks][e] = __uint_as_float(x[e]);
+  }
+  const float bf = buf_ld_f32(rb, f * 4);
+  bf16x8_t Whi[KS], Wlo[KS];             // W (fp32) as bf16 hi + lo B-operands
   u16x8_t ones_v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones_v[e] = 0x3F80;  // bf16 1.0: u = Phi^T 1 on the MFMA
@@ -91,13 +105,9 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
-      if (tok0 + row < n) {
-        kr[j] = ld_stream16(reinterpret_cast<const uint4*>(kp + (size_t)(tok0 + row) * D) + cc);
-        vr[j] = ld_stream16(reinterpret_cast<const uint4*>(vp + (size_t)(tok0 + row) * D) + cc);
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        vr[j] = make_uint4(0, 0, 0, 0);
-      }
+      const uint32_t off = (uint32_t)((tok0 + row) * D + cc * 8) * 2;
+      kr[j] = buf_ld16_nt(rk, off);
+      vr[j] = buf_ld16_nt(rv, off);
     }
   };
   // K and V rows as they are (16-byte writes)
@@ -187,35 +197,41 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       __syncthreads();
       // store the Phi tile rows (16-byte pieces, coalesced; rows are 8-byte aligned in LDS)
       constexpr int PCR = M / 8;
+      static_assert(TT * PCR % NT == 0, "Phi tile store shape");
 #pragma unroll
-      for (int j = 0; j < (TT * PCR + NT - 1) / NT; ++j) {
+      for (int j = 0; j < TT * PCR / NT; ++j) {
         const int chunk = tid + NT * j;
         const int row = chunk / PCR, cc = chunk % PCR;
-        if (chunk < TT * PCR && (FULL || tok0 + row < n)) {
-          const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
-          const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
-          *reinterpret_cast<uint4*>(php + (size_t)(tok0 + row) * M + cc * 8) = make_uint4(a.x, a.y, b.x, b.y);
-        }
+        const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
+        const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
+        buf_st16(rph, (uint32_t)((tok0 + row) * M + cc * 8) * 2, make_uint4(a.x, a.y, b.x, b.y));
       }
     }
   };
 
-  // two register stages in turn: tile t+2 loads while tile t is computed
+  // Two register stages in turn: tile t+2 loads while tile t is computed.  Every
+  // pass issues the same memory operations (tiles past the chunk load as zeros
+  // without touching memory, Phi stores past it are dropped, and a tile past an
+  // odd tile count is computed as padding), and the first two tiles are complete
+  // before the loop, so the wait before each staging step covers only the loads
+  // of the tile being staged, not the stores and loads issued after them.
   uint4 kA[LCH], vA[LCH], kB[LCH], vB[LCH];
   load_tile(kA, vA, 0);
-  if (TT < n) load_tile(kB, vB, TT);
+  load_tile(kB, vB, TT);
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing in flight on entry
+  split_w_values<KS>(wv, Whi, Wlo);
   for (int tok0 = 0; tok0 < n; tok0 += 2 * TT) {
     __syncthreads();
     stage_tile(kA, vA);
     __syncthreads();
-    if (tok0 + 2 * TT < n) load_tile(kA, vA, tok0 + 2 * TT);
+    load_tile(kA, vA, tok0 + 2 * TT);
     if (tok0 + TT <= n) compute_tile(tok0, std::true_type{});
     else compute_tile(tok0, std::false_type{});
-    if (tok0 + TT >= n) break;
     __syncthreads();
     stage_tile(kB, vB);
     __syncthreads();
-    if (tok0 + 3 * TT < n) load_tile(kB, vB, tok0 + 3 * TT);
+    load_tile(kB, vB, tok0 + 3 * TT);
     if (tok0 + 2 * TT <= n) compute_tile(tok0 + TT, std::true_type{});
     else compute_tile(tok0 + TT, std::false_type{});
   }

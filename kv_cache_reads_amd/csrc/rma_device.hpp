@@ -59,6 +59,30 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resource over [p, p + bytes).  The hardware range check makes a load at
+// an offset at or past the end return zero and drops such a store, so tiles that
+// run past a range need no branch around their memory operations (and the
+// compiler's wait counts stay exact across them).  Word 3 selects 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int kCpolNT = 2;  // nontemporal cache policy (read-once data)
+__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 // Raw 16-byte pieces of a row (for double buffering of loads).
 template <typename T> struct RowPieces;
 template <> struct RowPieces<uint16_t> { static constexpr int kElemsPerPiece = 8; };
@@ -276,22 +300,30 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_
 // B operands of one 16-feature tile for lane group g4: W (fp32) split into bf16
 // hi + lo parts (w = hi + lo + O(2^-17 |w|)).  `wrow` points at W[feature][8*g4].
 template <int KS>
-__device__ __forceinline__ void split_w_operands(const float* wrow, bf16x8_t (&Whi)[KS],
-                                                 bf16x8_t (&Wlo)[KS]) {
+__device__ __forceinline__ void split_w_values(const float (&w)[KS][8], bf16x8_t (&Whi)[KS],
+                                               bf16x8_t (&Wlo)[KS]) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const float* wr = wrow + 32 * ks;
     u16x8_t hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float w = wr[e];
-      const uint32_t hb = f32_to_bf16_bits(w);
+      const uint32_t hb = f32_to_bf16_bits(w[ks][e]);
       hi[e] = (unsigned short)hb;
-      lo[e] = (unsigned short)f32_to_bf16_bits(w - __uint_as_float(hb << 16));
+      lo[e] = (unsigned short)f32_to_bf16_bits(w[ks][e] - __uint_as_float(hb << 16));
     }
     Whi[ks] = as_bf16x8(hi);
     Wlo[ks] = as_bf16x8(lo);
   }
+}
+template <int KS>
+__device__ __forceinline__ void split_w_operands(const float* wrow, bf16x8_t (&Whi)[KS],
+                                                 bf16x8_t (&Wlo)[KS]) {
+  float w[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[ks][e] = wrow[32 * ks + e];
+  split_w_values<KS>(w, Whi, Wlo);
 }
 
 // Z = K W^T for 16 key rows x 16 features (v_mfma_f32_16x16x32_bf16).  `arow`
