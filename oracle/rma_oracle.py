@@ -259,6 +259,32 @@ def residual_true(q, keys, values, L, n_sink, n_tail, idx):
     return w @ _f64(values)[R], float(w.sum())
 
 
+def log_partitions(q, keys, L, n_sink, n_tail, n_gen=0, idx=None):
+    """Natural logarithms of the unshifted partition sums of the exponential
+    kernel (page §3: Eq. 1 for the whole context, the residual definitions
+    before Eq. 5 for R(q); §7.1 Table 3 compares log Z_R_hat with log Z_R):
+        log Z_full = log sum_{i < L + n_gen} e^{s_i},
+        log Z_mid  = log sum_{i in M} e^{s_i},
+        log Z_R    = log sum_{i in M minus K(q)} e^{s_i}
+    with s_i = q.k_i / sqrt(d_h).  log Z_R is -inf when the whole mid-region
+    is retrieved and None when idx is None.  float64 with a max shift."""
+    _, mid, _ = partition(L, n_sink, n_tail, n_gen)
+    q = _f64(q)
+    s = (_f64(keys)[:L + n_gen] @ q) / math.sqrt(q.shape[0])
+
+    def lse(x):
+        if x.size == 0:
+            return -math.inf
+        mx = float(x.max())
+        return mx + math.log(float(np.exp(x - mx).sum()))
+
+    z_r = None
+    if idx is not None:
+        R = np.setdiff1d(mid, np.asarray(idx, dtype=np.int64))
+        z_r = lse(s[R])
+    return lse(s), lse(s[mid]), z_r
+
+
 # ---------------------------------------------------------------- diagnostics
 def rel_l1(y, y_ref) -> float:
     """Relative l1 attention-output error (page §7.1 Table 3 metric, per query)."""

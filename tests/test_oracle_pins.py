@@ -316,3 +316,45 @@ def test_diagnostics():
     Kpeak = np.zeros((L, 8), np.float32)
     Kpeak[10] = 200.0 * q / np.linalg.norm(q)
     assert O.h_mid(q, Kpeak, L, ns, nt) < 1e-6
+
+
+def test_log_partitions_uniform_scores_closed_form():
+    # all-zero keys: every score is 0, so each partition sum is a token count
+    L, ns, nt, n_gen, Kret = 50, 3, 6, 2, 7
+    q = _rng(91).standard_normal(8)
+    keys = np.zeros((L + n_gen, 8))
+    idx = np.arange(ns + 5, ns + 5 + Kret)
+    zf, zm, zr = O.log_partitions(q, keys, L, ns, nt, n_gen, idx)
+    assert zf == pytest.approx(math.log(L + n_gen), abs=1e-14)
+    assert zm == pytest.approx(math.log(L - ns - nt), abs=1e-14)
+    assert zr == pytest.approx(math.log(L - ns - nt - Kret), abs=1e-14)
+    assert O.log_partitions(q, keys, L, ns, nt, n_gen, np.arange(ns, L - nt))[2] == -math.inf
+    assert O.log_partitions(q, keys, L, ns, nt, n_gen)[2] is None
+
+
+def test_log_partitions_split_into_exact_support_and_true_residual():
+    # Z_full = (exact-support mass over A, K(q), Gen) + (true residual mass over M minus K(q))
+    L, ns, nt, n_gen = 96, 3, 7, 3
+    q, K, V, W, b = _unit(92, L=L, n_gen=n_gen)
+    A, M, G = O.partition(L, ns, nt, n_gen)
+    idx = O.topk_indices(q, K[M], 13, first_index=ns)
+    m_star, _, Z_E = O.exact_terms(q, K, V, np.concatenate([A, idx, G]))
+    _, Z_R = O.residual_true(q, K, V, L, ns, nt, idx)
+    zf, zm, zr = O.log_partitions(q, K, L, ns, nt, n_gen, idx)
+    assert math.exp(zf) == pytest.approx(Z_E * math.exp(m_star) + Z_R, rel=1e-13)
+    assert zr == pytest.approx(math.log(Z_R), abs=1e-13)
+    s_mid = torch.from_numpy(K[M].astype(np.float64) @ q.astype(np.float64) / math.sqrt(8))
+    assert zm == pytest.approx(float(torch.logsumexp(s_mid, 0)), abs=1e-13)
+
+
+def test_log_partitions_shift_with_the_scores():
+    # adding alpha*sqrt(d)*q/|q|^2 to every key adds alpha to every score
+    L, ns, nt, n_gen, alpha = 80, 2, 5, 1, 1.75
+    q, K, V, W, b = _unit(93, L=L, n_gen=n_gen)
+    q = q.astype(np.float64)
+    K = K.astype(np.float64)
+    idx = O.topk_indices(q, K[ns:L - nt], 9, first_index=ns)
+    base = O.log_partitions(q, K, L, ns, nt, n_gen, idx)
+    shifted = O.log_partitions(q, K + alpha * math.sqrt(8) * q / (q @ q), L, ns, nt, n_gen, idx)
+    for a, b_ in zip(base, shifted):
+        assert b_ == pytest.approx(a + alpha, abs=1e-12)
