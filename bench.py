@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip timing the full-attention reference decode")
     ap.add_argument("--recompute-phi", action="store_true",
                     help="do not store the phi_k rows at prefill; the merge recomputes the retrieved "
                          "rows from their keys (bf16 keys; saves the rows' HBM, costs MFMA/VALU work "
@@ -151,6 +153,7 @@ class PathRunner:
         self.kdt = R._dt(inp.k.dtype)
         self.pdt = R._dt(cfg.torch_phi_dtype())
         self.Wm, self.bm = (None, None) if store_phi else (inp.W, inp.b)
+        self.yf = None
 
     def build(self, st):
         cfg, p = self.cfg, self.p
@@ -181,6 +184,15 @@ class PathRunner:
                                     p(self.u), 0, p(self.y[s]), None, p(self.ws), self.ws.numel(), st)
         assert r == 0, r
 
+    def full(self, s, st):
+        """The full-attention reference for decode step s (no diagnostics)."""
+        cfg, p = self.cfg, self.p
+        if self.yf is None:
+            self.yf = self.t.empty(cfg.steps, cfg.U, cfg.G, cfg.d, dtype=self.t.float32, device=self.k.device)
+        r = self.L.rma_decode_full(p(self.q[s]), cfg.G, ctypes.byref(self.kv), ctypes.byref(self.sp_dec[s]),
+                                   None, 0, None, p(self.yf[s]), None, p(self.ws), self.ws.numel(), st)
+        assert r == 0, r
+
     def step(self, st):
         """The whole path: prefill summaries, then every decode step."""
         self.build(st)
@@ -209,6 +221,69 @@ class PathRunner:
             traced("topk", lambda: self.topk(s, st))
             traced("merge", lambda: self.merge(s, st))
         return out
+
+
+def timed_replays(fn, n_copies, n, stream, use_graphs):
+    """Average microseconds of fn(i) (enqueues work for input copy i % n_copies),
+    replayed from per-copy HIP graphs when use_graphs."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn(0)  # outputs are allocated outside any capture
+    stream.synchronize()
+    run = fn
+    if use_graphs:
+        graphs = []
+        for r_i in range(n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn(r_i)
+            graphs.append(g)
+        run = lambda i: graphs[i % n_copies].replay()  # noqa: E731
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            run(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record()
+        for i in range(n):
+            run(i)
+        e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def decode_timing(args, cfg, runners, n_copies, stream, st, use_graphs, queries, log):
+    """The method's decode steps alone (phi_q, top-K, merge over summaries built
+    earlier) and the full-attention reference (rma_decode_full over every
+    position, no diagnostics) for the same decode steps, both replayed like the
+    whole step: the speed ratio of the method's decode against full attention."""
+    n = max(5, min(args.steps, 200))
+
+    def dec(i):
+        r = runners[i % n_copies]
+        for s in range(cfg.steps):
+            r.phi(s, st)
+            r.topk(s, st)
+            r.merge(s, st)
+
+    def full(i):
+        r = runners[i % n_copies]
+        for s in range(cfg.steps):
+            r.full(s, st)
+
+    dec_us = timed_replays(dec, n_copies, n, stream, use_graphs)
+    full_us = timed_replays(full, n_copies, n, stream, use_graphs)
+    e = 2 if cfg.kv_dtype == "bf16" else 4
+    nbytes = sum(cfg.U * (cfg.L + cfg.n_gen(s)) * cfg.d * e * 2 + cfg.U * cfg.G * cfg.d * 8
+                 for s in range(cfg.steps))
+    log(f"[bench] method decode {dec_us:.2f} us/step ({queries / dec_us:.3f} M queries/s); full-attention "
+        f"decode {full_us:.2f} us/step, {nbytes / 1e6:.1f} MB -> {nbytes / (full_us / 1e6) / 1e9:.1f} GB/s")
+    return dec_us, {"us_per_step": round(full_us, 2), "queries_per_s": round(queries / (full_us / 1e6), 1),
+                    "algorithmic_MB": round(nbytes / 1e6, 3),
+                    "GBps": round(nbytes / (full_us / 1e6) / 1e9, 1),
+                    "method_decode_speedup": round(full_us / dec_us, 3), "timed_steps": n}
 
 
 def cpu_baseline(cfg, inp, K, seconds):
@@ -295,6 +370,8 @@ def main():
     wsb = max(R.rma_workspace_bytes(R.RMA_OP_BUILD_SUMMARIES, inp.k, sp, 1, 0, cfg.m),
               R.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, inp.k, sp, cfg.G, K, cfg.m),
               R.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, inp.k, sp, cfg.G, K, cfg.m))
+    if not args.no_full:
+        wsb = max(wsb, R.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, inp.k, sp, cfg.G, 0, cfg.m))
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi) for c in copies]
     log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
@@ -433,6 +510,13 @@ def main():
             "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md",
         },
     }
+    if not args.no_full:
+        dec_us, out["config"]["full_exact_decode"] = decode_timing(args, cfg, runners, n_copies, stream, st,
+                                                                   graphs is not None, queries, log)
+        out["config"]["decode_only_us_per_step"] = round(dec_us, 2)
+        out["config"]["decode_only_queries_per_s"] = round(queries / (dec_us / 1e6), 1)
+        dbytes = step_bytes - nb["build"]
+        out["config"]["decode_only_GBps"] = round(dbytes / (dec_us / 1e6) / 1e9, 1)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, K, args.cpu_seconds)

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 2
+#define RMA_ABI_VERSION 3
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -100,6 +100,7 @@ typedef struct {
 #define RMA_OP_BUILD_SUMMARIES 1
 #define RMA_OP_DECODE_TOPK 2
 #define RMA_OP_DECODE_MERGE 3
+#define RMA_OP_DECODE_FULL 4
 
 /* rma_decode_merge() flags (page §5.2 Table 1 and §7.1 Table 3 variants). */
 #define RMA_MERGE_SUB 0u           /* Top-K+phi: subtract retrieved tokens (default) */
@@ -200,8 +201,37 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
                             const float* u_, uint32_t flags, float* y, float* stats,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rma_decode_full -- full exact attention of every query head over its unit's
+ * whole context, the reference the method approximates (page §3 Eq. 1, with
+ * the generated tokens of Eq. 11), and the page's comparison diagnostics
+ * (§6: entropy of the attention restricted to the mid-region; §7.1 Table 3:
+ * relative l1 output error and the residual log-partition error, for which
+ * log Z_R over R(q) = M minus K(q) is given here):
+ *   s_i = q.k_i / sqrt(d),  i in [0, L + n_gen),
+ *   y_full = sum_i e^{s_i} v_i / sum_i e^{s_i}.
+ * q: fp32 [n_units][G][d].  idx: NULL, or [n_units][G][K] ascending positions
+ *    inside M (as written by rma_decode_topk) that form K(q); entries outside M
+ *    or out of order make diag[2] meaningless but cannot fault.  K == 0 means
+ *    R(q) = M.  y_cmp: NULL, or fp32 [n_units][G][d], an output to compare with
+ *    y_full (e.g. rma_decode_merge's y).
+ * y_full: fp32 [n_units][G][d].  diag: NULL or fp32 [n_units][G][8] =
+ *    (log Z_full, log Z_mid, log Z_R, H_mid, rel_l1, max s_i, 0, 0), natural
+ *    logs of the unshifted sums sum e^{s_i} over the whole context, over M and
+ *    over R(q) (NaN when idx is NULL and K > 0; -inf for an empty set),
+ *    H_mid = -sum_M p_i log p_i / log L_mid with p renormalised over M (NaN
+ *    when L_mid < 2), rel_l1 = sum_j |y_cmp - y_full| / sum_j |y_full| (NaN
+ *    without y_cmp).
+ * K and V are read once per unit for all G heads; fp32 arithmetic.
+ * Workspace: rma_workspace_bytes(RMA_OP_DECODE_FULL, ...) (depends on G).
+ */
+rma_status rma_decode_full(const float* q, int32_t G, const rma_kv* kv, const rma_span* span,
+                           const int32_t* idx, int32_t K, const float* y_cmp, float* y_full,
+                           float* diag, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for `op` (one of RMA_OP_*); 0 on invalid arguments.  G and K
- * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK. */
+ * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK
+ * and RMA_OP_DECODE_FULL; K is ignored for RMA_OP_DECODE_FULL. */
 size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* span, int32_t G,
                            int32_t K, int32_t m);
 

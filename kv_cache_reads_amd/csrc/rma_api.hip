@@ -155,6 +155,25 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   return p;
 }
 
+FullPlan plan_full(const rma_kv& kv, const rma_span& sp, int G) {
+  FullPlan p{};
+  const int64_t T = sp.L + sp.n_gen;
+  const int64_t U = kv.n_units;
+  const int tile = kv.d == 64 ? 64 : 32;  // positions per block pass
+  if (T > 0) {
+    int64_t nc = std::max<int64_t>(ceil_div(T, kFullMaxChunk),
+                                   std::min<int64_t>(ceil_div(512, U), ceil_div(T, tile)));
+    const int64_t ch = ceil_div(ceil_div(T, nc), tile) * tile;
+    p.ch = (int)ch;
+    p.n_chunks = (int)ceil_div(T, ch);
+  }
+  size_t off = counter_bytes(U);
+  p.off_part = off;
+  off = align_up(off + (size_t)U * std::max(p.n_chunks, 1) * G * (kFullRecHead + kv.d) * 4);
+  p.total = off;
+  return p;
+}
+
 MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) {
   (void)m;
   MergePlan p{};
@@ -236,6 +255,9 @@ size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int
     case RMA_OP_DECODE_MERGE:
       if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp)) return 0;
       return plan_merge(*kv, *sp, G, K, m).total;
+    case RMA_OP_DECODE_FULL:
+      if (G < 1 || G > 8 || sp->n_gen < 0) return 0;
+      return plan_full(*kv, *sp, G).total;
     default:
       return 0;
   }
@@ -363,6 +385,32 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
   hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype,
                               phi_k ? nullptr : Wk, bk, P, m, S, u, flags, y, stats,
                               (uint8_t*)workspace, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_decode_full(const float* q, int32_t G, const rma_kv* kv, const rma_span* sp,
+                           const int32_t* idx, int32_t K, const float* y_cmp, float* y_full,
+                           float* diag, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, true);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(G >= 1 && G <= 8, RMA_ERR_UNSUPPORTED, "G %d not in 1..8", G);
+  RMA_CHECK(sp->L + sp->n_gen > 0, RMA_ERR_INVALID_ARG, "empty context (L + n_gen == 0)");
+  RMA_CHECK(K >= 0 && K <= l_mid(*sp), RMA_ERR_INVALID_ARG, "K %d outside [0, L_mid=%lld]", K,
+            (long long)l_mid(*sp));
+  RMA_CHECK(q && y_full, RMA_ERR_INVALID_ARG, "NULL q or y_full");
+  RMA_CHECK(aligned16(q) && aligned16(idx) && aligned16(y_cmp) && aligned16(y_full) &&
+                aligned16(diag),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  FullPlan pl = plan_full(*kv, *sp, G);
+  RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
+            "workspace is NULL or misaligned");
+  RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
+            workspace_bytes, pl.total);
+  TraceScope ts((hipStream_t)stream);
+  hipError_t e = launch_full(pl, q, G, *kv, *sp, K > 0 ? idx : nullptr, K, y_cmp, y_full, diag,
+                             (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return RMA_OK;
 }

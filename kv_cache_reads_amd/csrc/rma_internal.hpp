@@ -58,6 +58,17 @@ struct MergePlan {
 };
 MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
 
+// ------------------------------------------------------------- full attention
+constexpr int kFullThreads = 256;
+constexpr int kFullMaxChunk = 8192;   // positions per chunk (membership bits in LDS)
+constexpr int kFullRecHead = 8;       // floats before N in a chunk record
+
+struct FullPlan {
+  int n_chunks, ch;
+  size_t off_part, total;
+};
+FullPlan plan_full(const rma_kv& kv, const rma_span& sp, int G);
+
 // ------------------------------------------------------------- kernel timing
 // Benchmark instrumentation armed by rma_trace_arm: events recorded on the
 // call's stream before its first kernel and after each kernel.  Thread-local.
@@ -98,5 +109,9 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
                         const float* Wk, const float* bk, int P, int m, const float* S,
                         const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
                         hipStream_t st);
+
+hipError_t launch_full(const FullPlan& pl, const float* q, int G, const rma_kv& kv,
+                       const rma_span& sp, const int32_t* idx, int K, const float* y_cmp,
+                       float* y, float* diag, uint8_t* ws, hipStream_t st);
 
 }  // namespace rma

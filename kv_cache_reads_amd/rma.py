@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rma.h")
 
 RMA_OK, RMA_ERR_INVALID_ARG, RMA_ERR_UNSUPPORTED, RMA_ERR_WORKSPACE, RMA_ERR_HIP = 0, -1, -2, -3, -4
 RMA_F32, RMA_BF16 = 0, 1
-RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE = 1, 2, 3
+RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE, RMA_OP_DECODE_FULL = 1, 2, 3, 4
 RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
 RMA_WORKSPACE_COUNTER_BYTES = 262144
 
@@ -78,6 +78,7 @@ def lib():
     L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_merge.argtypes = [_VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _I32,
                                    _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_full.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_workspace_bytes.argtypes = [_I32, P_KV, P_SP, _I32, _I32, _I32]
     L.rma_workspace_bytes.restype = _SZ
     L.rma_status_string.argtypes = [_I32]
@@ -91,7 +92,8 @@ def lib():
     L.rma_trace_count.restype = _I32
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
-    for f in ("rma_phi_features", "rma_build_summaries", "rma_decode_topk", "rma_decode_merge"):
+    for f in ("rma_phi_features", "rma_build_summaries", "rma_decode_topk", "rma_decode_merge",
+              "rma_decode_full"):
         getattr(L, f).restype = _I32
     _lib = L
     return L
@@ -248,6 +250,26 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
                                   _p(sel_scores), K, _p(phi_k), pdt, _p(Wk), _p(bk), P, m, _p(S), _p(u),
                                   flags, _p(y), _p(stats), _p(w), w.numel(), _stream()))
     return (y, stats) if want_stats else y
+
+
+def rma_decode_full(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, span: Span,
+                    idx: Optional[torch.Tensor] = None, K: Optional[int] = None,
+                    y_cmp: Optional[torch.Tensor] = None, want_diag: bool = False,
+                    ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None):
+    """Full attention over [0, L + n_gen).  Returns y_full [U, G, d] (and diag
+    [U, G, 8] = (log Z_full, log Z_mid, log Z_R, H_mid, rel_l1, max s, 0, 0))."""
+    U, G, d = q.shape
+    if K is None:
+        K = idx.shape[2] if idx is not None else 0
+    if y is None:
+        y = torch.empty(U, G, d, dtype=torch.float32, device=q.device)
+    diag = torch.empty(U, G, 8, dtype=torch.float32, device=q.device) if want_diag else None
+    kv, sp = _kv(k, v), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE_FULL, ctypes.byref(kv), ctypes.byref(sp), G, K, 0))
+    w = _ws(ws, nb)
+    _check(lib().rma_decode_full(_p(q), G, ctypes.byref(kv), ctypes.byref(sp), _p(idx), K, _p(y_cmp),
+                                 _p(y), _p(diag), _p(w), w.numel(), _stream()))
+    return (y, diag) if want_diag else y
 
 
 def rma_abi_version() -> int:

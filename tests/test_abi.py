@@ -14,12 +14,12 @@ pytestmark = pytest.mark.skipif(not __import__("os").path.exists(R.LIB_PATH),
 def test_exports_every_declared_symbol():
     names = R.header_functions()
     assert set(names) >= {"rma_phi_features", "rma_build_summaries", "rma_decode_topk",
-                          "rma_decode_merge", "rma_workspace_bytes", "rma_status_string",
+                          "rma_decode_merge", "rma_decode_full", "rma_workspace_bytes", "rma_status_string",
                           "rma_last_error", "rma_abi_version"}
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 2
+    assert L.rma_abi_version() == 3
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -117,6 +117,29 @@ def test_workspace_sizes_are_monotone_in_K_and_units():
     kv = _kv()
     assert L.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(_sp()), 2, 5000, 0) == 0
     assert L.rma_workspace_bytes(99, ctypes.byref(kv), ctypes.byref(_sp()), 2, 10, 128) == 0
+
+
+def _full(kv, sp, G=2, K=0, q=0x2000, idx=None, ycmp=None, y=0x7000, diag=None, ws=0x6000, wsb=1 << 30):
+    return R.lib().rma_decode_full(q, G, ctypes.byref(kv), ctypes.byref(sp), idx, K, ycmp, y, diag, ws, wsb, None)
+
+
+def test_full_validation_errors():
+    L = R.lib()
+    kv, sp = _kv(), _sp()
+    assert _full(kv, sp, q=0) == R.RMA_ERR_INVALID_ARG                     # null q
+    assert _full(kv, sp, y=0) == R.RMA_ERR_INVALID_ARG                     # null y_full
+    assert _full(kv, sp, G=9) == R.RMA_ERR_UNSUPPORTED
+    assert _full(_kv(d=96), sp) == R.RMA_ERR_UNSUPPORTED
+    assert _full(kv, sp, K=2000, idx=0x4000) == R.RMA_ERR_INVALID_ARG      # K > L_mid
+    assert _full(kv, sp, diag=0x8004) == R.RMA_ERR_INVALID_ARG             # misaligned diag
+    assert _full(kv, _sp(L=0, ns=0, nt=0)) == R.RMA_ERR_INVALID_ARG         # empty context
+    assert _full(kv, sp, ws=0) == R.RMA_ERR_WORKSPACE
+    assert _full(kv, sp, wsb=16) == R.RMA_ERR_WORKSPACE
+    assert _full(_kv(T=1000), sp) == R.RMA_ERR_INVALID_ARG                 # t_cap < L
+    n = L.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, ctypes.byref(kv), ctypes.byref(sp), 2, 0, 0)
+    assert n > R.RMA_WORKSPACE_COUNTER_BYTES
+    assert L.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, ctypes.byref(kv), ctypes.byref(sp), 4, 0, 0) > n
+    assert _full(kv, sp, wsb=n - 1) == R.RMA_ERR_WORKSPACE
 
 
 def test_trace_arm_validation():
