@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-phi", action="store_true",
+                    help="compute phi_q with rma_phi_features instead of inside the merge")
     ap.add_argument("--no-full", action="store_true",
                     help="skip timing the full-attention reference decode")
     ap.add_argument("--recompute-phi", action="store_true",
@@ -89,21 +91,22 @@ def measured_traffic(kernel, workload, K):
 
 
 # ------------------------------------------------------------------ byte model
-def call_bytes(cfg, K, n_gen, store_phi=True):
+def call_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
     """Algorithmic HBM bytes of each call for one batch (inputs read once,
     outputs written once; workspace scratch excluded)."""
-    kb = kernel_bytes(cfg, K, n_gen, store_phi)
+    kb = kernel_bytes(cfg, K, n_gen, store_phi, fused_phi)
     return dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
                 topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"])
 
 
-def kernel_bytes(cfg, K, n_gen, store_phi=True):
+def kernel_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
     """Algorithmic HBM bytes of each kernel for one batch.  The builder reads the
     mid-region K and V rows once (and writes phi_k once when the rows are stored;
     its per-chunk partial sums are scratch); the reduce writes S, u, kappa; the scan reads the mid-region K
     rows once (score bins and candidate lists are scratch); the select writes the
     indices and their scores; the merge reads what one query's exact support and
-    residual need."""
+    residual need.  With fused_phi the merge computes f = phi_q(q) itself (it
+    reads Wq, bq instead of f, and no phi kernel runs)."""
     U, G, d, m, P = cfg.U, cfg.G, cfg.d, cfg.m, cfg.P
     Lm, na = cfg.L_mid, cfg.n_anchor
     e = 4 if cfg.kv_dtype == "f32" else 2
@@ -116,11 +119,12 @@ def kernel_bytes(cfg, K, n_gen, store_phi=True):
     return {
         "build_mfma_kernel": U * (2 * Lm * d * e + (Lm * m * ep if store_phi else 0)) + params,
         "build_reduce_kernel": U * (m * d * 4 + m * 4 + 4),
-        "phi_kernel": U * G * (d * 4 + m * 4) + params,
+        "phi_kernel": 0 if fused_phi else U * G * (d * 4 + m * 4) + params,
         "topk_scan_kernel": U * (Lm * d * e + 4) + U * G * d * 4,
         "topk_select_kernel": U * G * K * 8,
         "merge_kernel": U * G * (K * (d * e + phi_row + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
-        + U * (m * d * 4 + m * 4) + (0 if store_phi else params),
+        + U * (m * d * 4 + m * 4) + (0 if store_phi else params)
+        + (params - U * G * m * 4 if fused_phi else 0),
     }
 
 
@@ -128,7 +132,7 @@ def kernel_bytes(cfg, K, n_gen, store_phi=True):
 class PathRunner:
     """Prepared C-ABI calls for one copy of the inputs (no per-call allocation)."""
 
-    def __init__(self, R, cfg, inp, K, ws, torch, store_phi):
+    def __init__(self, R, cfg, inp, K, ws, torch, store_phi, fused_phi=True):
         self.R, self.cfg, self.K, self.t = R, cfg, K, torch
         L = R.lib()
         self.L = L
@@ -154,6 +158,8 @@ class PathRunner:
         self.pdt = R._dt(cfg.torch_phi_dtype())
         self.Wm, self.bm = (None, None) if store_phi else (inp.W, inp.b)
         self.yf = None
+        # f = phi_q(q): computed inside the merge (fused), or by rma_phi_features
+        self.fused_phi = fused_phi
 
     def build(self, st):
         cfg, p = self.cfg, self.p
@@ -178,7 +184,8 @@ class PathRunner:
 
     def merge(self, s, st):
         cfg, p = self.cfg, self.p
-        r = self.L.rma_decode_merge(p(self.q[s]), p(self.f[s]), cfg.G, ctypes.byref(self.kv),
+        f, Wq, bq = (None, self.W, self.b) if self.fused_phi else (self.f[s], None, None)
+        r = self.L.rma_decode_merge(p(self.q[s]), p(f), p(Wq), p(bq), cfg.G, ctypes.byref(self.kv),
                                     ctypes.byref(self.sp_dec[s]), p(self.idx[s]), p(self.sel[s]), self.K,
                                     p(self.phi_k), self.pdt, p(self.Wm), p(self.bm), cfg.P, cfg.m, p(self.S),
                                     p(self.u), 0, p(self.y[s]), None, p(self.ws), self.ws.numel(), st)
@@ -197,7 +204,8 @@ class PathRunner:
         """The whole path: prefill summaries, then every decode step."""
         self.build(st)
         for s in range(self.cfg.steps):
-            self.phi(s, st)
+            if not self.fused_phi:
+                self.phi(s, st)
             self.topk(s, st)
             self.merge(s, st)
 
@@ -217,7 +225,8 @@ class PathRunner:
 
         traced("build", lambda: self.build(st))
         for s in range(self.cfg.steps):
-            traced("phi", lambda: self.phi(s, st))
+            if not self.fused_phi:
+                traced("phi", lambda: self.phi(s, st))
             traced("topk", lambda: self.topk(s, st))
             traced("merge", lambda: self.merge(s, st))
         return out
@@ -264,7 +273,8 @@ def decode_timing(args, cfg, runners, n_copies, stream, st, use_graphs, queries,
     def dec(i):
         r = runners[i % n_copies]
         for s in range(cfg.steps):
-            r.phi(s, st)
+            if not r.fused_phi:
+                r.phi(s, st)
             r.topk(s, st)
             r.merge(s, st)
 
@@ -373,7 +383,8 @@ def main():
     if not args.no_full:
         wsb = max(wsb, R.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, inp.k, sp, cfg.G, 0, cfg.m))
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi) for c in copies]
+    fused_phi = not args.separate_phi
+    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi, fused_phi) for c in copies]
     log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
 
     stream = torch.cuda.Stream()
@@ -442,7 +453,7 @@ def main():
         for i in range(n_t):
             recs.append(runners[i % n_copies].traced_step(st, R))
     torch.cuda.synchronize()
-    names = ["build", "phi", "topk", "merge"]
+    names = ["build", "topk", "merge"] if fused_phi else ["build", "phi", "topk", "merge"]
     call_ms = {n: 0.0 for n in names}
     kern_ms, kern_n = {}, {}
     for rec in recs:
@@ -454,10 +465,10 @@ def main():
     dur = {n: call_ms[n] / n_t for n in names}                       # ms per step
     kavg = {k: kern_ms[k] / kern_n[k] for k in kern_ms}               # ms per launch
     launches = {k: kern_n[k] / n_t for k in kern_n}                  # launches per step
-    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi)
-    kb = kernel_bytes(cfg, K, cfg.n_gen(0), store_phi)
-    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi)[c] for s in range(cfg.steps)
-                                   for c in ("phi", "topk", "merge"))
+    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi)
+    kb = kernel_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi)
+    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi, fused_phi)[c]
+                                   for s in range(cfg.steps) for c in ("phi", "topk", "merge"))
     gbs = {n: nb[n] * (1 if n == "build" else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
     kgbs = {k: kb[k] / (kavg[k] / 1e3) / 1e9 for k in kavg}
     for n in names:
@@ -467,7 +478,7 @@ def main():
             f"{kb[k] / 1e6:8.2f} MB  {kgbs[k]:8.1f} GB/s")
     log(f"[bench] step {ms_per_step * 1e3:.2f} us, {step_bytes / 1e6:.1f} MB algorithmic "
         f"-> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; {value / 1e6:.3f} M queries/s")
-    decode_us = sum(dur[n] for n in ("phi", "topk", "merge")) * 1e3
+    decode_us = sum(dur[n] for n in names if n != "build") * 1e3
     dom = max(kavg, key=lambda k: kavg[k] * launches[k])     # most time per step
     achieved = kgbs[dom]
     traffic = measured_traffic(dom, cfg.name, K)
@@ -490,7 +501,8 @@ def main():
             "units": cfg.U, "query_heads_per_unit": cfg.G, "head_dim": cfg.d, "context": cfg.L,
             "anchors": [cfg.n_sink, cfg.n_tail], "K": K, "phi_features": cfg.m,
             "decode_steps": cfg.steps, "queries_per_step": queries,
-            "step": "prefill summaries + phi_q + top-K + merge",
+            "step": ("prefill summaries + top-K + merge (phi_q computed inside the merge)" if fused_phi
+                     else "prefill summaries + phi_q + top-K + merge"),
             "phi_k_rows": "stored" if store_phi else "recomputed at decode (not stored)",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
             "rotating_copies": n_copies, "launch": "hip_graph" if graphs is not None else "eager",

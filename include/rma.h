@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 3
+#define RMA_ABI_VERSION 4
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -179,7 +179,11 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
  *   against subtraction artifacts),
  *   y = (N_E + e^{-m*} nu_R) / (Z_E + e^{-m*} Z_R).
  * q: fp32 [n_units][G][d];  phi_q: fp32 [n_units][G][m] (any positive
- * features; rma_phi_features gives phi_q).  idx, sel_scores as written by
+ * features; rma_phi_features gives phi_q), or NULL with Wq, bq given: then
+ * f = elu(Wq q + bq) + 1 is computed inside this call (fp32; Wq fp32
+ * [n_param_sets][m][d], bq fp32 [n_param_sets][m], unit u uses set
+ * u % n_param_sets), which spares the separate rma_phi_features launch.  Wq,
+ * bq are ignored when phi_q is given.  idx, sel_scores as written by
  * rma_decode_topk (K per head).  phi_k, S, u_ as written/used by
  * rma_build_summaries.  When the subtraction needs Phi_K rows (RMA_MERGE_SUB,
  * 0 < K < L_mid) and phi_k is NULL, they are recomputed from the retrieved
@@ -194,7 +198,8 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
  * Requires n_sink + n_tail + n_gen + K > 0.
  * Workspace: rma_workspace_bytes(RMA_OP_DECODE_MERGE, ...).
  */
-rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
+rma_status rma_decode_merge(const float* q, const float* phi_q, const float* Wq,
+                            const float* bq, int32_t G, const rma_kv* kv,
                             const rma_span* span, const int32_t* idx, const float* sel_scores,
                             int32_t K, const void* phi_k, int32_t phi_dtype, const float* Wk,
                             const float* bk, int32_t n_param_sets, int32_t m, const float* S,

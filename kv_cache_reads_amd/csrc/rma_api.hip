@@ -344,7 +344,8 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
   return RMA_OK;
 }
 
-rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const rma_kv* kv,
+rma_status rma_decode_merge(const float* q, const float* phi_q, const float* Wq,
+                            const float* bq, int32_t G, const rma_kv* kv,
                             const rma_span* sp, const int32_t* idx, const float* sel, int32_t K,
                             const void* phi_k, int32_t phi_dtype, const float* Wk,
                             const float* bk, int32_t P, int32_t m, const float* S,
@@ -365,13 +366,16 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
   const bool need_res = flags != RMA_MERGE_NO_RESIDUAL;
   RMA_CHECK(q && y, RMA_ERR_INVALID_ARG, "NULL q or y");
   RMA_CHECK(K == 0 || (idx && sel), RMA_ERR_INVALID_ARG, "NULL idx or sel_scores");
-  RMA_CHECK(!need_res || (phi_q && S && u), RMA_ERR_INVALID_ARG, "NULL phi_q, S or u");
+  RMA_CHECK(!need_res || (S && u), RMA_ERR_INVALID_ARG, "NULL S or u");
+  RMA_CHECK(!need_res || phi_q || (Wq && bq && P >= 1), RMA_ERR_INVALID_ARG,
+            "NULL phi_q and no Wq/bq to compute it");
   const bool need_phik = flags == RMA_MERGE_SUB && K > 0 && K < l_mid(*sp);
   RMA_CHECK(!need_phik || phi_k != nullptr || (Wk != nullptr && bk != nullptr && P >= 1),
             RMA_ERR_INVALID_ARG, "NULL phi_k and no Wk/bk to recompute it");
   RMA_CHECK(!need_phik || phi_k != nullptr || (kv->dtype == RMA_BF16 && phi_dtype == RMA_BF16),
             RMA_ERR_UNSUPPORTED, "recomputed phi_k rows need bf16 keys and bf16 phi rounding");
-  RMA_CHECK(aligned16(q) && aligned16(phi_q) && aligned16(idx) && aligned16(sel) &&
+  RMA_CHECK(aligned16(q) && aligned16(phi_q) && aligned16(Wq) && aligned16(bq) &&
+                aligned16(idx) && aligned16(sel) &&
                 aligned16(phi_k) && aligned16(Wk) && aligned16(bk) && aligned16(S) &&
                 aligned16(u) && aligned16(y) && aligned16(stats),
             RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
@@ -382,7 +386,8 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, int32_t G, const
             workspace_bytes, pl.total);
   TraceScope ts((hipStream_t)stream);
   // stored rows take precedence; the recompute runs only when they are absent
-  hipError_t e = launch_merge(pl, q, phi_q, G, *kv, *sp, idx, sel, K, phi_k, phi_dtype,
+  hipError_t e = launch_merge(pl, q, phi_q, phi_q ? nullptr : Wq, bq, G, *kv, *sp, idx, sel, K,
+                              phi_k, phi_dtype,
                               phi_k ? nullptr : Wk, bk, P, m, S, u, flags, y, stats,
                               (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

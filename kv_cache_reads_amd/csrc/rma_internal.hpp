@@ -103,7 +103,8 @@ hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& 
                        const rma_span& sp, const float* kappa, int K, int32_t* idx,
                        float* sel_scores, uint8_t* ws, hipStream_t st);
 
-hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,
+hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, const float* Wq,
+                        const float* bq, int G,
                         const rma_kv& kv, const rma_span& sp, const int32_t* idx,
                         const float* sel, int K, const void* phi_k, int phi_dtype,
                         const float* Wk, const float* bk, int P, int m, const float* S,

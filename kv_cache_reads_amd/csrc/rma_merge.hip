@@ -62,7 +62,8 @@ struct RawPiece {
 // summaries contain.  Needs bf16 keys.
 template <typename KT, typename PT, int D, int M, bool RECOMP>
 __global__ void __launch_bounds__(kMergeThreads)
-merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G,
+merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
+             const float* __restrict__ Wq, const float* __restrict__ bq, int G,
              const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int L,
              int n_sink, int n_tail, int n_gen, const int32_t* __restrict__ idx,
              const float* __restrict__ sel, int K, const PT* __restrict__ phik, int L_mid,
@@ -96,6 +97,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
   __shared__ float s_wm[NW], s_wz[NW], s_wzk[NW];
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
+  __shared__ float s_f[M];          // f = phi_q(q) of this head
   // recompute: key rows of a batch of retrieved tokens, per-feature-tile partial
   // weights, and the weights w_i = f.phi_k(k_i) of the chunk's retrieved entries
   constexpr int TS = D == 64 ? 512 : 256;  // tokens per recompute batch (LDS bound)
@@ -152,16 +154,6 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     const float4 t = *reinterpret_cast<const float4*>(qg + part * CPL + i);
     qr[i] = t.x; qr[i + 1] = t.y; qr[i + 2] = t.z; qr[i + 3] = t.w;
   }
-  if (sub) {
-#pragma unroll
-    for (int i = 0; i < FPL; i += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(phi_q + (size_t)ug * M + part * FPL + i);
-      fr[i] = t.x; fr[i + 1] = t.y; fr[i + 2] = t.z; fr[i + 3] = t.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FPL; ++i) fr[i] = 0.f;
-  }
 
   // ---- operands of phi(q)^T S and u^T f, loaded now and used after the
   //      entries, so that their latency overlaps the gathers.  For one head
@@ -178,25 +170,14 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
     const size_t sst = rs ? D : 0;
 #pragma unroll
     for (int i = 0; i < FPB; ++i) sv[i] = Sp[sst * i];
-    // fb is the same for a whole wave: the f slice is a scalar (SGPR) load
-    const float* fp = rs ? phi_q + (size_t)ug * M + __builtin_amdgcn_readfirstlane(fb) * FPB : qg;
-#pragma unroll
-    for (int i = 0; i < FPB; i += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(fp + (rs ? i : 0));
-      fv[i] = t.x; fv[i + 1] = t.y; fv[i + 2] = t.z; fv[i + 3] = t.w;
-    }
   }
   constexpr int UPL = (M + kWave - 1) / kWave;   // u^T f terms per lane (last wave)
   float uu[UPL], uf[UPL];
 #pragma unroll
-  for (int i = 0; i < UPL; ++i) {
-    const int f = min(lane + kWave * i, M - 1);
-    uu[i] = rs ? u_[(size_t)u * M + f] : 0.f;
-    uf[i] = rs ? phi_q[(size_t)ug * M + f] : 0.f;
-  }
+  for (int i = 0; i < UPL; ++i) uu[i] = rs ? u_[(size_t)u * M + min(lane + kWave * i, M - 1)] : 0.f;
 
   // recompute operands of this wave's 16-feature tile (W split into bf16 hi + lo,
-  // bias, f), derived with the prologue loads in flight
+  // bias), derived with the prologue loads in flight
   constexpr int RKS = RECOMP ? D / 32 : 1;
   bf16x8_t rWhi[RKS], rWlo[RKS];
   float rbf = 0.f, rfq = 0.f;
@@ -205,8 +186,42 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
       const int f = (wave % NFT) * 16 + (lane & 15), pset = u % P;
       split_w_operands<RKS>(Wk + ((size_t)pset * M + f) * D + 8 * (lane >> 4), rWhi, rWlo);
       rbf = bk[(size_t)pset * M + f];
-      rfq = phi_q[(size_t)ug * M + f];
     }
+  }
+
+  // ---- f = phi_q(q) into LDS: the given features, or elu(Wq q + bq) + 1
+  //      computed here (NT/M threads per feature, fp32, fixed sum order)
+  if (resid) {
+    if (Wq != nullptr) {
+      constexpr int TPF = NT / M, EPT = D / TPF;
+      const int fi = tid / TPF, fpart = tid % TPF, pset = u % P;
+      const float* wr = Wq + ((size_t)pset * M + fi) * D + fpart * EPT;
+      const float* qs = qg + fpart * EPT;
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wr + i);
+        const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
+        z = __fmaf_rn(w4.x, x4.x, z);
+        z = __fmaf_rn(w4.y, x4.y, z);
+        z = __fmaf_rn(w4.z, x4.z, z);
+        z = __fmaf_rn(w4.w, x4.w, z);
+      }
+      z = lane_group_sum<TPF>(z);
+      if (fpart == 0) s_f[fi] = phi_elu1(z + bq[(size_t)pset * M + fi]);
+    } else {
+      for (int i = tid; i < M; i += NT) s_f[i] = phi_q[(size_t)ug * M + i];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < FPB; ++i) fv[i] = rs ? s_f[fb * FPB + i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < UPL; ++i) uf[i] = rs ? s_f[min(lane + kWave * i, M - 1)] : 0.f;
+  if constexpr (RECOMP) {
+    if (sub) rfq = s_f[(wave % NFT) * 16 + (lane & 15)];
   }
 
   // w_i of the retrieved entries [r0, cnt) of the staged chunk, into s_w
@@ -425,7 +440,8 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q, int G
 }
 
 template <typename KT, typename PT, int D>
-hipError_t launch_merge_t(const float* q, const float* phi_q, int G, const rma_kv& kv,
+hipError_t launch_merge_t(const float* q, const float* phi_q, const float* Wq, const float* bq,
+                          int G, const rma_kv& kv,
                           const rma_span& sp, const int32_t* idx, const float* sel, int K,
                           const void* phi_k, const float* Wk, const float* bk, int P, int m,
                           const float* S, const float* u, uint32_t flags, float* y, float* stats,
@@ -436,7 +452,7 @@ hipError_t launch_merge_t(const float* q, const float* phi_q, int G, const rma_k
   if constexpr (sizeof(KT) == 2 && sizeof(PT) == 2) {
     if (recomp) kern = m == 64 ? merge_kernel<KT, PT, D, 64, true> : merge_kernel<KT, PT, D, 128, true>;
   }
-  hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(kMergeThreads), 0, st, q, phi_q, G,
+  hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(kMergeThreads), 0, st, q, phi_q, Wq, bq, G,
                      static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
                      (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx, sel, K,
                      static_cast<const PT*>(phi_k), L_mid, Wk, bk, P, S, u, flags, y, stats,
@@ -446,7 +462,8 @@ hipError_t launch_merge_t(const float* q, const float* phi_q, int G, const rma_k
   return e;
 }
 
-hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, int G,
+hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, const float* Wq,
+                        const float* bq, int G,
                         const rma_kv& kv, const rma_span& sp, const int32_t* idx,
                         const float* sel, int K, const void* phi_k, int phi_dtype,
                         const float* Wk, const float* bk, int P, int m, const float* S,
@@ -455,9 +472,9 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
   (void)pl;
   (void)ws;
 #define RMA_MERGE_DISPATCH(KT, PT)                                                              \
-  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(q, phi_q, G, kv, sp, idx, sel, K, phi_k, Wk, bk, \
+  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(q, phi_q, Wq, bq, G, kv, sp, idx, sel, K, phi_k, Wk, bk, \
                                                  P, m, S, u, flags, y, stats, st)                \
-                    : launch_merge_t<KT, PT, 128>(q, phi_q, G, kv, sp, idx, sel, K, phi_k, Wk,   \
+                    : launch_merge_t<KT, PT, 128>(q, phi_q, Wq, bq, G, kv, sp, idx, sel, K, phi_k, Wk,   \
                                                   bk, P, m, S, u, flags, y, stats, st);
   if (kv.dtype == RMA_BF16) {
     if (phi_dtype == RMA_BF16) { RMA_MERGE_DISPATCH(uint16_t, uint16_t) }

@@ -76,8 +76,8 @@ def lib():
     L.rma_phi_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP]
     L.rma_build_summaries.argtypes = [P_KV, P_SP, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
-    L.rma_decode_merge.argtypes = [_VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _I32,
-                                   _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_merge.argtypes = [_VP, _VP, _VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
+                                   _I32, _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_full.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_workspace_bytes.argtypes = [_I32, P_KV, P_SP, _I32, _I32, _I32]
     L.rma_workspace_bytes.restype = _SZ
@@ -232,9 +232,11 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
                      phi_k: Optional[torch.Tensor], S: Optional[torch.Tensor], u: Optional[torch.Tensor],
                      flags: int = RMA_MERGE_SUB, m: Optional[int] = None, want_stats: bool = False,
                      ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None,
-                     Wk: Optional[torch.Tensor] = None, bk: Optional[torch.Tensor] = None):
+                     Wk: Optional[torch.Tensor] = None, bk: Optional[torch.Tensor] = None,
+                     Wq: Optional[torch.Tensor] = None, bq: Optional[torch.Tensor] = None):
     """Returns y [U, G, d] (and stats [U, G, 4] = (m*, Z_E, Z_R, retrieved phi mass)).
-    With phi_k None, the retrieved phi_k rows are recomputed from Wk, bk."""
+    With phi_k None, the retrieved phi_k rows are recomputed from Wk, bk; with
+    phi_q None, f = phi_q(q) is computed in the call from Wq, bq."""
     U, G, d = q.shape
     if m is None:
         m = S.shape[1] if S is not None else 128
@@ -245,8 +247,8 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
     nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE_MERGE, ctypes.byref(kv), ctypes.byref(sp), G, K, m))
     w = _ws(ws, nb)
     pdt = _dt(phi_k.dtype) if phi_k is not None else RMA_BF16
-    P = Wk.shape[0] if Wk is not None else 1
-    _check(lib().rma_decode_merge(_p(q), _p(phi_q), G, ctypes.byref(kv), ctypes.byref(sp), _p(idx),
+    P = Wk.shape[0] if Wk is not None else (Wq.shape[0] if Wq is not None else 1)
+    _check(lib().rma_decode_merge(_p(q), _p(phi_q), _p(Wq), _p(bq), G, ctypes.byref(kv), ctypes.byref(sp), _p(idx),
                                   _p(sel_scores), K, _p(phi_k), pdt, _p(Wk), _p(bk), P, m, _p(S), _p(u),
                                   flags, _p(y), _p(stats), _p(w), w.numel(), _stream()))
     return (y, stats) if want_stats else y

@@ -48,14 +48,17 @@ def hip_prefill(inp, ws=None, store_phi=True):
                                  phi_dtype=cfg.torch_phi_dtype(), ws=ws, store_phi=store_phi)
 
 
-def hip_decode(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None):
+def hip_decode(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None, fused_phi=False):
+    """fused_phi: the merge computes f = phi_q(q) from W, b itself."""
     cfg = inp.cfg
     phi_k, S, u, kappa = pre
     q = inp.q[step].contiguous()
-    f = R.rma_phi_features(q, inp.W, inp.b)
+    f = None if fused_phi else R.rma_phi_features(q, inp.W, inp.b)
     sp = decode_span(cfg, step)
     idx, sel = R.rma_decode_topk(q, inp.k, sp, kappa, K, ws=ws)
     recompute = dict(Wk=inp.W, bk=inp.b) if phi_k is None else {}
+    if fused_phi:
+        recompute.update(Wq=inp.W, bq=inp.b)
     y, stats = R.rma_decode_merge(q, f, inp.k, inp.v, sp, idx, sel, K, phi_k, S, u, flags=flags,
                                   want_stats=True, ws=ws, m=cfg.m, **recompute)
     return dict(idx=idx, sel=sel, y=y, stats=stats, f=f)

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 3
+    assert L.rma_abi_version() == 4
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -69,26 +69,33 @@ def test_build_and_merge_validation_errors():
     assert st == R.RMA_ERR_WORKSPACE
     # merge: empty exact support, unknown flags, NULL phi_q with residual
     sp0 = _sp(L=1024, ns=0, nt=0)
-    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kv), ctypes.byref(sp0), 0x2000, 0x2100, 0,
+    st = L.rma_decode_merge(0x1000, 0x1100, None, None, 2, ctypes.byref(kv), ctypes.byref(sp0), 0x2000, 0x2100, 0,
                             0x3000, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
     assert st == R.RMA_ERR_INVALID_ARG
-    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+    st = L.rma_decode_merge(0x1000, 0x1100, None, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
                             0x3000, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 7, 0x6000, None, 0x7000, 1 << 30, None)
     assert st == R.RMA_ERR_INVALID_ARG
-    st = L.rma_decode_merge(0x1000, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+    st = L.rma_decode_merge(0x1000, None, None, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+                            0x3000, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG
+    # phi_q computed in the call needs both Wq and bq, 16-byte aligned
+    st = L.rma_decode_merge(0x1000, None, 0x8000, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+                            0x3000, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
+    assert st == R.RMA_ERR_INVALID_ARG
+    st = L.rma_decode_merge(0x1000, None, 0x8004, 0x9000, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
                             0x3000, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000, 1 << 30, None)
     assert st == R.RMA_ERR_INVALID_ARG
     st = L.rma_phi_features(0x1000, R.RMA_F32, 1, 4, 4 * 64, 64, 0x2000, 0x3000, 100, 1, 0x4000,
                             R.RMA_F32, None)
     assert st == R.RMA_ERR_UNSUPPORTED
     # subtraction without phi_k rows needs Wk/bk to recompute them ...
-    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
+    st = L.rma_decode_merge(0x1000, 0x1100, None, None, 2, ctypes.byref(kv), ctypes.byref(sp), 0x2000, 0x2100, 10,
                             None, R.RMA_BF16, None, None, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000,
                             1 << 30, None)
     assert st == R.RMA_ERR_INVALID_ARG
     # ... and bf16 keys (the builder's rounding)
     kvf = _kv(dtype=R.RMA_F32)
-    st = L.rma_decode_merge(0x1000, 0x1100, 2, ctypes.byref(kvf), ctypes.byref(sp), 0x2000, 0x2100, 10,
+    st = L.rma_decode_merge(0x1000, 0x1100, None, None, 2, ctypes.byref(kvf), ctypes.byref(sp), 0x2000, 0x2100, 10,
                             None, R.RMA_BF16, 0x8000, 0x9000, 1, 128, 0x4000, 0x5000, 0, 0x6000, None, 0x7000,
                             1 << 30, None)
     assert st == R.RMA_ERR_UNSUPPORTED

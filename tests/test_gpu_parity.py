@@ -31,7 +31,7 @@ def _gen(cfg):
     return W.generate(cfg, device=DEV)
 
 
-def _run_case(cfg, units, Ks=None, steps=None, check_pre=True, store_phi=True):
+def _run_case(cfg, units, Ks=None, steps=None, check_pre=True, store_phi=True, fused_phi=False):
     inp = _gen(cfg)
     pre = hip_prefill(inp, store_phi=store_phi)
     torch.cuda.synchronize()
@@ -40,8 +40,8 @@ def _run_case(cfg, units, Ks=None, steps=None, check_pre=True, store_phi=True):
     gpu = {}
     for K in Ks:
         for st in steps:
-            out = hip_decode(inp, pre, K, st)
-            gpu[(K, st)] = {k: v.cpu() for k, v in out.items()}
+            out = hip_decode(inp, pre, K, st, fused_phi=fused_phi)
+            gpu[(K, st)] = {k: v.cpu() for k, v in out.items() if v is not None}
     torch.cuda.synchronize()
     worst = (0.0, 0.0)
     for u in units:
@@ -78,6 +78,31 @@ def test_small_configs_recomputed_phi_rows(name):
     _run_case(cfg, range(cfg.U), store_phi=False)
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs_phi_q_inside_merge(name):
+    """f = phi_q(q) computed inside the merge (no rma_phi_features launch)."""
+    cfg = SMALL[name]
+    log(f"case {name} (phi_q inside the merge)")
+    _run_case(cfg, range(cfg.U), fused_phi=True)
+    if cfg.kv_dtype == "bf16":
+        _run_case(cfg, range(cfg.U), store_phi=False, fused_phi=True)
+
+
+def test_phi_q_inside_merge_matches_separate_features():
+    """Both ways compute f = elu(W q + b) + 1 in fp32 (different sum orders):
+    the outputs agree to fp32 rounding of f."""
+    cfg = SMALL["c1_small"]
+    inp = _gen(cfg)
+    pre = hip_prefill(inp)
+    for flags in (R.RMA_MERGE_SUB, R.RMA_MERGE_NO_SUBTRACT, R.RMA_MERGE_NO_RESIDUAL):
+        a = hip_decode(inp, pre, cfg.K[0], 0, flags=flags)
+        b = hip_decode(inp, pre, cfg.K[0], 0, flags=flags, fused_phi=True)
+        ya, yb = a["y"].double(), b["y"].double()
+        rel = float(((ya - yb).norm(dim=-1) / ya.norm(dim=-1)).max())
+        log(f"flags {flags}: separate vs fused phi_q max rel {rel:.2e}")
+        assert rel <= 1e-5
+
+
 def test_recomputed_phi_rows_match_stored_rows():
     """The recompute uses the builder's projection, rounding and MFMA order, so
     the rows subtracted equal the rows summed: y agrees with the stored-row path
@@ -107,9 +132,10 @@ def test_c0_exact_ties_and_outputs():
 
 
 @pytest.mark.parametrize("store_phi", [True, False])
-def test_c1_full(store_phi):
+@pytest.mark.parametrize("fused_phi", [False, True])
+def test_c1_full(store_phi, fused_phi):
     cfg = W.CONFIGS["c1"]
-    _run_case(cfg, range(cfg.U), store_phi=store_phi)
+    _run_case(cfg, range(cfg.U), store_phi=store_phi, fused_phi=fused_phi)
 
 
 @pytest.mark.parametrize("store_phi", [True, False])
