@@ -389,7 +389,10 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   __shared__ int s_bcs[kSelMaxChunks];
   __shared__ int s_nrep[kSelMaxChunks];
   __shared__ uint32_t hist[NBS];
-  __shared__ uint32_t bmin[NBS], bmax[NBS];   // per-bin score extent (order-preserving keys)
+  __shared__ float s_cand[kSelBandMax];       // scores of the K-th score's bin
+  __shared__ int s_cnt;
+  __shared__ uint32_t s_xlo, s_xhi;           // extent of that bin (order-preserving keys)
+  __shared__ float s_t;
   __shared__ int s_buf[257];
   __shared__ int s_misc[8];
   __shared__ float s_fl[2 * NWV];
@@ -499,11 +502,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     lo = wave_min_dpp(lo);
     hi = wave_max_dpp(hi);
     if (lane == 0) { s_fl[wave] = lo; s_fl[NWV + wave] = hi; }
-    for (int b = tid; b < NBS; b += NT) {
-      hist[b] = 0u;
-      bmin[b] = 0xffffffffu;
-      bmax[b] = 0u;
-    }
+    for (int b = tid; b < NBS; b += NT) hist[b] = 0u;
     __syncthreads();
     lo = INFINITY;
     hi = -INFINITY;
@@ -514,14 +513,8 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
       const float t = __fmul_rn(__fsub_rn(x, lo), inv);
       return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
     };
-    // linear histogram over the range, with each bin's exact score extent
-    for (int i = tid; i < nE; i += NT) {
-      const float x = es[i];
-      const int b = ubin(x);
-      atomicAdd(&hist[b], 1u);
-      atomicMin(&bmin[b], ord_f32(x));
-      atomicMax(&bmax[b], ord_f32(x));
-    }
+    // linear histogram over the range
+    for (int i = tid; i < nE; i += NT) atomicAdd(&hist[ubin(es[i])], 1u);
     __syncthreads();
     // bin of the K-th largest score: thread t owns bins NBS-BPT*t-1 .. NBS-BPT*(t+1)
     // (descending)
@@ -536,17 +529,50 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
         int run = ex;
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
-          if (run < K && run + cb[j] >= K) s_misc[0] = NBS - BPT * tid - 1 - j;
+          if (run < K && run + cb[j] >= K) {
+            s_misc[0] = NBS - BPT * tid - 1 - j;
+            s_misc[1] = run;  // entries in the bins above
+          }
           run += cb[j];
         }
       }
+      if (tid == 0) { s_cnt = 0; s_xlo = 0xffffffffu; s_xhi = 0u; }
     }
     __syncthreads();
-    const int bK = s_misc[0];
-    // exact extent of that bin: the K-th largest score t lies in [xlo, xhi]
-    const float xlo = unord_f32(bmin[bK]), xhi = unord_f32(bmax[bK]);
-    th_lo = xlo - 2.5f * hp.eps;
-    th_hi = xhi + 2.5f * hp.eps;
+    const int bK = s_misc[0], rK = K - s_misc[1];  // the K-th score is the rK-th largest of bin bK
+    // the bin's members: their scores (up to kSelBandMax) and its exact extent
+    for (int i = tid; i < nE; i += NT) {
+      const float x = es[i];
+      if (ubin(x) == bK) {
+        const int j = atomicAdd(&s_cnt, 1);
+        if (j < kSelBandMax) s_cand[j] = x;
+        atomicMin(&s_xlo, ord_f32(x));
+        atomicMax(&s_xhi, ord_f32(x));
+      }
+    }
+    __syncthreads();
+    const int nm = s_cnt;
+    float t_lo = unord_f32(s_xlo), t_hi = unord_f32(s_xhi);
+    if (nm <= kSelBandMax) {
+      // t = the rK-th largest member score = the K-th largest fp32 score of the
+      // union (every member holding that value writes the same bits)
+      for (int j = tid; j < nm; j += NT) {
+        const float x = s_cand[j];
+        int gt = 0, ge = 0;
+        for (int k2 = 0; k2 < nm; ++k2) {
+          const float y = s_cand[k2];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < rK && rK <= ge) s_t = x;
+      }
+      __syncthreads();
+      t_lo = t_hi = s_t;
+    }
+    // the true K-th score lies within eps of t (or of the bin's extent when
+    // the bin is too full to rank): outside +-2.5 eps the fp32 order is exact
+    th_lo = t_lo - 2.5f * hp.eps;
+    th_hi = t_hi + 2.5f * hp.eps;
     // every chunk must have reported all of its tokens scoring >= th_lo
     const int blo = lin_bin(th_lo, hp);
     int bad = 0;
