@@ -14,8 +14,8 @@
 //     Z_R = sum_{M minus K(q)} e^{s-m}
 //   over the rows it reads; lanes and waves are then combined with max
 //   rescaling into one record per (unit, chunk, head).
-// full_combine  grid (units * G), 128 threads: combines the chunk records in
-//   chunk order, writes y_full = N / Z and the diagnostics.
+// full_combine  grid (units * G), 256 threads: combines the chunk records with
+//   a fixed order, writes y_full = N / Z and the diagnostics.
 #include "rma_device.hpp"
 #include "rma_internal.hpp"
 
@@ -292,54 +292,78 @@ full_partial_kernel(const float* __restrict__ q, const KT* __restrict__ kb,
   }
 }
 
-// One block per (unit, head): the chunk records in chunk order.  The maximum
-// comes first, so every record's scale is known before its sums are read and
-// the record loads are independent (issued in batches of eight).
+// One block per (unit, head).  The maximum over the chunk records comes first
+// (every thread a stride of chunks, then a block max), so every record's scale
+// is known before its sums are read; then NT/D groups of threads take every
+// (NT/D)-th chunk (record loads issued in batches of eight) and the group sums
+// are added in group order.
 template <int D>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(kFullCombineThreads)
 full_combine_kernel(const float* __restrict__ part, int G, int n_chunks, int L_mid, int resid_mode,
                     const float* __restrict__ y_cmp, float* __restrict__ y_full,
                     float* __restrict__ diag) {
-  constexpr int REC = kFullRecHead + D, BT = 8;
+  constexpr int NT = kFullCombineThreads, NWV = NT / kWave;
+  constexpr int REC = kFullRecHead + D, CG = NT / D, BT = 8;
+  __shared__ float s_red[NWV];
+  __shared__ float s_nn[CG][D];
+  __shared__ float s_st[CG][4];
+  __shared__ float s_l1[NWV][2];
   const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const int col = tid % D, grp = tid / D;
   const float* rec0 = part + ((size_t)u * n_chunks * G + g) * REC;
   const size_t cstride = (size_t)G * REC;
-  const int col = tid < D ? tid : 0;
   float M = -INFINITY;
-  for (int c0 = 0; c0 < n_chunks; c0 += BT) {
-    float mb[BT];
+  for (int c = tid; c < n_chunks; c += NT) M = fmaxf(M, rec0[(size_t)c * cstride]);
+  M = wave_max_dpp(M);
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = s_red[0];
 #pragma unroll
-    for (int i = 0; i < BT; ++i) mb[i] = rec0[(size_t)min(c0 + i, n_chunks - 1) * cstride];
-#pragma unroll
-    for (int i = 0; i < BT; ++i) M = fmaxf(M, mb[i]);
-  }
-  // sums relative to M in chunk order; T_M moves with each record's shift
-  Acc a{M, 0.f, 0.f, 0.f, 0.f};
-  float nn = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += BT) {
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_red[w]);
+  // sums relative to M; T_M moves with each record's shift
+  float z = 0.f, zm = 0.f, tm = 0.f, zr = 0.f, nn = 0.f;
+  for (int c0 = grp; c0 < n_chunks; c0 += CG * BT) {
     float r[BT][5], rn[BT];
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
-      const float* rc = rec0 + (size_t)min(c0 + i, n_chunks - 1) * cstride;
+      const float* rc = rec0 + (size_t)min(c0 + i * CG, n_chunks - 1) * cstride;
 #pragma unroll
       for (int j = 0; j < 5; ++j) r[i][j] = rc[j];
       rn[i] = rc[kFullRecHead + col];
     }
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
-      if (c0 + i < n_chunks) {
+      if (c0 + i * CG < n_chunks) {
         const bool live = r[i][0] != -INFINITY;
         const float sc = live ? __expf(r[i][0] - M) : 0.f;
         const float dm = live ? r[i][0] - M : 0.f;
-        a.z = __fmaf_rn(sc, r[i][1], a.z);
-        a.tm = __fmaf_rn(sc, r[i][3] + dm * r[i][2], a.tm);
-        a.zm = __fmaf_rn(sc, r[i][2], a.zm);
-        a.zr = __fmaf_rn(sc, r[i][4], a.zr);
+        z = __fmaf_rn(sc, r[i][1], z);
+        tm = __fmaf_rn(sc, r[i][3] + dm * r[i][2], tm);
+        zm = __fmaf_rn(sc, r[i][2], zm);
+        zr = __fmaf_rn(sc, r[i][4], zr);
         nn = __fmaf_rn(sc, rn[i], nn);
       }
     }
   }
-  const float yv = nn / a.z;
+  s_nn[grp][col] = nn;
+  if (col == 0) {
+    s_st[grp][0] = z;
+    s_st[grp][1] = zm;
+    s_st[grp][2] = tm;
+    s_st[grp][3] = zr;
+  }
+  __syncthreads();
+  z = 0.f, zm = 0.f, tm = 0.f, zr = 0.f, nn = 0.f;
+#pragma unroll
+  for (int k = 0; k < CG; ++k) {
+    nn += s_nn[k][col];
+    z += s_st[k][0];
+    zm += s_st[k][1];
+    tm += s_st[k][2];
+    zr += s_st[k][3];
+  }
+  const float yv = nn / z;
   float dl1 = 0.f, rl1 = 0.f;
   if (tid < D) {
     y_full[(size_t)ug * D + tid] = yv;
@@ -349,24 +373,25 @@ full_combine_kernel(const float* __restrict__ part, int G, int n_chunks, int L_m
     }
   }
   if (diag == nullptr) return;
-  __shared__ float s_l1[2][2];
   dl1 = wave_sum_dpp(dl1);
   rl1 = wave_sum_dpp(rl1);
-  if ((tid & (kWave - 1)) == 0) {
-    s_l1[tid >> 6][0] = dl1;
-    s_l1[tid >> 6][1] = rl1;
+  if (lane == 0) {
+    s_l1[wave][0] = dl1;
+    s_l1[wave][1] = rl1;
   }
   __syncthreads();
   if (tid == 0) {
+    float sd = 0.f, sr = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) { sd += s_l1[w][0]; sr += s_l1[w][1]; }
     float* dg = diag + (size_t)ug * 8;
-    const float lz = a.m + logf(a.z);
-    const float lzm = a.zm > 0.f ? a.m + logf(a.zm) : -INFINITY;
-    dg[0] = lz;
+    const float lzm = zm > 0.f ? M + logf(zm) : -INFINITY;
+    dg[0] = M + logf(z);
     dg[1] = lzm;
-    dg[2] = resid_mode == 0 ? NAN : (a.zr > 0.f ? a.m + logf(a.zr) : -INFINITY);
-    dg[3] = (L_mid >= 2 && a.zm > 0.f) ? (logf(a.zm) - a.tm / a.zm) / logf((float)L_mid) : NAN;
-    dg[4] = y_cmp != nullptr ? (s_l1[0][0] + s_l1[1][0]) / (s_l1[0][1] + s_l1[1][1]) : NAN;
-    dg[5] = a.m;
+    dg[2] = resid_mode == 0 ? NAN : (zr > 0.f ? M + logf(zr) : -INFINITY);
+    dg[3] = (L_mid >= 2 && zm > 0.f) ? (logf(zm) - tm / zm) / logf((float)L_mid) : NAN;
+    dg[4] = y_cmp != nullptr ? sd / sr : NAN;
+    dg[5] = M;
     dg[6] = 0.f;
     dg[7] = 0.f;
   }
@@ -412,7 +437,7 @@ static hipError_t launch_full_t(const FullPlan& pl, const float* q, int G, const
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
   // without a retrieved set (K == 0) the residual set is the whole mid-region
   const int resid_mode = (idx != nullptr || K == 0) ? 2 : 0;
-  full_combine_kernel<D><<<kv.n_units * G, 128, 0, st>>>(part, G, pl.n_chunks, L_mid, resid_mode,
+  full_combine_kernel<D><<<kv.n_units * G, kFullCombineThreads, 0, st>>>(part, G, pl.n_chunks, L_mid, resid_mode,
                                                          y_cmp, y, diag);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -62,6 +62,7 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
 constexpr int kFullThreads = 256;
 constexpr int kFullMaxChunk = 8192;   // positions per chunk (membership bits in LDS)
 constexpr int kFullRecHead = 8;       // floats before N in a chunk record
+constexpr int kFullCombineThreads = 256;
 
 struct FullPlan {
   int n_chunks, ch;
