@@ -146,6 +146,26 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
       s_sc[tid + NT * r] = ssc[r];
     }
   };
+  // f = phi_q(q): its operands are loaded first, so that computing it waits only
+  // for them (loads complete in issue order); without Wq the given features are
+  // read, and the loads read q instead (discarded)
+  constexpr int TPF = NT / M, EPT = D / TPF;     // threads per feature, elements each
+  const int fi = tid / TPF, fpart = tid % TPF;
+  const bool fcomp = resid && Wq != nullptr;
+  float wq[EPT], xq[EPT], fb0;
+  {
+    const int pset = u % P;
+    const float* wr = fcomp ? Wq + ((size_t)pset * M + fi) * D + fpart * EPT : qg;
+    const float* qs = qg + fpart * EPT;
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(wr + i);
+      const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
+      wq[i] = w4.x; wq[i + 1] = w4.y; wq[i + 2] = w4.z; wq[i + 3] = w4.w;
+      xq[i] = x4.x; xq[i + 1] = x4.y; xq[i + 2] = x4.z; xq[i + 3] = x4.w;
+    }
+    fb0 = fcomp ? bq[(size_t)pset * M + fi] : (resid && phi_q != nullptr ? phi_q[(size_t)ug * M + (tid % M)] : 0.f);
+  }
   stage_load(0);
 
   float qr[CPL], fr[FPL];
@@ -164,7 +184,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   constexpr int FB = NT / D;          // feature blocks
   constexpr int FPB = M / FB;         // features per block
   const int scol = tid % D, fb = tid / D;
-  float sv[FPB], fv[FPB];
+  float sv[FPB];
   {
     const float* Sp = rs ? S + (size_t)u * M * D + (size_t)fb * FPB * D + scol : qg;
     const size_t sst = rs ? D : 0;
@@ -172,7 +192,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
     for (int i = 0; i < FPB; ++i) sv[i] = Sp[sst * i];
   }
   constexpr int UPL = (M + kWave - 1) / kWave;   // u^T f terms per lane (last wave)
-  float uu[UPL], uf[UPL];
+  float uu[UPL];
 #pragma unroll
   for (int i = 0; i < UPL; ++i) uu[i] = rs ? u_[(size_t)u * M + min(lane + kWave * i, M - 1)] : 0.f;
 
@@ -191,35 +211,18 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
 
   // ---- f = phi_q(q) into LDS: the given features, or elu(Wq q + bq) + 1
   //      computed here (NT/M threads per feature, fp32, fixed sum order)
-  if (resid) {
-    if (Wq != nullptr) {
-      constexpr int TPF = NT / M, EPT = D / TPF;
-      const int fi = tid / TPF, fpart = tid % TPF, pset = u % P;
-      const float* wr = Wq + ((size_t)pset * M + fi) * D + fpart * EPT;
-      const float* qs = qg + fpart * EPT;
-      float z = 0.f;
+  if (fcomp) {
+    float z = 0.f;
 #pragma unroll
-      for (int i = 0; i < EPT; i += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wr + i);
-        const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
-        z = __fmaf_rn(w4.x, x4.x, z);
-        z = __fmaf_rn(w4.y, x4.y, z);
-        z = __fmaf_rn(w4.z, x4.z, z);
-        z = __fmaf_rn(w4.w, x4.w, z);
-      }
-      z = lane_group_sum<TPF>(z);
-      if (fpart == 0) s_f[fi] = phi_elu1(z + bq[(size_t)pset * M + fi]);
-    } else {
-      for (int i = tid; i < M; i += NT) s_f[i] = phi_q[(size_t)ug * M + i];
-    }
+    for (int i = 0; i < EPT; ++i) z = __fmaf_rn(wq[i], xq[i], z);
+    z = lane_group_sum<TPF>(z);
+    if (fpart == 0) s_f[fi] = phi_elu1(z + fb0);
+  } else if (resid && tid < M) {
+    s_f[tid] = fb0;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < FPB; ++i) fv[i] = rs ? s_f[fb * FPB + i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < UPL; ++i) uf[i] = rs ? s_f[min(lane + kWave * i, M - 1)] : 0.f;
   if constexpr (RECOMP) {
     if (sub) rfq = s_f[(wave % NFT) * 16 + (lane & 15)];
   }
@@ -353,13 +356,13 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   if (rs) {
     float p = 0.f;
 #pragma unroll
-    for (int i = 0; i < FPB; ++i) p = __fmaf_rn(fv[i], sv[i], p);
+    for (int i = 0; i < FPB; ++i) p = __fmaf_rn(s_f[fb * FPB + i], sv[i], p);  // f: LDS broadcast
     s_part[fb][scol] = p;
     if (wave == NW - 1) {
       float t = 0.f;
 #pragma unroll
       for (int i = 0; i < UPL; ++i)
-        if (lane + kWave * i < M) t = __fmaf_rn(uu[i], uf[i], t);
+        if (lane + kWave * i < M) t = __fmaf_rn(uu[i], s_f[lane + kWave * i], t);
       t = wave_sum_dpp(t);
       if (lane == 0) s_uf = t;
     }
