@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 4
+#define RMA_ABI_VERSION 5
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -101,6 +101,9 @@ typedef struct {
 #define RMA_OP_DECODE_TOPK 2
 #define RMA_OP_DECODE_MERGE 3
 #define RMA_OP_DECODE_FULL 4
+
+/* rma_build_summaries_range() flags. */
+#define RMA_BUILD_ACCUMULATE 1u    /* add to S, u (and raise kappa) instead of overwriting */
 
 /* rma_decode_merge() flags (page §5.2 Table 1 and §7.1 Table 3 variants). */
 #define RMA_MERGE_SUB 0u           /* Top-K+phi: subtract retrieved tokens (default) */
@@ -146,6 +149,30 @@ rma_status rma_build_summaries(const rma_kv* kv, const rma_span* span, const flo
                                const float* bk, int32_t m, int32_t n_param_sets, void* phi_k,
                                int32_t phi_dtype, float* S, float* u_, float* kappa,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rma_build_summaries_range -- the same summaries over the mid-region positions
+ * [m_begin, m_end) only (tokens n_sink + m_begin .. n_sink + m_end - 1), for a
+ * prefill that arrives in pieces or a shared prefix whose summaries are reused.
+ * The summaries are plain sums over tokens (page §4.1, Eq. 6), so they add over
+ * disjoint token sets: pieces appended with RMA_BUILD_ACCUMULATE give the
+ * whole-range result up to fp32 summation order (kappa exactly: a maximum).
+ * flags 0: S, u_, kappa are overwritten with the range's sums;
+ * flags RMA_BUILD_ACCUMULATE: S += range sums, u_ += range sums,
+ *   kappa = max(kappa, range bound); S, u_, kappa must hold earlier results.
+ * phi_k rows m_begin .. m_end-1 of [n_units][L_mid][m] are written (or read,
+ * with Wk == NULL); the rest of phi_k is untouched.  Other arguments as for
+ * rma_build_summaries, which equals this call on [0, L_mid) with flags 0.
+ * Errors: RMA_ERR_INVALID_ARG for 0 <= m_begin <= m_end <= L_mid violated or
+ * unknown flags.  Workspace: rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ...)
+ * for the same span suffices for any range.
+ */
+rma_status rma_build_summaries_range(const rma_kv* kv, const rma_span* span, int64_t m_begin,
+                                     int64_t m_end, uint32_t flags, const float* Wk,
+                                     const float* bk, int32_t m, int32_t n_param_sets,
+                                     void* phi_k, int32_t phi_dtype, float* S, float* u_,
+                                     float* kappa, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * rma_decode_topk -- exhaustive Top-K over the mid-region (page §1: exhaustive

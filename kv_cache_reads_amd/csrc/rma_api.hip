@@ -89,10 +89,9 @@ int64_t l_mid(const rma_span& sp) { return sp.L - sp.n_sink - sp.n_tail; }
 }  // namespace
 
 // ------------------------------------------------------------- plans
-BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_phi,
-                     int phi_dtype) {
+BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi, int phi_dtype) {
   BuildPlan p{};
-  const int64_t Lm = l_mid(sp);
+  const int64_t Lm = tokens;
   const int64_t U = kv.n_units;
   p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
   const int tile = p.mfma ? 64 : 32;
@@ -247,8 +246,8 @@ size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int
     case RMA_OP_BUILD_SUMMARIES:
       if (m != 64 && m != 128) return 0;
       // the larger of the two builder layouts (MFMA tiles are coarser)
-      return std::max(plan_build(*kv, *sp, m, true, RMA_BF16).total,
-                      plan_build(*kv, *sp, m, false, RMA_F32).total);
+      return std::max(plan_build(*kv, l_mid(*sp), m, true, RMA_BF16).total,
+                      plan_build(*kv, l_mid(*sp), m, false, RMA_F32).total);
     case RMA_OP_DECODE_TOPK:
       if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp)) return 0;
       return plan_topk(*kv, *sp, G, K).total;
@@ -290,9 +289,27 @@ rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float
                                const float* bk, int32_t m, int32_t P, void* phi_k,
                                int32_t phi_dtype, float* S, float* u, float* kappa,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv == nullptr || sp == nullptr) {
+    g_last_error[0] = 0;
+    return fail(RMA_ERR_INVALID_ARG, "kv or span is NULL");
+  }
+  return rma_build_summaries_range(kv, sp, 0, l_mid(*sp), 0u, Wk, bk, m, P, phi_k, phi_dtype, S, u,
+                                   kappa, workspace, workspace_bytes, stream);
+}
+
+rma_status rma_build_summaries_range(const rma_kv* kv, const rma_span* sp, int64_t m_begin,
+                                     int64_t m_end, uint32_t flags, const float* Wk,
+                                     const float* bk, int32_t m, int32_t P, void* phi_k,
+                                     int32_t phi_dtype, float* S, float* u, float* kappa,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   rma_status s = check_kv_span(kv, sp, true);
   if (s != RMA_OK) return s;
+  RMA_CHECK(flags == 0u || flags == RMA_BUILD_ACCUMULATE, RMA_ERR_INVALID_ARG, "unknown flags 0x%x",
+            flags);
+  RMA_CHECK(0 <= m_begin && m_begin <= m_end && m_end <= l_mid(*sp), RMA_ERR_INVALID_ARG,
+            "token range [%lld, %lld) outside the mid-region [0, %lld)", (long long)m_begin,
+            (long long)m_end, (long long)l_mid(*sp));
   RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
   RMA_CHECK(dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported phi dtype");
   RMA_CHECK(P >= 1, RMA_ERR_INVALID_ARG, "n_param_sets must be >= 1");
@@ -300,20 +317,21 @@ rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float
   RMA_CHECK(S && u && kappa, RMA_ERR_INVALID_ARG, "NULL output pointer");
   // phi_k may be NULL only when the MFMA builder computes the features (the rows
   // are then not stored; decode recomputes the retrieved ones)
-  RMA_CHECK(phi_k != nullptr || l_mid(*sp) == 0 ||
+  RMA_CHECK(phi_k != nullptr || m_end == m_begin ||
                 (Wk != nullptr && kv->dtype == RMA_BF16 && phi_dtype == RMA_BF16),
             RMA_ERR_INVALID_ARG, "phi_k is NULL (allowed only for bf16 keys with Wk given)");
   RMA_CHECK(aligned16(S) && aligned16(u) && aligned16(kappa) && aligned16(phi_k) &&
                 aligned16(Wk) && aligned16(bk),
             RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  BuildPlan pl = plan_build(*kv, *sp, m, Wk != nullptr, phi_dtype);
+  BuildPlan pl = plan_build(*kv, m_end - m_begin, m, Wk != nullptr, phi_dtype);
   RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
             "workspace is NULL or misaligned");
   RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
             workspace_bytes, pl.total);
   TraceScope ts((hipStream_t)stream);
-  hipError_t e = launch_build(pl, *kv, *sp, Wk, bk, m, P, phi_k, phi_dtype, S, u, kappa,
-                              (uint8_t*)workspace, (hipStream_t)stream);
+  hipError_t e = launch_build(pl, *kv, *sp, (int)m_begin, (int)(m_end - m_begin),
+                              flags == RMA_BUILD_ACCUMULATE, Wk, bk, m, P, phi_k, phi_dtype, S, u,
+                              kappa, (uint8_t*)workspace, (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return RMA_OK;
 }

@@ -37,9 +37,10 @@ __device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) *
 template <int D, int M, bool STORE>
 __global__ void __launch_bounds__(M * 4)
 build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
-                  int n_sink, int L_mid, int ch, int n_chunks, const float* __restrict__ W,
-                  const float* __restrict__ bias, int P, uint16_t* __restrict__ phik,
-                  float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
+                  int n_sink, int L_mid, int ch, int n_chunks, int m0, int len, int acc,
+                  const float* __restrict__ W, const float* __restrict__ bias, int P,
+                  uint16_t* __restrict__ phik, float* __restrict__ pS, float* __restrict__ pu,
+                  float* __restrict__ pk) {
   constexpr int NW = M / 16;              // one 16-feature tile per wave
   constexpr int NT = NW * 64;
   constexpr int TT = 64;                  // tokens per tile
@@ -65,8 +66,9 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
   const int p = u % P;
-  const int t0 = c * ch;
-  const int n = min(ch, L_mid - t0);
+  // chunk c of the mid-region positions [m0, m0 + len)
+  const int t0 = m0 + c * ch;
+  const int n = min(ch, m0 + len - t0);
   const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   uint16_t* php = STORE ? phik + ((size_t)u * L_mid + t0) * M : nullptr;
@@ -242,10 +244,17 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sp[(size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16] = Sacc[ct][r];
+    for (int r = 0; r < 4; ++r) {
+      // acc: the summaries already hold earlier tokens (one chunk writes them directly)
+      float* dst = Sp + (size_t)(fb + 4 * g4 + r) * D + ct * 16 + l16;
+      *dst = acc ? *dst + Sacc[ct][r] : Sacc[ct][r];
+    }
   if (l16 == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pu[((size_t)u * n_chunks + c) * M + fb + 4 * g4 + r] = Uacc[r];
+    for (int r = 0; r < 4; ++r) {
+      float* dst = pu + ((size_t)u * n_chunks + c) * M + fb + 4 * g4 + r;
+      *dst = acc ? *dst + Uacc[r] : Uacc[r];
+    }
   }
   kapmax = wave_max_dpp(kapmax);
   if (lane == 0) s_kap[wave] = kapmax;
@@ -254,7 +263,8 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     float mx = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_kap[w]);
-    pk[(size_t)u * n_chunks + c] = norm_upper(mx);
+    float* dst = pk + (size_t)u * n_chunks + c;
+    *dst = acc ? fmaxf(*dst, norm_upper(mx)) : norm_upper(mx);
   }
 }
 
@@ -262,7 +272,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
 template <typename KT, typename PT, int D, int M>
 __global__ void __launch_bounds__(256)
 build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int n_sink,
-                  int L_mid, int ch, int n_chunks, const float* __restrict__ W,
+                  int L_mid, int ch, int n_chunks, int m0, int len, int acc_in, const float* __restrict__ W,
                   const float* __restrict__ bias, int P, PT* __restrict__ phik,
                   float* __restrict__ pS, float* __restrict__ pu, float* __restrict__ pk) {
   constexpr int TT = 32;
@@ -272,8 +282,8 @@ build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t 
   __shared__ float s_kap[256];
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int p = u % P;
-  const int t0 = c * ch;
-  const int n = min(ch, L_mid - t0);
+  const int t0 = m0 + c * ch;   // chunk c of the mid-region positions [m0, m0 + len)
+  const int n = min(ch, m0 + len - t0);
   const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const KT* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   PT* php = phik + ((size_t)u * L_mid + t0) * M;
@@ -326,14 +336,21 @@ build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t 
   }
   float* Sp = pS + ((size_t)u * n_chunks + c) * M * D;
 #pragma unroll
-  for (int i = 0; i < cols_per; ++i) Sp[(size_t)f_s * D + c_s + i] = acc[i];
-  if (c_s == 0) pu[((size_t)u * n_chunks + c) * M + f_s] = uacc;
+  for (int i = 0; i < cols_per; ++i) {
+    float* dst = Sp + (size_t)f_s * D + c_s + i;
+    *dst = acc_in ? *dst + acc[i] : acc[i];
+  }
+  if (c_s == 0) {
+    float* dst = pu + ((size_t)u * n_chunks + c) * M + f_s;
+    *dst = acc_in ? *dst + uacc : uacc;
+  }
   s_kap[tid] = kap;
   __syncthreads();
   if (tid == 0) {
     float mx = 0.f;
     for (int i = 0; i < TT; ++i) mx = fmaxf(mx, s_kap[i]);
-    pk[(size_t)u * n_chunks + c] = mx;
+    float* dst = pk + (size_t)u * n_chunks + c;
+    *dst = acc_in ? fmaxf(*dst, mx) : mx;
   }
 }
 
@@ -345,7 +362,7 @@ build_valu_kernel(const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t 
 constexpr int kRedBatch = 16;
 __global__ void __launch_bounds__(256)
 build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
-                    const float* __restrict__ pk, int n_chunks, int M, int D,
+                    const float* __restrict__ pk, int n_chunks, int M, int D, int add,
                     float* __restrict__ S, float* __restrict__ u_, float* __restrict__ kappa) {
   __shared__ float4 part[4][64];
   const int u = blockIdx.y, tid = threadIdx.x, o = tid & 63, w = tid >> 6;
@@ -393,14 +410,22 @@ build_reduce_kernel(const float* __restrict__ pS, const float* __restrict__ pu,
       r.z += part[k][o].z;
       r.w += part[k][o].w;
     }
-    if (e < nS4) reinterpret_cast<float4*>(S + (size_t)u * M * D)[e] = r;
-    else reinterpret_cast<float4*>(u_ + (size_t)u * M)[e - nS4] = r;
+    float4* dst = e < nS4 ? reinterpret_cast<float4*>(S + (size_t)u * M * D) + e
+                          : reinterpret_cast<float4*>(u_ + (size_t)u * M) + (e - nS4);
+    if (add) {  // add to the summaries of earlier tokens
+      const float4 o = *dst;
+      r.x = o.x + r.x;
+      r.y = o.y + r.y;
+      r.z = o.z + r.z;
+      r.w = o.w + r.w;
+    }
+    *dst = r;
   }
   if (blockIdx.x == 0 && w == 1) {  // kappa: the chunk maxima spread over one wave
     float v = 0.f;
     for (int c = o; c < n_chunks; c += kWave) v = fmaxf(v, pk[(size_t)u * n_chunks + c]);
     v = wave_max_dpp(v);
-    if (o == 0) kappa[u] = v;
+    if (o == 0) kappa[u] = add ? fmaxf(kappa[u], v) : v;
   }
 }
 
@@ -448,10 +473,12 @@ phi_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const float* __r
 }
 
 // ====================================================================== launch
-hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, const float* W,
-                        const float* b, int m, int P, void* phi_k, int phi_dtype, float* S,
-                        float* u, float* kappa, uint8_t* ws, hipStream_t st) {
+hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, int m0, int len,
+                        bool acc, const float* W, const float* b, int m, int P, void* phi_k,
+                        int phi_dtype, float* S, float* u, float* kappa, uint8_t* ws,
+                        hipStream_t st) {
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
+  const int acc_direct = (acc && pl.n_chunks == 1) ? 1 : 0;   // partials never accumulate
   // one chunk per unit: the builder writes S, u and kappa itself
   const bool direct = pl.n_chunks == 1;
   float* pS = direct ? S : reinterpret_cast<float*>(ws + pl.off_S);
@@ -467,11 +494,11 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
   do {                                                                                         \
     if (ph != nullptr)                                                                         \
       hipLaunchKernelGGL((build_mfma_kernel<DD, MM, true>), grid, dim3(MM * 4), 0, st, kk, vv, \
-                         kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, ph,    \
+                         kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P, ph,    \
                          pS, pu, pk);                                                          \
     else                                                                                       \
       hipLaunchKernelGGL((build_mfma_kernel<DD, MM, false>), grid, dim3(MM * 4), 0, st, kk,    \
-                         vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P,    \
+                         vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P,    \
                          ph, pS, pu, pk);                                                      \
   } while (0)
       if (kv.d == 64 && m == 64) RMA_BM(64, 64);
@@ -483,7 +510,7 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
 #define RMA_BV1(KT, PT, DD, MM)                                                                   \
   hipLaunchKernelGGL((build_valu_kernel<KT, PT, DD, MM>), grid, dim3(256), 0, st,                  \
                      static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,   \
-                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, W, b, P, static_cast<PT*>(phi_k), pS, \
+                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P, static_cast<PT*>(phi_k), pS, \
                      pu, pk)
 #define RMA_BV(KT, PT)                                                 \
   do {                                                                 \
@@ -507,7 +534,7 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
   if (direct) return hipSuccess;
   const int blocks = (int)ceil_div((int64_t)m * kv.d / 4 + m / 4, 64);
   hipLaunchKernelGGL(build_reduce_kernel, dim3(blocks, kv.n_units), dim3(256), 0, st, pS, pu, pk,
-                     pl.n_chunks, m, kv.d, S, u, kappa);
+                     pl.n_chunks, m, kv.d, acc ? 1 : 0, S, u, kappa);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) trace_kernel(st, "build_reduce_kernel");
   return e;

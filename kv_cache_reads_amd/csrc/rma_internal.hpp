@@ -27,7 +27,8 @@ struct BuildPlan {
   int ch;            // tokens per chunk (multiple of the tile)
   size_t off_S, off_u, off_kap, total;
 };
-BuildPlan plan_build(const rma_kv& kv, const rma_span& sp, int m, bool computed_phi, int phi_dtype);
+// tokens: mid-region positions covered by one call (all of L_mid, or a range)
+BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi, int phi_dtype);
 
 // ------------------------------------------------------------- top-k
 constexpr int kScanThreads = 256;
@@ -96,9 +97,10 @@ hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int
                       int d, const float* W, const float* b, int m, int P, void* phi,
                       int phi_dtype, hipStream_t st);
 
-hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, const float* W,
-                        const float* b, int m, int P, void* phi_k, int phi_dtype, float* S,
-                        float* u, float* kappa, uint8_t* ws, hipStream_t st);
+hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, int m0, int len,
+                        bool acc, const float* W, const float* b, int m, int P, void* phi_k,
+                        int phi_dtype, float* S, float* u, float* kappa, uint8_t* ws,
+                        hipStream_t st);
 
 hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
                        const rma_span& sp, const float* kappa, int K, int32_t* idx,

@@ -23,6 +23,7 @@ RMA_OK, RMA_ERR_INVALID_ARG, RMA_ERR_UNSUPPORTED, RMA_ERR_WORKSPACE, RMA_ERR_HIP
 RMA_F32, RMA_BF16 = 0, 1
 RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE, RMA_OP_DECODE_FULL = 1, 2, 3, 4
 RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
+RMA_BUILD_ACCUMULATE = 1
 RMA_WORKSPACE_COUNTER_BYTES = 262144
 
 
@@ -75,6 +76,8 @@ def lib():
     P_KV, P_SP = ctypes.POINTER(_KV), ctypes.POINTER(_Span)
     L.rma_phi_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP]
     L.rma_build_summaries.argtypes = [P_KV, P_SP, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_build_summaries_range.argtypes = [P_KV, P_SP, _I64, _I64, _U32, _VP, _VP, _I32, _I32, _VP, _I32, _VP,
+                                            _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_merge.argtypes = [_VP, _VP, _VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
                                    _I32, _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
@@ -92,8 +95,8 @@ def lib():
     L.rma_trace_count.restype = _I32
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
-    for f in ("rma_phi_features", "rma_build_summaries", "rma_decode_topk", "rma_decode_merge",
-              "rma_decode_full"):
+    for f in ("rma_phi_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
+              "rma_decode_merge", "rma_decode_full"):
         getattr(L, f).restype = _I32
     _lib = L
     return L
@@ -208,6 +211,28 @@ def rma_build_summaries(k: torch.Tensor, v: torch.Tensor, span: Span, Wk: Option
     _check(lib().rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), _p(Wk), _p(bk), m, P, _p(phi_k),
                                      pdt, _p(S), _p(u), _p(kappa), _p(w), w.numel(), _stream()))
     return phi_k, S, u, kappa
+
+
+def rma_build_summaries_range(k: torch.Tensor, v: torch.Tensor, span: Span, m_begin: int, m_end: int,
+                              Wk: Optional[torch.Tensor], bk: Optional[torch.Tensor],
+                              phi_k: Optional[torch.Tensor], S: torch.Tensor, u: torch.Tensor,
+                              kappa: torch.Tensor, accumulate: bool = False,
+                              phi_dtype: torch.dtype = torch.bfloat16, ws: Optional[Workspace] = None):
+    """Summaries of the mid-region positions [m_begin, m_end): overwrite S, u,
+    kappa, or (accumulate) add to them; phi_k rows of the range are written
+    (phi_k may be None for bf16 keys with Wk: rows not stored)."""
+    U, _, d = k.shape
+    m = S.shape[1]
+    P = Wk.shape[0] if Wk is not None else 1
+    kv, sp = _kv(k, v), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_BUILD_SUMMARIES, ctypes.byref(kv), ctypes.byref(sp), 1, 0, m))
+    w = _ws(ws, nb)
+    pdt = _dt(phi_k.dtype) if phi_k is not None else _dt(phi_dtype)
+    _check(lib().rma_build_summaries_range(ctypes.byref(kv), ctypes.byref(sp), m_begin, m_end,
+                                           RMA_BUILD_ACCUMULATE if accumulate else 0, _p(Wk), _p(bk), m, P,
+                                           _p(phi_k), pdt, _p(S), _p(u), _p(kappa), _p(w), w.numel(),
+                                           _stream()))
+    return S, u, kappa
 
 
 def rma_decode_topk(q: torch.Tensor, k: torch.Tensor, span: Span, kappa: torch.Tensor, K: int,

@@ -14,12 +14,13 @@ pytestmark = pytest.mark.skipif(not __import__("os").path.exists(R.LIB_PATH),
 def test_exports_every_declared_symbol():
     names = R.header_functions()
     assert set(names) >= {"rma_phi_features", "rma_build_summaries", "rma_decode_topk",
-                          "rma_decode_merge", "rma_decode_full", "rma_workspace_bytes", "rma_status_string",
+                          "rma_decode_merge", "rma_decode_full", "rma_build_summaries_range",
+                          "rma_workspace_bytes", "rma_status_string",
                           "rma_last_error", "rma_abi_version"}
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 4
+    assert L.rma_abi_version() == 5
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -106,6 +107,24 @@ def test_build_and_merge_validation_errors():
     st = L.rma_build_summaries(ctypes.byref(kv), ctypes.byref(sp), None, None, 128, 1, None,
                                R.RMA_BF16, 0x3000, 0x4000, 0x5000, 0x6000, 1 << 30, None)
     assert st == R.RMA_ERR_INVALID_ARG
+
+
+def test_build_range_validation_errors():
+    L = R.lib()
+    kv, sp = _kv(), _sp()          # L_mid = 1024 - 36 = 988
+
+    def rng(a, b, flags=0, ws=0x6000):
+        return L.rma_build_summaries_range(ctypes.byref(kv), ctypes.byref(sp), a, b, flags, 0x1000, 0x1100,
+                                           128, 1, 0x2000, R.RMA_BF16, 0x3000, 0x4000, 0x5000, ws, 1 << 30,
+                                           None)
+    assert rng(-1, 10) == R.RMA_ERR_INVALID_ARG
+    assert rng(20, 10) == R.RMA_ERR_INVALID_ARG
+    assert rng(0, 989) == R.RMA_ERR_INVALID_ARG
+    assert b"outside the mid-region" in L.rma_last_error()
+    assert rng(0, 10, flags=2) == R.RMA_ERR_INVALID_ARG
+    assert rng(0, 10, ws=0) == R.RMA_ERR_WORKSPACE
+    assert L.rma_build_summaries(None, ctypes.byref(sp), 0x1000, 0x1100, 128, 1, 0x2000, R.RMA_BF16,
+                                 0x3000, 0x4000, 0x5000, 0x6000, 1 << 30, None) == R.RMA_ERR_INVALID_ARG
 
 
 def test_workspace_sizes_are_monotone_in_K_and_units():
