@@ -62,9 +62,9 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="d194635339350177", fetch_bytes=69247664, write_bytes=84025625),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="d194635339350177", fetch_bytes=33807778, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="d194635339350177", fetch_bytes=5998310, write_bytes=8192),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=69250670, write_bytes=84035264),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=33798605, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=7061072, write_bytes=8192),
 }
 
 
