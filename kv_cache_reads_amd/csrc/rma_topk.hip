@@ -246,26 +246,34 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 
   // ---- ordered compaction of the passing tokens (position order), all heads
   //      with one multi-value block scan
+  //      (each thread a contiguous run of at most PMAX tokens; one pass over the
+  //      scores keeps a bit per passing token, the write pass visits those only)
+  constexpr int PMAX = (CHMAX + kScanThreads - 1) / kScanThreads;
+  static_assert(PMAX <= 32, "one 32-bit pass mask per head");
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   int bcs[G], cnt[G], tot[G];
+  uint32_t pm[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) { bcs[g] = s_bc[g]; cnt[g] = 0; }
-  for (int i = i0; i < i1; ++i) {
+  for (int g = 0; g < G; ++g) { bcs[g] = s_bc[g]; pm[g] = 0u; }
 #pragma unroll
-    for (int g = 0; g < G; ++g) cnt[g] += (lin_bin(sc[g * CHMAX + i], hp[g]) >= bcs[g]);
+  for (int k = 0; k < PMAX; ++k) {
+    if (i0 + k < i1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        pm[g] |= (lin_bin(sc[g * CHMAX + i0 + k], hp[g]) >= bcs[g]) ? (1u << k) : 0u;
+    }
   }
+#pragma unroll
+  for (int g = 0; g < G; ++g) cnt[g] = __popc(pm[g]);
   block_excl_scan256_n<G>(cnt, s_buf, tot);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float2* dst = ent + ((size_t)(u * G + g) * n_chunks + c) * r_cap;
     int pos = cnt[g];
-    for (int i = i0; i < i1; ++i) {
-      const float s = sc[g * CHMAX + i];
-      if (lin_bin(s, hp[g]) >= bcs[g]) {
-        if (pos < r_cap) dst[pos] = make_float2(s, __int_as_float(t0 + i));
-        ++pos;
-      }
+    for (uint32_t mk = pm[g]; mk != 0u; mk &= mk - 1u, ++pos) {
+      const int i = i0 + __ffs(mk) - 1;
+      if (pos < r_cap) dst[pos] = make_float2(sc[g * CHMAX + i], __int_as_float(t0 + i));
     }
   }
   if (tid < G) {
