@@ -379,15 +379,16 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
   }
 }
 
-template <typename KT, int D>
-__global__ void __launch_bounds__(kSelThreads)
+template <typename KT, int D, int NT>
+__global__ void __launch_bounds__(NT)
 topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb, int64_t ustride,
                    int n_sink, int L_mid, int ch, int n_chunks, int r_cap, int K, int e_max,
                    const float4* __restrict__ hpw, const float2* __restrict__ ent,
                    const int2* __restrict__ meta, int32_t* __restrict__ idx_out,
                    float* __restrict__ sc_out, float inv_sqrt_d) {
   constexpr int NBS = kSelBins;
-  constexpr int NT = kSelThreads, NWV = NT / kWave;
+  constexpr int NWV = NT / kWave;
+  static_assert(NT >= kSelMaxChunks && NT >= 128, "one thread per chunk report and per query element");
   static_assert(NBS % NT == 0, "whole bins per thread");
   constexpr int SELF = 1 << 30;                // "selected" mark on a band member's position
   extern __shared__ __align__(16) float dyn[];
@@ -701,21 +702,28 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
                                       sp.n_sink, L_mid, pl, kappa, ent, meta, hpw);
   if (e != hipSuccess) return e;
   // dynamic LDS: the union (score, position) pairs, within the per-block limit
-  // left by the kernel's own (static) LDS
-  static size_t static_lds = 0;
-  if (static_lds == 0) {
+  // left by the kernel's own (static) LDS.  Many (unit, head) blocks with short
+  // report lists: 256 threads each, so that several share a CU; otherwise 1024.
+  const bool small = kv.n_units * G >= 1024 && (int64_t)pl.n_chunks * pl.r_cap <= 8 * 256;
+  static size_t static_lds[2] = {0, 0};
+  const void* kfn = small ? reinterpret_cast<const void*>(&topk_select_kernel<KT, D, 256>)
+                          : reinterpret_cast<const void*>(&topk_select_kernel<KT, D, kSelThreads>);
+  size_t& sl = static_lds[small ? 1 : 0];
+  if (sl == 0) {
     hipFuncAttributes attr{};
-    static_lds = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&topk_select_kernel<KT, D>)) ==
-                         hipSuccess
-                     ? attr.sharedSizeBytes
-                     : 32 * 1024;
+    sl = hipFuncGetAttributes(&attr, kfn) == hipSuccess ? attr.sharedSizeBytes : 32 * 1024;
   }
   int e_max = pl.e_max;
-  if (g_lds_limit > static_lds) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - static_lds) / 8);
+  if (g_lds_limit > sl) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - sl) / 8);
   const size_t lds = (size_t)std::max(e_max, 1) * 8;
-  hipLaunchKernelGGL((topk_select_kernel<KT, D>), dim3(kv.n_units * G), dim3(kSelThreads), lds, st, q, G,
-                     kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
-                     hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
+  if (small)
+    hipLaunchKernelGGL((topk_select_kernel<KT, D, 256>), dim3(kv.n_units * G), dim3(256), lds, st, q, G,
+                       kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
+                       hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
+  else
+    hipLaunchKernelGGL((topk_select_kernel<KT, D, kSelThreads>), dim3(kv.n_units * G), dim3(kSelThreads),
+                       lds, st, q, G, kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks,
+                       pl.r_cap, K, e_max, hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
   e = hipGetLastError();
   if (e == hipSuccess) trace_kernel(st, "topk_select_kernel");
   return e;

@@ -277,20 +277,22 @@ def test_workspace_reuse_across_unit_counts():
 
 
 # ------------------------------------------------------------------ adversarial selection
-def _topk_case(k, q, L, ns, nt, K):
+def _topk_case(k, q, L, ns, nt, K, units=(0,)):
     kd = k.to(DEV)
     v = torch.zeros_like(k)
     pre = R.rma_build_summaries(kd, v.to(DEV), R.Span(L, ns, nt, 0), torch.randn(1, 64, 64, device=DEV) / 8,
                                 torch.zeros(1, 64, device=DEV))
     idx, sel = R.rma_decode_topk(q.to(DEV), kd, R.Span(L, ns, nt, 0), pre[3], K)
-    kf = k[0].float().double().numpy()
-    for g in range(q.shape[1]):
-        ref = O.topk_indices(q[0, g].numpy(), kf[ns:L - nt], K, first_index=ns)
-        got = idx[0, g].cpu().numpy()
-        assert np.array_equal(got, ref), f"K={K} head {g}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
-        # selected scores are the fp32 scores of the selected tokens
-        s_ref = kf[got] @ q[0, g].double().numpy() / 8.0
-        assert np.allclose(sel[0, g].cpu().numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
+    for u in units:
+        kf = k[u].float().double().numpy()
+        for g in range(q.shape[1]):
+            ref = O.topk_indices(q[u, g].numpy(), kf[ns:L - nt], K, first_index=ns)
+            got = idx[u, g].cpu().numpy()
+            assert np.array_equal(got, ref), \
+                f"K={K} unit {u} head {g}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
+            # selected scores are the fp32 scores of the selected tokens
+            s_ref = kf[got] @ q[u, g].double().numpy() / 8.0
+            assert np.allclose(sel[u, g].cpu().numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
     return idx
 
 
@@ -334,3 +336,21 @@ def test_topk_sorted_keys_force_fallback():
     k[0, :, 0] = torch.linspace(-2, 2, L)
     _topk_case(k.bfloat16(), q, L, ns, nt, 500)
     _topk_case(k.bfloat16(), q, L, ns, nt, 5)
+
+
+def test_topk_many_units_use_small_select_blocks():
+    """U*G >= 1024 (query heads) selects with 256-thread blocks: the tie and
+    near-tie case and the forced exact fallback on that path."""
+    L, ns, nt, U, G = 3000, 4, 32, 256, 4
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn(U, L, 64, generator=g)
+    q = torch.randn(U, G, 64, generator=g)
+    qh = q[0, 0] / q[0, 0].norm()
+    pos = torch.randperm(L - ns - nt, generator=g)[:40] + ns
+    k[0, pos] = (3.0 * qh).bfloat16().float()           # exact ties at the boundary in unit 0
+    k[U - 1, :, 0] = torch.linspace(-2, 2, L)            # unit U-1: sorted scores for head 0 ...
+    k[U - 1, :, 1:] = 0.0
+    q[U - 1, 0] = 0.0
+    q[U - 1, 0, 0] = 1.0                                  # ... which forces the exact fallback
+    _topk_case(k.bfloat16(), q, L, ns, nt, 30, units=(0, 17, U - 1))
+    _topk_case(k.bfloat16(), q, L, ns, nt, 500, units=(0, U - 1))
