@@ -60,8 +60,8 @@ struct RawPiece {
 // from their keys with the summary builder's projection (same operands, same
 // MFMA order, same bf16 rounding), so the subtraction removes exactly what the
 // summaries contain.  Needs bf16 keys.
-template <typename KT, typename PT, int D, int M, bool RECOMP>
-__global__ void __launch_bounds__(kMergeThreads)
+template <typename KT, typename PT, int D, int M, bool RECOMP, int NTH>
+__global__ void __launch_bounds__(NTH, NTH == kMergeThreads ? 1 : 2)
 merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
              const float* __restrict__ Wq, const float* __restrict__ bq, int G,
              const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int L,
@@ -71,12 +71,13 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
              const float* __restrict__ S, const float* __restrict__ u_, uint32_t flags,
              float* __restrict__ y, float* __restrict__ stats, float inv_sqrt_d) {
   static_assert(!RECOMP || sizeof(KT) == 2, "recomputed phi rows need bf16 keys");
-  constexpr int NT = kMergeThreads, NW = NT / kWave;
+  static_assert(!RECOMP || NTH == kMergeThreads, "the recompute tiles assume the full block");
+  constexpr int NT = NTH, NW = NT / kWave;
   constexpr int LPE = 8;            // lanes per entry
   constexpr int NGR = NT / LPE;     // entry groups
   constexpr int CPL = D / LPE;      // value columns per lane
   constexpr int FPL = M / LPE;      // phi features per lane
-  constexpr int CH = kMergeChunk;   // entries staged in LDS at a time
+  constexpr int CH = kMergeChunk * NT / kMergeThreads;   // entries staged in LDS at a time
   constexpr int SPT = CH / NT;      // staged entries per thread
   // entries per group whose loads are in flight together (bounded by registers)
   constexpr int B = sizeof(KT) == 4 ? 2
@@ -451,11 +452,21 @@ hipError_t launch_merge_t(const float* q, const float* phi_q, const float* Wq, c
                           hipStream_t st) {
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
   const bool recomp = phi_k == nullptr && Wk != nullptr;
-  auto kern = m == 64 ? merge_kernel<KT, PT, D, 64, false> : merge_kernel<KT, PT, D, 128, false>;
-  if constexpr (sizeof(KT) == 2 && sizeof(PT) == 2) {
-    if (recomp) kern = m == 64 ? merge_kernel<KT, PT, D, 64, true> : merge_kernel<KT, PT, D, 128, true>;
+  // many (unit, head) blocks: 256 threads each, so that two blocks share a CU
+  // and one block's prologue or combine overlaps another's gathers
+  const bool small = D == 64 && !recomp && kv.n_units * G >= 2048;
+  auto kern = m == 64 ? merge_kernel<KT, PT, D, 64, false, kMergeThreads>
+                      : merge_kernel<KT, PT, D, 128, false, kMergeThreads>;
+  if constexpr (D == 64) {  // (at d = 128 the smaller block runs out of registers)
+    if (small)
+      kern = m == 64 ? merge_kernel<KT, PT, D, 64, false, 256> : merge_kernel<KT, PT, D, 128, false, 256>;
   }
-  hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(kMergeThreads), 0, st, q, phi_q, Wq, bq, G,
+  if constexpr (sizeof(KT) == 2 && sizeof(PT) == 2) {
+    if (recomp)
+      kern = m == 64 ? merge_kernel<KT, PT, D, 64, true, kMergeThreads>
+                     : merge_kernel<KT, PT, D, 128, true, kMergeThreads>;
+  }
+  hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(small ? 256 : kMergeThreads), 0, st, q, phi_q, Wq, bq, G,
                      static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
                      (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx, sel, K,
                      static_cast<const PT*>(phi_k), L_mid, Wk, bk, P, S, u, flags, y, stats,
