@@ -144,12 +144,33 @@ def test_c2_full_budget_sweep(store_phi):
     _run_case(cfg, range(cfg.U), store_phi=store_phi)
 
 
-@pytest.mark.parametrize("store_phi", [True, False])
-def test_c3_full_sampled_units(store_phi):
+@pytest.mark.parametrize("store_phi,fused_phi", [(True, False), (False, False), (True, True)])
+def test_c3_full_sampled_units(store_phi, fused_phi):
     cfg = W.CONFIGS["c3"]
     # units spread over requests, layers and kv heads
     units = [0, 7, 129, 517, 1030, 1555, 2047]
-    _run_case(cfg, units, check_pre=True, store_phi=store_phi)
+    _run_case(cfg, units, check_pre=True, store_phi=store_phi, fused_phi=fused_phi)
+
+
+def test_merge_variants_with_many_heads():
+    """>= 2048 query heads at d=64 use the 256-thread merge: all three variants,
+    both phi_q paths, against the oracle on sampled units."""
+    cfg = W.CONFIGS["c3"].with_(batch=4, layers=16, L=700, K=(12,), steps=2)
+    inp = _gen(cfg)
+    pre = hip_prefill(inp)
+    units = [0, 101, cfg.U - 1]
+    variants = {R.RMA_MERGE_SUB: "sub", R.RMA_MERGE_NO_RESIDUAL: "topk", R.RMA_MERGE_NO_SUBTRACT: "nosub"}
+    for flags, name in variants.items():
+        for fused in (False, True):
+            for st in range(cfg.steps):
+                out = hip_decode(inp, pre, cfg.K[0], st, flags=flags, fused_phi=fused)
+                y = out["y"].cpu()
+                for u in units:
+                    hu = host_unit(inp, u)
+                    ref_pre = oracle_prefill(cfg, hu)
+                    for g in range(cfg.G):
+                        y_ref, _, _ = oracle_decode(cfg, hu, ref_pre, cfg.K[0], st, g, variant=name)
+                        check_y(y[u, g].numpy(), y_ref, f"{name} fused={fused} u{u} g{g} s{st}")
 
 
 @pytest.mark.slow
