@@ -86,6 +86,19 @@ rma_status check_kv_span(const rma_kv* kv, const rma_span* sp, bool need_v) {
 
 int64_t l_mid(const rma_span& sp) { return sp.L - sp.n_sink - sp.n_tail; }
 
+// compute units of the current device (256 when it cannot be queried)
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    cus = (hipGetDevice(&dev) == hipSuccess &&
+           hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+              ? v
+              : 256;
+  }
+  return cus;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------- plans
@@ -98,6 +111,18 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
   if (Lm > 0) {
     // enough blocks to cover the chip (~2 per CU) with as few per-chunk partials as possible
     int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(512, U)));
+    // whole waves of MFMA builder blocks: with long chunks, a last wave that
+    // fills only part of the chip leaves the rest idle for a block's whole time.
+    // Blocks resident per CU: one at d = m = 128 (its registers), two otherwise.
+    if (p.mfma) {
+      const int64_t R = (int64_t)device_cus() * ((kv.d == 128 && m == 128) ? 1 : 2);
+      for (int64_t c = nc; c <= nc + 16 && ceil_div(Lm, c) >= 1024; ++c) {
+        if ((U * c) % R == 0 || U * c >= 8 * R) {
+          nc = c;
+          break;
+        }
+      }
+    }
     // chunks of at most 2^22 tokens keep the builder's 32-bit byte offsets in range
     nc = std::max<int64_t>(nc, ceil_div(Lm, int64_t(1) << 22));
     int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
