@@ -62,9 +62,10 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=69250670, write_bytes=84035264),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=33798605, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="84a74c78a919614c", fetch_bytes=7061072, write_bytes=8192),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=69250710, write_bytes=84035901),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=33832587, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=7060901, write_bytes=8192),
+    ("full_partial_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=67390003, write_bytes=589824),
 }
 
 
@@ -210,18 +211,19 @@ class PathRunner:
             self.merge(s, st)
 
     def traced_step(self, st, R):
-        """The whole path, eager, with every kernel bracketed by HIP events that
-        the library records on `st` (rma_trace_arm).  Returns one record per
-        call: (call name, [(kernel name, start event, end event), ...])."""
+        """The whole path, eager, with every kernel timed by a pair of HIP events
+        that its own dispatch stamps at its start and end (rma_trace_arm).
+        Returns one record per call: (call name, [(kernel name, start event,
+        end event), ...])."""
         t = self.t
         out = []
 
         def traced(name, fn):
-            evs = [t.cuda.Event(enable_timing=True) for _ in range(3)]
+            evs = [t.cuda.Event(enable_timing=True) for _ in range(4)]
             R.rma_trace_arm(evs)
             fn()
             names = R.rma_trace_kernels()
-            out.append((name, [(n, evs[j], evs[j + 1]) for j, n in enumerate(names)]))
+            out.append((name, [(n, evs[2 * j], evs[2 * j + 1]) for j, n in enumerate(names)]))
 
         traced("build", lambda: self.build(st))
         for s in range(self.cfg.steps):
@@ -445,8 +447,8 @@ def main():
     queries = cfg.U * cfg.G * cfg.steps
     value = queries / (ms_per_step / 1e3)
 
-    # ---- per-kernel durations: HIP events recorded by the library around each
-    # kernel on the stream it launches on (eager launches, queued ahead)
+    # ---- per-kernel durations: HIP events that each kernel's own dispatch stamps
+    # at its start and end (eager launches on the path's stream, queued ahead)
     n_t = int(max(5, min(200, args.steps, 2.0 / max(ms_per_step / 1e3, 1e-6))))
     recs = []
     with torch.cuda.stream(stream):

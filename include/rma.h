@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 5
+#define RMA_ABI_VERSION 6
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -278,20 +278,23 @@ int32_t rma_abi_version(void);
 
 /* Per-kernel timing, for benchmarks and profiling only (not part of the
  * method).  Arms a trace for the next entry point called on this thread that
- * enqueues kernels: that call records events[0] on its stream before its first
- * kernel and events[j] after its j-th kernel (j = 1 .. n_events-1; later
- * kernels are not bracketed), then disarms the trace.  `events` are hipEvent_t
- * handles owned by the caller, created with timing enabled on the stream's
- * device; the library keeps the handles until that call and never frees them.
- * n_events == 0 disarms.  Thread-local state; do not arm a trace for a call
- * that is being captured into a graph.
- * Errors: RMA_ERR_INVALID_ARG (n_events not 0 and not in 2..16, NULL handle). */
+ * enqueues kernels: its j-th kernel (j = 0 .. n_events/2 - 1; later kernels are
+ * not timed) is launched through hipExtLaunchKernel with events[2j] and
+ * events[2j+1], which its dispatch stamps when the kernel starts and when it
+ * ends, so their elapsed time is the kernel's execution time alone.  The call
+ * then disarms the trace.  `events` are hipEvent_t handles owned by the
+ * caller, created with timing enabled on the stream's device; the library
+ * keeps the handles until that call and never frees them.  n_events == 0
+ * disarms.  Thread-local state; do not arm a trace for a call that is being
+ * captured into a graph.
+ * Errors: RMA_ERR_INVALID_ARG (n_events not 0 and not even in 2..16, NULL
+ * handle). */
 rma_status rma_trace_arm(void* const* events, int32_t n_events);
 
-/* Kernels bracketed by the last traced call on this thread. */
+/* Kernels timed by the last traced call on this thread. */
 int32_t rma_trace_count(void);
 
-/* Name of the j-th bracketed kernel of that call (0-based), or NULL. */
+/* Name of the j-th timed kernel of that call (0-based), or NULL. */
 const char* rma_trace_name(int32_t j);
 
 #ifdef __cplusplus

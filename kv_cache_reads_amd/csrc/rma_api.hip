@@ -20,19 +20,14 @@ KernelTrace& trace() {
 
 namespace {
 
-// Brackets the kernels of one entry point when a trace is armed; disarms it on exit.
+// Spans one entry point when a trace is armed: its kernels take the armed event
+// pairs in launch order (launch_kernel); on exit the trace is disarmed.
 struct TraceScope {
-  explicit TraceScope(hipStream_t st) {
-    KernelTrace& t = trace();
-    if (t.n_events > 0) {
-      hipEventRecord(t.ev[0], st);
-      t.used = 1;
-    }
-  }
+  explicit TraceScope(hipStream_t) { trace().used = 0; }
   ~TraceScope() {
     KernelTrace& t = trace();
-    if (t.n_events > 0 && t.used > 0) {
-      t.count = t.used - 1;
+    if (t.n_events > 0) {
+      t.count = t.used / 2;
       t.n_events = 0;
       t.used = 0;
     }
@@ -242,8 +237,8 @@ rma_status rma_trace_arm(void* const* events, int32_t n_events) {
     t.used = 0;
     return RMA_OK;
   }
-  RMA_CHECK(events != nullptr && n_events >= 2 && n_events <= kTraceMax, RMA_ERR_INVALID_ARG,
-            "n_events must be 0 or in 2..%d", kTraceMax);
+  RMA_CHECK(events != nullptr && n_events >= 2 && n_events <= kTraceMax && n_events % 2 == 0,
+            RMA_ERR_INVALID_ARG, "n_events must be 0 or even in 2..%d", kTraceMax);
   for (int i = 0; i < n_events; ++i) {
     RMA_CHECK(events[i] != nullptr, RMA_ERR_INVALID_ARG, "event %d is NULL", i);
     t.ev[i] = (hipEvent_t)events[i];

@@ -486,20 +486,21 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
   float* pk = direct ? kappa : reinterpret_cast<float*>(ws + pl.off_kap);
   if (pl.n_chunks > 0) {
     const dim3 grid(pl.n_chunks, kv.n_units);
+    hipError_t e = hipSuccess;
     if (pl.mfma) {
       const uint16_t* kk = static_cast<const uint16_t*>(kv.k);
       const uint16_t* vv = static_cast<const uint16_t*>(kv.v);
       uint16_t* ph = static_cast<uint16_t*>(phi_k);
-#define RMA_BM(DD, MM)                                                                         \
-  do {                                                                                         \
-    if (ph != nullptr)                                                                         \
-      hipLaunchKernelGGL((build_mfma_kernel<DD, MM, true>), grid, dim3(MM * 4), 0, st, kk, vv, \
-                         kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P, ph,    \
-                         pS, pu, pk);                                                          \
-    else                                                                                       \
-      hipLaunchKernelGGL((build_mfma_kernel<DD, MM, false>), grid, dim3(MM * 4), 0, st, kk,    \
-                         vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P,    \
-                         ph, pS, pu, pk);                                                      \
+#define RMA_BM(DD, MM)                                                                               \
+  do {                                                                                               \
+    if (ph != nullptr)                                                                               \
+      e = launch_kernel("build_mfma_kernel", build_mfma_kernel<DD, MM, true>, grid, dim3(MM * 4), 0, \
+                        st, kk, vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len,   \
+                        acc_direct, W, b, P, ph, pS, pu, pk);                                        \
+    else                                                                                             \
+      e = launch_kernel("build_mfma_kernel", build_mfma_kernel<DD, MM, false>, grid, dim3(MM * 4), 0, \
+                        st, kk, vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len,   \
+                        acc_direct, W, b, P, ph, pS, pu, pk);                                        \
   } while (0)
       if (kv.d == 64 && m == 64) RMA_BM(64, 64);
       else if (kv.d == 64) RMA_BM(64, 128);
@@ -507,11 +508,11 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
       else RMA_BM(128, 128);
 #undef RMA_BM
     } else {
-#define RMA_BV1(KT, PT, DD, MM)                                                                   \
-  hipLaunchKernelGGL((build_valu_kernel<KT, PT, DD, MM>), grid, dim3(256), 0, st,                  \
-                     static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,   \
-                     sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P, static_cast<PT*>(phi_k), pS, \
-                     pu, pk)
+#define RMA_BV1(KT, PT, DD, MM)                                                                      \
+  e = launch_kernel("build_valu_kernel", build_valu_kernel<KT, PT, DD, MM>, grid, dim3(256), 0, st,  \
+                    static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,      \
+                    sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, W, b, P,              \
+                    static_cast<PT*>(phi_k), pS, pu, pk)
 #define RMA_BV(KT, PT)                                                 \
   do {                                                                 \
     if (kv.d == 64 && m == 64) RMA_BV1(KT, PT, 64, 64);                \
@@ -527,26 +528,22 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
 #undef RMA_BV1
 #undef RMA_BV
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    trace_kernel(st, pl.mfma ? "build_mfma_kernel" : "build_valu_kernel");
   }
   if (direct) return hipSuccess;
   const int blocks = (int)ceil_div((int64_t)m * kv.d / 4 + m / 4, 64);
-  hipLaunchKernelGGL(build_reduce_kernel, dim3(blocks, kv.n_units), dim3(256), 0, st, pS, pu, pk,
-                     pl.n_chunks, m, kv.d, acc ? 1 : 0, S, u, kappa);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) trace_kernel(st, "build_reduce_kernel");
-  return e;
+  return launch_kernel("build_reduce_kernel", build_reduce_kernel, dim3(blocks, kv.n_units),
+                       dim3(256), 0, st, pS, pu, pk, pl.n_chunks, m, kv.d, acc ? 1 : 0, S, u, kappa);
 }
 
 hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride, int d,
                       const float* W, const float* b, int m, int P, void* phi, int phi_dtype,
                       hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(rows, 8), n_units, m / 16);
-#define RMA_PHI1(XT, PT, DD)                                                                     \
-  hipLaunchKernelGGL((phi_kernel<XT, PT, DD>), grid, dim3(256), 0, st, static_cast<const XT*>(x), \
-                     xstride, (int)rows, W, b, m, P, static_cast<PT*>(phi))
+  hipError_t e = hipSuccess;
+#define RMA_PHI1(XT, PT, DD)                                                                         \
+  e = launch_kernel("phi_kernel", phi_kernel<XT, PT, DD>, grid, dim3(256), 0, st,                    \
+                    static_cast<const XT*>(x), xstride, (int)rows, W, b, m, P, static_cast<PT*>(phi))
 #define RMA_PHI(XT, PT)                    \
   do {                                     \
     if (d == 64) RMA_PHI1(XT, PT, 64);     \
@@ -559,8 +556,6 @@ hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int
   }
 #undef RMA_PHI1
 #undef RMA_PHI
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) trace_kernel(st, "phi_kernel");
   return e;
 }
 

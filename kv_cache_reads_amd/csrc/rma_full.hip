@@ -409,16 +409,17 @@ static hipError_t launch_full_t(const FullPlan& pl, const float* q, int G, const
   const dim3 grid(pl.n_chunks, kv.n_units);
   const bool memb = idx != nullptr && K > 0;
   const int T_all = (int)(sp.L + sp.n_gen);
-#define RMA_FP(GG)                                                                            \
-  do {                                                                                        \
-    if (memb)                                                                                 \
-      full_partial_kernel<KT, D, GG, true><<<grid, kFullThreads, 0, st>>>(                    \
-          q, kb, vb, kv.unit_stride, (int)sp.L, sp.n_sink, sp.n_tail, T_all, pl.ch,           \
-          pl.n_chunks, idx, K, part, isd);                                                    \
-    else                                                                                      \
-      full_partial_kernel<KT, D, GG, false><<<grid, kFullThreads, 0, st>>>(                   \
-          q, kb, vb, kv.unit_stride, (int)sp.L, sp.n_sink, sp.n_tail, T_all, pl.ch,           \
-          pl.n_chunks, idx, K, part, isd);                                                    \
+  hipError_t e = hipSuccess;
+#define RMA_FP(GG)                                                                                   \
+  do {                                                                                               \
+    if (memb)                                                                                        \
+      e = launch_kernel("full_partial_kernel", full_partial_kernel<KT, D, GG, true>, grid,           \
+                        dim3(kFullThreads), 0, st, q, kb, vb, kv.unit_stride, (int)sp.L, sp.n_sink,  \
+                        sp.n_tail, T_all, pl.ch, pl.n_chunks, idx, K, part, isd);                    \
+    else                                                                                             \
+      e = launch_kernel("full_partial_kernel", full_partial_kernel<KT, D, GG, false>, grid,          \
+                        dim3(kFullThreads), 0, st, q, kb, vb, kv.unit_stride, (int)sp.L, sp.n_sink,  \
+                        sp.n_tail, T_all, pl.ch, pl.n_chunks, idx, K, part, isd);                    \
   } while (0)
   switch (G) {
     case 1: RMA_FP(1); break;
@@ -431,18 +432,13 @@ static hipError_t launch_full_t(const FullPlan& pl, const float* q, int G, const
     default: RMA_FP(8); break;
   }
 #undef RMA_FP
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  trace_kernel(st, "full_partial_kernel");
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
   // without a retrieved set (K == 0) the residual set is the whole mid-region
   const int resid_mode = (idx != nullptr || K == 0) ? 2 : 0;
-  full_combine_kernel<D><<<kv.n_units * G, kFullCombineThreads, 0, st>>>(part, G, pl.n_chunks, L_mid, resid_mode,
-                                                         y_cmp, y, diag);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  trace_kernel(st, "full_combine_kernel");
-  return hipSuccess;
+  return launch_kernel("full_combine_kernel", full_combine_kernel<D>, dim3(kv.n_units * G),
+                       dim3(kFullCombineThreads), 0, st, part, G, pl.n_chunks, L_mid, resid_mode,
+                       y_cmp, y, diag);
 }
 
 hipError_t launch_full(const FullPlan& pl, const float* q, int G, const rma_kv& kv,

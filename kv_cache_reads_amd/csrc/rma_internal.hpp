@@ -2,9 +2,12 @@
 // A plan fixes the tiling of one call; the workspace size and every launch are
 // derived from the same plan, so they cannot disagree.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "../../include/rma.h"
 
@@ -72,24 +75,43 @@ struct FullPlan {
 FullPlan plan_full(const rma_kv& kv, const rma_span& sp, int G);
 
 // ------------------------------------------------------------- kernel timing
-// Benchmark instrumentation armed by rma_trace_arm: events recorded on the
-// call's stream before its first kernel and after each kernel.  Thread-local.
+// Benchmark instrumentation armed by rma_trace_arm: each kernel of the next call
+// takes the next pair of events, stamped by its own dispatch at the start and at
+// the end of its execution.  Thread-local.
 constexpr int kTraceMax = 16;
 struct KernelTrace {
   hipEvent_t ev[kTraceMax];
-  const char* name[kTraceMax];
+  const char* name[kTraceMax / 2];
   int n_events = 0;   // armed events (0 = off)
-  int used = 0;       // events recorded by the current call
-  int count = 0;      // kernels bracketed by the last traced call
+  int used = 0;       // events taken by the current call
+  int count = 0;      // kernels timed by the last traced call
 };
 KernelTrace& trace();
-// after each kernel launch of an entry point
-inline void trace_kernel(hipStream_t st, const char* name) {
-  KernelTrace& t = trace();
-  if (t.n_events > 0 && t.used > 0 && t.used < t.n_events) {
-    t.name[t.used - 1] = name;
-    hipEventRecord(t.ev[t.used++], st);
-  }
+
+// Enqueues kern<<<grid, block, shm, st>>>(args...).  With a trace armed and a
+// pair of events left, the launch goes through hipExtLaunchKernel with that pair.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(const char* name, void (*kern)(Params...), dim3 grid, dim3 block,
+                         uint32_t shm, hipStream_t st, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> vals(static_cast<Params>(args)...);
+  return std::apply(
+      [&](auto&... v) {
+        void* argv[] = {const_cast<void*>(static_cast<const void*>(&v))..., nullptr};
+        const void* fn = reinterpret_cast<const void*>(kern);
+        KernelTrace& t = trace();
+        if (t.n_events > 0 && t.used + 2 <= t.n_events) {
+          const hipError_t e = hipExtLaunchKernel(fn, grid, block, argv, shm, st, t.ev[t.used],
+                                                  t.ev[t.used + 1], 0);
+          if (e == hipSuccess) {
+            t.name[t.used / 2] = name;
+            t.used += 2;
+          }
+          return e;
+        }
+        return hipLaunchKernel(fn, grid, block, argv, shm, st);
+      },
+      vals);
 }
 
 // ------------------------------------------------------------- launchers

@@ -466,14 +466,11 @@ hipError_t launch_merge_t(const float* q, const float* phi_q, const float* Wq, c
       kern = m == 64 ? merge_kernel<KT, PT, D, 64, true, kMergeThreads>
                      : merge_kernel<KT, PT, D, 128, true, kMergeThreads>;
   }
-  hipLaunchKernelGGL(kern, dim3(kv.n_units * G), dim3(small ? 256 : kMergeThreads), 0, st, q, phi_q, Wq, bq, G,
-                     static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
-                     (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx, sel, K,
-                     static_cast<const PT*>(phi_k), L_mid, Wk, bk, P, S, u, flags, y, stats,
-                     1.0f / sqrtf((float)D));
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) trace_kernel(st, "merge_kernel");
-  return e;
+  return launch_kernel("merge_kernel", kern, dim3(kv.n_units * G), dim3(small ? 256 : kMergeThreads),
+                       0, st, q, phi_q, Wq, bq, G, static_cast<const KT*>(kv.k),
+                       static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
+                       sp.n_tail, (int)sp.n_gen, idx, sel, K, static_cast<const PT*>(phi_k), L_mid,
+                       Wk, bk, P, S, u, flags, y, stats, 1.0f / sqrtf((float)D));
 }
 
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, const float* Wq,

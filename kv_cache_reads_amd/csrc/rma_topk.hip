@@ -672,11 +672,12 @@ template <typename KT, int D>
 hipError_t launch_scan_g(int G, dim3 grid, hipStream_t st, const float* q, const KT* kb,
                          int64_t ustride, int n_sink, int L_mid, const TopkPlan& pl,
                          const float* kappa, float2* ent, int2* meta, float4* hpw) {
-#define RMA_SCAN_CASE(GG)                                                                     \
-  case GG:                                                                                    \
-    hipLaunchKernelGGL((topk_scan_kernel<KT, D, GG>), grid, dim3(kScanThreads), 0, st, q, kb, \
-                       ustride, n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_min, pl.r_cap, kappa, \
-                       ent, meta, hpw);                                                       \
+  hipError_t e = hipSuccess;
+#define RMA_SCAN_CASE(GG)                                                                            \
+  case GG:                                                                                           \
+    e = launch_kernel("topk_scan_kernel", topk_scan_kernel<KT, D, GG>, grid, dim3(kScanThreads), 0,  \
+                      st, q, kb, ustride, n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_min, pl.r_cap,     \
+                      kappa, ent, meta, hpw);                                                        \
     break;
   switch (G) {
     RMA_SCAN_CASE(1) RMA_SCAN_CASE(2) RMA_SCAN_CASE(3) RMA_SCAN_CASE(4)
@@ -684,8 +685,6 @@ hipError_t launch_scan_g(int G, dim3 grid, hipStream_t st, const float* q, const
     default: return hipErrorInvalidValue;
   }
 #undef RMA_SCAN_CASE
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) trace_kernel(st, "topk_scan_kernel");
   return e;
 }
 
@@ -717,16 +716,14 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
   if (g_lds_limit > sl) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - sl) / 8);
   const size_t lds = (size_t)std::max(e_max, 1) * 8;
   if (small)
-    hipLaunchKernelGGL((topk_select_kernel<KT, D, 256>), dim3(kv.n_units * G), dim3(256), lds, st, q, G,
-                       kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max,
-                       hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
-  else
-    hipLaunchKernelGGL((topk_select_kernel<KT, D, kSelThreads>), dim3(kv.n_units * G), dim3(kSelThreads),
-                       lds, st, q, G, kb, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks,
-                       pl.r_cap, K, e_max, hpw, ent, meta, idx, sel, 1.0f / sqrtf((float)D));
-  e = hipGetLastError();
-  if (e == hipSuccess) trace_kernel(st, "topk_select_kernel");
-  return e;
+    return launch_kernel("topk_select_kernel", topk_select_kernel<KT, D, 256>,
+                         dim3(kv.n_units * G), dim3(256), lds, st, q, G, kb, kv.unit_stride,
+                         sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max, hpw, ent, meta,
+                         idx, sel, 1.0f / sqrtf((float)D));
+  return launch_kernel("topk_select_kernel", topk_select_kernel<KT, D, kSelThreads>,
+                       dim3(kv.n_units * G), dim3(kSelThreads), lds, st, q, G, kb, kv.unit_stride,
+                       sp.n_sink, L_mid, pl.ch, pl.n_chunks, pl.r_cap, K, e_max, hpw, ent, meta,
+                       idx, sel, 1.0f / sqrtf((float)D));
 }
 
 }  // namespace

@@ -305,8 +305,9 @@ def rma_abi_version() -> int:
 
 def rma_trace_arm(events) -> None:
     """Arm per-kernel timing for the next call on this thread (benchmark
-    instrumentation): `events` are torch.cuda.Event(enable_timing=True); the
-    call records events[0] before its first kernel and events[j] after its j-th."""
+    instrumentation): `events` are torch.cuda.Event(enable_timing=True), an even
+    number; the call's j-th kernel is stamped with events[2j] when it starts and
+    events[2j+1] when it ends (hipExtLaunchKernel)."""
     L = lib()
     handles = []
     for e in events:
@@ -318,6 +319,6 @@ def rma_trace_arm(events) -> None:
 
 
 def rma_trace_kernels():
-    """Names of the kernels the last traced call bracketed, in launch order."""
+    """Names of the kernels the last traced call timed, in launch order."""
     L = lib()
     return [L.rma_trace_name(j).decode() for j in range(L.rma_trace_count())]

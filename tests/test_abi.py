@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 5
+    assert L.rma_abi_version() == 6
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -173,7 +173,9 @@ def test_trace_arm_validation():
     L = R.lib()
     VP = ctypes.c_void_p
     two = (VP * 2)(0x1000, 0x2000)
-    assert L.rma_trace_arm(two, 1) == R.RMA_ERR_INVALID_ARG              # one event brackets nothing
+    assert L.rma_trace_arm(two, 1) == R.RMA_ERR_INVALID_ARG              # one event times nothing
+    three = (VP * 3)(0x1000, 0x2000, 0x3000)
+    assert L.rma_trace_arm(three, 3) == R.RMA_ERR_INVALID_ARG            # events come in pairs
     assert L.rma_trace_arm(two, 17) == R.RMA_ERR_INVALID_ARG             # more than RMA_TRACE_MAX_EVENTS
     assert L.rma_trace_arm((VP * 2)(0x1000, None), 2) == R.RMA_ERR_INVALID_ARG
     assert L.rma_trace_arm(None, 2) == R.RMA_ERR_INVALID_ARG
