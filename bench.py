@@ -62,10 +62,10 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=69250710, write_bytes=84035901),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=33832587, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=7060901, write_bytes=8192),
-    ("full_partial_kernel", "c1", 328): dict(csrc="291cea8ab0e9d43f", fetch_bytes=67390003, write_bytes=589824),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="bf469dbc5e99e868", fetch_bytes=69250899, write_bytes=84032126),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="bf469dbc5e99e868", fetch_bytes=33832490, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="bf469dbc5e99e868", fetch_bytes=7072351, write_bytes=8192),
+    ("full_partial_kernel", "c1", 328): dict(csrc="bf469dbc5e99e868", fetch_bytes=67366841, write_bytes=589824),
 }
 
 
@@ -126,6 +126,9 @@ def kernel_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
         "merge_kernel": U * G * (K * (d * e + phi_row + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
         + U * (m * d * 4 + m * 4) + (0 if store_phi else params)
         + (params - U * G * m * 4 if fused_phi else 0),
+        # with a head's entries split over several blocks, this kernel writes y
+        # from their partials (scratch); the merge call's bytes are the merge's
+        "merge_combine_kernel": U * G * d * 4,
     }
 
 

@@ -104,13 +104,15 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
   p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
   const int tile = p.mfma ? 64 : 32;
   if (Lm > 0) {
-    // enough blocks to cover the chip (~2 per CU) with as few per-chunk partials as possible
+    // enough blocks to cover the chip with as few per-chunk partials as possible
     int64_t nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(512, U)));
-    // whole waves of MFMA builder blocks: with long chunks, a last wave that
-    // fills only part of the chip leaves the rest idle for a block's whole time.
-    // Blocks resident per CU: one at d = m = 128 (its registers), two otherwise.
     if (p.mfma) {
-      const int64_t R = (int64_t)device_cus() * ((kv.d == 128 && m == 128) ? 1 : 2);
+      // the MFMA builder's resident blocks (by its registers): one per CU at
+      // d = 128, two at d = 64; one wave of them covers the chip
+      const int64_t R = (int64_t)device_cus() * (kv.d == 128 ? 1 : 2);
+      nc = std::max<int64_t>(1, std::min<int64_t>(ceil_div(Lm, 256), ceil_div(R, U)));
+      // whole waves of blocks: with long chunks, a last wave that fills only
+      // part of the chip leaves the rest idle for a block's whole time
       for (int64_t c = nc; c <= nc + 16 && ceil_div(Lm, c) >= 1024; ++c) {
         if ((U * c) % R == 0 || U * c >= 8 * R) {
           nc = c;
@@ -197,14 +199,26 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) 
   (void)m;
   MergePlan p{};
   const int64_t U = kv.n_units;
-  const int64_t T = (int64_t)sp.n_sink + sp.n_tail + sp.n_gen + K;
-  (void)G;
-  // one block per (unit, head): no scratch beyond the (unused) counter region
-  p.sl = (int)T;
-  p.n_slices = 1;
-  p.part_floats = 0;
+  const int64_t T = std::max<int64_t>(1, (int64_t)sp.n_sink + sp.n_tail + sp.n_gen + K);
+  // One block per (unit, head) gathers its entries in rounds of `per_round`
+  // (eight lanes per entry, a few entries per lane group in flight).  When the
+  // heads alone leave most of the chip idle and a head needs three or more
+  // rounds, its entries are split into slices of about one round each, at most
+  // one block per CU in all (the merge block's registers allow one resident
+  // block), and a second kernel combines the slices.  (With two rounds the
+  // second kernel's launch costs about what the split saves.)
+  const int64_t per_round = kv.dtype == RMA_BF16 ? (kv.d == 64 ? 512 : 256) : 128;
+  const int64_t heads = U * G;
+  const int64_t rounds = ceil_div(T, per_round);
+  const int64_t ns = rounds < 3 ? 1
+                                : std::max<int64_t>(1, std::min<int64_t>({rounds,
+                                                                          (int64_t)device_cus() / heads,
+                                                                          (int64_t)kMergeCombineThreads}));
+  p.sl = (int)ceil_div(T, ns);
+  p.n_slices = (int)ceil_div(T, p.sl);   // no empty slice
+  p.part_floats = p.n_slices > 1 ? 4 + 3 * kv.d : 0;
   p.off_part = counter_bytes(U);
-  p.total = counter_bytes(U);
+  p.total = align_up(p.off_part + (size_t)heads * p.n_slices * p.part_floats * 4);
   return p;
 }
 

@@ -54,6 +54,7 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K);
 // ------------------------------------------------------------- merge
 constexpr int kMergeThreads = 512;    // one block per (unit, query head)
 constexpr int kMergeChunk = 2048;     // exact-support entries staged in LDS at a time
+constexpr int kMergeCombineThreads = 256;   // >= the most slices a head gets
 
 struct MergePlan {
   int n_slices, sl;          // slices of the per-head entry list, entries per slice

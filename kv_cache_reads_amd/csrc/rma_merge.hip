@@ -4,9 +4,10 @@
 // §4.2 Eq. 9 for the subtraction; §4.3 Eq. 10 for the merge; App. C.1 for the
 // clamp of the residual denominator).
 //
-// One block per (unit, query head).  The head's exact-support entries
+// One block per (unit, query head), or per (unit, query head, slice) when few
+// heads would leave most of the chip idle.  The head's exact-support entries
 //   [sinks | tail | generated | retrieved (idx)]   (n_a + n_gen + K entries)
-// are staged in LDS chunk by chunk.  Eight lanes share an entry; each 8-lane
+// (one contiguous slice of them) are staged in LDS chunk by chunk.  Eight lanes share an entry; each 8-lane
 // group takes every 64th entry, issues the row loads of four entries at once
 // (V row; K row for an anchor or generated token, whose score it computes;
 // phi_k row for a retrieved token) and keeps its own running max m:
@@ -15,7 +16,10 @@
 // The group partials are combined with max rescaling (fixed order) into m*,
 // N_E, Z_E.  phi(q)^T S is a matrix-vector product per head (fp32 VALU; its
 // loads are issued before the gathers and consumed after them); then the
-// subtraction, the clamp and one normalisation.
+// subtraction, the clamp and one normalisation.  With slices, each block writes
+// its partial (m, Z, sum w, N, sum w v; slice 0 also phi(q)^T S and u^T f) to the
+// workspace, and a second kernel (one block per head) combines the partials in
+// slice order, with max rescaling, and writes y.
 #include "rma_device.hpp"
 #include "rma_internal.hpp"
 
@@ -69,7 +73,8 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
              const float* __restrict__ sel, int K, const PT* __restrict__ phik, int L_mid,
              const float* __restrict__ Wk, const float* __restrict__ bk, int P,
              const float* __restrict__ S, const float* __restrict__ u_, uint32_t flags,
-             float* __restrict__ y, float* __restrict__ stats, float inv_sqrt_d) {
+             float* __restrict__ y, float* __restrict__ stats, float inv_sqrt_d, int n_slices,
+             int slice_len, float* __restrict__ sparts) {
   static_assert(!RECOMP || sizeof(KT) == 2, "recomputed phi rows need bf16 keys");
   static_assert(!RECOMP || NTH == kMergeThreads, "the recompute tiles assume the full block");
   constexpr int NT = NTH, NW = NT / kWave;
@@ -83,11 +88,13 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   constexpr int B = sizeof(KT) == 4 ? 2
                     : sizeof(PT) == 4 ? (D == 128 ? 2 : 4)
                     : D == 128 ? (RECOMP ? 3 : 4) : 8;
-  const int ug = blockIdx.x, u = ug / G, g = ug - u * G, tid = threadIdx.x;
+  const int ug = blockIdx.x / n_slices, u = ug / G, g = ug - u * G, tid = threadIdx.x;
+  const int slice = blockIdx.x - ug * n_slices;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
   const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
   const int T = n_ex + K;
+  const int e0 = slice * slice_len, e1 = min(T, e0 + slice_len);   // this block's entries
   const bool sub = (flags == RMA_MERGE_SUB) && K > 0;
   const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
   const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
@@ -133,10 +140,10 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
 #pragma unroll
     for (int r = 0; r < SPT; ++r) {
       const int j = c0 + tid + NT * r;
-      const bool ret = j >= n_ex && j < T;
+      const bool ret = j >= n_ex && j < e1;
       int pos = j < n_sink ? j : (j < n_a ? L - n_tail + (j - n_sink) : L + (j - n_a));
       if (ret) pos = min(max(ri[r], n_sink), n_sink + max(L_mid, 1) - 1);
-      spos[r] = j < T ? pos : n_sink;
+      spos[r] = j < e1 ? pos : n_sink;
       ssc[r] = ret ? rs[r] : 0.f;
     }
   };
@@ -167,7 +174,7 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
     }
     fb0 = fcomp ? bq[(size_t)pset * M + fi] : (resid && phi_q != nullptr ? phi_q[(size_t)ug * M + (tid % M)] : 0.f);
   }
-  stage_load(0);
+  stage_load(e0);
 
   float qr[CPL], fr[FPL];
 #pragma unroll
@@ -181,7 +188,8 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   //      this is a matrix-vector product: thread (column col, feature block fb)
   //      loads its FPB elements of S once (coalesced along the columns).
   //      Without a residual the loads read q instead and are discarded.
-  const bool rs = resid && !whole_mid;
+  // (with slices, the first slice of the head forms phi(q)^T S and u^T f)
+  const bool rs = resid && !whole_mid && slice == 0;
   constexpr int FB = NT / D;          // feature blocks
   constexpr int FPB = M / FB;         // features per block
   const int scol = tid % D, fb = tid / D;
@@ -281,14 +289,14 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   float Z = 0.f, ZK = 0.f, mrun = -INFINITY;
 
   // ---- exact-support entries, CH at a time
-  for (int c0 = 0; c0 < T; c0 += CH) {
-    if (c0 > 0) {
+  for (int c0 = e0; c0 < e1; c0 += CH) {
+    if (c0 > e0) {
       __syncthreads();  // the previous chunk's entries are consumed
       stage_load(c0);
     }
     stage_store();
     __syncthreads();
-    const int cnt = min(CH, T - c0);
+    const int cnt = min(CH, e1 - c0);
     if constexpr (RECOMP) {
       if (sub) recompute_w(c0, cnt);
     }
@@ -410,8 +418,39 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
     ZE += sw[w] * s_wz[w];
     ZKt += s_wzk[w];
   }
+  float uf = rs ? s_uf : 0.f;
+
+  // ---- slices: this block's partial to the workspace (combined by
+  //      merge_combine_kernel)
+  constexpr int PFL = 4 + 3 * D;     // floats per partial
+  if (n_slices > 1) {
+    float* pp = sparts + ((size_t)ug * n_slices + slice) * PFL;
+    if (tid == 0) {
+      pp[0] = ms;
+      pp[1] = ZE;
+      pp[2] = ZKt;
+      pp[3] = uf;
+    }
+    for (int col = tid; col < D; col += NT) {
+      float NE = 0.f, NKc = 0.f, fs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        NE += sw[w] * s_wn[w][col];
+        NKc += s_wk[w][col];
+      }
+      if (rs) {
+#pragma unroll
+        for (int k = 0; k < FB; ++k) fs += s_part[k][col];
+      }
+      pp[4 + col] = NE;
+      pp[4 + D + col] = NKc;
+      pp[4 + 2 * D + col] = fs;
+    }
+    return;
+  }
+
   float zr = 0.f;
-  if (resid && !whole_mid) zr = fmaxf(s_uf - (sub ? ZKt : 0.f), 0.f);
+  if (resid && !whole_mid) zr = fmaxf(uf - (sub ? ZKt : 0.f), 0.f);
   // y = (N_E + e^{-m*} nu) / (Z_E + e^{-m*} Z_R), scaled by e^{m* - Mx} with
   // Mx = max(m*, log Z_R) so that neither term overflows
   const float lz = zr > 0.f ? __logf(zr) : -INFINITY;
@@ -443,9 +482,77 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   }
 }
 
+// Combines the slice partials of each (unit, query head) in slice order: the
+// running maxima are rescaled to their largest, Z, N and sum w v are summed,
+// slice 0 holds phi(q)^T S and u^T f; then the subtraction, the clamp and the
+// one normalisation, exactly as at the end of merge_kernel.  One thread per
+// slice stages the partial headers in LDS; each column's sums over the slices
+// then run with their loads in flight together.
+template <int D>
+__global__ void __launch_bounds__(kMergeCombineThreads)
+merge_combine_kernel(const float* __restrict__ sparts, int n_slices, uint32_t flags, int K,
+                     int L_mid, float* __restrict__ y, float* __restrict__ stats) {
+  constexpr int PFL = 4 + 3 * D;
+  __shared__ float s_m[kMergeCombineThreads], s_z[kMergeCombineThreads], s_zk[kMergeCombineThreads];
+  __shared__ float s_sc[kMergeCombineThreads];
+  __shared__ float s_tot[4];
+  const int ug = blockIdx.x, tid = threadIdx.x;
+  const bool sub = (flags == RMA_MERGE_SUB) && K > 0;
+  const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
+  const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
+  const float* pb = sparts + (size_t)ug * n_slices * PFL;
+  if (tid < n_slices) {
+    const float* pk = pb + (size_t)tid * PFL;
+    s_m[tid] = pk[0];
+    s_z[tid] = pk[1];
+    s_zk[tid] = pk[2];
+  }
+  __syncthreads();
+  float mall = -INFINITY;
+  for (int k = 0; k < n_slices; ++k) mall = fmaxf(mall, s_m[k]);
+  if (tid < n_slices) s_sc[tid] = s_m[tid] == -INFINITY ? 0.f : __expf(s_m[tid] - mall);
+  __syncthreads();
+  if (tid == 0) {
+    float ZE = 0.f, ZK = 0.f;
+    for (int k = 0; k < n_slices; ++k) {
+      ZE += s_sc[k] * s_z[k];
+      ZK += s_zk[k];
+    }
+    float zr = 0.f;
+    if (resid && !whole_mid) zr = fmaxf(pb[3] - (sub ? ZK : 0.f), 0.f);
+    s_tot[0] = ZE;
+    s_tot[1] = ZK;
+    s_tot[2] = zr;
+    if (stats != nullptr) {
+      stats[(size_t)ug * 4 + 0] = mall;
+      stats[(size_t)ug * 4 + 1] = ZE;
+      stats[(size_t)ug * 4 + 2] = zr;
+      stats[(size_t)ug * 4 + 3] = ZK;
+    }
+  }
+  __syncthreads();
+  const float ZE = s_tot[0], zr = s_tot[2];
+  const float lz = zr > 0.f ? __logf(zr) : -INFINITY;
+  const float Mx = fmaxf(mall, lz);
+  const float a = __expf(mall - Mx);
+  const float bres = __expf(-Mx);
+  const float den = a * ZE + bres * zr;
+  for (int col = tid; col < D; col += kMergeCombineThreads) {
+    float NE = 0.f, NK = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < n_slices; ++k) {
+      const float* pk = pb + (size_t)k * PFL;
+      NE += s_sc[k] * pk[4 + col];
+      NK += pk[4 + D + col];
+    }
+    const float nu = (resid && !whole_mid) ? pb[4 + 2 * D + col] - (sub ? NK : 0.f) : 0.f;
+    y[(size_t)ug * D + col] = (a * NE + bres * nu) / den;
+  }
+}
+
 template <typename KT, typename PT, int D>
-hipError_t launch_merge_t(const float* q, const float* phi_q, const float* Wq, const float* bq,
-                          int G, const rma_kv& kv,
+hipError_t launch_merge_t(const MergePlan& pl, uint8_t* ws, const float* q, const float* phi_q,
+                          const float* Wq, const float* bq, int G, const rma_kv& kv,
                           const rma_span& sp, const int32_t* idx, const float* sel, int K,
                           const void* phi_k, const float* Wk, const float* bk, int P, int m,
                           const float* S, const float* u, uint32_t flags, float* y, float* stats,
@@ -466,11 +573,17 @@ hipError_t launch_merge_t(const float* q, const float* phi_q, const float* Wq, c
       kern = m == 64 ? merge_kernel<KT, PT, D, 64, true, kMergeThreads>
                      : merge_kernel<KT, PT, D, 128, true, kMergeThreads>;
   }
-  return launch_kernel("merge_kernel", kern, dim3(kv.n_units * G), dim3(small ? 256 : kMergeThreads),
-                       0, st, q, phi_q, Wq, bq, G, static_cast<const KT*>(kv.k),
-                       static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
-                       sp.n_tail, (int)sp.n_gen, idx, sel, K, static_cast<const PT*>(phi_k), L_mid,
-                       Wk, bk, P, S, u, flags, y, stats, 1.0f / sqrtf((float)D));
+  float* part = reinterpret_cast<float*>(ws + pl.off_part);
+  hipError_t e = launch_kernel("merge_kernel", kern, dim3(kv.n_units * G * pl.n_slices),
+                               dim3(small ? 256 : kMergeThreads), 0, st, q, phi_q, Wq, bq, G,
+                               static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v),
+                               kv.unit_stride, (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, idx,
+                               sel, K, static_cast<const PT*>(phi_k), L_mid, Wk, bk, P, S, u, flags,
+                               y, stats, 1.0f / sqrtf((float)D), pl.n_slices, pl.sl, part);
+  if (e != hipSuccess || pl.n_slices == 1) return e;
+  return launch_kernel("merge_combine_kernel", merge_combine_kernel<D>, dim3(kv.n_units * G),
+                       dim3(kMergeCombineThreads), 0, st, part, pl.n_slices, flags, K, L_mid, y,
+                       stats);
 }
 
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, const float* Wq,
@@ -480,13 +593,11 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
                         const float* Wk, const float* bk, int P, int m, const float* S,
                         const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
                         hipStream_t st) {
-  (void)pl;
-  (void)ws;
-#define RMA_MERGE_DISPATCH(KT, PT)                                                              \
-  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(q, phi_q, Wq, bq, G, kv, sp, idx, sel, K, phi_k, Wk, bk, \
-                                                 P, m, S, u, flags, y, stats, st)                \
-                    : launch_merge_t<KT, PT, 128>(q, phi_q, Wq, bq, G, kv, sp, idx, sel, K, phi_k, Wk,   \
-                                                  bk, P, m, S, u, flags, y, stats, st);
+#define RMA_MERGE_DISPATCH(KT, PT)                                                                \
+  return kv.d == 64 ? launch_merge_t<KT, PT, 64>(pl, ws, q, phi_q, Wq, bq, G, kv, sp, idx, sel, K,  \
+                                                 phi_k, Wk, bk, P, m, S, u, flags, y, stats, st)   \
+                    : launch_merge_t<KT, PT, 128>(pl, ws, q, phi_q, Wq, bq, G, kv, sp, idx, sel, K, \
+                                                  phi_k, Wk, bk, P, m, S, u, flags, y, stats, st);
   if (kv.dtype == RMA_BF16) {
     if (phi_dtype == RMA_BF16) { RMA_MERGE_DISPATCH(uint16_t, uint16_t) }
     RMA_MERGE_DISPATCH(uint16_t, float)
