@@ -84,6 +84,60 @@ def phi_features(x, W, b) -> np.ndarray:
     return np.where(z > 0.0, z + 1.0, np.exp(np.minimum(z, 0.0)))
 
 
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), through float32 first: the
+    value an fp32 accumulator holds is what the GPU rounds to bfloat16.  The
+    result is returned as float64 (every bfloat16 value is exact there)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    r = ((bits + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
+def phi_mlp(x, params, bf16_operands: bool = False) -> np.ndarray:
+    """The pages' feature-map family (f4), row-wise over x.
+
+    Page §4.4 ("Training phi"): phi_q and phi_k are head-specific one-block
+    ReZero MLPs; App. C.1 ("Why positivity matters"): their outputs are
+    exponentiated, so every feature is positive; §8 ("Scope and runtime"):
+    d_phi = 64.  App. C.2, which would give the architecture, is empty on the
+    page.  Reading (pinned by the parameter totals of §8, see the tests): an
+    input layer to width H = 512 with bias, one ReZero block
+    h1 = h0 + alpha * (W_2 act(W_1 h0 + b_1) + b_2) with two H x H layers, and
+    an output layer to d_phi with bias, exponentiated:
+
+        h0 = W_in x + b_in,  h1 = h0 + alpha (W_2 relu(W_1 h0 + b_1) + b_2),
+        phi(x) = exp(W_o h1 + b_o).
+
+    The block's activation is not given anywhere on the pages; ReLU is the
+    reading taken (parity for that choice is unpinned by the pages).
+
+    params: dict with W_in [H, d], b_in [H], W_1 [H, H], b_1 [H], W_2 [H, H],
+    b_2 [H], alpha (scalar), W_o [m, H], b_o [m].  Sums are float64.  With
+    bf16_operands, every operand of a matrix product (the weights, x, h0, the
+    activation and h1) is first rounded to bfloat16, as the GPU kernel's
+    matrix-core products take them; biases, alpha, the residual sum and the
+    exponential stay exact.
+    """
+    rb = round_bf16 if bf16_operands else (lambda a: _f64(a))
+    W_in, W_1, W_2, W_o = (rb(params[k]) for k in ("W_in", "W_1", "W_2", "W_o"))
+    b_in, b_1, b_2, b_o = (_f64(params[k]) for k in ("b_in", "b_1", "b_2", "b_o"))
+    alpha = float(params["alpha"])
+    x = rb(x)
+    h0 = rb(x @ W_in.T + b_in)
+    a = rb(np.maximum(h0 @ W_1.T + b_1, 0.0))
+    h1 = rb(h0 + alpha * (a @ W_2.T + b_2))
+    return np.exp(h1 @ W_o.T + b_o)
+
+
+def phi_mlp_param_count(d_h: int, width: int = 512, d_phi: int = 64) -> int:
+    """Parameters of one map under the architecture reading of phi_mlp: the
+    input, the two block and the output layers with their biases, and alpha."""
+    return (d_h * width + width) + 2 * (width * width + width) + 1 + (width * d_phi + d_phi)
+
+
 def summaries(phi_mid, v_mid):
     """Fixed-size summary states over the mid-region (page §1 and §4.1; Eq. 6):
     S = sum_i phi_k(k_i) v_i^T  (m x d_v),   u = sum_i phi_k(k_i)  (m)."""

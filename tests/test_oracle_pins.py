@@ -358,3 +358,104 @@ def test_log_partitions_shift_with_the_scores():
     shifted = O.log_partitions(q, K + alpha * math.sqrt(8) * q / (q @ q), L, ns, nt, n_gen, idx)
     for a, b_ in zip(base, shifted):
         assert b_ == pytest.approx(a + alpha, abs=1e-12)
+
+
+# ------------------------------------------------------------------ f4: MLP feature map
+def _mlp_params(rng, d, H, m, alpha=0.5):
+    return dict(W_in=rng.standard_normal((H, d)) / math.sqrt(d), b_in=0.1 * rng.standard_normal(H),
+                W_1=rng.standard_normal((H, H)) / math.sqrt(H), b_1=0.1 * rng.standard_normal(H),
+                W_2=rng.standard_normal((H, H)) / math.sqrt(H), b_2=0.1 * rng.standard_normal(H),
+                alpha=alpha, W_o=0.3 * rng.standard_normal((m, H)) / math.sqrt(H),
+                b_o=0.1 * rng.standard_normal(m))
+
+
+def test_phi_mlp_architecture_matches_the_pages_parameter_totals():
+    """§8 ("Scope and runtime"): at d_phi = 64 the phi modules hold 378.5M
+    parameters for the 1B backbone (16 layers, 32 query / 8 kv heads, d_h = 64)
+    and 559.3M for the 3B backbone (28 layers, 24 / 8 heads, d_h = 128).  One
+    phi_q per query head and one phi_k per kv head, each of the reading in
+    phi_mlp (width 512, biases on all four layers, one ReZero scalar), give
+    both totals; the nearby alternatives do not."""
+    def total(count, layers, hq, hkv):
+        return count * layers * (hq + hkv)
+    one_b = total(O.phi_mlp_param_count(64), 16, 32, 8)
+    three_b = total(O.phi_mlp_param_count(128), 28, 24, 8)
+    assert round(one_b / 1e6, 1) == 378.5 and round(three_b / 1e6, 1) == 559.3
+    # without biases, with a LayerNorm (2 x 512 more per map), or at width 256 / 1024: off
+    no_bias = lambda d: d * 512 + 2 * 512 * 512 + 512 * 64
+    assert round(total(no_bias(64), 16, 32, 8) / 1e6, 1) != 378.5
+    assert round(total(O.phi_mlp_param_count(64) + 1024, 16, 32, 8) / 1e6, 1) != 378.5
+    for w in (256, 1024):
+        assert round(total(O.phi_mlp_param_count(64, width=w), 16, 32, 8) / 1e6, 1) != 378.5
+
+
+def test_phi_mlp_without_the_block_is_one_affine_map():
+    """alpha = 0: the ReZero block adds nothing, so phi(x) = exp(W_o W_in x +
+    W_o b_in + b_o), one composed affine map (checked through torch float64)."""
+    rng = _rng(41)
+    p = _mlp_params(rng, 8, 16, 5, alpha=0.0)
+    x = rng.standard_normal((7, 8))
+    A = torch.from_numpy(p["W_o"]) @ torch.from_numpy(p["W_in"])
+    c = torch.from_numpy(p["W_o"]) @ torch.from_numpy(p["b_in"]) + torch.from_numpy(p["b_o"])
+    ref = torch.exp(torch.from_numpy(x) @ A.T + c).numpy()
+    assert np.allclose(O.phi_mlp(x, p), ref, rtol=1e-13, atol=0)
+
+
+def test_phi_mlp_dead_activation_leaves_the_block_bias():
+    """All first-layer pre-activations negative: relu gives 0, so the block adds
+    alpha * b_2 exactly: phi(x) = exp(W_o (W_in x + b_in + alpha b_2) + b_o)."""
+    rng = _rng(42)
+    p = _mlp_params(rng, 6, 12, 4, alpha=0.75)
+    p["b_1"] = np.full(12, -1e6)
+    x = rng.standard_normal((5, 6))
+    h = torch.from_numpy(x) @ torch.from_numpy(p["W_in"]).T + torch.from_numpy(p["b_in"] + 0.75 * p["b_2"])
+    ref = torch.exp(h @ torch.from_numpy(p["W_o"]).T + torch.from_numpy(p["b_o"])).numpy()
+    assert np.allclose(O.phi_mlp(x, p), ref, rtol=1e-13, atol=0)
+
+
+def test_phi_mlp_brute_force_tiny_network():
+    """Scalar loops over a 3-wide network with 2 inputs and 2 outputs."""
+    rng = _rng(43)
+    d, H, m = 2, 3, 2
+    p = _mlp_params(rng, d, H, m, alpha=0.3)
+    x = rng.standard_normal((4, d))
+    out = O.phi_mlp(x, p)
+    for r in range(4):
+        h0 = [sum(p["W_in"][j][i] * x[r][i] for i in range(d)) + p["b_in"][j] for j in range(H)]
+        a = [max(sum(p["W_1"][j][i] * h0[i] for i in range(H)) + p["b_1"][j], 0.0) for j in range(H)]
+        h1 = [h0[j] + 0.3 * (sum(p["W_2"][j][i] * a[i] for i in range(H)) + p["b_2"][j]) for j in range(H)]
+        for k in range(m):
+            z = sum(p["W_o"][k][i] * h1[i] for i in range(H)) + p["b_o"][k]
+            assert math.isclose(out[r][k], math.exp(z), rel_tol=1e-13)
+
+
+def test_phi_mlp_features_are_positive():
+    """App. C.1 ("Why positivity matters"): exponentiated outputs are positive."""
+    rng = _rng(44)
+    p = _mlp_params(rng, 64, 512, 64)
+    x = 3.0 * rng.standard_normal((50, 64))
+    assert (O.phi_mlp(x, p) > 0).all() and (O.phi_mlp(x, p, bf16_operands=True) > 0).all()
+
+
+def test_round_bf16_ties_to_even_and_exact_values():
+    vals = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20,
+                     -(1.0 + 2.0 ** -8), 2.0 - 2.0 ** -9, 0.0, -3.5, 2.0 ** -130])
+    want = np.array([1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -1.0, 2.0, 0.0, -3.5, 2.0 ** -130])
+    assert np.array_equal(O.round_bf16(vals), want)
+
+
+def test_phi_mlp_rounding_mirror_is_exact_on_representable_values():
+    """With weights, inputs, biases and every intermediate value exactly
+    representable in bfloat16, rounding the operands changes nothing."""
+    rng = _rng(45)
+    d, H, m = 4, 8, 3
+    p = dict(W_in=rng.integers(-1, 2, (H, d)).astype(float), b_in=rng.integers(-2, 3, H).astype(float),
+             W_1=rng.integers(-1, 2, (H, H)).astype(float), b_1=rng.integers(-2, 3, H).astype(float),
+             W_2=rng.integers(-1, 2, (H, H)).astype(float), b_2=rng.integers(-2, 3, H).astype(float),
+             alpha=0.5, W_o=0.125 * rng.integers(-1, 2, (m, H)).astype(float), b_o=np.zeros(m))
+    x = rng.integers(-3, 4, (6, d)).astype(float)
+    assert np.array_equal(O.phi_mlp(x, p, bf16_operands=True), O.phi_mlp(x, p))
+    # and a value that is not representable is rounded (the mirror is active)
+    p["W_in"][0, 0] = 1.0 + 2.0 ** -12
+    x[:, 0] = 1.0
+    assert not np.array_equal(O.phi_mlp(x, p, bf16_operands=True), O.phi_mlp(x, p))
