@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 6
+#define RMA_ABI_VERSION 7
 
 /* Leading bytes of every workspace that hold completion counters. */
 #define RMA_WORKSPACE_COUNTER_BYTES 262144
@@ -109,6 +109,48 @@ typedef struct {
 #define RMA_MERGE_SUB 0u           /* Top-K+phi: subtract retrieved tokens (default) */
 #define RMA_MERGE_NO_RESIDUAL 1u   /* selection-only Top-K: drop the residual */
 #define RMA_MERGE_NO_SUBTRACT 2u   /* NoSub: add the whole-mid estimate, no subtraction */
+
+/* Weights of n_param_sets MLP feature maps (rma_phi_mlp_features), device
+ * pointers, row-major [out][in] matrices: the matrix-core operands are bf16,
+ * the biases and the ReZero scalars fp32.  Width RMA_PHI_MLP_WIDTH. */
+#define RMA_PHI_MLP_WIDTH 512
+typedef struct {
+  const uint16_t* W_in;   /* bf16 [n_param_sets][512][d] */
+  const float* b_in;      /* fp32 [n_param_sets][512] */
+  const uint16_t* W_1;    /* bf16 [n_param_sets][512][512] */
+  const float* b_1;       /* fp32 [n_param_sets][512] */
+  const uint16_t* W_2;    /* bf16 [n_param_sets][512][512] */
+  const float* b_2;       /* fp32 [n_param_sets][512] */
+  const float* alpha;     /* fp32 [n_param_sets]: the ReZero block scale */
+  const uint16_t* W_o;    /* bf16 [n_param_sets][m][512] */
+  const float* b_o;       /* fp32 [n_param_sets][m] */
+} rma_phi_mlp;
+
+/*
+ * rma_phi_mlp_features -- the pages' feature-map family (§4.4: head-specific
+ * one-block ReZero MLPs; App. C.1 "Why positivity matters": exponentiated
+ * outputs; §8 "Scope and runtime": d_phi = 64, with parameter totals that fix
+ * width 512 and biases on every layer; the block's activation is not given,
+ * ReLU here):
+ *     h0 = W_in x + b_in,   h1 = h0 + alpha (W_2 relu(W_1 h0 + b_1) + b_2),
+ *     phi[u][r][:] = exp(W_o h1 + b_o),    parameter set p = u % n_param_sets.
+ * The products run on the matrix cores with bf16 operands (x, h0, relu(.), h1
+ * are rounded to bf16, nearest even, before they enter a product) and fp32
+ * sums; biases, alpha, the residual sum and exp are fp32.
+ * x:   [n_units][rows][d] of x_dtype, unit stride x_unit_stride elements, row
+ *      stride d.  For the keys of the mid-region pass k + n_sink*d, rows =
+ *      L_mid and the cache's unit stride (one map per kv head); for decode
+ *      queries [U][G][d] pass n_units = U*G, rows = 1 (one map per query head).
+ * phi: [n_units][rows][m] of phi_dtype, dense (m = 64 or 128).
+ * Stored phi_k rows feed rma_build_summaries with Wk == NULL; phi_q rows feed
+ * rma_decode_merge as phi_q.
+ * Errors: RMA_ERR_INVALID_ARG (NULL pointers, sizes, alignment),
+ * RMA_ERR_UNSUPPORTED (d, m or dtypes).
+ */
+rma_status rma_phi_mlp_features(const void* x, int32_t x_dtype, int32_t n_units, int64_t rows,
+                                int64_t x_unit_stride, int32_t d, const rma_phi_mlp* weights,
+                                int32_t m, int32_t n_param_sets, void* phi, int32_t phi_dtype,
+                                void* stream);
 
 /*
  * rma_phi_features -- positive feature map (page App. C.1 "Why positivity

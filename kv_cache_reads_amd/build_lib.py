@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librma.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["rma_api.hip", "rma_build.hip", "rma_topk.hip", "rma_merge.hip", "rma_full.hip"]
+SOURCES = ["rma_api.hip", "rma_build.hip", "rma_topk.hip", "rma_merge.hip", "rma_full.hip",
+           "rma_phi_mlp.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 ops stay disabled: ordinary float code is compiled to unpacked VALU ops
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

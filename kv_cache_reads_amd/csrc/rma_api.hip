@@ -319,6 +319,33 @@ rma_status rma_phi_features(const void* x, int32_t x_dtype, int32_t n_units, int
   return RMA_OK;
 }
 
+rma_status rma_phi_mlp_features(const void* x, int32_t x_dtype, int32_t n_units, int64_t rows,
+                                int64_t x_unit_stride, int32_t d, const rma_phi_mlp* w, int32_t m,
+                                int32_t P, void* phi, int32_t phi_dtype, void* stream) {
+  g_last_error[0] = 0;
+  RMA_CHECK(x && w && phi, RMA_ERR_INVALID_ARG, "NULL pointer argument");
+  RMA_CHECK(w->W_in && w->b_in && w->W_1 && w->b_1 && w->W_2 && w->b_2 && w->alpha && w->W_o &&
+                w->b_o,
+            RMA_ERR_INVALID_ARG, "NULL weight pointer");
+  RMA_CHECK(dtype_ok(x_dtype) && dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported dtype");
+  RMA_CHECK(d == 64 || d == 128, RMA_ERR_UNSUPPORTED, "d %d not in {64,128}", d);
+  RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
+  RMA_CHECK(n_units >= 1 && n_units <= 65535 && rows >= 0 && P >= 1, RMA_ERR_INVALID_ARG,
+            "bad sizes");
+  RMA_CHECK(rows <= INT32_MAX / 2, RMA_ERR_INVALID_ARG, "rows too large");
+  RMA_CHECK(x_unit_stride >= rows * d && x_unit_stride % 8 == 0, RMA_ERR_INVALID_ARG,
+            "x_unit_stride must be >= rows*d and a multiple of 8");
+  RMA_CHECK(aligned16(x) && aligned16(phi) && aligned16(w->W_in) && aligned16(w->W_1) &&
+                aligned16(w->W_2) && aligned16(w->W_o),
+            RMA_ERR_INVALID_ARG, "x, phi and the weight matrices must be 16-byte aligned");
+  if (rows == 0) return RMA_OK;
+  TraceScope ts((hipStream_t)stream);
+  hipError_t e = launch_phi_mlp(x, x_dtype, n_units, rows, x_unit_stride, d, w, m, P, phi,
+                                phi_dtype, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
 rma_status rma_build_summaries(const rma_kv* kv, const rma_span* sp, const float* Wk,
                                const float* bk, int32_t m, int32_t P, void* phi_k,
                                int32_t phi_dtype, float* S, float* u, float* kappa,

@@ -63,6 +63,9 @@ struct MergePlan {
 };
 MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
 
+// ------------------------------------------------------------- MLP feature map
+constexpr int kPhiMlpWidth = RMA_PHI_MLP_WIDTH;
+
 // ------------------------------------------------------------- full attention
 constexpr int kFullThreads = 256;
 constexpr int kFullMaxChunk = 8192;   // positions per chunk (membership bits in LDS)
@@ -136,6 +139,10 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
                         const float* Wk, const float* bk, int P, int m, const float* S,
                         const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
                         hipStream_t st);
+
+hipError_t launch_phi_mlp(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride,
+                          int d, const rma_phi_mlp* w, int m, int P, void* phi, int phi_dtype,
+                          hipStream_t st);
 
 hipError_t launch_full(const FullPlan& pl, const float* q, int G, const rma_kv& kv,
                        const rma_span& sp, const int32_t* idx, int K, const float* y_cmp,

@@ -61,6 +61,10 @@ class Span:
         return _Span(self.L, self.n_sink, self.n_tail, self.n_gen)
 
 
+class _PhiMlp(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_in", "b_in", "W_1", "b_1", "W_2", "b_2", "alpha", "W_o", "b_o")]
+
+
 _lib = None
 _VP, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
 
@@ -75,6 +79,8 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P_KV, P_SP = ctypes.POINTER(_KV), ctypes.POINTER(_Span)
     L.rma_phi_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP]
+    L.rma_phi_mlp_features.argtypes = [_VP, _I32, _I32, _I64, _I64, _I32, ctypes.POINTER(_PhiMlp), _I32, _I32,
+                                       _VP, _I32, _VP]
     L.rma_build_summaries.argtypes = [P_KV, P_SP, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_build_summaries_range.argtypes = [P_KV, P_SP, _I64, _I64, _U32, _VP, _VP, _I32, _I32, _VP, _I32, _VP,
                                             _VP, _VP, _VP, _SZ, _VP]
@@ -95,7 +101,7 @@ def lib():
     L.rma_trace_count.restype = _I32
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
-    for f in ("rma_phi_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
+    for f in ("rma_phi_features", "rma_phi_mlp_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
               "rma_decode_merge", "rma_decode_full"):
         getattr(L, f).restype = _I32
     _lib = L
@@ -179,6 +185,42 @@ def rma_phi_features(x: torch.Tensor, W: torch.Tensor, b: torch.Tensor,
     assert x.stride(2) == 1 and x.stride(1) == d
     _check(lib().rma_phi_features(_p(x), _dt(x.dtype), U, rows, x.stride(0), d, _p(W), _p(b), m, P,
                                   _p(out), _dt(out.dtype), _stream()))
+    return out
+
+
+PHI_MLP_WIDTH = 512
+_MLP_MATS = ("W_in", "W_1", "W_2", "W_o")
+_MLP_VECS = ("b_in", "b_1", "b_2", "alpha", "b_o")
+
+
+class PhiMlpWeights:
+    """Device weights of n_param_sets MLP feature maps (rma_phi_mlp_features):
+    the matrices as bf16 (round to nearest even from the given values), biases
+    and the ReZero scalars as fp32.  `params` maps the names of rma_phi_mlp to
+    tensors with a leading [n_param_sets] axis."""
+
+    def __init__(self, params: dict, device="cuda"):
+        for n in _MLP_MATS:
+            setattr(self, n, params[n].to(device=device, dtype=torch.float32).to(torch.bfloat16).contiguous())
+        for n in _MLP_VECS:
+            setattr(self, n, params[n].to(device=device, dtype=torch.float32).contiguous())
+        self.alpha = self.alpha.reshape(-1)
+        self.P, self.width, self.d = self.W_in.shape
+        self.m = self.W_o.shape[1]
+        assert self.width == PHI_MLP_WIDTH and self.W_1.shape == (self.P, 512, 512)
+        self._c = _PhiMlp(*(getattr(self, n).data_ptr() for n, _ in _PhiMlp._fields_))
+
+
+def rma_phi_mlp_features(x: torch.Tensor, w: PhiMlpWeights, phi_dtype: torch.dtype = torch.float32,
+                         out: Optional[torch.Tensor] = None):
+    """phi[u, r] = exp(W_o h1 + b_o) of the MLP map u % P (see rma.h);  x: [U, rows, d]
+    with dense rows (any unit stride)."""
+    U, rows, d = x.shape
+    if out is None:
+        out = torch.empty(U, rows, w.m, dtype=phi_dtype, device=x.device)
+    assert x.stride(2) == 1 and x.stride(1) == d and d == w.d
+    _check(lib().rma_phi_mlp_features(_p(x), _dt(x.dtype), U, rows, x.stride(0), d, ctypes.byref(w._c), w.m,
+                                      w.P, _p(out), _dt(out.dtype), _stream()))
     return out
 
 

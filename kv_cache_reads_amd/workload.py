@@ -222,3 +222,31 @@ def unit_to_host(inp: Inputs, units: Sequence[int]):
             b=inp.b[p].cpu(),
         ))
     return out
+
+
+def generate_phi_mlp(cfg: Config, which: str, m: int = 64, device="cpu",
+                     seed: Optional[int] = None) -> dict:
+    """Random weights of the MLP feature maps (width 512, the pages' family; no
+    training): one map per kv head for which="k" (cfg.P sets), one per query
+    head for which="q" (cfg.P * cfg.G sets, query head (u, g) -> u % P * G + g).
+
+    Scales keep every layer near unit variance: W_in ~ N(0, 1/d), W_1 ~
+    N(0, 2/512), W_2 ~ N(0, 1/512), W_o ~ N(0, 0.25/512), biases ~ N(0, 0.01),
+    alpha ~ U(0.25, 0.75), so the exponent W_o h1 + b_o stays within a few
+    units and the features within about [0.05, 20].  Own generator (seed
+    cfg.seed + 1000 for keys, + 2000 for queries): the other draws of the
+    workload do not change.
+    """
+    n_sets = cfg.P if which == "k" else cfg.P * cfg.G
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed((cfg.seed + (1000 if which == "k" else 2000)) if seed is None else seed)
+    f32, H, d = torch.float32, 512, cfg.d
+
+    def rn(*shape, std):
+        return torch.randn(*shape, generator=g, device=dev, dtype=f32) * std
+    return dict(W_in=rn(n_sets, H, d, std=1.0 / math.sqrt(d)), b_in=rn(n_sets, H, std=0.1),
+                W_1=rn(n_sets, H, H, std=math.sqrt(2.0 / H)), b_1=rn(n_sets, H, std=0.1),
+                W_2=rn(n_sets, H, H, std=1.0 / math.sqrt(H)), b_2=rn(n_sets, H, std=0.1),
+                alpha=0.25 + 0.5 * torch.rand(n_sets, generator=g, device=dev, dtype=f32),
+                W_o=rn(n_sets, m, H, std=0.5 / math.sqrt(H)), b_o=rn(n_sets, m, std=0.1))

@@ -13,14 +13,14 @@ pytestmark = pytest.mark.skipif(not __import__("os").path.exists(R.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     names = R.header_functions()
-    assert set(names) >= {"rma_phi_features", "rma_build_summaries", "rma_decode_topk",
+    assert set(names) >= {"rma_phi_features", "rma_phi_mlp_features", "rma_build_summaries", "rma_decode_topk",
                           "rma_decode_merge", "rma_decode_full", "rma_build_summaries_range",
                           "rma_workspace_bytes", "rma_status_string",
                           "rma_last_error", "rma_abi_version"}
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 6
+    assert L.rma_abi_version() == 7
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -182,3 +182,33 @@ def test_trace_arm_validation():
     assert L.rma_trace_arm(two, 2) == R.RMA_OK
     assert L.rma_trace_arm(None, 0) == R.RMA_OK                          # disarm
     assert L.rma_trace_count() == 0 and L.rma_trace_name(0) is None
+
+
+def test_phi_mlp_validation():
+    """MLP feature map: argument checks only (no HIP call is reached)."""
+    L = R.lib()
+    ptr = 0x100000
+    w = R._PhiMlp(*([ptr] * 9))
+    wb = ctypes.byref(w)
+    ok = dict(x=ptr, xd=R.RMA_BF16, U=2, rows=100, st=100 * 64, d=64, m=64, P=1, phi=ptr, pd=R.RMA_BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.rma_phi_mlp_features(a["x"], a["xd"], a["U"], a["rows"], a["st"], a["d"],
+                                      kw.get("weights", wb), a["m"], a["P"], a["phi"], a["pd"], None)
+    assert call(x=None) == R.RMA_ERR_INVALID_ARG
+    assert call(phi=None) == R.RMA_ERR_INVALID_ARG
+    assert call(weights=None) == R.RMA_ERR_INVALID_ARG
+    bad = R._PhiMlp(*([ptr] * 8 + [0]))                        # b_o missing
+    assert call(weights=ctypes.byref(bad)) == R.RMA_ERR_INVALID_ARG
+    assert call(d=96) == R.RMA_ERR_UNSUPPORTED
+    assert call(m=32) == R.RMA_ERR_UNSUPPORTED
+    assert call(xd=7) == R.RMA_ERR_UNSUPPORTED
+    assert call(U=0) == R.RMA_ERR_INVALID_ARG
+    assert call(P=0) == R.RMA_ERR_INVALID_ARG
+    assert call(st=99 * 64) == R.RMA_ERR_INVALID_ARG           # unit stride < rows * d
+    assert call(x=ptr + 2) == R.RMA_ERR_INVALID_ARG            # misaligned
+    odd = R._PhiMlp(*([ptr] * 2 + [ptr + 4] + [ptr] * 6))      # W_1 misaligned
+    assert call(weights=ctypes.byref(odd)) == R.RMA_ERR_INVALID_ARG
+    assert call(rows=0) == R.RMA_OK                            # nothing to do
+

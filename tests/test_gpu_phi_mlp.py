@@ -1,0 +1,138 @@
+"""GPU parity of the pages' MLP feature map (one-block ReZero MLP, exponentiated
+output; page §4.4, App. C.1, §8) and of the decode path built on it.
+
+Feature rows: the kernel multiplies bf16 operands with fp32 sums; the oracle
+(oracle.phi_mlp with bf16_operands) rounds the same operands at the same
+points and sums in float64.  What remains is fp32 summation order.  Almost
+everywhere it changes a feature by ~1e-6 relative; where it moves an
+intermediate value (h0, the activation, h1) across a bf16 rounding boundary,
+that element changes by one bf16 step (2^-8 relative) and the exponent of the
+features that read it by up to |W_o| |h1| 2^-8 (~1.5e-3 at these weight
+scales; a row can take a few such steps).  The bar, per row set: every feature
+within 1e-2 relative (those steps), and the bulk exact: bf16 rows at least
+90 % bit-identical to the rounded oracle value, fp32 rows with a median
+relative error <= 2e-4.  A systematic mistake (a dropped bias or term, a wrong
+scale) moves every feature and fails the second part.
+
+Path: phi_k rows from the kernel feed the summary build (rows injected), f =
+phi_q(q) from the kernel feeds the merge.  The oracle computes its own rows and
+features; the decode output meets the usual bar (bit-exact Top-K, 2e-3 abs /
+1e-2 rel).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity_util import R, W, check_y, decode_span, log, prefill_span
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host_params(params, p):
+    return {k: v[p].double().cpu().numpy() if v.dim() > 1 else float(v[p]) for k, v in params.items()}
+
+
+def _check_rows(got, ref, bf16, what):
+    got = got.double().cpu().numpy()
+    rel = np.abs(got - ref) / ref
+    assert (ref > 0).all() and (got > 0).all(), f"{what}: non-positive feature"
+    assert rel.max() <= 1e-2, f"{what}: worst relative error {rel.max():.2e} (tol 1e-2)"
+    if bf16:
+        same = float((got == O.round_bf16(ref)).mean())
+        assert same >= 0.9, f"{what}: only {same:.3f} of the bf16 rows equal the rounded oracle"
+    else:
+        same = float(np.median(rel))
+        assert same <= 2e-4, f"{what}: median relative error {same:.2e} (tol 2e-4)"
+    return float(rel.max()), same
+
+
+# (d, m, x dtype, phi dtype, units, rows, param sets)
+SHAPES = [
+    (64, 64, torch.bfloat16, torch.bfloat16, 3, 300 + 5, 2),
+    (128, 64, torch.bfloat16, torch.bfloat16, 2, 129, 2),
+    (64, 128, torch.bfloat16, torch.float32, 2, 64, 1),
+    (64, 64, torch.float32, torch.float32, 40, 1, 8),       # decode queries: one row per unit
+    (128, 64, torch.float32, torch.bfloat16, 9, 3, 9),
+    (128, 128, torch.float32, torch.float32, 5, 77, 5),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"d{s[0]}m{s[1]}{str(s[2])[-4:]}{str(s[3])[-4:]}U{s[4]}r{s[5]}")
+def test_phi_mlp_rows_match_oracle(shape):
+    d, m, xdt, pdt, U, rows, P = shape
+    cfg = W.CONFIGS["c1"].with_(d=d, h_kv=P, h_q=P, layers=1, seed=11)
+    params = W.generate_phi_mlp(cfg, "k", m=m)
+    w = R.PhiMlpWeights(params)
+    g = torch.Generator().manual_seed(5)
+    x = (1.5 * torch.randn(U, rows + 7, d, generator=g))[:, 3:3 + rows]   # unit stride > rows * d
+    xg = x.to(xdt).to(DEV)
+    xs = torch.empty(U, rows + 8, d, dtype=xdt, device=DEV)
+    xs[:, :rows] = xg
+    phi = R.rma_phi_mlp_features(xs[:, :rows], w, phi_dtype=pdt)
+    torch.cuda.synchronize()
+    # all rows of the call together (a rounding step moves a whole row, and a
+    # unit may hold one row only)
+    ref = np.stack([O.phi_mlp(xg[u].double().cpu().numpy(), _host_params(params, u % P), bf16_operands=True)
+                    for u in range(U)])
+    worst, bulk = _check_rows(phi, ref, pdt == torch.bfloat16, f"d{d} m{m} U{U} rows {rows}")
+    log(f"phi_mlp d{d} m{m}: worst rel {worst:.2e}, " +
+        (f"bf16-identical {bulk:.3f}" if pdt == torch.bfloat16 else f"median rel {bulk:.2e}"))
+
+
+def _mlp_path(cfg, K, steps):
+    torch.manual_seed(0)
+    inp = W.generate(cfg, device=DEV)
+    pk = W.generate_phi_mlp(cfg, "k", m=cfg.m, device=DEV)
+    pq = W.generate_phi_mlp(cfg, "q", m=cfg.m, device=DEV)
+    wk, wq = R.PhiMlpWeights(pk), R.PhiMlpWeights(pq)
+    sp = prefill_span(cfg)
+    kmid = inp.k[:, cfg.n_sink:cfg.n_sink + cfg.L_mid]
+    phi_k = R.rma_phi_mlp_features(kmid, wk, phi_dtype=torch.bfloat16)
+    _, S, u, kappa = R.rma_build_summaries(inp.k, inp.v, sp, None, None, phi_k=phi_k, m=cfg.m)
+    outs = []
+    for s in steps:
+        q = inp.q[s].contiguous()
+        f = R.rma_phi_mlp_features(q.view(cfg.U * cfg.G, 1, cfg.d), wq).view(cfg.U, cfg.G, cfg.m)
+        dsp = decode_span(cfg, s)
+        idx, sel = R.rma_decode_topk(q, inp.k, dsp, kappa, K)
+        y, _ = R.rma_decode_merge(q, f, inp.k, inp.v, dsp, idx, sel, K, phi_k, S, u, m=cfg.m, want_stats=True)
+        outs.append((s, idx.cpu(), y.cpu()))
+    torch.cuda.synchronize()
+    return inp, pk, pq, phi_k, outs
+
+
+PATHS = {
+    "d64": (W.CONFIGS["c1"].with_(L=4096 + 37, m=64), 41),
+    "d128": (W.CONFIGS["c2"].with_(L=3000 + 11, m=64), 60),
+    "d64_gen": (W.CONFIGS["c3"].with_(batch=1, layers=2, L=2000 + 3, K=(25,), m=64, steps=2), 25),
+}
+
+
+@pytest.mark.parametrize("name", list(PATHS))
+def test_decode_with_mlp_features_matches_oracle(name):
+    cfg, K = PATHS[name]
+    steps = list(range(cfg.steps))
+    inp, pk, pq, phi_k, outs = _mlp_path(cfg, K, steps)
+    worst = 0.0
+    units = sorted({0, cfg.U // 2, cfg.U - 1})
+    for uu in units:
+        k = inp.k[uu].float().cpu().numpy().astype(np.float64)
+        v = inp.v[uu].float().cpu().numpy().astype(np.float64)
+        mid = slice(cfg.n_sink, cfg.n_sink + cfg.L_mid)
+        hk = _host_params(pk, uu % cfg.P)
+        phi_ref = O.round_bf16(O.phi_mlp(k[mid], hk, bf16_operands=True))   # stored as bf16
+        _check_rows(phi_k[uu], phi_ref, True, f"{name} phi_k unit {uu}")
+        S, u_ = O.summaries(phi_ref, v[mid])
+        for s, idx, y in outs:
+            for g in range(cfg.G):
+                q = inp.q[s, uu, g].double().cpu().numpy()
+                hq = _host_params(pq, (uu % cfg.P) * cfg.G + g)
+                f = O.phi_mlp(q[None], hq, bf16_operands=True)[0]
+                y_ref, idx_ref, _ = O.decode_query(q, f, k, v, phi_ref, S, u_, cfg.L, cfg.n_sink, cfg.n_tail,
+                                                   cfg.n_gen(s), K)
+                assert np.array_equal(idx[uu, g].numpy().astype(np.int64), idx_ref)
+                a, _ = check_y(y[uu, g].numpy(), y_ref, f"{name} u{uu} g{g} s{s}")
+                worst = max(worst, a)
+    log(f"{name}: MLP-feature decode, worst |y - oracle| {worst:.2e}")
