@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+MLP_WIDTH = 512
 METRIC = "decode queries/s + achieved HBM GB/s (% peak), 1B-shape GQA, 32K ctx, 1% budget"
 
 
@@ -50,6 +52,9 @@ def parse():
                     help="do not store the phi_k rows at prefill; the merge recomputes the retrieved "
                          "rows from their keys (bf16 keys; saves the rows' HBM, costs MFMA/VALU work "
                          "at every decode step)")
+    ap.add_argument("--phi", choices=("elu", "mlp"), default="elu",
+                    help="feature map: elu(Wx+b)+1 (the workloads' form, default) or the pages' MLP family "
+                         "(one-block ReZero MLP, width 512, exponentiated output, d_phi = 64)")
     ap.add_argument("--copy-probe-mb", type=float, default=0.0,
                     help="first run a plain fp32 copy-like kernel (neg) of this size, for calibrating "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -92,12 +97,18 @@ def measured_traffic(kernel, workload, K):
 
 
 # ------------------------------------------------------------------ byte model
-def call_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
+def call_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True, mlp=False):
     """Algorithmic HBM bytes of each call for one batch (inputs read once,
-    outputs written once; workspace scratch excluded)."""
+    outputs written once; workspace scratch excluded).  With mlp, the MLP
+    features: phik = phi_k rows of the keys, build = summaries over those rows,
+    phi = phi_q of the queries."""
     kb = kernel_bytes(cfg, K, n_gen, store_phi, fused_phi)
-    return dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
-                topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"])
+    out = dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
+               topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"], phik=0)
+    if mlp:
+        out.update(phik=kb["phi_mlp_kernel"], build=kb["build_valu_kernel"] + kb["build_reduce_kernel"],
+                   phi=kb["phi_mlp_small_kernel"])
+    return out
 
 
 def kernel_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
@@ -129,15 +140,35 @@ def kernel_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
         # with a head's entries split over several blocks, this kernel writes y
         # from their partials (scratch); the merge call's bytes are the merge's
         "merge_combine_kernel": U * G * d * 4,
+        # MLP features (the pages' family): keys of the mid-region in, phi_k rows
+        # out, and each map's bf16 weights and fp32 biases once
+        "phi_mlp_kernel": U * Lm * (d * e + m * ep) + P * mlp_weight_bytes(d, m),
+        "phi_mlp_small_kernel": U * G * (d * 4 + m * 4) + P * G * mlp_weight_bytes(d, m),
+        # summaries over given phi_k rows: rows, V and (for kappa) K read once
+        "build_valu_kernel": U * (Lm * m * ep + 2 * Lm * d * e),
     }
+
+
+def mlp_weight_bytes(d, m):
+    H = MLP_WIDTH
+    return 2 * (H * d + 2 * H * H + m * H) + 4 * (3 * H + 1 + m)
+
+
+def kernel_flops(cfg):
+    """Matrix-core flops per launch of the MLP feature kernels (2 per multiply-add)."""
+    U, G, d, m, H = cfg.U, cfg.G, cfg.d, cfg.m, MLP_WIDTH
+    per_row = 2 * (d * H + 2 * H * H + H * m)
+    return {"phi_mlp_kernel": U * cfg.L_mid * per_row, "phi_mlp_small_kernel": U * G * per_row}
 
 
 # ------------------------------------------------------------------ runner
 class PathRunner:
     """Prepared C-ABI calls for one copy of the inputs (no per-call allocation)."""
 
-    def __init__(self, R, cfg, inp, K, ws, torch, store_phi, fused_phi=True):
+    def __init__(self, R, cfg, inp, K, ws, torch, store_phi, fused_phi=True, mlp=None):
         self.R, self.cfg, self.K, self.t = R, cfg, K, torch
+        # mlp: (phi_k weights, phi_q weights) of the MLP feature maps, or None
+        self.mlp = mlp
         L = R.lib()
         self.L = L
         dev = inp.k.device
@@ -163,11 +194,22 @@ class PathRunner:
         self.Wm, self.bm = (None, None) if store_phi else (inp.W, inp.b)
         self.yf = None
         # f = phi_q(q): computed inside the merge (fused), or by rma_phi_features
-        self.fused_phi = fused_phi
+        # (or by the MLP feature kernel)
+        self.fused_phi = fused_phi and mlp is None
+        if mlp is not None:
+            self.kmid = inp.k[:, cfg.n_sink:cfg.n_sink + cfg.L_mid]
+
+    def phik(self, st):
+        """MLP features only: phi_k rows of the keys of the mid-region."""
+        cfg, wk = self.cfg, self.mlp[0]
+        r = self.L.rma_phi_mlp_features(self.p(self.kmid), self.kdt, cfg.U, cfg.L_mid, self.kmid.stride(0), cfg.d,
+                                        ctypes.byref(wk._c), cfg.m, wk.P, self.p(self.phi_k), self.pdt, st)
+        assert r == 0, r
 
     def build(self, st):
         cfg, p = self.cfg, self.p
-        r = self.L.rma_build_summaries(ctypes.byref(self.kv), ctypes.byref(self.sp_pre), p(self.W), p(self.b),
+        W, b = (None, None) if self.mlp is not None else (self.W, self.b)   # MLP rows are given
+        r = self.L.rma_build_summaries(ctypes.byref(self.kv), ctypes.byref(self.sp_pre), p(W), p(b),
                                        cfg.m, cfg.P, p(self.phi_k), self.pdt, p(self.S), p(self.u),
                                        p(self.kappa), p(self.ws), self.ws.numel(), st)
         assert r == 0, r
@@ -175,8 +217,13 @@ class PathRunner:
     def phi(self, s, st):
         cfg, p = self.cfg, self.p
         q = self.q[s]
-        r = self.L.rma_phi_features(p(q), 0, cfg.U, cfg.G, q.stride(0), cfg.d, p(self.W), p(self.b), cfg.m,
-                                    cfg.P, p(self.f[s]), 0, st)
+        if self.mlp is not None:   # one map per query head: U*G one-row units
+            wq = self.mlp[1]
+            r = self.L.rma_phi_mlp_features(p(q), 0, cfg.U * cfg.G, 1, cfg.d, cfg.d, ctypes.byref(wq._c), cfg.m,
+                                            wq.P, p(self.f[s]), 0, st)
+        else:
+            r = self.L.rma_phi_features(p(q), 0, cfg.U, cfg.G, q.stride(0), cfg.d, p(self.W), p(self.b), cfg.m,
+                                        cfg.P, p(self.f[s]), 0, st)
         assert r == 0, r
 
     def topk(self, s, st):
@@ -206,6 +253,8 @@ class PathRunner:
 
     def step(self, st):
         """The whole path: prefill summaries, then every decode step."""
+        if self.mlp is not None:
+            self.phik(st)
         self.build(st)
         for s in range(self.cfg.steps):
             if not self.fused_phi:
@@ -228,6 +277,8 @@ class PathRunner:
             names = R.rma_trace_kernels()
             out.append((name, [(n, evs[2 * j], evs[2 * j + 1]) for j, n in enumerate(names)]))
 
+        if self.mlp is not None:
+            traced("phik", lambda: self.phik(st))
         traced("build", lambda: self.build(st))
         for s in range(self.cfg.steps):
             if not self.fused_phi:
@@ -301,8 +352,9 @@ def decode_timing(args, cfg, runners, n_copies, stream, st, use_graphs, queries,
                     "method_decode_speedup": round(full_us / dec_us, 3), "timed_steps": n}
 
 
-def cpu_baseline(cfg, inp, K, seconds):
-    """The oracle (numpy fp64) on host cores: prefill + decode of whole units."""
+def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
+    """The oracle (numpy fp64) on host cores: prefill + decode of whole units
+    (with mlp_mode, its MLP feature maps on the same seeded weights)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     import oracle as O
@@ -315,6 +367,10 @@ def cpu_baseline(cfg, inp, K, seconds):
                     q=inp.q[:, u].cpu().numpy(), W=inp.W[p].cpu().numpy(), b=inp.b[p].cpu().numpy())
 
     _, M, _ = O.partition(cfg.L, cfg.n_sink, cfg.n_tail)
+    if mlp_mode:
+        from kv_cache_reads_amd import workload as Wl
+        pk, pq = (Wl.generate_phi_mlp(cfg, which, m=cfg.m) for which in "kq")
+        hp = lambda par, i: {k: v[i].double().numpy() if v.dim() > 1 else float(v[i]) for k, v in par.items()}
     with threadpool_limits(limits=ncpu):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         nq, units, dt = 0, 0, 0.0
@@ -323,11 +379,18 @@ def cpu_baseline(cfg, inp, K, seconds):
             for uidx in range(cfg.U):
                 hu = host(uidx)                      # host copy, not timed
                 t1 = time.perf_counter()
-                P, S, uu = O.prefill_unit(hu["k"][M], hu["v"][M], hu["W"], hu["b"])
+                if mlp_mode:
+                    P = O.round_bf16(O.phi_mlp(hu["k"][M], hp(pk, uidx % cfg.P), bf16_operands=True))
+                    S, uu = O.summaries(P, hu["v"][M])
+                else:
+                    P, S, uu = O.prefill_unit(hu["k"][M], hu["v"][M], hu["W"], hu["b"])
                 for s in range(cfg.steps):
                     for g in range(cfg.G):
                         q = hu["q"][s, g]
-                        f = O.phi_features(q[None], hu["W"], hu["b"])[0]
+                        if mlp_mode:
+                            f = O.phi_mlp(q[None], hp(pq, uidx % cfg.P * cfg.G + g), bf16_operands=True)[0]
+                        else:
+                            f = O.phi_features(q[None], hu["W"], hu["b"])[0]
                         O.decode_query(q, f, hu["k"], hu["v"], P, S, uu, cfg.L, cfg.n_sink, cfg.n_tail,
                                        cfg.n_gen(s), K)
                         nq += 1
@@ -354,6 +417,9 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = Wl.CONFIGS[args.config]
+    mlp_mode = args.phi == "mlp"
+    if mlp_mode:
+        cfg = cfg.with_(m=64)          # d_phi = 64 (the pages' setting)
     K = args.K if args.K is not None else cfg.K[0]
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     log(f"[bench] workload {cfg.name}: {cfg.desc}; K={K}")
@@ -388,8 +454,12 @@ def main():
     if not args.no_full:
         wsb = max(wsb, R.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, inp.k, sp, cfg.G, 0, cfg.m))
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    fused_phi = not args.separate_phi
-    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi, fused_phi) for c in copies]
+    fused_phi = not args.separate_phi and not mlp_mode
+    mlp = None
+    if mlp_mode:
+        store_phi = True
+        mlp = tuple(R.PhiMlpWeights(Wl.generate_phi_mlp(cfg, which, m=cfg.m, device="cuda")) for which in "kq")
+    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi, fused_phi, mlp) for c in copies]
     log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
 
     stream = torch.cuda.Stream()
@@ -459,6 +529,8 @@ def main():
             recs.append(runners[i % n_copies].traced_step(st, R))
     torch.cuda.synchronize()
     names = ["build", "topk", "merge"] if fused_phi else ["build", "phi", "topk", "merge"]
+    if mlp_mode:
+        names = ["phik"] + names
     call_ms = {n: 0.0 for n in names}
     kern_ms, kern_n = {}, {}
     for rec in recs:
@@ -470,23 +542,37 @@ def main():
     dur = {n: call_ms[n] / n_t for n in names}                       # ms per step
     kavg = {k: kern_ms[k] / kern_n[k] for k in kern_ms}               # ms per launch
     launches = {k: kern_n[k] / n_t for k in kern_n}                  # launches per step
-    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi)
+    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi, mlp_mode)
     kb = kernel_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi)
-    step_bytes = nb["build"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi, fused_phi)[c]
+    step_bytes = nb["build"] + nb["phik"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi, fused_phi, mlp_mode)[c]
                                    for s in range(cfg.steps) for c in ("phi", "topk", "merge"))
-    gbs = {n: nb[n] * (1 if n == "build" else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
+    prefill_calls = ("build", "phik")
+    gbs = {n: nb[n] * (1 if n in prefill_calls else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
     kgbs = {k: kb[k] / (kavg[k] / 1e3) / 1e9 for k in kavg}
+    kfl = kernel_flops(cfg)
+    ktf = {k: kfl[k] / (kavg[k] / 1e3) / 1e12 for k in kavg if k in kfl}      # TFLOP/s
     for n in names:
         log(f"[bench] {n:6s} {dur[n] * 1e3:9.2f} us/step  {gbs[n]:8.1f} GB/s")
     for k in kavg:
         log(f"[bench]   {k:22s} {kavg[k] * 1e3:9.2f} us/launch x{launches[k]:.0f}  "
-            f"{kb[k] / 1e6:8.2f} MB  {kgbs[k]:8.1f} GB/s")
+            f"{kb[k] / 1e6:8.2f} MB  {kgbs[k]:8.1f} GB/s" + (f"  {ktf[k]:8.1f} TFLOP/s" if k in ktf else ""))
     log(f"[bench] step {ms_per_step * 1e3:.2f} us, {step_bytes / 1e6:.1f} MB algorithmic "
         f"-> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; {value / 1e6:.3f} M queries/s")
-    decode_us = sum(dur[n] for n in names if n != "build") * 1e3
+    decode_us = sum(dur[n] for n in names if n not in prefill_calls) * 1e3
     dom = max(kavg, key=lambda k: kavg[k] * launches[k])     # most time per step
     achieved = kgbs[dom]
     traffic = measured_traffic(dom, cfg.name, K)
+    if dom in ktf:   # a matrix-core contraction: its own bf16 peak
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ktf[dom], 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ktf[dom] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": kfl[dom], "algorithmic_bytes_per_launch": kb[dom],
+                "avg_launch_us": round(kavg[dom] * 1e3, 3),
+                "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md"}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(kavg[dom] * 1e3, 3),
+                "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md"}
 
     out = {
         "metric": METRIC,
@@ -506,8 +592,12 @@ def main():
             "units": cfg.U, "query_heads_per_unit": cfg.G, "head_dim": cfg.d, "context": cfg.L,
             "anchors": [cfg.n_sink, cfg.n_tail], "K": K, "phi_features": cfg.m,
             "decode_steps": cfg.steps, "queries_per_step": queries,
-            "step": ("prefill summaries + top-K + merge (phi_q computed inside the merge)" if fused_phi
+            "step": ("prefill MLP phi_k + summaries over those rows + MLP phi_q + top-K + merge" if mlp_mode
+                     else "prefill summaries + top-K + merge (phi_q computed inside the merge)" if fused_phi
                      else "prefill summaries + phi_q + top-K + merge"),
+            "phi": ("MLP family: one-block ReZero MLP, width 512, exponentiated output, d_phi 64, random "
+                    "weights, bf16 matrix-core operands" if mlp_mode else "elu(Wx+b)+1"),
+            **({"per_kernel_TFLOPs": {k: round(v, 1) for k, v in ktf.items()}} if ktf else {}),
             "phi_k_rows": "stored" if store_phi else "recomputed at decode (not stored)",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
             "rotating_copies": n_copies, "launch": "hip_graph" if graphs is not None else "eager",
@@ -519,24 +609,18 @@ def main():
             "per_kernel_GBps": {k: round(kgbs[k], 1) for k in kavg},
             "decode_only_queries_per_s": round(queries / (decode_us / 1e6), 1),
         },
-        "roofline": {
-            "bound": "hbm", "kernel": dom,
-            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(kavg[dom] * 1e3, 3),
-            "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md",
-        },
+        "roofline": roof,
     }
     if not args.no_full:
         dec_us, out["config"]["full_exact_decode"] = decode_timing(args, cfg, runners, n_copies, stream, st,
                                                                    graphs is not None, queries, log)
         out["config"]["decode_only_us_per_step"] = round(dec_us, 2)
         out["config"]["decode_only_queries_per_s"] = round(queries / (dec_us / 1e6), 1)
-        dbytes = step_bytes - nb["build"]
+        dbytes = step_bytes - nb["build"] - nb["phik"]
         out["config"]["decode_only_GBps"] = round(dbytes / (dec_us / 1e6) / 1e9, 1)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, K, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, K, args.cpu_seconds, mlp_mode)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -195,10 +195,11 @@ hipError_t launch_phi_mlp(const void* x, int x_dtype, int n_units, int64_t rows,
   const int rt = small ? 16 : 64;
   const dim3 grid((unsigned)ceil_div(rows, rt), (unsigned)n_units);
   hipError_t e = hipSuccess;
-#define RMA_MLP1(XT, PT, DD, MM, RR)                                                               \
-  e = launch_kernel("phi_mlp_kernel", phi_mlp_kernel<XT, PT, DD, MM, RR>, grid, dim3(kMlpThreads), \
-                    0, st, static_cast<const XT*>(x), xstride, (int)rows, w->W_in, w->b_in, w->W_1, \
-                    w->b_1, w->W_2, w->b_2, w->alpha, w->W_o, w->b_o, P, static_cast<PT*>(phi))
+#define RMA_MLP1(XT, PT, DD, MM, RR)                                                                 \
+  e = launch_kernel(RR == 16 ? "phi_mlp_small_kernel" : "phi_mlp_kernel",                            \
+                    phi_mlp_kernel<XT, PT, DD, MM, RR>, grid, dim3(kMlpThreads), 0, st,              \
+                    static_cast<const XT*>(x), xstride, (int)rows, w->W_in, w->b_in, w->W_1, w->b_1, \
+                    w->W_2, w->b_2, w->alpha, w->W_o, w->b_o, P, static_cast<PT*>(phi))
 #define RMA_MLP(XT, PT)                                                     \
   do {                                                                      \
     if (d == 64 && m == 64) {                                               \
