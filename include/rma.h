@@ -111,18 +111,22 @@ typedef struct {
 #define RMA_MERGE_NO_SUBTRACT 2u   /* NoSub: add the whole-mid estimate, no subtraction */
 
 /* Weights of n_param_sets MLP feature maps (rma_phi_mlp_features), device
- * pointers, row-major [out][in] matrices: the matrix-core operands are bf16,
- * the biases and the ReZero scalars fp32.  Width RMA_PHI_MLP_WIDTH. */
+ * pointers.  The matrices are bf16 in the matrix-core tile order: a matrix W
+ * with N outputs and K inputs (element W[n][k]) is stored per parameter set as
+ * [K/32][N/16][64][8], element (n, k) at
+ *   ((k/32 * N/16 + n/16) * 64 + (n%16 + 16 * (k%32)/8)) * 8 + k%8,
+ * so that the weight pieces one wave multiplies together are one contiguous
+ * kilobyte.  Biases and the ReZero scalars are fp32.  Width RMA_PHI_MLP_WIDTH. */
 #define RMA_PHI_MLP_WIDTH 512
 typedef struct {
-  const uint16_t* W_in;   /* bf16 [n_param_sets][512][d] */
+  const uint16_t* W_in;   /* bf16, N = 512, K = d, tile order */
   const float* b_in;      /* fp32 [n_param_sets][512] */
-  const uint16_t* W_1;    /* bf16 [n_param_sets][512][512] */
+  const uint16_t* W_1;    /* bf16, N = K = 512, tile order */
   const float* b_1;       /* fp32 [n_param_sets][512] */
-  const uint16_t* W_2;    /* bf16 [n_param_sets][512][512] */
+  const uint16_t* W_2;    /* bf16, N = K = 512, tile order */
   const float* b_2;       /* fp32 [n_param_sets][512] */
   const float* alpha;     /* fp32 [n_param_sets]: the ReZero block scale */
-  const uint16_t* W_o;    /* bf16 [n_param_sets][m][512] */
+  const uint16_t* W_o;    /* bf16, N = m, K = 512, tile order */
   const float* b_o;       /* fp32 [n_param_sets][m] */
 } rma_phi_mlp;
 

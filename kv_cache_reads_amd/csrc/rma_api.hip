@@ -101,7 +101,9 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
   BuildPlan p{};
   const int64_t Lm = tokens;
   const int64_t U = kv.n_units;
-  p.mfma = computed_phi && kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
+  // bf16 K/V and bf16 rows (computed, or given): the matrix-core builder
+  (void)computed_phi;
+  p.mfma = kv.dtype == RMA_BF16 && phi_dtype == RMA_BF16;
   const int tile = p.mfma ? 64 : 32;
   if (Lm > 0) {
     // enough blocks to cover the chip with as few per-chunk partials as possible

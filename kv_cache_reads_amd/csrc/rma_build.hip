@@ -34,7 +34,9 @@ namespace rma {
 __device__ __forceinline__ float norm_upper(float sumsq) { return sqrtf(sumsq) * (1.0f + 1e-5f); }
 
 // ====================================================================== MFMA builder
-template <int D, int M, bool STORE>
+// INJ: the Phi rows are given (read from phik) instead of computed; step 1 is
+// skipped and the rows' tile is staged in LDS beside K and V.
+template <int D, int M, bool STORE, bool INJ>
 __global__ void __launch_bounds__(M * 4)
 build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb, int64_t ustride,
                   int n_sink, int L_mid, int ch, int n_chunks, int m0, int len, int acc,
@@ -52,15 +54,18 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   constexpr int VROW = D + 16;            // Vs row stride (bf16): rows 32 dwords + 8 (mod 64) apart,
                                           // so the 8 rows one transposing read touches per
                                           // half-wave cover the 64 banks once
-  constexpr int PROW = M + 4;             // Phi staging row stride: 8 B pad -> the 4 lane groups
+  constexpr int PROW = INJ ? M + 16        // given rows: read back transposed, as Vs
+                          : M + 4;        // Phi staging row stride: 8 B pad -> the 4 lane groups
                                           // of a step-1 tile land 8 banks apart
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   constexpr int LCH = TT * CPR / NT;      // 16-byte chunks per thread per tile (K or V)
+  constexpr int PCH = INJ ? TT * (M / 8) / NT : 1;   // 16-byte chunks per thread of a given Phi tile
   static_assert(LCH >= 1 && TT * CPR % NT == 0, "tile shape");
+  static_assert(!(INJ && STORE), "given rows are not stored");
 
   __shared__ __align__(16) uint16_t Ks[TT * KROW];
   __shared__ __align__(16) uint16_t Vs[TT * VROW];
-  __shared__ __align__(16) uint16_t Ps[STORE ? TT * PROW : 8];
+  __shared__ __align__(16) uint16_t Ps[(STORE || INJ) ? TT * PROW : 8];
   __shared__ float s_kap[NW];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -71,10 +76,10 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const int n = min(ch, m0 + len - t0);
   const uint16_t* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
   const uint16_t* vp = vb + (size_t)u * ustride + (size_t)(n_sink + t0) * D;
-  uint16_t* php = STORE ? phik + ((size_t)u * L_mid + t0) * M : nullptr;
+  uint16_t* php = (STORE || INJ) ? phik + ((size_t)u * L_mid + t0) * M : nullptr;
   // range-checked views of this chunk: rows past n load as zeros, Phi stores past n drop
   const auto rk = make_rsrc(kp, (uint32_t)n * D * 2), rv = make_rsrc(vp, (uint32_t)n * D * 2);
-  const auto rph = make_rsrc(php, STORE ? (uint32_t)n * M * 2 : 0u);
+  const auto rph = make_rsrc(php, (STORE || INJ) ? (uint32_t)n * M * 2 : 0u);
   const int f = wave * 16 + l16;          // this lane's feature in step 1
 
   // this lane's W row piece and bias, issued ahead of the first tiles (buffer
@@ -82,15 +87,18 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   const auto rw = make_rsrc(W + (size_t)p * M * D, M * D * 4);
   const auto rb = make_rsrc(bias + (size_t)p * M, M * 4);
   float wv[KS][8];
+  float bf = 0.f;
+  if constexpr (!INJ) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t wo = (f * D + 32 * ks + 8 * g4) * 4;
-    const uint4 a = buf_ld16(rw, wo), b = buf_ld16(rw, wo + 16);
-    const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t wo = (f * D + 32 * ks + 8 * g4) * 4;
+      const uint4 a = buf_ld16(rw, wo), b = buf_ld16(rw, wo + 16);
+      const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wv[ks][e] = __uint_as_float(x[e]);
+      for (int e = 0; e < 8; ++e) wv[ks][e] = __uint_as_float(x[e]);
+    }
+    bf = buf_ld_f32(rb, f * 4);
   }
-  const float bf = buf_ld_f32(rb, f * 4);
   bf16x8_t Whi[KS], Wlo[KS];             // W (fp32) as bf16 hi + lo B-operands
   u16x8_t ones_v;
 #pragma unroll
@@ -102,7 +110,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   for (int ct = 0; ct < CT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float kapmax = 0.f;
 
-  auto load_tile = [&](uint4 (&kr)[LCH], uint4 (&vr)[LCH], int tok0) {
+  auto load_tile = [&](uint4 (&kr)[LCH], uint4 (&vr)[LCH], uint4 (&pr)[PCH], int tok0) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + NT * j;
@@ -111,15 +119,31 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       kr[j] = buf_ld16_nt(rk, off);
       vr[j] = buf_ld16_nt(rv, off);
     }
+    if constexpr (INJ) {
+#pragma unroll
+      for (int j = 0; j < PCH; ++j) {
+        const int chunk = tid + NT * j;
+        const int row = chunk / (M / 8), cc = chunk % (M / 8);
+        pr[j] = buf_ld16_nt(rph, (uint32_t)((tok0 + row) * M + cc * 8) * 2);
+      }
+    }
   };
-  // K and V rows as they are (16-byte writes)
-  auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH]) {
+  // K and V rows (and given Phi rows) as they are (16-byte writes)
+  auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH], const uint4 (&pr)[PCH]) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
       *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kr[j];
       *reinterpret_cast<uint4*>(Vs + row * VROW + cc * 8) = vr[j];
+    }
+    if constexpr (INJ) {
+#pragma unroll
+      for (int j = 0; j < PCH; ++j) {
+        const int chunk = tid + NT * j;
+        const int row = chunk / (M / 8), cc = chunk % (M / 8);
+        *reinterpret_cast<uint4*>(Ps + row * PROW + cc * 8) = pr[j];
+      }
     }
   };
   // Step-2 B operand of one 16-column tile: eight tokens of one V column per lane,
@@ -129,12 +153,13 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   // 4-token block and at columns 4*(l'%4) .. +3 of the tile, and lane j gets the
   // four tokens of column j.
   const int tr_row = 4 * g4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
-  auto ld_tr = [&](int row, int col) {
+  auto ld_tr_in = [&](const uint16_t* tile, int stride, int row, int col) {
     typedef short v4s __attribute__((ext_vector_type(4)));
     const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s*)(Vs + row * VROW + col));
+        (__attribute__((address_space(3))) v4s*)(tile + row * stride + col));
     return __builtin_bit_cast(uint2, r);
   };
+  auto ld_tr = [&](int row, int col) { return ld_tr_in(Vs, VROW, row, col); };
   auto compute_tile = [&](int tok0, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     // kappa: the largest squared key norm (NT/TT threads per token row, bf16 pair
@@ -157,9 +182,19 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       if (FULL || tok0 + row < n) kapmax = fmaxf(kapmax, ss);
     }
     // step 1: Z = K W^T for this wave's features, epilogue phi, bf16 pairs kept
+    // (given rows: the four tokens of this lane's feature, read transposed;
+    // rows past the chunk were loaded as zeros)
     uint32_t phv[NTT][2];
+    if constexpr (INJ) {
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
+      for (int tt = 0; tt < NTT; ++tt) {
+        const uint2 r = ld_tr_in(Ps, PROW, tt * 16 + tr_row, wave * 16 + tr_col);
+        phv[tt][0] = r.x;
+        phv[tt][1] = r.y;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < (INJ ? 0 : NTT); ++tt) {
       const f32x4 acc = proj_tile16<KS>(Ks + (tt * 16 + l16) * KROW + 8 * g4, Whi, Wlo);
       float ph[4];
 #pragma unroll
@@ -217,23 +252,23 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   // odd tile count is computed as padding), and the first two tiles are complete
   // before the loop, so the wait before each staging step covers only the loads
   // of the tile being staged, not the stores and loads issued after them.
-  uint4 kA[LCH], vA[LCH], kB[LCH], vB[LCH];
-  load_tile(kA, vA, 0);
-  load_tile(kB, vB, TT);
+  uint4 kA[LCH], vA[LCH], kB[LCH], vB[LCH], pA[PCH], pB[PCH];
+  load_tile(kA, vA, pA, 0);
+  load_tile(kB, vB, pB, TT);
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing in flight on entry
-  split_w_values<KS>(wv, Whi, Wlo);
+  if constexpr (!INJ) split_w_values<KS>(wv, Whi, Wlo);
   for (int tok0 = 0; tok0 < n; tok0 += 2 * TT) {
     __syncthreads();
-    stage_tile(kA, vA);
+    stage_tile(kA, vA, pA);
     __syncthreads();
-    load_tile(kA, vA, tok0 + 2 * TT);
+    load_tile(kA, vA, pA, tok0 + 2 * TT);
     if (tok0 + TT <= n) compute_tile(tok0, std::true_type{});
     else compute_tile(tok0, std::false_type{});
     __syncthreads();
-    stage_tile(kB, vB);
+    stage_tile(kB, vB, pB);
     __syncthreads();
-    load_tile(kB, vB, tok0 + 3 * TT);
+    load_tile(kB, vB, pB, tok0 + 3 * TT);
     if (tok0 + 2 * TT <= n) compute_tile(tok0 + TT, std::true_type{});
     else compute_tile(tok0 + TT, std::false_type{});
   }
@@ -491,22 +526,22 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
       const uint16_t* kk = static_cast<const uint16_t*>(kv.k);
       const uint16_t* vv = static_cast<const uint16_t*>(kv.v);
       uint16_t* ph = static_cast<uint16_t*>(phi_k);
+#define RMA_BM1(DD, MM, STO, INJ)                                                                    \
+  e = launch_kernel("build_mfma_kernel", build_mfma_kernel<DD, MM, STO, INJ>, grid, dim3(MM * 4), 0, st, \
+                    kk, vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len, acc_direct, \
+                    W, b, P, ph, pS, pu, pk)
 #define RMA_BM(DD, MM)                                                                               \
   do {                                                                                               \
-    if (ph != nullptr)                                                                               \
-      e = launch_kernel("build_mfma_kernel", build_mfma_kernel<DD, MM, true>, grid, dim3(MM * 4), 0, \
-                        st, kk, vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len,   \
-                        acc_direct, W, b, P, ph, pS, pu, pk);                                        \
-    else                                                                                             \
-      e = launch_kernel("build_mfma_kernel", build_mfma_kernel<DD, MM, false>, grid, dim3(MM * 4), 0, \
-                        st, kk, vv, kv.unit_stride, sp.n_sink, L_mid, pl.ch, pl.n_chunks, m0, len,   \
-                        acc_direct, W, b, P, ph, pS, pu, pk);                                        \
+    if (W == nullptr) RMA_BM1(DD, MM, false, true);   /* given rows */                               \
+    else if (ph != nullptr) RMA_BM1(DD, MM, true, false);                                            \
+    else RMA_BM1(DD, MM, false, false);                                                              \
   } while (0)
       if (kv.d == 64 && m == 64) RMA_BM(64, 64);
       else if (kv.d == 64) RMA_BM(64, 128);
       else if (m == 64) RMA_BM(128, 64);
       else RMA_BM(128, 128);
 #undef RMA_BM
+#undef RMA_BM1
     } else {
 #define RMA_BV1(KT, PT, DD, MM)                                                                      \
   e = launch_kernel("build_valu_kernel", build_valu_kernel<KT, PT, DD, MM>, grid, dim3(256), 0, st,  \

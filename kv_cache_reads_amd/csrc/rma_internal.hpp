@@ -25,7 +25,7 @@ inline size_t counter_bytes(int64_t /*n_units*/) { return kCounterBytes; }
 
 // ------------------------------------------------------------- build
 struct BuildPlan {
-  bool mfma;         // bf16 K/V, bf16 phi, computed phi -> MFMA builder
+  bool mfma;         // bf16 K/V and bf16 phi rows (computed or given) -> MFMA builder
   int n_chunks;      // token chunks per unit
   int ch;            // tokens per chunk (multiple of the tile)
   size_t off_S, off_u, off_kap, total;

@@ -11,7 +11,8 @@
 // unit on the matrix cores (v_mfma_f32_16x16x32_bf16: bf16 operands, fp32
 // sums).  The activations stay in LDS as bf16 (the operands of the next
 // product); each wave owns a quarter of every layer's output columns and
-// streams its weight rows from L2 as the B operand, one 32-wide k-step ahead.
+// streams its weight rows from L2 as the B operand, several 32-wide k-steps ahead
+// (the next layer's first pieces are issued before this layer's epilogue).
 #include "rma_device.hpp"
 #include "rma_internal.hpp"
 
@@ -26,40 +27,62 @@ constexpr int kMlpThreads = kMlpWaves * 64;
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// acc[rt][ct] += A[rt*16 .., k] * W[col0 + ct*16 .., k]^T over k in [0, 32*KS):
-// A from LDS (row stride AROW bf16), W row-major [n][ldw] bf16 in global memory.
-// The lane's A piece: row l16 of the row tile, k = 32*ks + 8*g4 .. +8; its B
-// piece: weight row col0 + ct*16 + l16, the same k.
-template <int RTT, int NCT, int KS, int AROW>
-__device__ __forceinline__ void mfma_layer(const uint16_t* As, const uint16_t* W, int ldw, int col0,
+// The weight pieces of one layer in flight: a ring of DEPTH k-steps of B
+// pieces.  W (N x 32*KS) is in the matrix-core tile order [k-step][column tile
+// of 16][lane][8], so that one wave's pieces of a (k-step, column tile) are
+// one contiguous kilobyte; the lane's piece is weight row col0 + ct*16 + l16,
+// k = 32*ks + 8*g4 .. +8.
+template <int NCT, int KS, int NPF>
+struct WeightRing {
+  static constexpr int DEPTH = NPF < KS ? NPF : KS;
+  uint4 q[DEPTH][NCT];
+  const uint16_t* wl;
+  int n_tiles;
+  __device__ __forceinline__ uint4 piece(int ks, int ct) const {
+    return ldg16(wl + ((size_t)ks * n_tiles + ct) * 512);
+  }
+  // the first DEPTH - 1 k-steps: issued ahead (before the previous layer's
+  // epilogue and barrier, which do not touch the weights)
+  __device__ __forceinline__ void start(const uint16_t* W, int n_tiles_, int col0) {
+    const int lane = threadIdx.x & 63;
+    n_tiles = n_tiles_;
+    wl = W + ((size_t)(col0 / 16) * 64 + lane) * 8;
+#pragma unroll
+    for (int st = 0; st < DEPTH - 1; ++st)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) q[st][ct] = piece(st, ct);
+  }
+};
+
+// acc[rt][ct] = A[rt*16 .., k] * W[col0 + ct*16 .., k]^T over k in [0, 32*KS),
+// A from LDS (row stride AROW bf16), the weights through a started ring.  The
+// lane's A piece: row l16 of the row tile, k = 32*ks + 8*g4 .. +8.
+template <int RTT, int NCT, int KS, int AROW, int NPF>
+__device__ __forceinline__ void mfma_layer(const uint16_t* As, WeightRing<NCT, KS, NPF>& ring,
                                            f32x4 (&acc)[RTT][NCT]) {
+  constexpr int DEPTH = WeightRing<NCT, KS, NPF>::DEPTH;
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RTT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wl = W + (size_t)(col0 + l16) * ldw + 8 * g4;
-  uint4 bc[NCT], bn[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) bc[ct] = ldg16(wl + (size_t)ct * 16 * ldw);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (ks + 1 < KS) {
+    if (ks + DEPTH - 1 < KS) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) bn[ct] = ldg16(wl + (size_t)ct * 16 * ldw + 32 * (ks + 1));
+      for (int ct = 0; ct < NCT; ++ct) ring.q[(ks + DEPTH - 1) % DEPTH][ct] = ring.piece(ks + DEPTH - 1, ct);
     }
+    // keep the prefetch ahead of this step's products (the scheduler would
+    // otherwise sink the loads next to their use to save registers)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rt = 0; rt < RTT; ++rt) {
       const bf16x8_t a = as_bf16x8(
           *reinterpret_cast<const u16x8_t*>(As + (rt * 16 + l16) * AROW + 32 * ks + 8 * g4));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bc[ct]),
-                                                              acc[rt][ct], 0, 0, 0);
-    }
-    if (ks + 1 < KS) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) bc[ct] = bn[ct];
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8_t, ring.q[ks % DEPTH][ct]), acc[rt][ct], 0, 0, 0);
     }
   }
 }
@@ -82,6 +105,7 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
   constexpr int RTT = RT / 16;             // 16-row MFMA tiles
   constexpr int CTW = H / kMlpWaves / 16;  // hidden column tiles per wave (8)
   constexpr int OTW = M / kMlpWaves / 16;  // output column tiles per wave (1 or 2)
+  constexpr int NPF = RT == 16 ? 6 : 3;     // weight k-steps in flight (registers allow)
   static_assert(RT % 16 == 0 && M % (16 * kMlpWaves) == 0, "tile shape");
 
   __shared__ __align__(16) uint16_t Xs[RT * XROW];
@@ -115,6 +139,8 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
     }
   }
   const int hc0 = wave * (H / kMlpWaves);   // this wave's hidden columns
+  WeightRing<CTW, D / 32, NPF> r_in;
+  r_in.start(Win + (size_t)p * H * D, H / 16, hc0);
   float bias[CTW];
 #pragma unroll
   for (int ct = 0; ct < CTW; ++ct) bias[ct] = bin[(size_t)p * H + hc0 + ct * 16 + l16];
@@ -122,7 +148,9 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
 
   f32x4 acc[RTT][CTW];
   // ---- h0 = W_in x + b_in
-  mfma_layer<RTT, CTW, D / 32, XROW>(Xs, Win + (size_t)p * H * D, D, hc0, acc);
+  mfma_layer<RTT, CTW, D / 32, XROW, NPF>(Xs, r_in, acc);
+  WeightRing<CTW, H / 32, NPF> r_1;
+  r_1.start(W1 + (size_t)p * H * H, H / 16, hc0);
 #pragma unroll
   for (int rt = 0; rt < RTT; ++rt)
 #pragma unroll
@@ -135,7 +163,9 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
   __syncthreads();
 
   // ---- a = relu(W_1 h0 + b_1)
-  mfma_layer<RTT, CTW, H / 32, HROW>(Hs, W1 + (size_t)p * H * H, H, hc0, acc);
+  mfma_layer<RTT, CTW, H / 32, HROW, NPF>(Hs, r_1, acc);
+  WeightRing<CTW, H / 32, NPF> r_2;
+  r_2.start(W2 + (size_t)p * H * H, H / 16, hc0);
 #pragma unroll
   for (int rt = 0; rt < RTT; ++rt)
 #pragma unroll
@@ -150,7 +180,10 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
   __syncthreads();
 
   // ---- h1 = h0 + alpha (W_2 a + b_2), over h0 in place (this wave's columns)
-  mfma_layer<RTT, CTW, H / 32, HROW>(As, W2 + (size_t)p * H * H, H, hc0, acc);
+  mfma_layer<RTT, CTW, H / 32, HROW, NPF>(As, r_2, acc);
+  const int oc0 = wave * (M / kMlpWaves);   // this wave's output columns
+  WeightRing<OTW, H / 32, NPF> r_o;
+  r_o.start(Wo + (size_t)p * M * H, M / 16, oc0);
 #pragma unroll
   for (int rt = 0; rt < RTT; ++rt)
 #pragma unroll
@@ -160,7 +193,6 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
         uint16_t& h = Hs[(rt * 16 + 4 * g4 + r) * HROW + hc0 + ct * 16 + l16];
         h = bf16_bits(bf16_to_f32(h) + al * (acc[rt][ct][r] + bias[ct]));
       }
-  const int oc0 = wave * (M / kMlpWaves);   // this wave's output columns
   float obias[OTW];
 #pragma unroll
   for (int ct = 0; ct < OTW; ++ct) obias[ct] = bo[(size_t)p * M + oc0 + ct * 16 + l16];
@@ -168,7 +200,7 @@ phi_mlp_kernel(const XT* __restrict__ x, int64_t xstride, int rows, const uint16
 
   // ---- phi = exp(W_o h1 + b_o)
   f32x4 oacc[RTT][OTW];
-  mfma_layer<RTT, OTW, H / 32, HROW>(Hs, Wo + (size_t)p * M * H, H, oc0, oacc);
+  mfma_layer<RTT, OTW, H / 32, HROW, NPF>(Hs, r_o, oacc);
   PT* out = phi + ((size_t)u * rows + r0) * M;
 #pragma unroll
   for (int rt = 0; rt < RTT; ++rt)

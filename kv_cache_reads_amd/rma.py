@@ -193,21 +193,30 @@ _MLP_MATS = ("W_in", "W_1", "W_2", "W_o")
 _MLP_VECS = ("b_in", "b_1", "b_2", "alpha", "b_o")
 
 
+def mlp_tile_order(W: torch.Tensor) -> torch.Tensor:
+    """[P][N][K] -> the matrix-core tile order of rma.h, [P][K/32][N/16][64][8]:
+    lane l = n%16 + 16 * ((k%32) / 8) of tile (k/32, n/16) holds k%8 = 0..7."""
+    P, N, K = W.shape
+    return W.reshape(P, N // 16, 16, K // 32, 4, 8).permute(0, 3, 1, 4, 2, 5).contiguous()
+
+
 class PhiMlpWeights:
     """Device weights of n_param_sets MLP feature maps (rma_phi_mlp_features):
-    the matrices as bf16 (round to nearest even from the given values), biases
-    and the ReZero scalars as fp32.  `params` maps the names of rma_phi_mlp to
-    tensors with a leading [n_param_sets] axis."""
+    the matrices as bf16 (round to nearest even from the given values) in the
+    tile order rma.h defines, biases and the ReZero scalars as fp32.  `params`
+    maps the names of rma_phi_mlp to tensors with a leading [n_param_sets] axis
+    and [out][in] matrices."""
 
     def __init__(self, params: dict, device="cuda"):
         for n in _MLP_MATS:
-            setattr(self, n, params[n].to(device=device, dtype=torch.float32).to(torch.bfloat16).contiguous())
+            W = params[n].to(device=device, dtype=torch.float32).to(torch.bfloat16)
+            setattr(self, n, mlp_tile_order(W))
         for n in _MLP_VECS:
             setattr(self, n, params[n].to(device=device, dtype=torch.float32).contiguous())
         self.alpha = self.alpha.reshape(-1)
-        self.P, self.width, self.d = self.W_in.shape
-        self.m = self.W_o.shape[1]
-        assert self.width == PHI_MLP_WIDTH and self.W_1.shape == (self.P, 512, 512)
+        self.P, self.width, self.d = params["W_in"].shape
+        self.m = params["W_o"].shape[1]
+        assert self.width == PHI_MLP_WIDTH and tuple(params["W_1"].shape[1:]) == (512, 512)
         self._c = _PhiMlp(*(getattr(self, n).data_ptr() for n, _ in _PhiMlp._fields_))
 
 

@@ -212,3 +212,16 @@ def test_phi_mlp_validation():
     assert call(weights=ctypes.byref(odd)) == R.RMA_ERR_INVALID_ARG
     assert call(rows=0) == R.RMA_OK                            # nothing to do
 
+
+
+def test_mlp_tile_order_matches_the_header_formula():
+    """PhiMlpWeights' layout helper against the element formula in rma.h."""
+    import torch
+    P, N, K = 2, 64, 96
+    W = torch.arange(P * N * K, dtype=torch.float32).reshape(P, N, K)
+    T = R.mlp_tile_order(W).reshape(P, -1)
+    for p in range(P):
+        for n in (0, 5, 17, 63):
+            for k in (0, 7, 8, 31, 32, 95):
+                off = ((k // 32 * (N // 16) + n // 16) * 64 + (n % 16 + 16 * ((k % 32) // 8))) * 8 + k % 8
+                assert T[p, off] == W[p, n, k]
