@@ -136,3 +136,27 @@ def test_decode_with_mlp_features_matches_oracle(name):
                 a, _ = check_y(y[uu, g].numpy(), y_ref, f"{name} u{uu} g{g} s{s}")
                 worst = max(worst, a)
     log(f"{name}: MLP-feature decode, worst |y - oracle| {worst:.2e}")
+
+
+def test_full_c1_with_mlp_features_sampled_units():
+    """The full c1 workload (32K context, K = 328) on the MLP features, in the
+    configuration bench.py --phi mlp times; the oracle checks two units (every
+    query head) end to end: phi_k rows, top-K and outputs."""
+    cfg = W.CONFIGS["c1"].with_(m=64)
+    K = cfg.K[0]
+    inp, pk, pq, phi_k, outs = _mlp_path(cfg, K, [0])
+    for uu in (1, cfg.U - 2):
+        k = inp.k[uu].float().cpu().numpy().astype(np.float64)
+        v = inp.v[uu].float().cpu().numpy().astype(np.float64)
+        mid = slice(cfg.n_sink, cfg.n_sink + cfg.L_mid)
+        phi_ref = O.round_bf16(O.phi_mlp(k[mid], _host_params(pk, uu % cfg.P), bf16_operands=True))
+        _check_rows(phi_k[uu], phi_ref, True, f"c1 phi_k unit {uu}")
+        S, u_ = O.summaries(phi_ref, v[mid])
+        _, idx, y = outs[0]
+        for g in range(cfg.G):
+            q = inp.q[0, uu, g].double().cpu().numpy()
+            f = O.phi_mlp(q[None], _host_params(pq, (uu % cfg.P) * cfg.G + g), bf16_operands=True)[0]
+            y_ref, idx_ref, _ = O.decode_query(q, f, k, v, phi_ref, S, u_, cfg.L, cfg.n_sink, cfg.n_tail, 0, K)
+            assert np.array_equal(idx[uu, g].numpy().astype(np.int64), idx_ref)
+            check_y(y[uu, g].numpy(), y_ref, f"c1 mlp u{uu} g{g}")
+    log("c1 with MLP features: sampled units match the oracle")
