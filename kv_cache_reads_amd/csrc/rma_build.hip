@@ -63,9 +63,12 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
   static_assert(LCH >= 1 && TT * CPR % NT == 0, "tile shape");
   static_assert(!(INJ && STORE), "given rows are not stored");
 
-  __shared__ __align__(16) uint16_t Ks[TT * KROW];
-  __shared__ __align__(16) uint16_t Vs[TT * VROW];
-  __shared__ __align__(16) uint16_t Ps[(STORE || INJ) ? TT * PROW : 8];
+  // two buffers of each tile: tile j is computed from buffer j % 2 while tile
+  // j + 1 is staged into the other, so one barrier per tile orders both
+  constexpr int KBUF = TT * KROW, VBUF = TT * VROW, PBUF = (STORE || INJ) ? TT * PROW : 4;
+  __shared__ __align__(16) uint16_t Ks[2 * KBUF];
+  __shared__ __align__(16) uint16_t Vs[2 * VBUF];
+  __shared__ __align__(16) uint16_t Ps[2 * PBUF];
   __shared__ float s_kap[NW];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -129,20 +132,20 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     }
   };
   // K and V rows (and given Phi rows) as they are (16-byte writes)
-  auto stage_tile = [&](const uint4 (&kr)[LCH], const uint4 (&vr)[LCH], const uint4 (&pr)[PCH]) {
+  auto stage_tile = [&](int b, const uint4 (&kr)[LCH], const uint4 (&vr)[LCH], const uint4 (&pr)[PCH]) {
 #pragma unroll
     for (int j = 0; j < LCH; ++j) {
       const int chunk = tid + NT * j;
       const int row = chunk / CPR, cc = chunk % CPR;
-      *reinterpret_cast<uint4*>(Ks + row * KROW + cc * 8) = kr[j];
-      *reinterpret_cast<uint4*>(Vs + row * VROW + cc * 8) = vr[j];
+      *reinterpret_cast<uint4*>(Ks + b * KBUF + row * KROW + cc * 8) = kr[j];
+      *reinterpret_cast<uint4*>(Vs + b * VBUF + row * VROW + cc * 8) = vr[j];
     }
     if constexpr (INJ) {
 #pragma unroll
       for (int j = 0; j < PCH; ++j) {
         const int chunk = tid + NT * j;
         const int row = chunk / (M / 8), cc = chunk % (M / 8);
-        *reinterpret_cast<uint4*>(Ps + row * PROW + cc * 8) = pr[j];
+        *reinterpret_cast<uint4*>(Ps + b * PBUF + row * PROW + cc * 8) = pr[j];
       }
     }
   };
@@ -159,9 +162,12 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         (__attribute__((address_space(3))) v4s*)(tile + row * stride + col));
     return __builtin_bit_cast(uint2, r);
   };
-  auto ld_tr = [&](int row, int col) { return ld_tr_in(Vs, VROW, row, col); };
-  auto compute_tile = [&](int tok0, auto full_tag) {
+  auto compute_tile = [&](int tok0, auto buf_tag, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int b = decltype(buf_tag)::value;
+    const uint16_t* const Kb = Ks + b * KBUF;
+    uint16_t* const Pb = Ps + b * PBUF;
+    auto ld_tr = [&](int row, int col) { return ld_tr_in(Vs + b * VBUF, VROW, row, col); };
     // kappa: the largest squared key norm (NT/TT threads per token row, bf16 pair
     // dots; the root is taken once per chunk)
     {
@@ -170,7 +176,7 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; e += 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(Ks + row * KROW + qd * EPT + e);
+        const uint4 w = *reinterpret_cast<const uint4*>(Kb + row * KROW + qd * EPT + e);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -188,14 +194,14 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
     if constexpr (INJ) {
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const uint2 r = ld_tr_in(Ps, PROW, tt * 16 + tr_row, wave * 16 + tr_col);
+        const uint2 r = ld_tr_in(Pb, PROW, tt * 16 + tr_row, wave * 16 + tr_col);
         phv[tt][0] = r.x;
         phv[tt][1] = r.y;
       }
     }
 #pragma unroll
     for (int tt = 0; tt < (INJ ? 0 : NTT); ++tt) {
-      const f32x4 acc = proj_tile16<KS>(Ks + (tt * 16 + l16) * KROW + 8 * g4, Whi, Wlo);
+      const f32x4 acc = proj_tile16<KS>(Kb + (tt * 16 + l16) * KROW + 8 * g4, Whi, Wlo);
       float ph[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -207,10 +213,10 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
       phv[tt][1] = p23;
       if constexpr (STORE) {
         const int row0 = tt * 16 + 4 * g4;
-        Ps[(row0 + 0) * PROW + f] = (uint16_t)p01;
-        Ps[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
-        Ps[(row0 + 2) * PROW + f] = (uint16_t)p23;
-        Ps[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
+        Pb[(row0 + 0) * PROW + f] = (uint16_t)p01;
+        Pb[(row0 + 1) * PROW + f] = (uint16_t)(p01 >> 16);
+        Pb[(row0 + 2) * PROW + f] = (uint16_t)p23;
+        Pb[(row0 + 3) * PROW + f] = (uint16_t)(p23 >> 16);
       }
     }
     // step 2: S += Phi^T V, u += Phi^T 1 over 32-token blocks.  Hardware k-slot e
@@ -230,48 +236,60 @@ build_mfma_kernel(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ 
         Sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aph, Bv, Sacc[ct], 0, 0, 0);
       }
     }
-    if constexpr (STORE) {
-      __syncthreads();
-      // store the Phi tile rows (16-byte pieces, coalesced; rows are 8-byte aligned in LDS)
-      constexpr int PCR = M / 8;
-      static_assert(TT * PCR % NT == 0, "Phi tile store shape");
+  };
+  // store the Phi rows of the tile at tok0 from buffer b, after the barrier that
+  // follows its computation (16-byte pieces, coalesced; rows are 8-byte aligned in
+  // LDS).  tok0 = -TT, before the first tile, gives offsets that wrap past the
+  // range, so those stores are dropped like the ones past the chunk.
+  auto store_rows = [&](int tok0, int b) {
+    constexpr int PCR = M / 8;
+    static_assert(TT * PCR % NT == 0, "Phi tile store shape");
 #pragma unroll
-      for (int j = 0; j < TT * PCR / NT; ++j) {
-        const int chunk = tid + NT * j;
-        const int row = chunk / PCR, cc = chunk % PCR;
-        const uint2 a = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8);
-        const uint2 b = *reinterpret_cast<const uint2*>(Ps + row * PROW + cc * 8 + 4);
-        buf_st16(rph, (uint32_t)((tok0 + row) * M + cc * 8) * 2, make_uint4(a.x, a.y, b.x, b.y));
-      }
+    for (int j = 0; j < TT * PCR / NT; ++j) {
+      const int chunk = tid + NT * j;
+      const int row = chunk / PCR, cc = chunk % PCR;
+      const uint2 x = *reinterpret_cast<const uint2*>(Ps + b * PBUF + row * PROW + cc * 8);
+      const uint2 y = *reinterpret_cast<const uint2*>(Ps + b * PBUF + row * PROW + cc * 8 + 4);
+      buf_st16(rph, (uint32_t)((tok0 + row) * M + cc * 8) * 2, make_uint4(x.x, x.y, y.x, y.y));
     }
   };
 
-  // Two register stages in turn: tile t+2 loads while tile t is computed.  Every
-  // pass issues the same memory operations (tiles past the chunk load as zeros
-  // without touching memory, Phi stores past it are dropped, and a tile past an
-  // odd tile count is computed as padding), and the first two tiles are complete
-  // before the loop, so the wait before each staging step covers only the loads
-  // of the tile being staged, not the stores and loads issued after them.
+  // Tile j: its K/V (and given Phi) registers load three tiles ahead, they are
+  // staged into LDS buffer j % 2 one tile ahead, and the Phi rows it leaves in
+  // that buffer are stored one tile after; one barrier closes each tile.  Two
+  // register stages alternate.  Every pass issues the same memory operations
+  // (tiles past the chunk load as zeros without touching memory, Phi stores
+  // outside it are dropped, and a tile past an odd tile count is computed as
+  // padding), so the wait before each staging step covers only the loads of the
+  // tile being staged, not the stores and loads issued after them.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   uint4 kA[LCH], vA[LCH], kB[LCH], vB[LCH], pA[PCH], pB[PCH];
   load_tile(kA, vA, pA, 0);
   load_tile(kB, vB, pB, TT);
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing in flight on entry
   if constexpr (!INJ) split_w_values<KS>(wv, Whi, Wlo);
+  stage_tile(0, kA, vA, pA);
+  load_tile(kA, vA, pA, 2 * TT);
+  __syncthreads();
+  int t_last = -TT;
   for (int tok0 = 0; tok0 < n; tok0 += 2 * TT) {
-    __syncthreads();
-    stage_tile(kA, vA, pA);
-    __syncthreads();
-    load_tile(kA, vA, pA, tok0 + 2 * TT);
-    if (tok0 + TT <= n) compute_tile(tok0, std::true_type{});
-    else compute_tile(tok0, std::false_type{});
-    __syncthreads();
-    stage_tile(kB, vB, pB);
-    __syncthreads();
+    stage_tile(1, kB, vB, pB);
     load_tile(kB, vB, pB, tok0 + 3 * TT);
-    if (tok0 + 2 * TT <= n) compute_tile(tok0 + TT, std::true_type{});
-    else compute_tile(tok0 + TT, std::false_type{});
+    if constexpr (STORE) store_rows(tok0 - TT, 1);
+    if (tok0 + TT <= n) compute_tile(tok0, B0{}, std::true_type{});
+    else compute_tile(tok0, B0{}, std::false_type{});
+    __syncthreads();
+    stage_tile(0, kA, vA, pA);
+    load_tile(kA, vA, pA, tok0 + 4 * TT);
+    if constexpr (STORE) store_rows(tok0, 0);
+    if (tok0 + 2 * TT <= n) compute_tile(tok0 + TT, B1{}, std::true_type{});
+    else compute_tile(tok0 + TT, B1{}, std::false_type{});
+    __syncthreads();
+    t_last = tok0 + TT;
   }
+  if constexpr (STORE) store_rows(t_last, 1);
 
   // ---- partials of this chunk
   float* Sp = pS + ((size_t)u * n_chunks + c) * M * D;

@@ -279,6 +279,23 @@ __device__ __forceinline__ void st_elem(uint16_t* p, size_t i, float v) {
 }
 
 // ---------------------------------------------------------------- misc
+// Quotient by a divisor d >= 1 that is only known at run time, for 0 <= i < 2^31
+// - d with a quotient below 2^22.  The compiler's integer division by a variable
+// is a long sequence with a reciprocal of its own; here the float estimate
+// i * (1/d) carries three roundings of relative 2^-24 each, so it is within one
+// of floor(i / d), and two integer checks make it exact.
+struct FastDiv {
+  int d;
+  float inv;
+  __device__ explicit FastDiv(int d_) : d(d_), inv(1.0f / (float)d_) {}
+  __device__ __forceinline__ int quo(int i) const {
+    int c = (int)((float)i * inv);
+    c -= (c * d > i) ? 1 : 0;
+    c += ((c + 1) * d <= i) ? 1 : 0;
+    return c;
+  }
+};
+
 __device__ __forceinline__ float phi_elu1(float z) { return z > 0.f ? z + 1.f : __expf(z); }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32); the

@@ -25,6 +25,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace rma {
 
 // N elements of type T as raw 16-byte words: loaded early, unpacked at use.
@@ -300,65 +302,73 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
     if constexpr (RECOMP) {
       if (sub) recompute_w(c0, cnt);
     }
-    for (int jb = grp; jb < cnt; jb += NGR * B) {
-      RawPiece<KT, CPL> vr[B], kr[B];
-      RawPiece<PT, FPL> pr[B];
-      float scs[B];
-      int kind[B];  // 0: none, 1: anchor or generated (scored here), 2: retrieved
+    // Exactly scored entries (anchors and generated tokens: the list's first
+    // n_ex) and retrieved ones in two passes.  Within a pass every entry slot
+    // issues the same loads without a branch (a slot past the pass's end reads
+    // the pass's first entry again and adds nothing), so all of a group's loads
+    // are in flight before the first one is used.
+    const int n_exc = min(max(n_ex - c0, 0), cnt);
+    auto gather = [&](int lo, int hi, auto ex_tag) {
+      constexpr bool EX = decltype(ex_tag)::value;
+      const bool ld_phi = !EX && !RECOMP && sub;   // uniform
+      for (int jb = lo + grp; jb < hi; jb += NGR * B) {
+        RawPiece<KT, CPL> vr[B], kr[B];
+        RawPiece<PT, FPL> pr[B];
+        float scs[B];
+        int jcs[B];
 #pragma unroll
-      for (int e = 0; e < B; ++e) {
-        const int jj = jb + e * NGR;
-        vr[e].zero();
-        kr[e].zero();
-        pr[e].zero();
-        kind[e] = 0;
-        scs[e] = 0.f;
-        if (jj < cnt) {
-          const int pos = s_pos[jj];
-          const bool ex = c0 + jj < n_ex;
-          kind[e] = ex ? 1 : 2;
-          scs[e] = s_sc[jj];
+        for (int e = 0; e < B; ++e) {
+          const int jj = jb + e * NGR;
+          const int jc = jj < hi ? jj : lo;
+          const int pos = s_pos[jc];
+          jcs[e] = jc;
+          scs[e] = s_sc[jc];
           vr[e].load(vunit + (size_t)pos * D + part * CPL);
-          if (ex) kr[e].load(kunit + (size_t)pos * D + part * CPL);
-          else if (sub && !RECOMP) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
+          if constexpr (EX) kr[e].load(kunit + (size_t)pos * D + part * CPL);
+          else kr[e].zero();
+          if (ld_phi) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
+          else pr[e].zero();
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+          // both dots on every lane (zeros where unused), so the 8-lane sums
+          // never run under divergent control flow
+          float kv[CPL], ph[FPL], vv[CPL];
+          kr[e].unpack(kv);
+          pr[e].unpack(ph);
+          float a = 0.f, w = 0.f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) a = __fmaf_rn(qr[i], kv[i], a);
+#pragma unroll
+          for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+          a = lane_group_sum<LPE>(a);
+          w = lane_group_sum<LPE>(w);
+          if constexpr (RECOMP) w = (!EX && sub) ? s_w[jcs[e]] : 0.f;
+          if (jb + e * NGR < hi) {  // uniform within the group
+            const float s = EX ? a * inv_sqrt_d : scs[e];
+            if (s > mrun) {
+              const float r = __expf(mrun - s);  // 0 while nothing is accumulated
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) N[c] *= r;
+              Z *= r;
+              mrun = s;
+            }
+            const float ew = __expf(s - mrun);
+            vr[e].unpack(vv);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              N[c] = __fmaf_rn(ew, vv[c], N[c]);
+              NK[c] = __fmaf_rn(w, vv[c], NK[c]);
+            }
+            Z += ew;
+            ZK += w;
+          }
         }
       }
-#pragma unroll
-      for (int e = 0; e < B; ++e) {
-        // both dots on every lane (zeros where unused), so the 8-lane sums
-        // never run under divergent control flow
-        float kv[CPL], ph[FPL], vv[CPL];
-        kr[e].unpack(kv);
-        pr[e].unpack(ph);
-        float a = 0.f, w = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) a = __fmaf_rn(qr[i], kv[i], a);
-#pragma unroll
-        for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
-        a = lane_group_sum<LPE>(a);
-        w = lane_group_sum<LPE>(w);
-        if constexpr (RECOMP) w = (kind[e] == 2 && sub) ? s_w[jb + e * NGR] : 0.f;
-        if (kind[e] != 0) {  // uniform within the group
-          const float s = kind[e] == 1 ? a * inv_sqrt_d : scs[e];
-          if (s > mrun) {
-            const float r = __expf(mrun - s);  // 0 while nothing is accumulated
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) N[c] *= r;
-            Z *= r;
-            mrun = s;
-          }
-          const float ew = __expf(s - mrun);
-          vr[e].unpack(vv);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            N[c] = __fmaf_rn(ew, vv[c], N[c]);
-            NK[c] = __fmaf_rn(w, vv[c], NK[c]);
-          }
-          Z += ew;
-          ZK += w;
-        }
-      }
-    }
+    };
+    gather(0, n_exc, std::true_type{});
+    gather(n_exc, cnt, std::false_type{});
   }
 
   // ---- phi(q)^T S (per feature block) and u^T f

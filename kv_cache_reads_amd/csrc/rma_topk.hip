@@ -409,6 +409,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   __shared__ DD s_bdd[kSelBandMax];
   __shared__ int s_bidx[kSelBandMax];
   __shared__ float s_qf[128];
+  __shared__ float4 s_hp4;
 
   const int ug = blockIdx.x, u = ug / G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
@@ -419,11 +420,13 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   float* so = sc_out + (size_t)ug * K;
   const KT* kunit = kb + (size_t)u * ustride;
 
-  const float4 hp4 = hpw[ug];  // written by the scan: identical binning and error bound
-  const HeadParams hp{hp4.x, hp4.y, hp4.z};
-  if (tid < D) s_qf[tid] = qg[tid];
-  // When every report slot fits SPEC per thread, all slots are loaded together
-  // with the chunk counts (one round trip; slot (c, j) is valid for j < count_c)
+  // Every input of the block is requested before any is used (one memory round
+  // trip): the head's parameters, the query, the chunk counts and, when every
+  // report slot fits SPEC per thread, all report slots (slot (c, j) is valid for
+  // j < count_c).  The loads are unconditional (indices clamped into range), so
+  // none waits inside a branch before the others are issued.
+  const float4 hp_in = hpw[ug];  // written by the scan: identical binning and error bound
+  const float q_in = qg[min(tid, D - 1)];
   constexpr int SPEC = 8;
   const int nslots_all = n_chunks * r_cap;
   const bool spec = nslots_all <= SPEC * NT;
@@ -432,10 +435,12 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
 #pragma unroll
     for (int k = 0; k < SPEC; ++k) sv[k] = en[min(tid + k * NT, nslots_all - 1)];
   }
+  const int2 mm = mt[max(0, min(tid, n_chunks - 1))];
+  if (tid == 0) s_hp4 = hp_in;
+  if (tid < D) s_qf[tid] = q_in;
   // chunk reports: one thread per chunk (n_chunks <= 256), offsets by a block scan
   int w_c = 0, trunc = 0;
   if (tid < n_chunks) {
-    const int2 mm = mt[tid];
     trunc = mm.y > r_cap;
     w_c = min(mm.y, r_cap);
     s_bcs[tid] = mm.x;
@@ -446,16 +451,19 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   if (tid < n_chunks) s_off[tid] = off_c;
   if (tid == 0) s_off[n_chunks] = nE;
   trunc = __syncthreads_or(trunc);
+  const float4 hp4 = s_hp4;
+  const HeadParams hp{hp4.x, hp4.y, hp4.z};
   int wmax = (int)wave_max_dpp((float)w_c);
   if (lane == 0) s_wred[wave] = wmax;
   __syncthreads();
   wmax = 0;
 #pragma unroll
   for (int w = 0; w < NWV; ++w) wmax = max(wmax, s_wred[w]);
+  const FastDiv by_wmax(max(wmax, 1)), by_rcap(max(r_cap, 1));
 
   if (K == L_mid) {  // every mid token is selected; the chunks reported all of them in order
     for (int i = tid; i < n_chunks * wmax; i += NT) {
-      const int c = i / wmax, j = i - c * wmax;
+      const int c = by_wmax.quo(i), j = i - c * wmax;
       if (j < s_off[c + 1] - s_off[c]) {
         const float2 e = en[(size_t)c * r_cap + j];
         io[s_off[c] + j] = n_sink + __float_as_int(e.y);
@@ -475,7 +483,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
 #pragma unroll
       for (int k = 0; k < SPEC; ++k) {
         const int i = tid + k * NT;
-        const int c = i / r_cap, j = i - c * r_cap;
+        const int c = by_rcap.quo(i), j = i - c * r_cap;
         if (i < nslots_all && j < s_off[c + 1] - s_off[c]) {
           es[s_off[c] + j] = sv[k].x;
           ep[s_off[c] + j] = __float_as_int(sv[k].y);
@@ -493,7 +501,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int i = i0 + k * NT + tid;
-          const int c = i / wmax, j = i - c * wmax;
+          const int c = by_wmax.quo(i), j = i - c * wmax;
           dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
           if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
         }
