@@ -379,6 +379,15 @@ __device__ void exact_fallback(const float* qf, const KT* kunit, int n_sink, int
   }
 }
 
+// One empty statement that takes eight pairs of values loaded from LDS: the
+// compiler can neither sink a read into the branch that later uses it nor wait
+// for one before the next is issued.
+__device__ __forceinline__ void pin_pairs8(int (&a)[8], int (&b)[8]) {
+  asm volatile("" : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]),
+               "+v"(a[3]), "+v"(b[3]), "+v"(a[4]), "+v"(b[4]), "+v"(a[5]), "+v"(b[5]),
+               "+v"(a[6]), "+v"(b[6]), "+v"(a[7]), "+v"(b[7]));
+}
+
 template <typename KT, int D, int NT>
 __global__ void __launch_bounds__(NT)
 topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb, int64_t ustride,
@@ -422,18 +431,24 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
 
   // Every input of the block is requested before any is used (one memory round
   // trip): the head's parameters, the query, the chunk counts and, when every
-  // report slot fits SPEC per thread, all report slots (slot (c, j) is valid for
-  // j < count_c).  The loads are unconditional (indices clamped into range), so
-  // none waits inside a branch before the others are issued.
+  // chunk's report slots fit SPEC per thread, all report slots (slot (c, j) is
+  // valid for j < count_c).  The loads are unconditional (indices clamped into
+  // range), so none waits inside a branch before the others are issued.
+  // Slots map to threads by chunk: a power-of-two group of tpc threads per chunk
+  // (thread t serves chunk t >> lg_t), so no slot index needs a division.
   const float4 hp_in = hpw[ug];  // written by the scan: identical binning and error bound
   const float q_in = qg[min(tid, D - 1)];
   constexpr int SPEC = 8;
-  const int nslots_all = n_chunks * r_cap;
-  const bool spec = nslots_all <= SPEC * NT;
+  static_assert((NT & (NT - 1)) == 0, "power-of-two block");
+  const int lg_c = n_chunks > 1 ? 32 - __clz(n_chunks - 1) : 0;   // ceil(log2(n_chunks)) <= 8
+  const int lg_t = __builtin_ctz(NT) - lg_c, tpc = 1 << lg_t;
+  const int my_c = tid >> lg_t, my_s = tid & (tpc - 1);
+  const bool spec = r_cap <= SPEC * tpc;
   float2 sv[SPEC];
   if (spec) {
+    const int cbase = min(my_c, n_chunks - 1) * r_cap;
 #pragma unroll
-    for (int k = 0; k < SPEC; ++k) sv[k] = en[min(tid + k * NT, nslots_all - 1)];
+    for (int k = 0; k < SPEC; ++k) sv[k] = en[cbase + min(my_s + k * tpc, r_cap - 1)];
   }
   const int2 mm = mt[max(0, min(tid, n_chunks - 1))];
   if (tid == 0) s_hp4 = hp_in;
@@ -459,7 +474,7 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
   wmax = 0;
 #pragma unroll
   for (int w = 0; w < NWV; ++w) wmax = max(wmax, s_wred[w]);
-  const FastDiv by_wmax(max(wmax, 1)), by_rcap(max(r_cap, 1));
+  const FastDiv by_wmax(max(wmax, 1));
 
   if (K == L_mid) {  // every mid token is selected; the chunks reported all of them in order
     for (int i = tid; i < n_chunks * wmax; i += NT) {
@@ -480,13 +495,16 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     // the union in LDS (report order = position order) and its score range
     float lo = INFINITY, hi = -INFINITY;
     if (spec) {
+      // this thread's chunk: its offset and count (none for a thread past the chunks)
+      const int cc = min(my_c, n_chunks - 1);
+      const int o0 = s_off[cc];
+      const int wc = my_c < n_chunks ? s_off[cc + 1] - o0 : 0;
 #pragma unroll
       for (int k = 0; k < SPEC; ++k) {
-        const int i = tid + k * NT;
-        const int c = by_rcap.quo(i), j = i - c * r_cap;
-        if (i < nslots_all && j < s_off[c + 1] - s_off[c]) {
-          es[s_off[c] + j] = sv[k].x;
-          ep[s_off[c] + j] = __float_as_int(sv[k].y);
+        const int j = my_s + k * tpc;
+        if (j < wc) {
+          es[o0 + j] = sv[k].x;
+          ep[o0 + j] = __float_as_int(sv[k].y);
           lo = fminf(lo, sv[k].x);
           hi = fmaxf(hi, sv[k].x);
         }
@@ -497,13 +515,22 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
       const int nslots = n_chunks * wmax;
       for (int i0 = 0; i0 < nslots; i0 += 8 * NT) {
         float2 e[8];
-        int dst[8];
+        int dst[8], o0[8], o1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = min(by_wmax.quo(i0 + k * NT + tid), n_chunks - 1);
+          o0[k] = s_off[c];
+          o1[k] = s_off[c + 1];
+        }
+        pin_pairs8(o0, o1);
+        // a slot outside the reports loads a valid slot of the last chunk and
+        // drops it, so no load waits inside a branch
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int i = i0 + k * NT + tid;
-          const int c = by_wmax.quo(i), j = i - c * wmax;
-          dst[k] = (i < nslots && j < s_off[c + 1] - s_off[c]) ? s_off[c] + j : -1;
-          if (dst[k] >= 0) e[k] = en[(size_t)c * r_cap + j];
+          const int c = min(by_wmax.quo(i), n_chunks - 1), j = i - c * wmax;
+          dst[k] = ((i < nslots) & (j < o1[k] - o0[k])) ? o0[k] + j : -1;
+          e[k] = en[(size_t)c * r_cap + min(j, r_cap - 1)];
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -648,14 +675,14 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
     const int per = (nE + NT - 1) / NT;
     const int i0 = min(nE, tid * per), i1 = min(nE, i0 + per);
     int cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += (es[i] > th_hi) || (ep[i] & SELF);
+    for (int i = i0; i < i1; ++i) cnt += (es[i] > th_hi) | ((ep[i] & SELF) != 0);
     int total;
     int pos = block_excl_scan<NT>(cnt, s_buf, total);
     if (total != K) {
       fallback = true;  // uniform: every thread sees the same total
     } else {
       for (int i = i0; i < i1; ++i) {
-        if ((es[i] > th_hi) || (ep[i] & SELF)) {
+        if ((es[i] > th_hi) | ((ep[i] & SELF) != 0)) {
           if (pos < K) {
             io[pos] = n_sink + (ep[i] & ~SELF);
             so[pos] = es[i] * inv_sqrt_d;
