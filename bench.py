@@ -67,10 +67,10 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="7ee6f2ddbed6309d", fetch_bytes=69246569, write_bytes=84039096),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="7ee6f2ddbed6309d", fetch_bytes=33825869, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="7ee6f2ddbed6309d", fetch_bytes=7072338, write_bytes=8192),
-    ("full_partial_kernel", "c1", 328): dict(csrc="7ee6f2ddbed6309d", fetch_bytes=67368161, write_bytes=589824),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=69265259, write_bytes=84054016),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=33826127, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=7074383, write_bytes=8192),
+    ("full_partial_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=67367391, write_bytes=589824),
 }
 
 
