@@ -375,3 +375,49 @@ def test_topk_many_units_use_small_select_blocks():
     q[U - 1, 0, 0] = 1.0                                  # ... which forces the exact fallback
     _topk_case(k.bfloat16(), q, L, ns, nt, 30, units=(0, 17, U - 1))
     _topk_case(k.bfloat16(), q, L, ns, nt, 500, units=(0, U - 1))
+
+
+def _select_layout(L, ns, nt, U, G, K, d=64):
+    """The plan's chunking of the mid-region and the select's slot layout (the
+    rule the library applies): (chunks, report capacity, grouped).  With a
+    1024-thread select block each chunk's report slots belong to a group of
+    1024 / 2^ceil(log2(chunks)) threads; when the capacity exceeds eight slots
+    per thread of that group the wide-union path runs instead."""
+    Lm = L - ns - nt
+    tile = 64 if d == 64 else 32
+    ch_max = max(tile, (8192 // G) // tile * tile)
+    lo, hi = -(-Lm // ch_max), min(256, -(-Lm // tile))
+    nc = max(lo, min(-(-512 // U), hi))
+    ch = -(-(-(-Lm // nc)) // tile) * tile
+    chunks = -(-Lm // ch)
+    if K >= Lm:
+        r_cap = ch
+    else:
+        mu = K / chunks
+        rmin = max(16, (math.ceil(mu + 5 * math.sqrt(mu) + 8) + 7) // 8 * 8)
+        r_cap = min(ch, 2 * min(ch, rmin) + 32)
+    tpc = 1024 >> ((chunks - 1).bit_length() if chunks > 1 else 0)
+    return chunks, r_cap, r_cap <= 8 * tpc
+
+
+# (L, U, G, K, chunks, grouped): one chunk; chunk counts that are not powers of
+# two on both report layouts (the wide one when the budget is large); a chunk
+# count whose groups are four threads wide
+SELECT_LAYOUTS = [
+    (100, 1, 2, 10, 1, True),
+    (5000, 1, 3, 50, 78, True),
+    (3000, 2, 4, 300, 47, True),
+    (12000, 8, 1, 2000, 63, False),
+    (20000, 1, 3, 200, 156, False),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_LAYOUTS, ids=lambda c: f"L{c[0]}U{c[1]}G{c[2]}K{c[3]}")
+def test_topk_report_layouts(case):
+    L, U, G, K, chunks, grouped = case
+    ns, nt = 4, 32
+    assert _select_layout(L, ns, nt, U, G, K)[0::2] == (chunks, grouped), _select_layout(L, ns, nt, U, G, K)
+    g = torch.Generator().manual_seed(L + K)
+    k = torch.randn(U, L, 64, generator=g)
+    q = torch.randn(U, G, 64, generator=g)
+    _topk_case(k.bfloat16(), q, L, ns, nt, K, units=tuple(range(U)))
