@@ -67,10 +67,10 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=69265259, write_bytes=84054016),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=33826127, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=7074383, write_bytes=8192),
-    ("full_partial_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=67367391, write_bytes=589824),
+    ("build_mfma_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=69264497, write_bytes=84049512),
+    ("topk_scan_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=33832736, write_bytes=636576),
+    ("merge_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=7074332, write_bytes=8192),
+    ("full_partial_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=67368312, write_bytes=589824),
 }
 
 
@@ -288,32 +288,56 @@ class PathRunner:
         return out
 
 
+def capture_rounds(torch, fn, n_copies, stream, start=0):
+    """HIP graphs for timed runs: `round` holds one call of fn for every input copy
+    (copies start, start + 1, ... mod n_copies, in turn), `single[i]` one call for
+    copy i.  A graph launch has a fixed cost of a few microseconds at its
+    boundary; a round pays it once per n_copies steps, as a serving loop that
+    captures several decode steps in one graph does."""
+    single = []
+    for r_i in range(n_copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn(r_i)
+        single.append(g)
+    rnd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rnd, stream=stream):
+        for j in range(n_copies):
+            fn((start + j) % n_copies)
+    return rnd, single
+
+
+def replay_steps(rnd, single, n_copies, n, start=0):
+    """Enqueues exactly n steps: whole rounds, then single steps that continue the
+    rotation where the rounds left it."""
+    for _ in range(n // n_copies):
+        rnd.replay()
+    for i in range(n % n_copies):
+        single[(start + i) % n_copies].replay()
+
+
 def timed_replays(fn, n_copies, n, stream, use_graphs):
     """Average microseconds of fn(i) (enqueues work for input copy i % n_copies),
-    replayed from per-copy HIP graphs when use_graphs."""
+    replayed from HIP graphs of whole rounds over the copies when use_graphs."""
     import torch
     with torch.cuda.stream(stream):
         fn(0)  # outputs are allocated outside any capture
     stream.synchronize()
-    run = fn
     if use_graphs:
-        graphs = []
-        for r_i in range(n_copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn(r_i)
-            graphs.append(g)
-        run = lambda i: graphs[i % n_copies].replay()  # noqa: E731
+        rnd, single = capture_rounds(torch, fn, n_copies, stream)
+        run_n = lambda k: replay_steps(rnd, single, n_copies, k)  # noqa: E731
+    else:
+        def run_n(k):
+            for i in range(k):
+                fn(i)
     with torch.cuda.stream(stream):
-        for i in range(3):
-            run(i)
+        run_n(3)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record()
-        for i in range(n):
-            run(i)
+        run_n(n)
         e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n * 1e3
@@ -471,39 +495,36 @@ def main():
     y_eager = runners[0].y.clone()
     idx_eager = runners[0].idx.clone()
 
+    # timed steps continue the rotation over the copies where the warm-up left it
+    start = args.warmup % n_copies
     graphs = None
     if not args.eager:
         try:
-            graphs = []
-            for r in runners:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    r.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                graphs.append(g)
-            # replay checks against the eager result, with eager work in between
-            for rep in range(3):
+            rnd, graphs = capture_rounds(
+                torch, lambda i: runners[i].step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)),
+                n_copies, stream, start)
+            # replay checks against the eager result, with eager work in between:
+            # the single-step graph of copy 0, then a whole round
+            for rep in range(4):
                 runners[0].y.zero_()
-                graphs[0].replay()
+                (graphs[0] if rep < 3 else rnd).replay()
                 torch.cuda.synchronize()
                 assert torch.equal(runners[0].y, y_eager) and torch.equal(runners[0].idx, idx_eager), \
                     "graph replay differs from eager"
                 with torch.cuda.stream(stream):
                     runners[0].step(st)
                 stream.synchronize()
-            log("[bench] HIP graph replays match the eager run")
+            log(f"[bench] HIP graph replays match the eager run (single steps and rounds of {n_copies})")
         except Exception as ex:  # fall back to eager launches
             log(f"[bench] graph capture unavailable ({ex}); timing eager launches")
             graphs = None
 
-    def run_step(i):
-        if graphs is not None:
-            graphs[i % n_copies].replay()
-        else:
-            runners[i % n_copies].step(st)
-
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            run_step(i)
+            if graphs is not None:
+                graphs[i % n_copies].replay()
+            else:
+                runners[i % n_copies].step(st)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps, synchronised on both sides
@@ -512,8 +533,11 @@ def main():
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         e0.record()
-        for i in range(args.steps):
-            run_step(args.warmup + i)
+        if graphs is not None:
+            replay_steps(rnd, graphs, n_copies, args.steps, start)
+        else:
+            for i in range(args.steps):
+                runners[(start + i) % n_copies].step(st)
         e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
@@ -600,7 +624,7 @@ def main():
             **({"per_kernel_TFLOPs": {k: round(v, 1) for k, v in ktf.items()}} if ktf else {}),
             "phi_k_rows": "stored" if store_phi else "recomputed at decode (not stored)",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
-            "rotating_copies": n_copies, "launch": "hip_graph" if graphs is not None else "eager",
+            "rotating_copies": n_copies, "launch": f"hip_graph, rounds of {n_copies} steps" if graphs is not None else "eager",
             "step_algorithmic_MB": round(step_bytes / 1e6, 3),
             "step_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "per_call_us": {n: round(dur[n] * 1e3, 2) for n in names},
