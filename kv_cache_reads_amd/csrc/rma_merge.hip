@@ -7,10 +7,12 @@
 // One block per (unit, query head), or per (unit, query head, slice) when few
 // heads would leave most of the chip idle.  The head's exact-support entries
 //   [sinks | tail | generated | retrieved (idx)]   (n_a + n_gen + K entries)
-// (one contiguous slice of them) are staged in LDS chunk by chunk.  Eight lanes share an entry; each 8-lane
-// group takes every 64th entry, issues the row loads of four entries at once
-// (V row; K row for an anchor or generated token, whose score it computes;
-// phi_k row for a retrieved token) and keeps its own running max m:
+// (one contiguous slice of them) are staged in LDS chunk by chunk.  Eight lanes
+// share an entry; each 8-lane group takes every NGR-th entry (64 groups in 512
+// threads), one kind at a time: first the anchors and generated tokens (V and K
+// rows; it computes their scores), then the retrieved tokens (V and phi_k rows).
+// It issues the row loads of a batch of entries (8 at d = 64 with bf16 rows,
+// fewer for wider rows) before it uses any, and keeps its own running max m:
 //   N = sum e^{s_i - m} v_i,  Z = sum e^{s_i - m},
 //   w_i = f.Phi_K[i],  nuK = sum_{K(q)} w_i v_i,  ZK = sum_{K(q)} w_i.
 // The group partials are combined with max rescaling (fixed order) into m*,
