@@ -432,7 +432,7 @@ def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark times one GPU: --gpus must be 1 "
                                    "(the units of a batch shard across GPUs with no communication)"}))
         sys.exit(2)
     import torch

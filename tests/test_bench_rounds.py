@@ -29,3 +29,14 @@ def test_replay_steps_counts_and_rotation(n_copies, steps, start):
     bench.replay_steps(rnd, single, n_copies, steps, start)
     assert len(log) == steps
     assert log == [(start + i) % n_copies for i in range(steps)]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import json
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "--gpus must be 1" in msg["error"]
