@@ -267,7 +267,10 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
  * flags: RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL (selection-only Top-K) or
  *        RMA_MERGE_NO_SUBTRACT (NoSub).
  * y: fp32 [n_units][G][d].  stats: NULL or fp32 [n_units][G][4] =
- *    (m*, Z_E, Z_R (unshifted, after the clamp), sum_{K(q)} w_i).
+ *    (m*, Z_E, Z_R (unshifted, after the clamp), sum_{K(q)} w_i); the last
+ *    is 0 unless the subtraction runs (RMA_MERGE_SUB with 0 < K < L_mid).
+ * With K == L_mid (RMA_MERGE_SUB) the residual is exactly zero: no phi_k row
+ * is read, and phi_k, Wk and bk may all be NULL.
  * Requires n_sink + n_tail + n_gen + K > 0.
  * Workspace: rma_workspace_bytes(RMA_OP_DECODE_MERGE, ...).
  */

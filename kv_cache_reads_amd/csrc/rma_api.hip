@@ -81,20 +81,30 @@ rma_status check_kv_span(const rma_kv* kv, const rma_span* sp, bool need_v) {
 
 int64_t l_mid(const rma_span& sp) { return sp.L - sp.n_sink - sp.n_tail; }
 
-// compute units of the current device (256 when it cannot be queried)
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    cus = (hipGetDevice(&dev) == hipSuccess &&
-           hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-              ? v
-              : 256;
-  }
-  return cus;
-}
+// compute units of the current device
+int device_cus() { return device_info().cus; }
 
 }  // namespace
+
+const DeviceInfo& device_info() {
+  static std::once_flag once[kMaxDevices];
+  static DeviceInfo info[kMaxDevices];
+  static const DeviceInfo fallback{256, 64 * 1024};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fallback;
+  std::call_once(once[dev], [dev] {
+    int cus = 0, lds = 0;
+    info[dev].cus = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                            cus > 0
+                        ? cus
+                        : fallback.cus;
+    info[dev].lds_per_block =
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && lds > 0
+            ? (size_t)lds
+            : fallback.lds_per_block;
+  });
+  return info[dev];
+}
 
 // ------------------------------------------------------------- plans
 BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi, int phi_dtype) {

@@ -7,6 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 
 #include "../../include/rma.h"
@@ -22,6 +23,32 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // lands on counters another call (with a different unit count) relies on.
 constexpr size_t kCounterBytes = 65536 * 4;
 inline size_t counter_bytes(int64_t /*n_units*/) { return kCounterBytes; }
+
+// ------------------------------------------------------------- device
+// Properties of the calling thread's current HIP device, queried once per
+// device (std::call_once per device id, so concurrent first calls are safe) and
+// read-only afterwards.  Devices beyond kMaxDevices, or a failed query, get
+// conservative defaults.
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  int cus;               // compute units
+  size_t lds_per_block;  // bytes of LDS one workgroup may use
+};
+const DeviceInfo& device_info();
+
+// Static LDS bytes of a kernel (a property of its code object, the same on
+// every gfx950 device): queried on first use, a thread-safe function-local
+// static per kernel.
+template <typename Kern>
+size_t kernel_static_lds(Kern* kfn) {
+  static const size_t bytes = [kfn] {
+    hipFuncAttributes attr{};
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kfn)) == hipSuccess
+               ? (size_t)attr.sharedSizeBytes
+               : (size_t)32 * 1024;
+  }();
+  return bytes;
+}
 
 // ------------------------------------------------------------- build
 struct BuildPlan {

@@ -99,7 +99,10 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
   const int T = n_ex + K;
   const int e0 = slice * slice_len, e1 = min(T, e0 + slice_len);   // this block's entries
-  const bool sub = (flags == RMA_MERGE_SUB) && K > 0;
+  // the subtraction runs only when part of the mid-region stays unretrieved:
+  // with K == L_mid the residual is exactly zero and no phi_k row is read
+  // (the caller may then pass neither rows nor Wk)
+  const bool sub = (flags == RMA_MERGE_SUB) && K > 0 && K < L_mid;
   const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
   const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
 
@@ -509,7 +512,7 @@ merge_combine_kernel(const float* __restrict__ sparts, int n_slices, uint32_t fl
   __shared__ float s_sc[kMergeCombineThreads];
   __shared__ float s_tot[4];
   const int ug = blockIdx.x, tid = threadIdx.x;
-  const bool sub = (flags == RMA_MERGE_SUB) && K > 0;
+  const bool sub = (flags == RMA_MERGE_SUB) && K > 0 && K < L_mid;
   const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
   const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
   const float* pb = sparts + (size_t)ug * n_slices * PFL;

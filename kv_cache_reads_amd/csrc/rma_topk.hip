@@ -701,8 +701,6 @@ topk_select_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb
 // ====================================================================== launch
 namespace {
 
-size_t g_lds_limit = 0;
-
 template <typename KT, int D>
 hipError_t launch_scan_g(int G, dim3 grid, hipStream_t st, const float* q, const KT* kb,
                          int64_t ustride, int n_sink, int L_mid, const TopkPlan& pl,
@@ -739,16 +737,11 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
   // left by the kernel's own (static) LDS.  Many (unit, head) blocks with short
   // report lists: 256 threads each, so that several share a CU; otherwise 1024.
   const bool small = kv.n_units * G >= 1024 && (int64_t)pl.n_chunks * pl.r_cap <= 8 * 256;
-  static size_t static_lds[2] = {0, 0};
-  const void* kfn = small ? reinterpret_cast<const void*>(&topk_select_kernel<KT, D, 256>)
-                          : reinterpret_cast<const void*>(&topk_select_kernel<KT, D, kSelThreads>);
-  size_t& sl = static_lds[small ? 1 : 0];
-  if (sl == 0) {
-    hipFuncAttributes attr{};
-    sl = hipFuncGetAttributes(&attr, kfn) == hipSuccess ? attr.sharedSizeBytes : 32 * 1024;
-  }
+  const size_t sl = small ? kernel_static_lds(&topk_select_kernel<KT, D, 256>)
+                           : kernel_static_lds(&topk_select_kernel<KT, D, kSelThreads>);
+  const size_t lds_limit = device_info().lds_per_block;
   int e_max = pl.e_max;
-  if (g_lds_limit > sl) e_max = (int)std::min<size_t>(e_max, (g_lds_limit - sl) / 8);
+  if (lds_limit > sl) e_max = (int)std::min<size_t>(e_max, (lds_limit - sl) / 8);
   const size_t lds = (size_t)std::max(e_max, 1) * 8;
   if (small)
     return launch_kernel("topk_select_kernel", topk_select_kernel<KT, D, 256>,
@@ -766,14 +759,6 @@ hipError_t launch_topk_t(const TopkPlan& pl, const float* q, int G, const rma_kv
 hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
                        const rma_span& sp, const float* kappa, int K, int32_t* idx, float* sel,
                        uint8_t* ws, hipStream_t st) {
-  if (g_lds_limit == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess)
-      g_lds_limit = (size_t)v;
-    else
-      g_lds_limit = 64 * 1024;
-  }
   if (kv.dtype == RMA_BF16) {
     if (kv.d == 64) return launch_topk_t<uint16_t, 64>(pl, q, G, kv, sp, kappa, K, idx, sel, ws, st);
     return launch_topk_t<uint16_t, 128>(pl, q, G, kv, sp, kappa, K, idx, sel, ws, st);

@@ -215,6 +215,31 @@ def test_ideal_factorisation_recovers_full_attention():
             check_y(y[0, g].numpy(), y_full, f"codebook K={K} g={g}")
 
 
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float32])
+def test_whole_mid_retrieved_needs_no_phi_rows(kv_dtype):
+    """K = |M| with the subtraction variant: the residual is exactly zero, so the
+    merge reads no phi_k row and accepts neither rows nor Wk (a regression test:
+    the rows used to be loaded through the NULL pointer).  y equals full
+    attention over the prefill segment and the generated tokens (Eq. 1)."""
+    L, ns, nt, G, ngen = 700, 4, 32, 3, 2
+    k, v, q = _manual_unit(L=L, G=G, ngen=ngen, kv_dtype=kv_dtype)
+    K = L - ns - nt
+    kd, vd, qd = k.to(DEV), v.to(DEV), q.to(DEV)
+    sp = R.Span(L, ns, nt, ngen)
+    kappa = torch.full((1,), float(k[0].float().norm(dim=-1).max()) * 1.001, device=DEV)
+    idx, sel = R.rma_decode_topk(qd, kd, sp, kappa, K)
+    f = torch.ones(1, G, 128, device=DEV)
+    S = torch.zeros(1, 128, 64, device=DEV)
+    u = torch.zeros(1, 128, device=DEV)
+    y, stats = R.rma_decode_merge(qd, f, kd, vd, sp, idx, sel, K, None, S, u, want_stats=True)
+    y = y.cpu()
+    kf, vf = k[0].double().numpy(), v[0].double().numpy()
+    for g in range(G):
+        y_full = O.full_attention(q[0, g].numpy(), kf, vf, L + ngen)
+        check_y(y[0, g].numpy(), y_full, f"K = |M| without phi rows, g={g}")
+    assert torch.all(stats[..., 2] == 0) and torch.all(stats[..., 3] == 0)
+
+
 def test_zero_features_give_selection_only_topk():
     k, v, q = _manual_unit(L=4000, G=3, ngen=2)
     cfgW = torch.randn(1, 128, 64) / 8
