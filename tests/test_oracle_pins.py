@@ -459,3 +459,66 @@ def test_phi_mlp_rounding_mirror_is_exact_on_representable_values():
     p["W_in"][0, 0] = 1.0 + 2.0 ** -12
     x[:, 0] = 1.0
     assert not np.array_equal(O.phi_mlp(x, p, bf16_operands=True), O.phi_mlp(x, p))
+
+
+# ------------------------------------------------------------------ references and diagnostics
+@pytest.mark.parametrize("n_gen", [0, 3])
+def test_full_attention_matches_sdpa_over_exactly_n_tokens(n_gen):
+    """Eq. 1 over [0, L + n_gen): against torch SDPA in float64.  A key planted
+    just past the range would dominate the softmax if it were included, and the
+    last in-range key dominates if it were dropped, so an off-by-one in the
+    token count fails by far more than the tolerance."""
+    L, d = 50, 8
+    q, K, V, _, _ = _unit(91, L=L, n_gen=n_gen + 1, d=d)
+    n = L + n_gen
+    qh = q / np.linalg.norm(q)
+    K[n] = 40.0 * qh               # outside: must not count
+    K[n - 1] = 6.0 * qh            # inside: carries most of the weight
+    got = O.full_attention(q, K, V, n)
+    np.testing.assert_allclose(got, _sdpa(q, K[:n], V[:n]), rtol=0, atol=1e-13)
+    assert np.abs(got - _sdpa(q, K[:n + 1], V[:n + 1])).max() > 1e-2
+    assert np.abs(got - _sdpa(q, K[:n - 1], V[:n - 1])).max() > 1e-2
+
+
+def test_kappa_max_matches_scalar_loops():
+    """The largest key 2-norm, by plain Python loops over rows and components."""
+    r = _rng(92)
+    K = r.standard_normal((37, 8))
+    K[36] *= 5.0                    # the maximum sits on the last row
+    ref = max(math.sqrt(sum(float(x) * float(x) for x in row)) for row in K)
+    assert O.kappa_max(K) == pytest.approx(ref, rel=1e-15)
+    assert O.kappa_max(np.zeros((0, 8))) == 0.0
+    assert O.kappa_max(np.array([[3.0, -4.0]])) == 5.0
+
+
+def test_rel_l1_hand_computed_pair():
+    """sum |y - y_ref| / sum |y_ref| (§7.1 Table 3 metric): |(1,-2,3) - (2,-2,1)|_1
+    = 3 over |(2,-2,1)|_1 = 5.  Dividing by the other vector's norm would give
+    3/6, by the 2-norm 3/3."""
+    assert O.rel_l1([1.0, -2.0, 3.0], [2.0, -2.0, 1.0]) == pytest.approx(0.6, rel=1e-15)
+    assert O.rel_l1([2.0, -2.0, 1.0], [1.0, -2.0, 3.0]) == pytest.approx(0.5, rel=1e-15)
+
+
+def test_log_partition_error_sign():
+    """log Z_R_hat - log Z_R (§7.1 Table 3, §7.2): negative for an
+    under-estimate.  Z_R_hat = Z_R / e gives exactly -1, Z_R * e^2 gives +2."""
+    Z = 123.25
+    assert O.log_partition_error(Z / math.e, Z) == pytest.approx(-1.0, abs=1e-14)
+    assert O.log_partition_error(Z * math.e ** 2, Z) == pytest.approx(2.0, abs=1e-14)
+
+
+@pytest.mark.parametrize("Kret", [1, 7, 30, 72])
+def test_nosub_under_ideal_features_double_counts_the_retrieved_tokens(Kret):
+    """NoSub (§5.2 Table 1 caption: the variant leaves out the retrieved-token
+    subtraction).  Under the codebook features of Eq. 7, S^T f and u^T f are
+    the exact whole-mid sums, so NoSub gives (N_full + nu_K) / (Z_full + Z_K):
+    softmax attention over the whole context with the retrieved keys counted a
+    second time.  SDPA over that multiset pins it; a NoSub that still
+    subtracted would equal full attention instead."""
+    L, ns, nt, n_gen = 80, 2, 5, 2
+    q, K, V, Pk, f, S, u = _codebook_unit(41, L=L, ns=ns, nt=nt, n_gen=n_gen)
+    y_ns, idx, _ = O.decode_query(q, f, K, V, Pk, S, u, L, ns, nt, n_gen, K=Kret, variant="nosub")
+    Kd = np.concatenate([K, K[idx]])
+    Vd = np.concatenate([V, V[idx]])
+    np.testing.assert_allclose(y_ns, _sdpa(q, Kd, Vd), rtol=0, atol=1e-12)
+    assert np.abs(y_ns - _sdpa(q, K, V)).max() > 1e-4
