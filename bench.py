@@ -404,7 +404,7 @@ def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
                 hu = host(uidx)                      # host copy, not timed
                 t1 = time.perf_counter()
                 if mlp_mode:
-                    P = O.round_bf16(O.phi_mlp(hu["k"][M], hp(pk, uidx % cfg.P), bf16_operands=True))
+                    P = O.phi_mlp(hu["k"][M], hp(pk, uidx % cfg.P))
                     S, uu = O.summaries(P, hu["v"][M])
                 else:
                     P, S, uu = O.prefill_unit(hu["k"][M], hu["v"][M], hu["W"], hu["b"])
@@ -412,7 +412,7 @@ def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
                     for g in range(cfg.G):
                         q = hu["q"][s, g]
                         if mlp_mode:
-                            f = O.phi_mlp(q[None], hp(pq, uidx % cfg.P * cfg.G + g), bf16_operands=True)[0]
+                            f = O.phi_mlp(q[None], hp(pq, uidx % cfg.P * cfg.G + g))[0]
                         else:
                             f = O.phi_features(q[None], hu["W"], hu["b"])[0]
                         O.decode_query(q, f, hu["k"], hu["v"], P, S, uu, cfg.L, cfg.n_sink, cfg.n_tail,

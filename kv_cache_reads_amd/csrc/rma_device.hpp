@@ -215,12 +215,18 @@ __device__ __forceinline__ uint64_t ord_f64(double x) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// ---------------------------------------------------------------- exact-ish dot
+// ---------------------------------------------------------------- band dot
 // Double-double dot product of an fp32 query with a stored key row.  Every
-// product q_j*k_j is exact in fp64 (24x8 or 24x24 significand bits); TwoSum
-// keeps the rounding error of each addition, so (hi, lo) carries the sum with
-// error of order d * 2^-106 * sum|q_j k_j|.  Distinct exact scores further apart
-// than that are ordered correctly; identical keys give bitwise identical pairs.
+// product q_j*k_j is exact in fp64 (24x8 or 24x24 significand bits, exponents
+// far inside fp64's range).  TwoSum keeps the rounding error of each addition
+// exactly, so the only rounding is in c, the plain fp64 sum of those errors.
+// Each error is a multiple of 2^E (E = the lowest last-bit exponent among the
+// nonzero products) and below half an ulp of the running sum, so c is exact
+// whenever the products' last bits span at most 58 - 2 log2(d) binades (46 at
+// d = 64, 44 at d = 128).  Then (hi, lo) is the canonical pair of the exact
+// score and comparing pairs is exact; identical keys always give identical
+// pairs.  Otherwise the pair is within (d + 2) 2^-106 sum|q_j k_j| of the exact
+// score, and only distinct scores closer than twice that can be misordered.
 struct DD { double hi, lo; };
 
 __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {

@@ -96,7 +96,7 @@ def round_bf16(x) -> np.ndarray:
     return np.where(np.isnan(f), np.nan, out)
 
 
-def phi_mlp(x, params, bf16_operands: bool = False) -> np.ndarray:
+def phi_mlp(x, params, bf16_operands: bool = False, return_terms: bool = False, operand_round=None):
     """The pages' feature-map family (f4), row-wise over x.
 
     Page §4.4 ("Training phi"): phi_q and phi_k are head-specific one-block
@@ -119,17 +119,31 @@ def phi_mlp(x, params, bf16_operands: bool = False) -> np.ndarray:
     bf16_operands, every operand of a matrix product (the weights, x, h0, the
     activation and h1) is first rounded to bfloat16, as the GPU kernel's
     matrix-core products take them; biases, alpha, the residual sum and the
-    exponential stay exact.
+    exponential stay exact.  With return_terms, also returns the intermediate
+    values (x, h0, r = W_1 h0 + b_1, a = relu(r), t = W_2 a + b_2, h1, z =
+    W_o h1 + b_o) and the matrices used, for error analysis.  operand_round, a
+    function applied at those same rounding points in place of the bfloat16
+    rounding, serves the error model of the tests.
     """
-    rb = round_bf16 if bf16_operands else (lambda a: _f64(a))
+    if operand_round is not None:
+        rb = operand_round
+    else:
+        rb = round_bf16 if bf16_operands else (lambda a: _f64(a))
     W_in, W_1, W_2, W_o = (rb(params[k]) for k in ("W_in", "W_1", "W_2", "W_o"))
     b_in, b_1, b_2, b_o = (_f64(params[k]) for k in ("b_in", "b_1", "b_2", "b_o"))
     alpha = float(params["alpha"])
     x = rb(x)
     h0 = rb(x @ W_in.T + b_in)
-    a = rb(np.maximum(h0 @ W_1.T + b_1, 0.0))
-    h1 = rb(h0 + alpha * (a @ W_2.T + b_2))
-    return np.exp(h1 @ W_o.T + b_o)
+    r = h0 @ W_1.T + b_1
+    a = rb(np.maximum(r, 0.0))
+    t = a @ W_2.T + b_2
+    h1 = rb(h0 + alpha * t)
+    z = h1 @ W_o.T + b_o
+    phi = np.exp(z)
+    if return_terms:
+        return phi, dict(x=x, h0=h0, r=r, a=a, t=t, h1=h1, z=z, W_in=W_in, W_1=W_1, W_2=W_2,
+                         W_o=W_o, alpha=alpha)
+    return phi
 
 
 def phi_mlp_param_count(d_h: int, width: int = 512, d_phi: int = 64) -> int:

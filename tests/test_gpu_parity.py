@@ -323,83 +323,103 @@ def test_workspace_reuse_across_unit_counts():
 
 
 # ------------------------------------------------------------------ adversarial selection
+# Every adversarial case runs for both head dims and both key dtypes: the scan,
+# the select's band rescoring and the exact fallback are instantiated per
+# (key dtype, d).
+KEY_KINDS = [(64, torch.bfloat16), (128, torch.bfloat16), (64, torch.float32), (128, torch.float32)]
+KEY_IDS = [f"d{d}-{str(t).split('.')[-1]}" for d, t in KEY_KINDS]
+
+
 def _topk_case(k, q, L, ns, nt, K, units=(0,)):
+    d = k.shape[2]
     kd = k.to(DEV)
     v = torch.zeros_like(k)
-    pre = R.rma_build_summaries(kd, v.to(DEV), R.Span(L, ns, nt, 0), torch.randn(1, 64, 64, device=DEV) / 8,
+    pre = R.rma_build_summaries(kd, v.to(DEV), R.Span(L, ns, nt, 0), torch.randn(1, 64, d, device=DEV) / 8,
                                 torch.zeros(1, 64, device=DEV))
     idx, sel = R.rma_decode_topk(q.to(DEV), kd, R.Span(L, ns, nt, 0), pre[3], K)
     for u in units:
-        kf = k[u].float().double().numpy()
+        kf = k[u].double().numpy()
         for g in range(q.shape[1]):
             ref = O.topk_indices(q[u, g].numpy(), kf[ns:L - nt], K, first_index=ns)
             got = idx[u, g].cpu().numpy()
             assert np.array_equal(got, ref), \
-                f"K={K} unit {u} head {g}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
+                f"d={d} {k.dtype} K={K} unit {u} head {g}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
             # selected scores are the fp32 scores of the selected tokens
-            s_ref = kf[got] @ q[u, g].double().numpy() / 8.0
+            s_ref = kf[got] @ q[u, g].double().numpy() / math.sqrt(d)
             assert np.allclose(sel[u, g].cpu().numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
     return idx
 
 
+def _one_ulp_apart(base, i, dtype):
+    """A copy of `base` (already in `dtype`) with component i % d moved by -1, 0
+    or +1 unit in the last place of that dtype."""
+    kk = base.clone()
+    if dtype == torch.bfloat16:
+        kk.view(torch.int16)[i % kk.numel()] += (i % 3) - 1
+    else:
+        kk.view(torch.int32)[i % kk.numel()] += (i % 3) - 1
+    return kk.float()
+
+
+@pytest.mark.parametrize("d,dtype", KEY_KINDS, ids=KEY_IDS)
 @pytest.mark.parametrize("K", [1, 7, 300, 1999, 2000 - 36 - 1, 2000 - 36])
-def test_topk_all_equal_keys(K):
+def test_topk_all_equal_keys(K, d, dtype):
     L, ns, nt = 2000, 4, 32
-    k = torch.ones(1, L, 64).bfloat16()
-    q = torch.randn(1, 2, 64)
+    k = torch.ones(1, L, d).to(dtype)
+    q = torch.randn(1, 2, d)
     if K <= L - ns - nt:
         _topk_case(k, q, L, ns, nt, K)
 
 
-def test_topk_planted_ties_and_near_ties_at_the_boundary():
+@pytest.mark.parametrize("d,dtype", KEY_KINDS, ids=KEY_IDS)
+def test_topk_planted_ties_and_near_ties_at_the_boundary(d, dtype):
     L, ns, nt, K = 6000, 4, 64, 50
     g = torch.Generator().manual_seed(3)
-    k = torch.randn(1, L, 64, generator=g)
-    q = torch.randn(1, 4, 64, generator=g)
+    k = torch.randn(1, L, d, generator=g)
+    q = torch.randn(1, 4, d, generator=g)
     qh = q[0, 0] / q[0, 0].norm()
     # 60 copies of one key straddle the K-th boundary (exact ties -> lower index)
     pos = torch.randperm(L - ns - nt, generator=g)[:60] + ns
-    k[0, pos] = (3.0 * qh).bfloat16().float()
-    # near-ties: keys one bf16 ulp apart in one component
-    base = (2.5 * qh).bfloat16()
+    k[0, pos] = (3.0 * qh).to(dtype).float()
+    # near-ties: keys one ulp (of the key dtype) apart in one component
+    base = (2.5 * qh).to(dtype)
     pos2 = torch.randperm(L - ns - nt, generator=g)[:40] + ns
     for i, p in enumerate(pos2.tolist()):
-        kk = base.clone()
-        bits = kk.view(torch.int16)
-        bits[i % 64] += (i % 3) - 1
-        k[0, p] = kk.float()
-    _topk_case(k.bfloat16(), q, L, ns, nt, K)
-    _topk_case(k.bfloat16(), q, L, ns, nt, 75)
+        k[0, p] = _one_ulp_apart(base, i, dtype)
+    _topk_case(k.to(dtype), q, L, ns, nt, K)
+    _topk_case(k.to(dtype), q, L, ns, nt, 75)
 
 
-def test_topk_sorted_keys_force_fallback():
+@pytest.mark.parametrize("d,dtype", KEY_KINDS, ids=KEY_IDS)
+def test_topk_sorted_keys_force_fallback(d, dtype):
     # scores increase with position: every chunk holds only top tokens at its end;
     # the per-chunk reports cannot certify completeness and the exact path runs
     L, ns, nt = 3000, 4, 32
-    q = torch.zeros(1, 1, 64)
+    q = torch.zeros(1, 1, d)
     q[0, 0, 0] = 1.0
-    k = torch.zeros(1, L, 64)
+    k = torch.zeros(1, L, d)
     k[0, :, 0] = torch.linspace(-2, 2, L)
-    _topk_case(k.bfloat16(), q, L, ns, nt, 500)
-    _topk_case(k.bfloat16(), q, L, ns, nt, 5)
+    _topk_case(k.to(dtype), q, L, ns, nt, 500)
+    _topk_case(k.to(dtype), q, L, ns, nt, 5)
 
 
-def test_topk_many_units_use_small_select_blocks():
+@pytest.mark.parametrize("d,dtype", KEY_KINDS, ids=KEY_IDS)
+def test_topk_many_units_use_small_select_blocks(d, dtype):
     """U*G >= 1024 (query heads) selects with 256-thread blocks: the tie and
     near-tie case and the forced exact fallback on that path."""
     L, ns, nt, U, G = 3000, 4, 32, 256, 4
     g = torch.Generator().manual_seed(5)
-    k = torch.randn(U, L, 64, generator=g)
-    q = torch.randn(U, G, 64, generator=g)
+    k = torch.randn(U, L, d, generator=g)
+    q = torch.randn(U, G, d, generator=g)
     qh = q[0, 0] / q[0, 0].norm()
     pos = torch.randperm(L - ns - nt, generator=g)[:40] + ns
-    k[0, pos] = (3.0 * qh).bfloat16().float()           # exact ties at the boundary in unit 0
+    k[0, pos] = (3.0 * qh).to(dtype).float()            # exact ties at the boundary in unit 0
     k[U - 1, :, 0] = torch.linspace(-2, 2, L)            # unit U-1: sorted scores for head 0 ...
     k[U - 1, :, 1:] = 0.0
     q[U - 1, 0] = 0.0
     q[U - 1, 0, 0] = 1.0                                  # ... which forces the exact fallback
-    _topk_case(k.bfloat16(), q, L, ns, nt, 30, units=(0, 17, U - 1))
-    _topk_case(k.bfloat16(), q, L, ns, nt, 500, units=(0, U - 1))
+    _topk_case(k.to(dtype), q, L, ns, nt, 30, units=(0, 17, U - 1))
+    _topk_case(k.to(dtype), q, L, ns, nt, 500, units=(0, U - 1))
 
 
 def _select_layout(L, ns, nt, U, G, K, d=64):

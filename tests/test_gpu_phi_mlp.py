@@ -1,29 +1,29 @@
 """GPU parity of the pages' MLP feature map (one-block ReZero MLP, exponentiated
-output; page §4.4, App. C.1, §8) and of the decode path built on it.
+output; page §4.4, App. C.1, §8) and of the decode path built on it, against
+the plain fp64 definition (oracle.phi_mlp without any rounding).
 
-Feature rows: the kernel multiplies bf16 operands with fp32 sums; the oracle
-(oracle.phi_mlp with bf16_operands) rounds the same operands at the same
-points and sums in float64.  What remains is fp32 summation order.  Almost
-everywhere it changes a feature by ~1e-6 relative; where it moves an
-intermediate value (h0, the activation, h1) across a bf16 rounding boundary,
-that element changes by one bf16 step (2^-8 relative) and the exponent of the
-features that read it by up to |W_o| |h1| 2^-8 (~1.5e-3 at these weight
-scales; a row can take a few such steps).  The bar, per row set: every feature
-within 1e-2 relative (those steps), and the bulk exact: bf16 rows at least
-90 % bit-identical to the rounded oracle value, fp32 rows with a median
-relative error <= 2e-4.  A systematic mistake (a dropped bias or term, a wrong
-scale) moves every feature and fails the second part.
+Feature rows: the kernel multiplies bf16 operands (x, the weights, h0, the
+activation, h1, each rounded to nearest even) with fp32 sums, so its features
+differ from the definition by the propagated rounding.  The per-feature
+tolerance comes from the rounding model of tests/mlp_bound.py: 8 standard
+deviations of the exponent's change when every rounding point gets an
+independent relative error uniform in [-2^-8, 2^-8], plus fp32 summation and
+the storage rounding of bf16 rows.  A systematic mistake (a dropped bias or
+term, a wrong scale) moves the exponents by far more.  How often the kernel's
+rows equal the oracle's rounding mirror (oracle.phi_mlp with bf16_operands)
+is logged as a statistic, not asserted.
 
 Path: phi_k rows from the kernel feed the summary build (rows injected), f =
-phi_q(q) from the kernel feeds the merge.  The oracle computes its own rows and
-features; the decode output meets the usual bar (bit-exact Top-K, 2e-3 abs /
-1e-2 rel).
+phi_q(q) from the kernel feeds the merge.  The oracle computes its own rows,
+summaries and features from the plain definition; the decode output meets the
+usual bar (bit-exact Top-K, 2e-3 abs / 1e-2 rel).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+from mlp_bound import check_rows
 from parity_util import R, W, check_y, decode_span, log, prefill_span
 
 pytestmark = pytest.mark.gpu
@@ -34,18 +34,24 @@ def _host_params(params, p):
     return {k: v[p].double().cpu().numpy() if v.dim() > 1 else float(v[p]) for k, v in params.items()}
 
 
-def _check_rows(got, ref, bf16, what):
+def _check_rows(got, x, params, bf16, what):
+    """got: the kernel's rows for inputs x (float64 [rows, d]); the plain
+    definition with the rounding-model tolerance, and the mirror statistic."""
     got = got.double().cpu().numpy()
-    rel = np.abs(got - ref) / ref
-    assert (ref > 0).all() and (got > 0).all(), f"{what}: non-positive feature"
-    assert rel.max() <= 1e-2, f"{what}: worst relative error {rel.max():.2e} (tol 1e-2)"
+    try:
+        ratio, med = check_rows(got, x, params, bf16)
+    except AssertionError as e:
+        raise AssertionError(f"{what}: {e}") from None
+    mirror = O.phi_mlp(x, params, bf16_operands=True)
     if bf16:
-        same = float((got == O.round_bf16(ref)).mean())
-        assert same >= 0.9, f"{what}: only {same:.3f} of the bf16 rows equal the rounded oracle"
+        same = float((got == O.round_bf16(mirror)).mean())
+        log(f"{what}: worst {ratio:.2f} of the tolerance, median rel {med:.2e} vs the definition; "
+            f"{same:.3f} of the rows bit-identical to the rounding mirror")
     else:
-        same = float(np.median(rel))
-        assert same <= 2e-4, f"{what}: median relative error {same:.2e} (tol 2e-4)"
-    return float(rel.max()), same
+        same = float(np.median(np.abs(got - mirror) / mirror))
+        log(f"{what}: worst {ratio:.2f} of the tolerance, median rel {med:.2e} vs the definition; "
+            f"median rel {same:.2e} vs the rounding mirror")
+    return ratio
 
 
 # (d, m, x dtype, phi dtype, units, rows, param sets)
@@ -72,13 +78,17 @@ def test_phi_mlp_rows_match_oracle(shape):
     xs[:, :rows] = xg
     phi = R.rma_phi_mlp_features(xs[:, :rows], w, phi_dtype=pdt)
     torch.cuda.synchronize()
-    # all rows of the call together (a rounding step moves a whole row, and a
-    # unit may hold one row only)
-    ref = np.stack([O.phi_mlp(xg[u].double().cpu().numpy(), _host_params(params, u % P), bf16_operands=True)
-                    for u in range(U)])
-    worst, bulk = _check_rows(phi, ref, pdt == torch.bfloat16, f"d{d} m{m} U{U} rows {rows}")
-    log(f"phi_mlp d{d} m{m}: worst rel {worst:.2e}, " +
-        (f"bf16-identical {bulk:.3f}" if pdt == torch.bfloat16 else f"median rel {bulk:.2e}"))
+    for u in range(U):
+        _check_rows(phi[u], xg[u].double().cpu().numpy(), _host_params(params, u % P), pdt == torch.bfloat16,
+                    f"phi_mlp d{d} m{m} unit {u} of {U}, {rows} rows")
+
+
+def _sample_rows(n, seed, k=384):
+    """Seeded sample of row indices (the rounding model's trials cost a few
+    forward passes per row), always with the first and last row."""
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(n, size=min(k, n), replace=False)
+    return np.unique(np.concatenate([pick, [0, n - 1]]))
 
 
 def _mlp_path(cfg, K, steps):
@@ -122,14 +132,15 @@ def test_decode_with_mlp_features_matches_oracle(name):
         v = inp.v[uu].float().cpu().numpy().astype(np.float64)
         mid = slice(cfg.n_sink, cfg.n_sink + cfg.L_mid)
         hk = _host_params(pk, uu % cfg.P)
-        phi_ref = O.round_bf16(O.phi_mlp(k[mid], hk, bf16_operands=True))   # stored as bf16
-        _check_rows(phi_k[uu], phi_ref, True, f"{name} phi_k unit {uu}")
+        phi_ref = O.phi_mlp(k[mid], hk)                                     # the plain definition
+        rows = _sample_rows(cfg.L_mid, uu)
+        _check_rows(phi_k[uu][torch.from_numpy(rows).to(phi_k.device)], k[mid][rows], hk, True, f"{name} phi_k unit {uu} ({rows.size} rows)")
         S, u_ = O.summaries(phi_ref, v[mid])
         for s, idx, y in outs:
             for g in range(cfg.G):
                 q = inp.q[s, uu, g].double().cpu().numpy()
                 hq = _host_params(pq, (uu % cfg.P) * cfg.G + g)
-                f = O.phi_mlp(q[None], hq, bf16_operands=True)[0]
+                f = O.phi_mlp(q[None], hq)[0]
                 y_ref, idx_ref, _ = O.decode_query(q, f, k, v, phi_ref, S, u_, cfg.L, cfg.n_sink, cfg.n_tail,
                                                    cfg.n_gen(s), K)
                 assert np.array_equal(idx[uu, g].numpy().astype(np.int64), idx_ref)
@@ -149,13 +160,15 @@ def test_full_c1_with_mlp_features_sampled_units():
         k = inp.k[uu].float().cpu().numpy().astype(np.float64)
         v = inp.v[uu].float().cpu().numpy().astype(np.float64)
         mid = slice(cfg.n_sink, cfg.n_sink + cfg.L_mid)
-        phi_ref = O.round_bf16(O.phi_mlp(k[mid], _host_params(pk, uu % cfg.P), bf16_operands=True))
-        _check_rows(phi_k[uu], phi_ref, True, f"c1 phi_k unit {uu}")
+        hk = _host_params(pk, uu % cfg.P)
+        phi_ref = O.phi_mlp(k[mid], hk)                                     # the plain definition
+        rows = _sample_rows(cfg.L_mid, uu)
+        _check_rows(phi_k[uu][torch.from_numpy(rows).to(phi_k.device)], k[mid][rows], hk, True, f"c1 phi_k unit {uu} ({rows.size} rows)")
         S, u_ = O.summaries(phi_ref, v[mid])
         _, idx, y = outs[0]
         for g in range(cfg.G):
             q = inp.q[0, uu, g].double().cpu().numpy()
-            f = O.phi_mlp(q[None], _host_params(pq, (uu % cfg.P) * cfg.G + g), bf16_operands=True)[0]
+            f = O.phi_mlp(q[None], _host_params(pq, (uu % cfg.P) * cfg.G + g))[0]
             y_ref, idx_ref, _ = O.decode_query(q, f, k, v, phi_ref, S, u_, cfg.L, cfg.n_sink, cfg.n_tail, 0, K)
             assert np.array_equal(idx[uu, g].numpy().astype(np.int64), idx_ref)
             check_y(y[uu, g].numpy(), y_ref, f"c1 mlp u{uu} g{g}")
