@@ -41,11 +41,11 @@
  *    nothing is launched and the outputs are untouched.  rma_last_error()
  *    gives a message for the calling thread's last failed call.
  *  - Workspace: calls that need scratch take (workspace, workspace_bytes);
- *    rma_workspace_bytes() gives the size.  The first RMA_WORKSPACE_COUNTER_BYTES
- *    bytes of every workspace hold completion counters that must be zero
- *    before the first use (e.g. allocate it zero-filled); every call leaves
- *    them zero again, so one workspace can serve any sequence of calls on one
- *    stream.  Calls that may run concurrently need distinct workspaces.
+ *    rma_workspace_bytes() gives the size.  A workspace holds per-call scratch
+ *    only: every byte a call's kernels read from it is written earlier in the
+ *    same call, so it needs no initialisation and one workspace can serve any
+ *    sequence of calls on one stream.  Calls that may run concurrently need
+ *    distinct workspaces.
  *  - NaN/Inf inputs are not checked; outputs are then unspecified (no fault).
  */
 #ifndef RMA_H_
@@ -58,10 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 7
-
-/* Leading bytes of every workspace that hold completion counters. */
-#define RMA_WORKSPACE_COUNTER_BYTES 262144
+#define RMA_ABI_VERSION 8
 
 /* Most events one kernel trace can hold (rma_trace_arm). */
 #define RMA_TRACE_MAX_EVENTS 16

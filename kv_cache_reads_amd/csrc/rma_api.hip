@@ -10,7 +10,6 @@
 #include "rma_internal.hpp"
 
 namespace rma {
-static_assert(kCounterBytes == RMA_WORKSPACE_COUNTER_BYTES, "counter region size");
 static_assert(kTraceMax == RMA_TRACE_MAX_EVENTS, "trace size");
 
 KernelTrace& trace() {
@@ -138,7 +137,7 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);
   }
-  size_t off = counter_bytes(U);
+  size_t off = 0;
   const size_t nc = (size_t)std::max(p.n_chunks, 1);
   p.off_S = off;
   off = align_up(off + (size_t)U * nc * m * kv.d * 4);
@@ -176,7 +175,7 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
     }
     p.e_max = (int)std::min<int64_t>(kSelMaxEntries, (int64_t)p.n_chunks * p.r_cap);
   }
-  size_t off = counter_bytes(U);
+  size_t off = 0;
   p.off_ent = off;
   off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * std::max(p.r_cap, 1) * 8);
   p.off_meta = off;
@@ -200,7 +199,7 @@ FullPlan plan_full(const rma_kv& kv, const rma_span& sp, int G) {
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(T, ch);
   }
-  size_t off = counter_bytes(U);
+  size_t off = 0;
   p.off_part = off;
   off = align_up(off + (size_t)U * std::max(p.n_chunks, 1) * G * (kFullRecHead + kv.d) * 4);
   p.total = off;
@@ -229,7 +228,7 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) 
   p.sl = (int)ceil_div(T, ns);
   p.n_slices = (int)ceil_div(T, p.sl);   // no empty slice
   p.part_floats = p.n_slices > 1 ? 4 + 3 * kv.d : 0;
-  p.off_part = counter_bytes(U);
+  p.off_part = 0;
   p.total = align_up(p.off_part + (size_t)heads * p.n_slices * p.part_floats * 4);
   return p;
 }

@@ -18,11 +18,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Completion counters (one uint32 per unit, up to the 65535-unit limit) lead
-// every workspace at a fixed size, so that scratch written by one call never
-// lands on counters another call (with a different unit count) relies on.
-constexpr size_t kCounterBytes = 65536 * 4;
-inline size_t counter_bytes(int64_t /*n_units*/) { return kCounterBytes; }
+// Workspaces hold per-call scratch only: every byte a kernel reads from one is
+// written earlier in the same call, so a workspace needs no initialisation.
 
 // ------------------------------------------------------------- device
 // Properties of the calling thread's current HIP device, queried once per

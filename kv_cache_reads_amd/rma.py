@@ -24,7 +24,6 @@ RMA_F32, RMA_BF16 = 0, 1
 RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE, RMA_OP_DECODE_FULL = 1, 2, 3, 4
 RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
 RMA_BUILD_ACCUMULATE = 1
-RMA_WORKSPACE_COUNTER_BYTES = 262144
 
 
 class RmaError(RuntimeError):
@@ -145,8 +144,9 @@ def _kv(k: torch.Tensor, v: Optional[torch.Tensor]) -> _KV:
 
 
 class Workspace:
-    """A zero-initialised device buffer reused across calls on one stream (the
-    library leaves its counters zeroed after every call)."""
+    """A device buffer reused across calls on one stream.  It holds per-call
+    scratch only (every byte a call reads is written earlier in that call), so
+    it needs no initialisation."""
 
     def __init__(self, device=None):
         self.device = device
@@ -154,7 +154,7 @@ class Workspace:
 
     def get(self, nbytes: int) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8,
+            self.buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8,
                                    device=self.device or torch.device("cuda"))
         return self.buf
 

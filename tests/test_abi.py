@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 7
+    assert L.rma_abi_version() == 8
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -163,7 +163,7 @@ def test_full_validation_errors():
     assert _full(kv, sp, wsb=16) == R.RMA_ERR_WORKSPACE
     assert _full(_kv(T=1000), sp) == R.RMA_ERR_INVALID_ARG                 # t_cap < L
     n = L.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, ctypes.byref(kv), ctypes.byref(sp), 2, 0, 0)
-    assert n > R.RMA_WORKSPACE_COUNTER_BYTES
+    assert n > 0
     assert L.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, ctypes.byref(kv), ctypes.byref(sp), 4, 0, 0) > n
     assert _full(kv, sp, wsb=n - 1) == R.RMA_ERR_WORKSPACE
 
