@@ -307,7 +307,8 @@ rma_status rma_decode_full(const float* q, int32_t G, const rma_kv* kv, const rm
                            const int32_t* idx, int32_t K, const float* y_cmp, float* y_full,
                            float* diag, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for `op` (one of RMA_OP_*); 0 on invalid arguments.  G and K
+/* Workspace bytes for `op` (one of RMA_OP_*), at least 256; 0 on invalid
+ * arguments.  G and K
  * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK
  * and RMA_OP_DECODE_FULL; K is ignored for RMA_OP_DECODE_FULL. */
 size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* span, int32_t G,

@@ -145,7 +145,7 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
   off = align_up(off + (size_t)U * nc * m * 4);
   p.off_kap = off;
   off = align_up(off + (size_t)U * nc * 4);
-  p.total = off;
+  p.total = std::max(off, kAlign);   // never 0: 0 means invalid arguments
   return p;
 }
 
@@ -182,7 +182,7 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   off = align_up(off + (size_t)U * G * std::max(p.n_chunks, 1) * 8);
   p.off_hp = off;
   off = align_up(off + (size_t)U * G * 16);
-  p.total = off;
+  p.total = std::max(off, kAlign);   // never 0: 0 means invalid arguments
   p.sel_lds = align_up((size_t)p.e_max * 8 + 16, 16);
   return p;
 }
@@ -202,7 +202,7 @@ FullPlan plan_full(const rma_kv& kv, const rma_span& sp, int G) {
   size_t off = 0;
   p.off_part = off;
   off = align_up(off + (size_t)U * std::max(p.n_chunks, 1) * G * (kFullRecHead + kv.d) * 4);
-  p.total = off;
+  p.total = std::max(off, kAlign);   // never 0: 0 means invalid arguments
   return p;
 }
 
@@ -229,7 +229,7 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) 
   p.n_slices = (int)ceil_div(T, p.sl);   // no empty slice
   p.part_floats = p.n_slices > 1 ? 4 + 3 * kv.d : 0;
   p.off_part = 0;
-  p.total = align_up(p.off_part + (size_t)heads * p.n_slices * p.part_floats * 4);
+  p.total = std::max(align_up(p.off_part + (size_t)heads * p.n_slices * p.part_floats * 4), kAlign);
   return p;
 }
 
