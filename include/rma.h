@@ -307,6 +307,28 @@ rma_status rma_decode_full(const float* q, int32_t G, const rma_kv* kv, const rm
                            const int32_t* idx, int32_t K, const float* y_cmp, float* y_full,
                            float* diag, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rma_decode_topk_static -- rma_decode_topk with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call's scratch
+ * lives in a device array the library owns, RMA_STATIC_SCRATCH_BYTES on every
+ * GPU the library runs on (held until the process ends); the call itself
+ * allocates and frees nothing.  Arguments, results and errors are those of
+ * rma_decode_topk, plus RMA_ERR_WORKSPACE (before anything is enqueued) when
+ * the call needs more scratch than the array holds, i.e. when
+ * rma_workspace_bytes(RMA_OP_DECODE_TOPK, ...) exceeds RMA_STATIC_SCRATCH_BYTES
+ * (the 1B and 3B single-layer workloads at 32K and 64K fit), and RMA_ERR_HIP
+ * when the array's address cannot be obtained on the current device.  Every
+ * call on one GPU uses that GPU's one array: calls that may overlap on one GPU
+ * (other streams, other threads) race, and the caller must serialise them.
+ * Nothing in the array needs to start at zero: every byte a call reads from it
+ * is written earlier in the same call.
+ */
+#define RMA_STATIC_SCRATCH_BYTES (16u << 20)
+rma_status rma_decode_topk_static(const float* q, int32_t G, const rma_kv* kv, const rma_span* span,
+                                  const float* kappa, int32_t K, int32_t* idx, float* sel_scores,
+                                  void* stream);
+
 /* Workspace bytes for `op` (one of RMA_OP_*), at least 256; 0 on invalid
  * arguments.  G and K
  * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK

@@ -105,6 +105,40 @@ const DeviceInfo& device_info() {
   return info[dev];
 }
 
+// ------------------------------------------------------------- static scratch
+// Scratch of rma_decode_topk_static: one array per GPU (the runtime places a
+// copy of every __device__ variable on each device the code object is loaded
+// on).  In host code `scratch` names a host-side stand-in, not a device
+// address, so it is never passed to a kernel or a copy: its address on the
+// current device is obtained once per device (with that device current) and
+// kept per device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+struct StaticScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+StaticScratch g_static_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StaticScratch& s = g_static_scratch[dev];
+  std::call_once(s.once, [&s] {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    s.ptr = s.err == hipSuccess ? p : nullptr;
+  });
+  *ptr = s.ptr;
+  return s.err;
+}
+
 // ------------------------------------------------------------- plans
 BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi, int phi_dtype) {
   BuildPlan p{};
@@ -429,6 +463,35 @@ rma_status rma_decode_topk(const float* q, int32_t G, const rma_kv* kv, const rm
             workspace_bytes, pl.total);
   TraceScope ts((hipStream_t)stream);
   hipError_t e = launch_topk(pl, q, G, *kv, *sp, kappa, K, idx, sel_scores, (uint8_t*)workspace,
+                             (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_decode_topk_static(const float* q, int32_t G, const rma_kv* kv, const rma_span* sp,
+                                  const float* kappa, int32_t K, int32_t* idx, float* sel_scores,
+                                  void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, false);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(G >= 1 && G <= 8, RMA_ERR_UNSUPPORTED, "G %d not in 1..8", G);
+  RMA_CHECK(K >= 0 && K <= l_mid(*sp), RMA_ERR_INVALID_ARG, "K %d outside [0, L_mid=%lld]", K,
+            (long long)l_mid(*sp));
+  if (K == 0) return RMA_OK;
+  RMA_CHECK(q && kappa && idx && sel_scores, RMA_ERR_INVALID_ARG, "NULL pointer argument");
+  RMA_CHECK(aligned16(q) && aligned16(kappa) && aligned16(idx) && aligned16(sel_scores),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  TopkPlan pl = plan_topk(*kv, *sp, G, K);
+  RMA_CHECK(pl.n_chunks <= kSelMaxChunks, RMA_ERR_UNSUPPORTED, "mid-region too long for G=%d", G);
+  RMA_CHECK(pl.total <= kStaticScratchBytes, RMA_ERR_WORKSPACE,
+            "this call needs %zu bytes of scratch, more than the library's static %zu",
+            pl.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  const hipError_t se = static_scratch(&ws);
+  RMA_CHECK(se == hipSuccess && ws != nullptr, RMA_ERR_HIP,
+            "address of the static scratch on this device: %s", hipGetErrorString(se));
+  TraceScope ts((hipStream_t)stream);
+  hipError_t e = launch_topk(pl, q, G, *kv, *sp, kappa, K, idx, sel_scores, (uint8_t*)ws,
                              (hipStream_t)stream);
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return RMA_OK;

@@ -33,6 +33,11 @@ struct DeviceInfo {
 };
 const DeviceInfo& device_info();
 
+// Device address of the library's static scratch on the current device
+// (rma_decode_topk_static), looked up once per device.
+constexpr size_t kStaticScratchBytes = RMA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** ptr);
+
 // Static LDS bytes of a kernel (a property of its code object, the same on
 // every gfx950 device): queried on first use, a thread-safe function-local
 // static per kernel.

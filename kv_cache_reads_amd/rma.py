@@ -84,6 +84,7 @@ def lib():
     L.rma_build_summaries_range.argtypes = [P_KV, P_SP, _I64, _I64, _U32, _VP, _VP, _I32, _I32, _VP, _I32, _VP,
                                             _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_topk.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode_topk_static.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP]
     L.rma_decode_merge.argtypes = [_VP, _VP, _VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
                                    _I32, _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_full.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
@@ -101,7 +102,7 @@ def lib():
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
     for f in ("rma_phi_features", "rma_phi_mlp_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
-              "rma_decode_merge", "rma_decode_full"):
+              "rma_decode_topk_static", "rma_decode_merge", "rma_decode_full"):
         getattr(L, f).restype = _I32
     _lib = L
     return L
@@ -300,6 +301,24 @@ def rma_decode_topk(q: torch.Tensor, k: torch.Tensor, span: Span, kappa: torch.T
     w = _ws(ws, nb)
     _check(lib().rma_decode_topk(_p(q), G, ctypes.byref(kv), ctypes.byref(sp), _p(kappa), K, _p(idx),
                                  _p(sel_scores), _p(w), w.numel(), _stream()))
+    return idx, sel_scores
+
+
+RMA_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def rma_decode_topk_static(q: torch.Tensor, k: torch.Tensor, span: Span, kappa: torch.Tensor, K: int,
+                           idx: Optional[torch.Tensor] = None, sel_scores: Optional[torch.Tensor] = None):
+    """rma_decode_topk with the library's static scratch (no workspace; the
+    call allocates nothing on the device when idx and sel_scores are given)."""
+    U, G, d = q.shape
+    if idx is None:
+        idx = torch.empty(U, G, K, dtype=torch.int32, device=q.device)
+    if sel_scores is None:
+        sel_scores = torch.empty(U, G, K, dtype=torch.float32, device=q.device)
+    kv, sp = _kv(k, None), span._c()
+    _check(lib().rma_decode_topk_static(_p(q), G, ctypes.byref(kv), ctypes.byref(sp), _p(kappa), K, _p(idx),
+                                        _p(sel_scores), _stream()))
     return idx, sel_scores
 
 

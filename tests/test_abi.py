@@ -225,3 +225,18 @@ def test_mlp_tile_order_matches_the_header_formula():
             for k in (0, 7, 8, 31, 32, 95):
                 off = ((k // 32 * (N // 16) + n // 16) * 64 + (n % 16 + 16 * ((k % 32) // 8))) * 8 + k % 8
                 assert T[p, off] == W[p, n, k]
+
+
+def test_static_topk_refuses_oversized_calls_before_any_hip_call():
+    """rma_decode_topk_static: a call whose scratch exceeds the static array is
+    refused during validation (RMA_ERR_WORKSPACE), with no device touched."""
+    L = R.lib()
+    U, T, d = 2048, 4096, 64
+    kv = _kv(U=U, T=T)
+    sp = _sp(L=T, ns=4, nt=64)
+    need = L.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(sp), 4, 40, 0)
+    assert need > R.RMA_STATIC_SCRATCH_BYTES
+    r = L.rma_decode_topk_static(0x2000, 4, ctypes.byref(kv), ctypes.byref(sp), 0x3000, 40, 0x4000, 0x5000, None)
+    assert r == R.RMA_ERR_WORKSPACE
+    assert b"static" in L.rma_last_error()
+    assert L.rma_decode_topk_static(0x2000, 4, ctypes.byref(kv), ctypes.byref(sp), 0x3000, 0, 0, 0, None) == R.RMA_OK
