@@ -98,6 +98,7 @@ typedef struct {
 #define RMA_OP_DECODE_TOPK 2
 #define RMA_OP_DECODE_MERGE 3
 #define RMA_OP_DECODE_FULL 4
+#define RMA_OP_DECODE 5
 
 /* rma_build_summaries_range() flags. */
 #define RMA_BUILD_ACCUMULATE 1u    /* add to S, u (and raise kappa) instead of overwriting */
@@ -280,6 +281,34 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, const float* Wq,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rma_decode -- one decode step of Top-K+phi: rma_decode_topk followed by
+ * rma_decode_merge in one call (page §1: the exhaustive Top-K fixes the exact
+ * support; §3 Eq. 3-4 and 11, §4.2 Eq. 9, §4.3 Eq. 10: exact terms, the
+ * subtraction, the residual and one normalisation).  The scan of
+ * rma_decode_topk runs first; then one block per query head selects its K
+ * tokens and merges them in the same kernel, the selection going straight
+ * from on-chip memory into the gathers (when the head's candidate lists and
+ * selection fit the block's on-chip memory and the phi_k rows are stored;
+ * otherwise the separate select and merge kernels run on the same scan).
+ * Results equal the two calls' up to fp32 summation order: the same indices
+ * and selected scores, y within a few fp32 ulps.
+ * Arguments as for those two calls: q, G, kv, span, kappa, K as for
+ * rma_decode_topk; phi_q, Wq, bq, phi_k, phi_dtype, Wk, bk, n_param_sets, m,
+ * S, u_, flags, y, stats as for rma_decode_merge.  idx, sel_scores: NULL (not
+ * written) or, both given, [n_units][G][K] outputs as rma_decode_topk writes
+ * them.  kappa may be NULL when K == 0.
+ * Workspace: rma_workspace_bytes(RMA_OP_DECODE, ...) (depends on G, K, m).
+ * Errors: those of the two calls; RMA_ERR_INVALID_ARG also when only one of
+ * idx and sel_scores is given.
+ */
+rma_status rma_decode(const float* q, const float* phi_q, const float* Wq, const float* bq, int32_t G,
+                      const rma_kv* kv, const rma_span* span, const float* kappa, int32_t K,
+                      const void* phi_k, int32_t phi_dtype, const float* Wk, const float* bk,
+                      int32_t n_param_sets, int32_t m, const float* S, const float* u_,
+                      uint32_t flags, int32_t* idx, float* sel_scores, float* y, float* stats,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rma_decode_full -- full exact attention of every query head over its unit's
  * whole context, the reference the method approximates (page §3 Eq. 1, with
  * the generated tokens of Eq. 11), and the page's comparison diagnostics
@@ -330,9 +359,9 @@ rma_status rma_decode_topk_static(const float* q, int32_t G, const rma_kv* kv, c
                                   void* stream);
 
 /* Workspace bytes for `op` (one of RMA_OP_*), at least 256; 0 on invalid
- * arguments.  G and K
- * are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for RMA_OP_DECODE_TOPK
- * and RMA_OP_DECODE_FULL; K is ignored for RMA_OP_DECODE_FULL. */
+ * arguments.  G and K are ignored for RMA_OP_BUILD_SUMMARIES; m is ignored for
+ * RMA_OP_DECODE_TOPK and RMA_OP_DECODE_FULL; K is ignored for
+ * RMA_OP_DECODE_FULL. */
 size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* span, int32_t G,
                            int32_t K, int32_t m);
 

@@ -267,6 +267,39 @@ MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m) 
   return p;
 }
 
+DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m, int phi_dtype,
+                       bool recompute) {
+  DecodePlan p{};
+  p.topk = plan_topk(kv, sp, G, K);
+  p.merge = plan_merge(kv, sp, G, K, m);
+  const int64_t heads = (int64_t)kv.n_units * G;
+  // one 1024-thread block per head while the heads leave most of the chip free;
+  // with many heads smaller blocks, several to a CU
+  // (fp32 keys at d = 128 need more than the 128 registers a 1024-thread
+  // block leaves each lane)
+  p.fused_threads = heads < 1024 && !(kv.dtype == RMA_F32 && kv.d == 128) ? 1024
+                    : (kv.d == 64 ? 256 : 512);
+  p.e_max = p.topk.e_max;
+  bool fused = K > 0 && !recompute;
+  if (fused) {
+    const size_t dyn = (size_t)(2 * (int64_t)p.e_max + 2 * (int64_t)K) * 4 + 16;
+    fused = dyn + fused_static_lds(kv.dtype, phi_dtype, kv.d, m, p.fused_threads) <=
+            device_info().lds_per_block;
+  }
+  p.fused = fused;
+  // the separate path's regions are always reserved, so the size does not
+  // depend on the device
+  size_t off = align_up(p.topk.total);
+  p.off_idx = off;
+  off = align_up(off + (size_t)heads * K * 4);
+  p.off_sel = off;
+  off = align_up(off + (size_t)heads * K * 4);
+  p.off_merge = off;
+  off = align_up(off + p.merge.total);
+  p.total = std::max(off, kAlign);
+  return p;
+}
+
 }  // namespace rma
 
 using namespace rma;
@@ -333,6 +366,9 @@ size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int
     case RMA_OP_DECODE_MERGE:
       if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp)) return 0;
       return plan_merge(*kv, *sp, G, K, m).total;
+    case RMA_OP_DECODE:
+      if (G < 1 || G > 8 || K < 0 || K > l_mid(*sp) || (m != 64 && m != 128)) return 0;
+      return plan_decode(*kv, *sp, G, K, m, RMA_BF16, false).total;
     case RMA_OP_DECODE_FULL:
       if (G < 1 || G > 8 || sp->n_gen < 0) return 0;
       return plan_full(*kv, *sp, G).total;
@@ -543,6 +579,72 @@ rma_status rma_decode_merge(const float* q, const float* phi_q, const float* Wq,
                               phi_k, phi_dtype,
                               phi_k ? nullptr : Wk, bk, P, m, S, u, flags, y, stats,
                               (uint8_t*)workspace, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
+rma_status rma_decode(const float* q, const float* phi_q, const float* Wq, const float* bq,
+                      int32_t G, const rma_kv* kv, const rma_span* sp, const float* kappa,
+                      int32_t K, const void* phi_k, int32_t phi_dtype, const float* Wk,
+                      const float* bk, int32_t P, int32_t m, const float* S, const float* u,
+                      uint32_t flags, int32_t* idx, float* sel, float* y, float* stats,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  rma_status s = check_kv_span(kv, sp, true);
+  if (s != RMA_OK) return s;
+  RMA_CHECK(G >= 1 && G <= 8, RMA_ERR_UNSUPPORTED, "G %d not in 1..8", G);
+  RMA_CHECK(m == 64 || m == 128, RMA_ERR_UNSUPPORTED, "m %d not in {64,128}", m);
+  RMA_CHECK(dtype_ok(phi_dtype), RMA_ERR_UNSUPPORTED, "unsupported phi dtype");
+  RMA_CHECK(flags == RMA_MERGE_SUB || flags == RMA_MERGE_NO_RESIDUAL ||
+                flags == RMA_MERGE_NO_SUBTRACT,
+            RMA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  RMA_CHECK(K >= 0 && K <= l_mid(*sp), RMA_ERR_INVALID_ARG, "K %d outside [0, L_mid=%lld]", K,
+            (long long)l_mid(*sp));
+  RMA_CHECK((int64_t)sp->n_sink + sp->n_tail + sp->n_gen + K > 0, RMA_ERR_INVALID_ARG,
+            "empty exact support (no anchors, generated or retrieved tokens)");
+  const bool need_res = flags != RMA_MERGE_NO_RESIDUAL;
+  RMA_CHECK(q && y, RMA_ERR_INVALID_ARG, "NULL q or y");
+  RMA_CHECK(K == 0 || kappa, RMA_ERR_INVALID_ARG, "NULL kappa");
+  RMA_CHECK((idx == nullptr) == (sel == nullptr), RMA_ERR_INVALID_ARG,
+            "idx and sel_scores must be given together");
+  RMA_CHECK(!need_res || (S && u), RMA_ERR_INVALID_ARG, "NULL S or u");
+  RMA_CHECK(!need_res || phi_q || (Wq && bq && P >= 1), RMA_ERR_INVALID_ARG,
+            "NULL phi_q and no Wq/bq to compute it");
+  const bool need_phik = flags == RMA_MERGE_SUB && K > 0 && K < l_mid(*sp);
+  RMA_CHECK(!need_phik || phi_k != nullptr || (Wk != nullptr && bk != nullptr && P >= 1),
+            RMA_ERR_INVALID_ARG, "NULL phi_k and no Wk/bk to recompute it");
+  RMA_CHECK(!need_phik || phi_k != nullptr || (kv->dtype == RMA_BF16 && phi_dtype == RMA_BF16),
+            RMA_ERR_UNSUPPORTED, "recomputed phi_k rows need bf16 keys and bf16 phi rounding");
+  RMA_CHECK(aligned16(q) && aligned16(phi_q) && aligned16(Wq) && aligned16(bq) &&
+                aligned16(kappa) && aligned16(idx) && aligned16(sel) && aligned16(phi_k) &&
+                aligned16(Wk) && aligned16(bk) && aligned16(S) && aligned16(u) && aligned16(y) &&
+                aligned16(stats),
+            RMA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const bool recompute = need_phik && phi_k == nullptr;
+  DecodePlan pl = plan_decode(*kv, *sp, G, K, m, phi_dtype, recompute);
+  RMA_CHECK(K == 0 || pl.topk.n_chunks <= kSelMaxChunks, RMA_ERR_UNSUPPORTED,
+            "mid-region too long for G=%d", G);
+  RMA_CHECK(workspace != nullptr && aligned16(workspace), RMA_ERR_WORKSPACE,
+            "workspace is NULL or misaligned");
+  RMA_CHECK(workspace_bytes >= pl.total, RMA_ERR_WORKSPACE, "workspace %zu < required %zu",
+            workspace_bytes, pl.total);
+  TraceScope ts((hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  hipError_t e = hipSuccess;
+  if (K > 0) e = launch_topk_scan(pl.topk, q, G, *kv, *sp, kappa, ws, st);
+  if (e == hipSuccess && pl.fused) {
+    e = launch_decode_fused(pl, q, G, *kv, *sp, K, idx, sel, phi_q, phi_q ? nullptr : Wq, bq, P,
+                            phi_k, phi_dtype, m, S, u, flags, y, stats, ws, st);
+  } else if (e == hipSuccess) {
+    int32_t* ii = idx ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+    float* ss = sel ? sel : reinterpret_cast<float*>(ws + pl.off_sel);
+    if (K > 0) e = launch_topk_select(pl.topk, q, G, *kv, *sp, K, ii, ss, ws, st);
+    if (e == hipSuccess)
+      e = launch_merge(pl.merge, q, phi_q, phi_q ? nullptr : Wq, bq, G, *kv, *sp, ii, ss, K, phi_k,
+                       phi_dtype, phi_k ? nullptr : Wk, bk, P, m, S, u, flags, y, stats,
+                       ws + pl.off_merge, st);
+  }
   RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return RMA_OK;
 }

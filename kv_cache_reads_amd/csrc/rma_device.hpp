@@ -97,6 +97,39 @@ __device__ __forceinline__ void unpack_piece(const uint4& w, const float*, float
   out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
 }
 
+// N elements of type T as raw 16-byte words: loaded early, unpacked at use.
+template <typename T, int N>
+struct RawPiece {
+  static constexpr int W = N * (int)sizeof(T) / 16;
+  static_assert(W >= 1 && N * (int)sizeof(T) % 16 == 0, "pieces are whole 16-byte words");
+  uint4 w[W];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p4[i];
+  }
+  __device__ __forceinline__ void unpack(float (&out)[N]) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const uint32_t x[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          out[8 * i + 2 * k] = bf16lo(x[k]);
+          out[8 * i + 2 * k + 1] = bf16hi(x[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[4 * i + k] = __uint_as_float(x[k]);
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------- DPP sums
 // Butterfly sums inside groups of 2/4/8/16 lanes with DPP row permutations.
 // After lane_group_sum<N>, every lane of an aligned N-lane group holds the sum.

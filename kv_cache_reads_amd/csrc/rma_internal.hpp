@@ -38,16 +38,18 @@ const DeviceInfo& device_info();
 constexpr size_t kStaticScratchBytes = RMA_STATIC_SCRATCH_BYTES;
 hipError_t static_scratch(void** ptr);
 
-// Static LDS bytes of a kernel (a property of its code object, the same on
-// every gfx950 device): queried on first use, a thread-safe function-local
-// static per kernel.
-template <typename Kern>
-size_t kernel_static_lds(Kern* kfn) {
-  static const size_t bytes = [kfn] {
+// Static LDS bytes of the kernel Kern (a property of its code object, the same
+// on every gfx950 device): queried on first use, a thread-safe function-local
+// static per kernel.  The kernel is a template argument so that every kernel
+// has its own cache (instantiations that differ only in non-type template
+// parameters share one function type).  A failed query reads as "does not fit".
+template <auto Kern>
+size_t kernel_static_lds() {
+  static const size_t bytes = [] {
     hipFuncAttributes attr{};
-    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kfn)) == hipSuccess
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(Kern)) == hipSuccess
                ? (size_t)attr.sharedSizeBytes
-               : (size_t)32 * 1024;
+               : (size_t)1 << 30;
   }();
   return bytes;
 }
@@ -91,6 +93,23 @@ struct MergePlan {
   size_t off_part, total;
 };
 MergePlan plan_merge(const rma_kv& kv, const rma_span& sp, int G, int K, int m);
+
+// ------------------------------------------------------------- fused decode
+// rma_decode: the scan of rma_decode_topk, then either the fused select-and-merge
+// kernel (one block per head; when its union, list and static LDS fit) or the
+// separate select and merge kernels on the same scan output.
+struct DecodePlan {
+  TopkPlan topk;       // the scan's chunks and reports (workspace offset 0)
+  bool fused;
+  int fused_threads;   // 256, 512 or 1024
+  int e_max;           // union slots of the fused kernel
+  MergePlan merge;     // the separate path
+  size_t off_idx, off_sel, off_merge, total;
+};
+DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m, int phi_dtype,
+                       bool recompute);
+// static LDS of the fused kernel instantiation a plan would launch
+size_t fused_static_lds(int kv_dtype, int phi_dtype, int d, int m, int nt);
 
 // ------------------------------------------------------------- MLP feature map
 constexpr int kPhiMlpWidth = RMA_PHI_MLP_WIDTH;
@@ -157,6 +176,11 @@ hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& s
                         int phi_dtype, float* S, float* u, float* kappa, uint8_t* ws,
                         hipStream_t st);
 
+hipError_t launch_topk_scan(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
+                            const rma_span& sp, const float* kappa, uint8_t* ws, hipStream_t st);
+hipError_t launch_topk_select(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
+                              const rma_span& sp, int K, int32_t* idx, float* sel, uint8_t* ws,
+                              hipStream_t st);
 hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
                        const rma_span& sp, const float* kappa, int K, int32_t* idx,
                        float* sel_scores, uint8_t* ws, hipStream_t st);
@@ -168,6 +192,13 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
                         const float* Wk, const float* bk, int P, int m, const float* S,
                         const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
                         hipStream_t st);
+
+hipError_t launch_decode_fused(const DecodePlan& pl, const float* q, int G, const rma_kv& kv,
+                               const rma_span& sp, int K, int32_t* idx, float* sel,
+                               const float* phi_q, const float* Wq, const float* bq, int P,
+                               const void* phi_k, int phi_dtype, int m, const float* S,
+                               const float* u, uint32_t flags, float* y, float* stats, uint8_t* ws,
+                               hipStream_t st);
 
 hipError_t launch_phi_mlp(const void* x, int x_dtype, int n_units, int64_t rows, int64_t xstride,
                           int d, const rma_phi_mlp* w, int m, int P, void* phi, int phi_dtype,

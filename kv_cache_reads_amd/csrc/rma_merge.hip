@@ -31,39 +31,6 @@
 
 namespace rma {
 
-// N elements of type T as raw 16-byte words: loaded early, unpacked at use.
-template <typename T, int N>
-struct RawPiece {
-  static constexpr int W = N * (int)sizeof(T) / 16;
-  static_assert(W >= 1 && N * (int)sizeof(T) % 16 == 0, "pieces are whole 16-byte words");
-  uint4 w[W];
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  __device__ __forceinline__ void load(const T* p) {
-    const uint4* p4 = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = p4[i];
-  }
-  __device__ __forceinline__ void unpack(float (&out)[N]) const {
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      const uint32_t x[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          out[8 * i + 2 * k] = bf16lo(x[k]);
-          out[8 * i + 2 * k + 1] = bf16hi(x[k]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) out[4 * i + k] = __uint_as_float(x[k]);
-      }
-    }
-  }
-};
-
 // RECOMP: phi_k rows are not stored; the retrieved tokens' rows are recomputed
 // from their keys with the summary builder's projection (same operands, same
 // MFMA order, same bf16 rounding), so the subtraction removes exactly what the

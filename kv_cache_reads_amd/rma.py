@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rma.h")
 
 RMA_OK, RMA_ERR_INVALID_ARG, RMA_ERR_UNSUPPORTED, RMA_ERR_WORKSPACE, RMA_ERR_HIP = 0, -1, -2, -3, -4
 RMA_F32, RMA_BF16 = 0, 1
-RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE, RMA_OP_DECODE_FULL = 1, 2, 3, 4
+RMA_OP_BUILD_SUMMARIES, RMA_OP_DECODE_TOPK, RMA_OP_DECODE_MERGE, RMA_OP_DECODE_FULL, RMA_OP_DECODE = 1, 2, 3, 4, 5
 RMA_MERGE_SUB, RMA_MERGE_NO_RESIDUAL, RMA_MERGE_NO_SUBTRACT = 0, 1, 2
 RMA_BUILD_ACCUMULATE = 1
 
@@ -87,6 +87,8 @@ def lib():
     L.rma_decode_topk_static.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP]
     L.rma_decode_merge.argtypes = [_VP, _VP, _VP, _VP, _I32, P_KV, P_SP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
                                    _I32, _I32, _VP, _VP, _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.rma_decode.argtypes = [_VP, _VP, _VP, _VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _I32, _VP, _VP, _I32, _I32,
+                             _VP, _VP, _U32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_decode_full.argtypes = [_VP, _I32, P_KV, P_SP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.rma_workspace_bytes.argtypes = [_I32, P_KV, P_SP, _I32, _I32, _I32]
     L.rma_workspace_bytes.restype = _SZ
@@ -102,7 +104,7 @@ def lib():
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
     for f in ("rma_phi_features", "rma_phi_mlp_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
-              "rma_decode_topk_static", "rma_decode_merge", "rma_decode_full"):
+              "rma_decode_topk_static", "rma_decode_merge", "rma_decode", "rma_decode_full"):
         getattr(L, f).restype = _I32
     _lib = L
     return L
@@ -347,6 +349,40 @@ def rma_decode_merge(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Te
                                   _p(sel_scores), K, _p(phi_k), pdt, _p(Wk), _p(bk), P, m, _p(S), _p(u),
                                   flags, _p(y), _p(stats), _p(w), w.numel(), _stream()))
     return (y, stats) if want_stats else y
+
+
+def rma_decode(q: torch.Tensor, phi_q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, span: Span,
+               kappa: Optional[torch.Tensor], K: int, phi_k: Optional[torch.Tensor], S: Optional[torch.Tensor],
+               u: Optional[torch.Tensor], flags: int = RMA_MERGE_SUB, m: Optional[int] = None,
+               want_idx: bool = False, want_stats: bool = False, ws: Optional[Workspace] = None,
+               y: Optional[torch.Tensor] = None, Wk: Optional[torch.Tensor] = None,
+               bk: Optional[torch.Tensor] = None, Wq: Optional[torch.Tensor] = None,
+               bq: Optional[torch.Tensor] = None, phi_dtype: Optional[torch.dtype] = None):
+    """One decode step (Top-K + merge in one call).  Returns y [U, G, d], plus
+    (idx [U, G, K], sel_scores [U, G, K]) with want_idx and stats [U, G, 4]
+    with want_stats, in the order y, idx, sel, stats."""
+    U, G, d = q.shape
+    if m is None:
+        m = S.shape[1] if S is not None else 128
+    if y is None:
+        y = torch.empty(U, G, d, dtype=torch.float32, device=q.device)
+    idx = torch.empty(U, G, K, dtype=torch.int32, device=q.device) if want_idx else None
+    sel = torch.empty(U, G, K, dtype=torch.float32, device=q.device) if want_idx else None
+    stats = torch.empty(U, G, 4, dtype=torch.float32, device=q.device) if want_stats else None
+    kv, sp = _kv(k, v), span._c()
+    nb = int(lib().rma_workspace_bytes(RMA_OP_DECODE, ctypes.byref(kv), ctypes.byref(sp), G, K, m))
+    w = _ws(ws, nb)
+    pdt = _dt(phi_k.dtype) if phi_k is not None else _dt(phi_dtype or torch.bfloat16)
+    P = Wk.shape[0] if Wk is not None else (Wq.shape[0] if Wq is not None else 1)
+    _check(lib().rma_decode(_p(q), _p(phi_q), _p(Wq), _p(bq), G, ctypes.byref(kv), ctypes.byref(sp), _p(kappa), K,
+                            _p(phi_k), pdt, _p(Wk), _p(bk), P, m, _p(S), _p(u), flags, _p(idx), _p(sel), _p(y),
+                            _p(stats), _p(w), w.numel(), _stream()))
+    out = (y,)
+    if want_idx:
+        out += (idx, sel)
+    if want_stats:
+        out += (stats,)
+    return out[0] if len(out) == 1 else out
 
 
 def rma_decode_full(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, span: Span,

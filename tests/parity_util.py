@@ -115,3 +115,24 @@ def check_summaries(cfg, gpu_pre, u, ref_pre, v_mid):
     assert np.all(np.abs(ug - ur) <= 2.0 ** -8 * ur + 1e-4), "u"
     kg = float(kappa[u].item())
     assert kap <= kg <= kap * (1 + 2e-5) + 1e-30, f"kappa {kg} vs {kap}"
+
+
+def hip_decode_one_call(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None, fused_phi=False,
+                        want_idx=True):
+    """The same step as hip_decode through rma_decode (Top-K and merge in one
+    call)."""
+    cfg = inp.cfg
+    phi_k, S, u, kappa = pre
+    q = inp.q[step].contiguous()
+    f = None if fused_phi else R.rma_phi_features(q, inp.W, inp.b)
+    sp = decode_span(cfg, step)
+    extra = dict(Wk=inp.W, bk=inp.b) if phi_k is None else {}
+    if fused_phi:
+        extra.update(Wq=inp.W, bq=inp.b)
+    out = R.rma_decode(q, f, inp.k, inp.v, sp, kappa, K, phi_k, S, u, flags=flags, m=cfg.m,
+                       want_idx=want_idx, want_stats=True, ws=ws, phi_dtype=cfg.torch_phi_dtype(), **extra)
+    if want_idx:
+        y, idx, sel, stats = out
+        return dict(idx=idx, sel=sel, y=y, stats=stats, f=f)
+    y, stats = out
+    return dict(y=y, stats=stats, f=f)
