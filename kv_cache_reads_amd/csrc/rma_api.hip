@@ -279,10 +279,10 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
   // block leaves each lane)
   p.fused_threads = heads < 1024 && !(kv.dtype == RMA_F32 && kv.d == 128) ? 1024
                     : (kv.d == 64 ? 256 : 512);
-  p.e_max = p.topk.e_max;
-  bool fused = K > 0 && !recompute;
+  bool fused = K > 0 && !recompute && p.topk.n_chunks <= kSelMaxChunks &&
+               fused_slots_fit(p.topk.n_chunks, p.fused_threads);
   if (fused) {
-    const size_t dyn = (size_t)(2 * (int64_t)p.e_max + 2 * (int64_t)K) * 4 + 16;
+    const size_t dyn = fused_dyn_bytes(p.topk.n_chunks, p.topk.r_cap, K, kv.d, p.fused_threads);
     fused = dyn + fused_static_lds(kv.dtype, phi_dtype, kv.d, m, p.fused_threads) <=
             device_info().lds_per_block;
   }

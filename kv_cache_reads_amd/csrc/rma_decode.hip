@@ -6,24 +6,28 @@
 // clamp of the residual denominator).
 //
 // rma_decode runs the scan of rma_decode_topk, then this kernel, grid U * G.
-// A block first issues every load it will need before the selection's result:
-// the chunk reports of its head (HeadSelect::load), then the query, the
-// feature map's operands (or the given features), S and u, and the first rows
-// of the anchors and generated tokens.  While the selection's reports are the
-// only loads it waits for, the others arrive; then, in order:
-//   1. f = phi_q(q) into LDS; phi(q)^T S per feature block and u^T f;
-//   2. the exact terms of the anchors and generated tokens (eight lanes per
-//      entry, a running max per 8-lane group);
-//   3. the selection (rma_select.hpp): the K positions, ascending, and their
-//      scaled fp32 scores into an LDS list (and to idx / sel when asked);
+// A block first issues every load it needs before the selection's result: its
+// head's chunk reports and chunk table, the query, the feature map's operands
+// (or the given features), S and u, and one exactly scored row per 8-lane
+// group.  Then, in order (each step behind one barrier):
+//   1. wave 0: each chunk's offset in the union (a wave scan of the counts);
+//      everyone: f = phi_q(q) into LDS;
+//   2. the reports into the union (compacted, position order) and its score
+//      range; phi(q)^T S per feature block and u^T f;
+//   3. the selection (block_select in rma_select.hpp, the exact fallback if it
+//      fails): the K positions, ascending, and their scaled fp32 scores into
+//      an LDS list (and to idx / sel when asked);
 //   4. the retrieved tokens from that list: their V and phi_k rows are
 //      gathered with every load of a batch issued before the first is used;
-//      e^{s - m} v, w = f.phi_k and w v accumulate in the same groups;
-//   5. the groups and waves combine with max rescaling in a fixed order, the
-//      subtraction, the clamp and one normalisation.
-// Steps 2 and 4 are the merge kernel's gathers; the arithmetic and its order
-// within a group are the same, only the source of the retrieved entries
-// differs (the LDS list instead of idx / sel in memory).
+//      e^{s - m} v, w = f.phi_k and w v accumulate per 8-lane group with a
+//      running max; the anchors' and generated tokens' exact terms are added
+//      while the first batch loads;
+//   5. the combine: the block's largest running max, one rescale per group,
+//      the two groups of a 16-lane row added by DPP, the pair sums added in
+//      pair order through LDS (deterministic); then the subtraction, the clamp
+//      and one normalisation.
+// The arithmetic of a term is the merge kernel's; the order of the sums
+// differs (the fused kernel spreads a head's entries over more groups).
 #include "rma_select.hpp"
 
 #include <math.h>
@@ -36,7 +40,7 @@ template <typename KT, typename PT, int D, int M, int NT>
 __global__ void __launch_bounds__(NT)
 decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb,
                     const KT* __restrict__ vb, int64_t ustride, int L, int n_sink, int n_tail,
-                    int n_gen, int L_mid, int ch, int n_chunks, int r_cap, int K, int e_max,
+                    int n_gen, int L_mid, int ch, int n_chunks, int r_cap, int K,
                     const float4* __restrict__ hpw, const float2* __restrict__ ent,
                     const int2* __restrict__ meta, int32_t* __restrict__ idx_out,
                     float* __restrict__ sc_out, const float* __restrict__ phi_q,
@@ -49,17 +53,44 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   constexpr int NGR = NT / LPE;     // entry groups
   constexpr int CPL = D / LPE;      // value columns per lane
   constexpr int FPL = M / LPE;      // phi features per lane
+  constexpr int SPEC = kFusedSpec<NT>;     // report slots per thread
   // retrieved entries per group whose row loads are in flight together: as in
   // the merge kernel, halved in 1024-thread blocks (128 VGPRs per lane; 128
   // groups x 4 entries already keep 512 entries in flight)
   constexpr int B0 = sizeof(KT) == 4 ? 2 : sizeof(PT) == 4 ? (D == 128 ? 2 : 4) : D == 128 ? 4 : 8;
   constexpr int B = NT == 1024 ? (B0 > 1 ? B0 / 2 : 1) : B0;
-  constexpr int BX = 2;             // exactly scored entries per group per batch
+  constexpr int NV = 2 * D + 2;     // combined values: N[D], sum w v [D], Z, sum w
+  constexpr int NP = NT / 16;       // group pairs (two groups per 16-lane row)
+  // dynamic LDS: the union of the chunk reports (scores, positions; room for
+  // n_chunks r_cap entries rounded up to whole batches of the selection's rows),
+  // then the list of the K selected (positions, scaled scores); after the
+  // gathers the combine reuses it from the start
   extern __shared__ __align__(16) float dyn[];
-  float* es = dyn;                                        // selection: union scores
-  int* ep = reinterpret_cast<int*>(dyn + e_max);          // selection: union positions
-  int* lpos = reinterpret_cast<int*>(dyn + 2 * e_max);    // the K selected positions
-  float* lsc = dyn + 2 * e_max + K;                       // and their scaled scores
+  constexpr int UB = kWaveSelRows * kWave;
+  const int PS = (n_chunks * r_cap + UB - 1) / UB * UB;
+  float* es = dyn;
+  int* ep = reinterpret_cast<int*>(dyn + PS);
+  int* lpos = reinterpret_cast<int*>(dyn + 2 * PS);
+  float* lsc = dyn + 2 * PS + K;
+  float* red = dyn;
+
+  static_assert(kSelMaxChunks == 4 * kWave, "four chunks per lane of wave 0");
+  __shared__ int s_off[kSelMaxChunks], s_bcs[kSelMaxChunks], s_nrep[kSelMaxChunks];
+  __shared__ int s_nE, s_trunc;
+  __shared__ float s_rlo[NW], s_rhi[NW];
+  __shared__ float s_qf[D];
+  __shared__ uint32_t s_hist[kSelBins];
+  __shared__ float s_cand[kSelBandMax];
+  __shared__ int s_bslot[kSelBandMax];
+  __shared__ DD s_bdd[kSelBandMax];
+  __shared__ int s_misc[8];
+  __shared__ int s_buf[kSelThreads / kWave + 1];
+  __shared__ int s_wcnt[NW];
+  __shared__ float s_wm[NW];
+  __shared__ float s_fin[NV];
+  __shared__ float s_part[NT / D][D];
+  __shared__ float s_uf;
+  __shared__ float s_f[M];          // f = phi_q(q) of this head
 
   const int ug = blockIdx.x, u = ug / G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -71,37 +102,43 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
   const bool rs = resid && !whole_mid;   // phi(q)^T S and u^T f are needed
 
-  __shared__ float s_wn[NW][D], s_wk[NW][D];
-  __shared__ float s_wm[NW], s_wz[NW], s_wzk[NW];
-  __shared__ float s_part[NT / D][D];
-  __shared__ float s_uf;
-  __shared__ float s_f[M];          // f = phi_q(q) of this head
-
   const KT* kunit = kb + (size_t)u * ustride;
   const KT* vunit = vb + (size_t)u * ustride;
   const float* qg = q + (size_t)ug * D;
+  const int2* mt = meta + (size_t)ug * n_chunks;
+  const float2* en = ent + (size_t)ug * n_chunks * r_cap;
 
-  // ---- 1. the selection's loads (this kernel runs only with K >= 1)
-  HeadSelect<KT, D, NT> sel;
-  sel.ug = ug;
-  sel.qg = qg;
-  sel.mt = meta + (size_t)ug * n_chunks;
-  sel.en = ent + (size_t)ug * n_chunks * r_cap;
-  sel.kunit = kunit;
-  sel.n_sink = n_sink;
-  sel.L_mid = L_mid;
-  sel.ch = ch;
-  sel.n_chunks = n_chunks;
-  sel.r_cap = r_cap;
-  sel.K = K;
-  sel.e_max = e_max;
-  sel.inv_sqrt_d = inv_sqrt_d;
-  sel.load(hpw);
-
-  // ---- 2. the merge's loads: f's operands (or the given features), q, S, u
+  // ---- 1. loads.  The selection's: the head's parameters, the chunk table, and
+  //      the report slots (a power-of-two group of tpc threads per chunk; thread
+  //      t serves chunk t >> lg_t, its slots my_s + k tpc, so no slot index needs
+  //      a division); the first SPEC tpc slots of each chunk now, the rest (only
+  //      where r_cap exceeds them) in later rounds
+  const f32x4 hp_in = *reinterpret_cast<const f32x4*>(hpw + ug);
+  const int lg_c = n_chunks > 1 ? 32 - __clz(n_chunks - 1) : 0;
+  const int lg_t = __builtin_ctz(NT) - lg_c, tpc = 1 << lg_t;
+  const int my_c = tid >> lg_t, my_s = tid & (tpc - 1);
+  const int cc = min(my_c, n_chunks - 1);
+  const int2 m_mine = mt[cc];
+  float2 sv2[SPEC];
+#pragma unroll
+  for (int k = 0; k < SPEC; ++k) sv2[k] = en[(size_t)cc * r_cap + min(my_s + k * tpc, r_cap - 1)];
+  // the chunk table: four chunks per lane of wave 0, which computes the offsets
+  int2 mc[4];
+  if (wave == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mc[k] = mt[min(lane * 4 + k, n_chunks - 1)];
+  }
+  const float q_in = qg[min(tid, D - 1)];
+  // the merge's: f's operands (or the given features), q, S, u
   constexpr int TPF = NT / M, EPT = D / TPF;     // threads per feature, elements each
   const int fi = tid / TPF, fpart = tid % TPF;
   const bool fcomp = resid && Wq != nullptr;
+  float qr[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; i += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(qg + part * CPL + i);
+    qr[i] = t.x; qr[i + 1] = t.y; qr[i + 2] = t.z; qr[i + 3] = t.w;
+  }
   float wq[EPT], xq[EPT], fb0;
   {
     const int pset = u % P;
@@ -110,18 +147,18 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
     for (int i = 0; i < EPT; i += 4) {
       const float4 w4 = *reinterpret_cast<const float4*>(wr + i);
-      const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
       wq[i] = w4.x; wq[i + 1] = w4.y; wq[i + 2] = w4.z; wq[i + 3] = w4.w;
-      xq[i] = x4.x; xq[i + 1] = x4.y; xq[i + 2] = x4.z; xq[i + 3] = x4.w;
+      if constexpr (TPF != LPE) {
+        const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
+        xq[i] = x4.x; xq[i + 1] = x4.y; xq[i + 2] = x4.z; xq[i + 3] = x4.w;
+      }
+    }
+    if constexpr (TPF == LPE) {   // fpart == part, EPT == CPL: the same elements as qr
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) xq[i] = qr[i];
     }
     fb0 = fcomp ? bq[(size_t)pset * M + fi]
                 : (resid && phi_q != nullptr ? phi_q[(size_t)ug * M + (tid % M)] : 0.f);
-  }
-  float qr[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; i += 4) {
-    const float4 t = *reinterpret_cast<const float4*>(qg + part * CPL + i);
-    qr[i] = t.x; qr[i + 1] = t.y; qr[i + 2] = t.z; qr[i + 3] = t.w;
   }
   // phi(q)^T S: thread (column scol, feature block fb) holds its FPB elements of
   // S (coalesced along the columns); without a residual the loads read q
@@ -140,26 +177,59 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   float uu[UPL];
 #pragma unroll
   for (int i = 0; i < UPL; ++i) uu[i] = rs ? u_[(size_t)u * M + min(lane + kWave * i, M - 1)] : 0.f;
-
-  // position of exactly scored entry j: sinks, tail, generated tokens
+  // the exactly scored rows (sinks, tail, generated tokens): group g takes rows
+  // g, g + NGR, ...; the first now, scored while the retrieved rows load
   auto ex_pos = [&](int j) {
     return j < n_sink ? j : (j < n_a ? L - n_tail + (j - n_sink) : L + (j - n_a));
   };
-  // the first batch of exactly scored rows (the rest, if any, after it)
-  RawPiece<KT, CPL> xv[BX], xk[BX];
-  const int xlo = 0, xhi = n_ex;
-  auto load_ex = [&](int jb) {
-#pragma unroll
-    for (int e = 0; e < BX; ++e) {
-      const int jj = jb + e * NGR;
-      const int pos = ex_pos(jj < xhi ? jj : xlo);
-      xv[e].load(vunit + (size_t)pos * D + part * CPL);
-      xk[e].load(kunit + (size_t)pos * D + part * CPL);
-    }
-  };
-  if (n_ex > 0) load_ex(grp);
+  RawPiece<KT, CPL> xv, xk;
+  {
+    const int pos = ex_pos(grp < n_ex ? grp : 0);
+    xv.load(vunit + (size_t)pos * D + part * CPL);
+    xk.load(kunit + (size_t)pos * D + part * CPL);
+  }
+  const BlockSelLds wl{s_hist, s_cand, s_bslot, s_bdd, s_misc, s_wcnt};
+  init_block_select<NT>(wl);
 
-  // ---- f = phi_q(q) into LDS, then phi(q)^T S and u^T f
+  // ---- 2. wave 0: each chunk's offset in the union (a wave scan of the counts
+  //      it reported, at most r_cap each), the chunk table, empty entries after
+  //      the union up to a whole batch of rows.  Everyone: q for the band
+  //      rescoring, f = phi_q(q).
+  if (wave == 0) {
+    int wc4[4], ls = 0;
+    bool tr = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = lane * 4 + k;
+      wc4[k] = c < n_chunks ? min(mc[k].y, r_cap) : 0;
+      tr |= c < n_chunks && mc[k].y > r_cap;   // the chunk withheld tokens
+      ls += wc4[k];
+    }
+    const int incl = wave_incl_scan_dpp(ls);
+    int o = incl - ls;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = lane * 4 + k;
+      if (c < n_chunks) {
+        s_off[c] = o;
+        s_bcs[c] = mc[k].x;
+        s_nrep[c] = mc[k].y;
+      }
+      o += wc4[k];
+    }
+    const int nE = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const bool trunc = __ballot(tr) != 0ull;
+    const int pad = (nE + UB - 1) / UB * UB;
+    for (int i = nE + lane; i < pad; i += kWave) {
+      es[i] = -INFINITY;
+      ep[i] = 0;
+    }
+    if (lane == 0) {
+      s_nE = nE;
+      s_trunc = trunc;
+    }
+  }
+  if (tid < D) s_qf[tid] = q_in;
   if (fcomp) {
     float z = 0.f;
 #pragma unroll
@@ -170,10 +240,42 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     s_f[tid] = fb0;
   }
   __syncthreads();
+
+  // ---- 3. the reports into the union (chunk c's j-th at s_off[c] + j) and its
+  //      score range; phi(q)^T S per feature block and u^T f
+  {
+    float rlo = INFINITY, rhi = -INFINITY;
+    if (my_c < n_chunks) {
+      const int wc = min(m_mine.y, r_cap), o0 = s_off[my_c];
+      for (int j0 = 0;;) {
+#pragma unroll
+        for (int k = 0; k < SPEC; ++k) {
+          const int j = j0 + my_s + k * tpc;
+          if (j < wc) {
+            es[o0 + j] = sv2[k].x;
+            ep[o0 + j] = __float_as_int(sv2[k].y);
+            rlo = fminf(rlo, sv2[k].x);
+            rhi = fmaxf(rhi, sv2[k].x);
+          }
+        }
+        j0 += SPEC * tpc;
+        if (j0 >= wc) break;
+#pragma unroll
+        for (int k = 0; k < SPEC; ++k)
+          sv2[k] = en[(size_t)cc * r_cap + min(j0 + my_s + k * tpc, r_cap - 1)];
+      }
+    }
+    rlo = wave_min_dpp(rlo);
+    rhi = wave_max_dpp(rhi);
+    if (lane == 0) {
+      s_rlo[wave] = rlo;
+      s_rhi[wave] = rhi;
+    }
+  }
   if (rs) {
     float p = 0.f;
 #pragma unroll
-    for (int i = 0; i < FPB; ++i) p = __fmaf_rn(s_f[fb * FPB + i], sv[i], p);
+    for (int i = 0; i < FPB; ++i) p = __fmaf_rn(s_f[fb * FPB + i], sv[i], p);  // f: LDS broadcast
     s_part[fb][scol] = p;
     if (wave == NW - 1) {
       float t = 0.f;
@@ -184,13 +286,38 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       if (lane == 0) s_uf = t;
     }
   }
+  __syncthreads();
+
+  // ---- 4. the selection, the whole block (the exact fallback when it fails)
+  SelOut out;
+  out.lpos = lpos;
+  out.lsc = lsc;
+  if (idx_out != nullptr) {
+    out.io = idx_out + (size_t)ug * K;
+    out.so = sc_out + (size_t)ug * K;
+  }
+  {
+    const HeadParams hp{hp_in[0], hp_in[1], hp_in[2]};
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lo = fminf(lo, s_rlo[w]);
+      hi = fmaxf(hi, s_rhi[w]);
+    }
+    const bool ok = block_select<KT, D, NT>(es, ep, s_nE, lo, hi, s_bcs, s_nrep, n_chunks, ch, L_mid,
+                                            n_sink, K, s_trunc != 0, hp, s_qf, kunit, inv_sqrt_d, wl, out);
+    if (!ok) {   // uniform: a chunk withheld tokens or the band was too wide
+      __syncthreads();
+      exact_fallback<KT, D, NT>(s_qf, kunit, n_sink, L_mid, K, out, inv_sqrt_d, s_hist, s_misc, s_buf);
+    }
+  }
+  __syncthreads();   // the list
 
   // the group's running sums: N = sum e^{s - m} v, Z = sum e^{s - m} over the
-  // exact support; NK = sum w v, ZK = sum w over the retrieved entries (those
-  // two start after the selection, so they are not live across it)
+  // exact support; NK = sum w v, ZK = sum w over the retrieved entries
   float N[CPL], NK[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) N[c] = 0.f;
+  for (int c = 0; c < CPL; ++c) { N[c] = 0.f; NK[c] = 0.f; }
   float Z = 0.f, ZK = 0.f, mrun = -INFINITY;
   auto add_exp = [&](float s, const float (&vv)[CPL]) {
     if (s > mrun) {
@@ -205,42 +332,20 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     for (int c = 0; c < CPL; ++c) N[c] = __fmaf_rn(ew, vv[c], N[c]);
     Z += ew;
   };
-
-  // ---- 2. exactly scored entries (anchors, generated tokens)
-  for (int jb = grp; jb < n_ex; jb += NGR * BX) {
-    if (jb != grp) load_ex(jb);
-    __builtin_amdgcn_sched_barrier(0);
+  // an exactly scored row: its score q.k / sqrt(d) and its term
+  auto add_exact = [&](const RawPiece<KT, CPL>& rk, const RawPiece<KT, CPL>& rv) {
+    float kv[CPL], vv[CPL];
+    rk.unpack(kv);
+    float a = 0.f;
 #pragma unroll
-    for (int e = 0; e < BX; ++e) {
-      float kv[CPL], vv[CPL];
-      xk[e].unpack(kv);
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) a = __fmaf_rn(qr[i], kv[i], a);
-      a = lane_group_sum<LPE>(a);
-      if (jb + e * NGR < xhi) {  // uniform within the group
-        xv[e].unpack(vv);
-        add_exp(a * inv_sqrt_d, vv);
-      }
-    }
-  }
+    for (int i = 0; i < CPL; ++i) a = __fmaf_rn(s_qf[part * CPL + i], kv[i], a);   // q from LDS
+    a = lane_group_sum<LPE>(a);
+    rv.unpack(vv);
+    add_exp(a * inv_sqrt_d, vv);
+  };
+  bool ex_due = grp < n_ex;   // the group's first exact row, loaded at the start
 
-  // ---- 3. the selection into the LDS list
-  {
-    SelOut out;
-    out.lpos = lpos;
-    out.lsc = lsc;
-    if (idx_out != nullptr) {
-      out.io = idx_out + (size_t)ug * K;
-      out.so = sc_out + (size_t)ug * K;
-    }
-    sel.run(es, ep, out);
-  }
-  __syncthreads();   // the list (and s_part, s_uf) complete
-
-  // ---- 4. retrieved entries from the list
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) NK[c] = 0.f;
+  // ---- 5. retrieved entries from the list
   float fr[FPL];
 #pragma unroll
   for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
@@ -259,6 +364,10 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       else pr[e].zero();
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
+    if (ex_due) {   // uniform within the group; scored while the batch loads
+      add_exact(xk, xv);
+      ex_due = false;
+    }
 #pragma unroll
     for (int e = 0; e < B; ++e) {
       float ph[FPL], vv[CPL];
@@ -276,48 +385,61 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       }
     }
   }
+  if (ex_due) add_exact(xk, xv);
+  for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
+    const int pos = ex_pos(j);
+    xv.load(vunit + (size_t)pos * D + part * CPL);
+    xk.load(kunit + (size_t)pos * D + part * CPL);
+    add_exact(xk, xv);
+  }
 
-  // ---- 5. combine the eight groups of each wave (lanes l, l^8, l^16, l^32 hold
-  //      the same columns), then the waves through LDS, rescaling to the larger max
-#pragma unroll
-  for (int sh = LPE; sh < kWave; sh <<= 1) {
-    const float mo = __shfl_xor(mrun, sh, kWave);
-    const float mn = fmaxf(mrun, mo);
-    const float ra = mrun == -INFINITY ? 0.f : __expf(mrun - mn);
-    const float rb = mo == -INFINITY ? 0.f : __expf(mo - mn);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      N[c] = ra * N[c] + rb * __shfl_xor(N[c], sh, kWave);
-      NK[c] += __shfl_xor(NK[c], sh, kWave);
-    }
-    Z = ra * Z + rb * __shfl_xor(Z, sh, kWave);
-    ZK += __shfl_xor(ZK, sh, kWave);
-    mrun = mn;
+  // ---- 6. combine.  The block's largest running max; every group rescales to
+  //      it; the two groups of a 16-lane row add (row rotation by 8); the pair
+  //      sums go through LDS and are added in pair order (deterministic).
+  {
+    const float wm = wave_max_dpp(mrun);
+    if (lane == 0) s_wm[wave] = wm;
   }
-  if (lane < LPE) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      s_wn[wave][part * CPL + c] = N[c];
-      s_wk[wave][part * CPL + c] = NK[c];
-    }
-    if (lane == 0) {
-      s_wm[wave] = mrun;
-      s_wz[wave] = Z;
-      s_wzk[wave] = ZK;
-    }
-  }
-  __syncthreads();
+  __syncthreads();   // also: every gather has read the list, so its LDS is free
   float ms = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
-  float sw[NW];
-  float ZE = 0.f, ZKt = 0.f;
+  {
+    const float r = mrun == -INFINITY ? 0.f : __expf(mrun - ms);
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    sw[w] = s_wm[w] == -INFINITY ? 0.f : __expf(s_wm[w] - ms);
-    ZE += sw[w] * s_wz[w];
-    ZKt += s_wzk[w];
+    for (int c = 0; c < CPL; ++c) {
+      N[c] *= r;
+      N[c] += dpp_f<0x128>(N[c]);      // row_ror:8: the other group of the row
+      NK[c] += dpp_f<0x128>(NK[c]);
+    }
+    Z *= r;
+    Z += dpp_f<0x128>(Z);
+    ZK += dpp_f<0x128>(ZK);
+    if ((lane & 15) < LPE) {
+      float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NV;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        rp[part * CPL + c] = N[c];
+        rp[D + part * CPL + c] = NK[c];
+      }
+      if (part == 0) {
+        rp[2 * D] = Z;
+        rp[2 * D + 1] = ZK;
+      }
+    }
   }
+  __syncthreads();
+  for (int j0 = 0; j0 < NV; j0 += NT / 8) {
+    const int j = j0 + tid / 8, sl = tid % 8;
+    float acc = 0.f;
+    if (j < NV) {
+      for (int pp = sl; pp < NP; pp += 8) acc += red[(size_t)pp * NV + j];
+    }
+    acc = lane_group_sum<8>(acc);
+    if (sl == 0 && j < NV) s_fin[j] = acc;
+  }
+  __syncthreads();
+  const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
   const float uf = rs ? s_uf : 0.f;
   float zr = 0.f;
   if (rs) zr = fmaxf(uf - (sub ? ZKt : 0.f), 0.f);
@@ -329,20 +451,14 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const float bres = __expf(-Mx);
   const float den = a * ZE + bres * zr;
   for (int col = tid; col < D; col += NT) {
-    float NE = 0.f, NKc = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      NE += sw[w] * s_wn[w][col];
-      NKc += s_wk[w][col];
-    }
     float nu = 0.f;
     if (rs) {
       float fs = 0.f;
 #pragma unroll
       for (int k = 0; k < FB; ++k) fs += s_part[k][col];
-      nu = fs - (sub ? NKc : 0.f);
+      nu = fs - (sub ? s_fin[D + col] : 0.f);
     }
-    y[(size_t)ug * D + col] = (a * NE + bres * nu) / den;
+    y[(size_t)ug * D + col] = (a * s_fin[col] + bres * nu) / den;
   }
   if (stats != nullptr && tid == 0) {
     stats[(size_t)ug * 4 + 0] = ms;
@@ -364,14 +480,14 @@ hipError_t launch_fused_nt(const DecodePlan& pl, const float* q, int G, const rm
   const TopkPlan& tp = pl.topk;
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
   auto kern = decode_fused_kernel<KT, PT, D, M, NT>;
-  const size_t lds = (size_t)(2 * pl.e_max + 2 * K) * 4 + 16;
+  const size_t lds = fused_dyn_bytes(tp.n_chunks, tp.r_cap, K, D, NT);
   // the plan checked the fit; a launch that would not fit is refused here too
   if (lds + kernel_static_lds<&decode_fused_kernel<KT, PT, D, M, NT>>() > device_info().lds_per_block)
     return hipErrorInvalidConfiguration;
   return launch_kernel("decode_fused_kernel", kern, dim3(kv.n_units * G), dim3(NT), (uint32_t)lds, st, q,
                        G, static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
                        (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, tp.n_chunks,
-                       tp.r_cap, K, pl.e_max, reinterpret_cast<const float4*>(ws + tp.off_hp),
+                       tp.r_cap, K, reinterpret_cast<const float4*>(ws + tp.off_hp),
                        reinterpret_cast<const float2*>(ws + tp.off_ent),
                        reinterpret_cast<const int2*>(ws + tp.off_meta), idx, sel, phi_q, Wq, bq, P,
                        static_cast<const PT*>(phi_k), S, u, flags, y, stats, 1.0f / sqrtf((float)D));

@@ -299,6 +299,51 @@ __device__ DD dd_dot(const float* q, const T* krow) {
   return r;
 }
 
+// The same double-double dot by a group of P = D sizeof(T) / 16 consecutive
+// lanes, each loading one 16-byte piece of the row: lane `part` sums its
+// elements as above, then the partial pairs meet in a butterfly of TwoSums.  A
+// lane pair computes the same TwoSum (its error term is exact in either
+// argument order) and the same sum of error terms, so every lane of the group
+// returns the same pair.  The exactness condition and the bound above hold
+// unchanged: any order makes d - 1 additions whose running sums are bounded by
+// sum|q_j k_j| and whose error terms are multiples of 2^E.
+template <typename T, int D>
+struct DDGroup {
+  static constexpr int E = 16 / (int)sizeof(T);   // elements per lane
+  static constexpr int P = D / E;                  // lanes per row
+};
+template <typename T, int D>
+__device__ __forceinline__ DD dd_dot_group(const float* q, const T* krow, int part) {
+  constexpr int E = DDGroup<T, D>::E, P = DDGroup<T, D>::P;
+  static_assert(P >= 1 && (P & (P - 1)) == 0 && P <= 64, "power-of-two lane groups within a wave");
+  RawPiece<T, E> w;
+  w.load(krow + part * E);
+  float kv[E];
+  w.unpack(kv);
+  double s = 0.0, c = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double p = (double)q[part * E + e] * (double)kv[e];
+    double t, err;
+    two_sum(s, p, t, err);
+    s = t;
+    c += err;
+  }
+#pragma unroll
+  for (int off = P / 2; off >= 1; off >>= 1) {
+    const double so = __shfl_xor(s, off), co = __shfl_xor(c, off);
+    double t, err;
+    two_sum(s, so, t, err);
+    s = t;
+    c = (c + co) + err;
+  }
+  DD r;
+  two_sum(s, c, r.hi, r.lo);
+  if (r.hi == 0.0) r.hi = 0.0;  // canonical +0
+  if (r.lo == 0.0) r.lo = 0.0;
+  return r;
+}
+
 // a > b in the (exact score desc, position asc) order
 __device__ __forceinline__ bool dd_key_greater(DD a, int ia, DD b, int ib) {
   if (a.hi != b.hi) return a.hi > b.hi;

@@ -73,6 +73,7 @@ constexpr int kSelBandMax = 512;        // band members resolved in LDS
 constexpr int kSelMaxEntries = 16384;   // union entries held in LDS by a select block
 constexpr int kSelBins = 1024;          // linear bins over the union's score range
 constexpr int kSelThreads = 1024;       // select block size
+constexpr int kWaveSelRows = 8;         // rows of 64 entries per load batch of the one-wave selection
 
 struct TopkPlan {
   int n_chunks, ch, r_min, r_cap;
@@ -102,12 +103,23 @@ struct DecodePlan {
   TopkPlan topk;       // the scan's chunks and reports (workspace offset 0)
   bool fused;
   int fused_threads;   // 256, 512 or 1024
-  int e_max;           // union slots of the fused kernel
   MergePlan merge;     // the separate path
   size_t off_idx, off_sel, off_merge, total;
 };
 DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m, int phi_dtype,
                        bool recompute);
+// report slots each thread of the fused kernel loads per round (a chunk's slots
+// are spread over the 2^(log2 NT - ceil(log2 n_chunks)) threads it gets)
+template <int NT> constexpr int kFusedSpec = 8;
+inline bool fused_slots_fit(int n_chunks, int nt) { return n_chunks >= 1 && n_chunks <= nt; }
+// dynamic LDS of the fused kernel: the union of the chunk reports and the
+// selected list, or (reusing it) the combine's group-pair sums
+inline size_t fused_dyn_bytes(int n_chunks, int r_cap, int K, int d, int nt) {
+  const size_t ub = (size_t)kWaveSelRows * 64;   // whole load batches of the one-wave selection
+  const size_t a = 2 * (((size_t)n_chunks * r_cap + ub - 1) / ub * ub) + 2 * (size_t)K;
+  const size_t b = (size_t)(nt / 16) * (2 * d + 2);
+  return (a > b ? a : b) * 4 + 16;
+}
 // static LDS of the fused kernel instantiation a plan would launch
 size_t fused_static_lds(int kv_dtype, int phi_dtype, int d, int m, int nt);
 

@@ -538,4 +538,242 @@ struct HeadSelect {
   }
 };
 
+
+// ---------------------------------------------------------------- few-barrier selection
+// The exact selection of HeadSelect::run by a whole block, in as few barrier
+// phases as the data dependences allow (for the fused decode kernel).  Steps
+// whose input every wave can read (the K-th bin from the histogram, the rank
+// of that bin's members, the chunk certificate) are computed by every wave
+// redundantly instead of by one wave behind a barrier.
+//
+// Input: the union of the chunk reports in LDS in report order (= position
+// order): score es[i] and mid position ep[i] for i < nE, followed by empty
+// entries (es = -inf, ep = 0) up to a whole row of 64; the union's score range
+// [lo, hi]; the chunk table (threshold bin, reported count); w.hist zeroed and
+// w.misc initialised (init_block_select) behind a barrier.  The steps:
+//   histogram over [lo, hi] | the bin bK of the K-th largest score, its members
+//   and extent | t = the K-th largest fp32 score (rank among the members), the
+//   completeness certificate of every chunk for t - 2.5 eps, the count above
+//   t + 2.5 eps and the band [t - 2.5 eps, t + 2.5 eps] | the band's
+//   double-double scores (one lane group per member) when it must be split |
+//   rank and mark | the ordered output: wave w owns a contiguous range of rows,
+//   counts its entries | and writes them at the sum of the lower waves' counts.
+// Returns false (the same on every thread) when the block must run the exact
+// fallback (a chunk withheld tokens, too few entries, band too wide); `out`
+// is untouched then.  The caller puts a barrier before any use of `out`.
+struct BlockSelLds {
+  uint32_t* hist;   // kSelBins
+  float* cand;      // kSelBandMax: scores of the K-th bin's members
+  int* bslot;       // kSelBandMax: band members' entries
+  DD* bdd;          // kSelBandMax: their double-double scores
+  int* misc;        // 8: [0] members, [1] / [2] ordered min / max member, [3] count above, [4] band, [5] t
+  int* wcnt;        // one per wave
+};
+
+template <int NT>
+__device__ __forceinline__ void init_block_select(const BlockSelLds& w) {
+  for (int b = threadIdx.x; b < kSelBins; b += NT) w.hist[b] = 0u;
+  if (threadIdx.x < 8) w.misc[threadIdx.x] = threadIdx.x == 1 ? (int)0xffffffffu : 0;
+}
+
+template <typename KT, int D, int NT>
+__device__ bool block_select(const float* es, int* ep, int nE, float lo, float hi, const int* s_bcs,
+                             const int* s_nrep, int n_chunks, int ch, int L_mid, int n_sink, int K,
+                             bool trunc, const HeadParams& hp, const float* qf, const KT* kunit,
+                             float inv_sqrt_d, const BlockSelLds& w, const SelOut& out) {
+  constexpr int NBS = kSelBins;
+  constexpr int NW = NT / kWave;
+  constexpr int BPL = NBS / kWave;             // histogram bins per lane (each wave reads them all)
+  constexpr int SELF = 1 << 30;                // "taken" mark on a band member's position
+  static_assert(BPL % 4 == 0, "whole 16-byte histogram reads");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (trunc || nE < K) return false;
+  const int rows = (nE + kWave - 1) / kWave;
+
+  const bool whole = K == L_mid;   // every mid token is selected (the chunks reported all)
+  float th_lo = -INFINITY, th_hi = -INFINITY;
+  if (!whole) {
+    const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
+    auto ubin = [&](float x) {
+      const float t = __fmul_rn(__fsub_rn(x, lo), inv);
+      return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
+    };
+    // ---- histogram over [lo, hi]
+    for (int i = tid; i < nE; i += NT) atomicAdd(&w.hist[ubin(es[i])], 1u);
+    __syncthreads();
+    // ---- every wave: the bin of the K-th largest (lane l owns the 16 bins
+    //      NBS-16(l+1) .. NBS-16l-1, read as four 16-byte words) ...
+    int cb[BPL], ls = 0;
+    {
+      const uint4* h4 = reinterpret_cast<const uint4*>(w.hist + NBS - BPL * (lane + 1));
+#pragma unroll
+      for (int j = 0; j < BPL / 4; ++j) {
+        const uint4 v = h4[j];
+        cb[4 * j] = (int)v.x; cb[4 * j + 1] = (int)v.y; cb[4 * j + 2] = (int)v.z; cb[4 * j + 3] = (int)v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) ls += cb[j];
+    }
+    const int incl = wave_incl_scan_dpp(ls);
+    const int owner = __ffsll((long long)__ballot(incl >= K)) - 1;
+    int bK = 0, above = 0;
+    {
+      // descending within the lane: bin NBS-BPL*lane-1-j is cb[BPL-1-j]
+      int run = incl - ls, b = 0, a = 0;
+      bool found = false;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        const int c = cb[BPL - 1 - j];
+        if (!found && run + c >= K) {
+          b = NBS - 1 - BPL * lane - j;
+          a = run;
+          found = true;
+        }
+        run += c;
+      }
+      bK = __builtin_amdgcn_readlane(b, owner);
+      above = __builtin_amdgcn_readlane(a, owner);
+    }
+    const int rK = K - above;   // the K-th score is the rK-th largest member of bin bK
+    // ... and its members: scores appended (order free), extent
+    {
+      float xlo = INFINITY, xhi = -INFINITY;
+      for (int r = wave; r < rows; r += NW) {
+        const float x = es[r * kWave + lane];
+        const bool m = x > -INFINITY && ubin(x) == bK;
+        const uint64_t bm = __ballot(m);
+        if (bm != 0ull) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&w.misc[0], (int)__popcll(bm));
+          base = __builtin_amdgcn_readlane(base, 0);
+          const int o = base + lanes_below(bm);
+          if (m && o < kSelBandMax) w.cand[o] = x;
+        }
+        xlo = m ? fminf(xlo, x) : xlo;
+        xhi = m ? fmaxf(xhi, x) : xhi;
+      }
+      xlo = wave_min_dpp(xlo);
+      xhi = wave_max_dpp(xhi);
+      if (lane == 0 && xlo <= xhi) {
+        atomicMin(reinterpret_cast<uint32_t*>(&w.misc[1]), ord_f32(xlo));
+        atomicMax(reinterpret_cast<uint32_t*>(&w.misc[2]), ord_f32(xhi));
+      }
+    }
+    __syncthreads();
+    const int nm = w.misc[0];
+    float t_lo = unord_f32((uint32_t)w.misc[1]), t_hi = unord_f32((uint32_t)w.misc[2]);
+    if (nm <= kSelBandMax) {
+      // t = the rK-th largest member (every member holding that value agrees)
+      float t = -INFINITY;
+      if (nm <= kWave) {     // every wave ranks them
+        if (lane < nm) {
+          const float x = w.cand[lane];
+          int gt = 0, ge = 0;
+          for (int k2 = 0; k2 < nm; ++k2) {
+            const float y = w.cand[k2];
+            gt += y > x;
+            ge += y >= x;
+          }
+          if (gt < rK && rK <= ge) t = x;
+        }
+        t = wave_max_dpp(t);
+      } else {               // the block ranks them
+        for (int j = tid; j < nm; j += NT) {
+          const float x = w.cand[j];
+          int gt = 0, ge = 0;
+          for (int k2 = 0; k2 < nm; ++k2) {
+            const float y = w.cand[k2];
+            gt += y > x;
+            ge += y >= x;
+          }
+          if (gt < rK && rK <= ge) w.misc[5] = __float_as_int(x);
+        }
+        __syncthreads();
+        t = __int_as_float(w.misc[5]);
+      }
+      t_lo = t_hi = t;
+    }
+    th_lo = t_lo - 2.5f * hp.eps;
+    th_hi = t_hi + 2.5f * hp.eps;
+    // ---- every wave: each chunk must have reported all of its tokens >= th_lo
+    {
+      const int blo = lin_bin(th_lo, hp);
+      bool bad = false;
+      for (int c = lane; c < n_chunks; c += kWave) {
+        const int n_c = min(ch, L_mid - c * ch);
+        bad |= s_nrep[c] != n_c && s_bcs[c] > blo;
+      }
+      if (__ballot(bad) != 0ull) return false;
+    }
+    // ---- the count above th_hi and the band, appended (order free)
+    {
+      int nin = 0;
+      for (int r = wave; r < rows; r += NW) {
+        const float x = es[r * kWave + lane];
+        nin += (int)__popcll(__ballot(x > th_hi));
+        const bool inb = x > -INFINITY && x <= th_hi && x >= th_lo;
+        const uint64_t bm = __ballot(inb);
+        if (bm != 0ull) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&w.misc[4], (int)__popcll(bm));
+          base = __builtin_amdgcn_readlane(base, 0);
+          const int o = base + lanes_below(bm);
+          if (inb && o < kSelBandMax) w.bslot[o] = r * kWave + lane;
+        }
+      }
+      if (lane == 0 && nin > 0) atomicAdd(&w.misc[3], nin);
+    }
+    __syncthreads();
+    const int nb = w.misc[4], kp = K - w.misc[3];
+    if (nb > kSelBandMax || kp < 1 || nb < kp) return false;
+    if (nb > kp) {
+      // ---- the band's double-double scores, one lane group per member
+      constexpr int P = DDGroup<KT, D>::P;
+      for (int b = tid / P; b < nb; b += NT / P) {   // uniform within the group
+        const DD d = dd_dot_group<KT, D>(qf, kunit + (size_t)(n_sink + ep[w.bslot[b]]) * D, tid % P);
+        if (tid % P == 0) w.bdd[b] = d;
+      }
+      __syncthreads();
+      // rank by (exact score desc, position asc); positions masked since marks
+      // of other threads may already be set
+      for (int b = tid; b < nb; b += NT) {
+        const DD mine = w.bdd[b];
+        const int mp = ep[w.bslot[b]] & ~SELF;
+        int rank = 0;
+        for (int b2 = 0; b2 < nb; ++b2) rank += dd_key_greater(w.bdd[b2], ep[w.bslot[b2]] & ~SELF, mine, mp);
+        if (rank < kp) ep[w.bslot[b]] = mp | SELF;
+      }
+    } else {
+      for (int b = tid; b < nb; b += NT) ep[w.bslot[b]] |= SELF;
+    }
+    __syncthreads();
+  }
+  // ---- the ordered output: wave w owns rows [w RW, (w + 1) RW)
+  const int RW = (rows + NW - 1) / NW;
+  const int r0 = min(rows, wave * RW), r1 = min(rows, r0 + RW);
+  auto taken = [&](float x, int e) { return x > -INFINITY && (whole || x > th_hi || (e & SELF) != 0); };
+  int cnt = 0;
+  for (int r = r0; r < r1; ++r)
+    cnt += (int)__popcll(__ballot(taken(es[r * kWave + lane], ep[r * kWave + lane])));
+  if (lane == 0) w.wcnt[wave] = cnt;
+  __syncthreads();
+  int o = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int c = w.wcnt[v];
+    o += v < wave ? c : 0;
+    total += c;
+  }
+  if (total != K) return false;
+  for (int r = r0; r < r1; ++r) {
+    const float x = es[r * kWave + lane];
+    const int e = ep[r * kWave + lane];
+    const bool tk = taken(x, e);
+    const uint64_t bm = __ballot(tk);
+    if (tk) out.put(o + lanes_below(bm), n_sink + (e & ~SELF), x * inv_sqrt_d);
+    o += (int)__popcll(bm);
+  }
+  return true;
+}
+
 }  // namespace rma
