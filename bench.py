@@ -1,17 +1,21 @@
 #!/usr/bin/env python3
-"""Benchmark of the Top-K+phi residual-mass-accounting path on one MI355X.
+"""Benchmark of Top-K+phi residual-mass-accounting decode on one MI355X.
 
-One step = one pass of the whole path over one batch of the workload:
-prefill summaries (S, u; rma_build_summaries), then for every
-decode step of the workload phi_q (rma_phi_features), the exhaustive Top-K
-(rma_decode_topk) and the exact branch + subtraction + residual + single
-normalisation (rma_decode_merge).  Default workload: the 1B-shaped GQA layer at
-32K context with a 1 % budget (8 kv heads x 4 query heads, d=64, K=328).
+The headline is the method's decode: one timed step is one decode pass over
+the workload's batch (every query head of every unit, every decode step of the
+workload) through rma_decode: the exhaustive scan, then the fused selection
+and merge (exact terms, retrieved-token subtraction, residual, single
+normalisation), with f = phi_q(q) computed inside.  The prefill summaries
+(rma_build_summaries) are built before timing and reported in a block of
+their own, with their bandwidth and matrix-core use; the whole path (build +
+decode per step) is reported as an extra rate.  Default workload: the
+1B-shaped GQA layer at 32K context with a 1 % budget (8 kv heads x 4 query
+heads, d = 64, K = 328).
 
 Inputs are resident in HBM before timing starts.  Steps rotate over copies of
-the inputs whose total exceeds 1 GB so that no step is served from the 256 MB
-last-level cache.  Each step is replayed from a HIP graph (compared against an
-eager run first).  Prints one JSON line.
+the inputs whose total exceeds 1 GB, so that no step is served from the 256 MB
+last-level cache.  Steps are replayed from HIP graphs (checked against an eager
+run first).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config c1]
 """
@@ -27,8 +31,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores
 MLP_WIDTH = 512
 METRIC = "decode queries/s + achieved HBM GB/s (% peak), 1B-shape GQA, 32K ctx, 1% budget"
 
@@ -44,14 +48,15 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode with the two calls rma_decode_topk + rma_decode_merge instead of rma_decode")
     ap.add_argument("--separate-phi", action="store_true",
-                    help="compute phi_q with rma_phi_features instead of inside the merge")
-    ap.add_argument("--no-full", action="store_true",
-                    help="skip timing the full-attention reference decode")
+                    help="compute phi_q with rma_phi_features instead of inside the decode")
+    ap.add_argument("--no-full", action="store_true", help="skip timing the full-attention reference decode")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming read / copy ceilings")
     ap.add_argument("--recompute-phi", action="store_true",
-                    help="do not store the phi_k rows at prefill; the merge recomputes the retrieved "
-                         "rows from their keys (bf16 keys; saves the rows' HBM, costs MFMA/VALU work "
-                         "at every decode step)")
+                    help="do not store the phi_k rows at prefill; decode recomputes the retrieved rows from "
+                         "their keys (bf16 keys; saves the rows' HBM, costs matrix-core work per step)")
     ap.add_argument("--phi", choices=("elu", "mlp"), default="elu",
                     help="feature map: elu(Wx+b)+1 (the workloads' form, default) or the pages' MLP family "
                          "(one-block ReZero MLP, width 512, exponentiated output, d_phi = 64)")
@@ -65,13 +70,7 @@ def parse():
 # Bytes per launch from rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 # dispatch) of this script, each scaled by what the same counter reads for a plain
 # copy of known size.  A record holds only for the kernel sources it was taken on.
-TRAFFIC = {
-    # c1 (K=328); FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 from a 1.024 GB neg copy
-    ("build_mfma_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=69264497, write_bytes=84049512),
-    ("topk_scan_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=33832736, write_bytes=636576),
-    ("merge_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=7074332, write_bytes=8192),
-    ("full_partial_kernel", "c1", 328): dict(csrc="c4f432f3331a987a", fetch_bytes=67368312, write_bytes=589824),
-}
+TRAFFIC = {}
 
 
 def csrc_digest():
@@ -96,57 +95,67 @@ def measured_traffic(kernel, workload, K):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
-# ------------------------------------------------------------------ byte model
-def call_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True, mlp=False):
-    """Algorithmic HBM bytes of each call for one batch (inputs read once,
-    outputs written once; workspace scratch excluded).  With mlp, the MLP
-    features: phik = phi_k rows of the keys, build = summaries over those rows,
-    phi = phi_q of the queries."""
-    kb = kernel_bytes(cfg, K, n_gen, store_phi, fused_phi)
-    out = dict(build=kb["build_mfma_kernel"] + kb["build_reduce_kernel"], phi=kb["phi_kernel"],
-               topk=kb["topk_scan_kernel"] + kb["topk_select_kernel"], merge=kb["merge_kernel"], phik=0)
-    if mlp:
-        out.update(phik=kb["phi_mlp_kernel"], build=kb["build_valu_kernel"] + kb["build_reduce_kernel"],
-                   phi=kb["phi_mlp_small_kernel"])
-    return out
-
-
+# ------------------------------------------------------------------ byte and flop model
 def kernel_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
-    """Algorithmic HBM bytes of each kernel for one batch.  The builder reads the
-    mid-region K and V rows once (and writes phi_k once when the rows are stored;
-    its per-chunk partial sums are scratch); the reduce writes S, u, kappa; the scan reads the mid-region K
-    rows once (score bins and candidate lists are scratch); the select writes the
-    indices and their scores; the merge reads what one query's exact support and
-    residual need.  With fused_phi the merge computes f = phi_q(q) itself (it
-    reads Wq, bq instead of f, and no phi kernel runs)."""
+    """Algorithmic HBM bytes of each kernel for one batch: inputs read once,
+    outputs written once; workspace scratch (chunk reports, partial sums) is
+    excluded.  The scan reads the mid-region keys once; the select writes the
+    indices and their scores; the merge (and the fused select-and-merge kernel)
+    reads one query's exact support, its retrieved phi_k rows and the unit's
+    S, u.  With fused_phi the decode computes f = phi_q(q) itself (it reads
+    Wq, bq instead of f).  The fused kernel counts the 4-byte kept score of
+    each retrieved entry as the two-call path does (the selection's output),
+    although there it never leaves the chip."""
     U, G, d, m, P = cfg.U, cfg.G, cfg.d, cfg.m, cfg.P
     Lm, na = cfg.L_mid, cfg.n_anchor
     e = 4 if cfg.kv_dtype == "f32" else 2
     ep = 4 if cfg.phi_dtype == "f32" else 2
     params = P * (m * d * 4 + m * 4)
-    # phi_k rows are either stored by the builder and gathered by the merge
-    # (default), or not stored, the merge recomputing the retrieved ones from
-    # their key rows (which it then reads instead)
     phi_row = m * ep if store_phi else d * e
+    merge = (U * G * (K * (d * e + phi_row + 4) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
+             + U * (m * d * 4 + m * 4) + (0 if store_phi else params)
+             + (params - U * G * m * 4 if fused_phi else 0))
     return {
         "build_mfma_kernel": U * (2 * Lm * d * e + (Lm * m * ep if store_phi else 0)) + params,
         "build_reduce_kernel": U * (m * d * 4 + m * 4 + 4),
         "phi_kernel": 0 if fused_phi else U * G * (d * 4 + m * 4) + params,
         "topk_scan_kernel": U * (Lm * d * e + 4) + U * G * d * 4,
         "topk_select_kernel": U * G * K * 8,
-        "merge_kernel": U * G * (K * (d * e + phi_row + 8) + (na + n_gen) * 2 * d * e + d * 4 + m * 4 + d * 4)
-        + U * (m * d * 4 + m * 4) + (0 if store_phi else params)
-        + (params - U * G * m * 4 if fused_phi else 0),
-        # with a head's entries split over several blocks, this kernel writes y
-        # from their partials (scratch); the merge call's bytes are the merge's
+        "merge_kernel": merge + U * G * K * 4,       # it also reads the indices
+        "decode_fused_kernel": merge,
         "merge_combine_kernel": U * G * d * 4,
-        # MLP features (the pages' family): keys of the mid-region in, phi_k rows
-        # out, and each map's bf16 weights and fp32 biases once
         "phi_mlp_kernel": U * Lm * (d * e + m * ep) + P * mlp_weight_bytes(d, m),
         "phi_mlp_small_kernel": U * G * (d * 4 + m * 4) + P * G * mlp_weight_bytes(d, m),
-        # summaries over given phi_k rows: rows, V and (for kappa) K read once
         "build_valu_kernel": U * (Lm * m * ep + 2 * Lm * d * e),
+        "full_partial_kernel": U * (cfg.L + n_gen) * 2 * d * e + U * G * d * 4,
     }
+
+
+def decode_step_bytes(cfg, K, n_gen, store_phi=True, fused_phi=True):
+    """Algorithmic bytes of one decode step of the batch (scan + selection +
+    merge; the method's own minimum traffic)."""
+    kb = kernel_bytes(cfg, K, n_gen, store_phi, fused_phi)
+    return kb["topk_scan_kernel"] + kb["decode_fused_kernel"] + kb["phi_kernel"]
+
+
+def build_bytes(cfg, store_phi=True):
+    kb = kernel_bytes(cfg, 0, 0, store_phi)
+    return kb["build_mfma_kernel"] + kb["build_reduce_kernel"]
+
+
+def build_flops(cfg):
+    """Matrix-core work of the summary build for one batch.  Algorithmic: the
+    projection K W^T and the contraction Phi^T [V | 1], 2 L_mid m (d + d + 1)
+    per unit.  Issued: what the builder's MFMA instructions compute, 16x16x32
+    bf16 tiles (16384 flops each): per 64-token tile and 16-feature slice,
+    4 (d/32) 2 for the projection (W split into bf16 high and low parts) and
+    2 (1 + d/16) for S and u; tiles = ceil(L_mid / 64) per unit (chunk
+    boundaries add under 1 %)."""
+    U, d, m, Lm = cfg.U, cfg.d, cfg.m, cfg.L_mid
+    algo = U * 2 * Lm * m * (2 * d + 1)
+    per_tile = 4 * (d // 32) * 2 + 2 * (1 + d // 16)
+    issued = U * math.ceil(Lm / 64) * (m // 16) * per_tile * 16 * 16 * 32 * 2
+    return algo, issued
 
 
 def mlp_weight_bytes(d, m):
@@ -154,7 +163,7 @@ def mlp_weight_bytes(d, m):
     return 2 * (H * d + 2 * H * H + m * H) + 4 * (3 * H + 1 + m)
 
 
-def kernel_flops(cfg):
+def mlp_flops(cfg):
     """Matrix-core flops per launch of the MLP feature kernels (2 per multiply-add)."""
     U, G, d, m, H = cfg.U, cfg.G, cfg.d, cfg.m, MLP_WIDTH
     per_row = 2 * (d * H + 2 * H * H + H * m)
@@ -165,16 +174,15 @@ def kernel_flops(cfg):
 class PathRunner:
     """Prepared C-ABI calls for one copy of the inputs (no per-call allocation)."""
 
-    def __init__(self, R, cfg, inp, K, ws, torch, store_phi, fused_phi=True, mlp=None):
+    def __init__(self, R, cfg, inp, K, ws, torch, store_phi, fused_phi=True, mlp=None, separate=False):
         self.R, self.cfg, self.K, self.t = R, cfg, K, torch
-        # mlp: (phi_k weights, phi_q weights) of the MLP feature maps, or None
-        self.mlp = mlp
+        self.mlp = mlp                      # (phi_k weights, phi_q weights) of the MLP maps, or None
+        self.separate = separate            # decode with rma_decode_topk + rma_decode_merge
         L = R.lib()
         self.L = L
         dev = inp.k.device
         U, G, d, m = cfg.U, cfg.G, cfg.d, cfg.m
         self.k, self.v, self.q, self.W, self.b = inp.k, inp.v, inp.q, inp.W, inp.b
-        # phi_k rows: stored by the builder, or (None) recomputed by the merge
         self.phi_k = torch.empty(U, cfg.L_mid, m, dtype=cfg.torch_phi_dtype(), device=dev) if store_phi else None
         self.S = torch.empty(U, m, d, dtype=torch.float32, device=dev)
         self.u = torch.empty(U, m, dtype=torch.float32, device=dev)
@@ -193,9 +201,7 @@ class PathRunner:
         self.pdt = R._dt(cfg.torch_phi_dtype())
         self.Wm, self.bm = (None, None) if store_phi else (inp.W, inp.b)
         self.yf = None
-        # f = phi_q(q): computed inside the merge (fused), or by rma_phi_features
-        # (or by the MLP feature kernel)
-        self.fused_phi = fused_phi and mlp is None
+        self.fused_phi = fused_phi and mlp is None     # f = phi_q(q) computed inside the decode
         if mlp is not None:
             self.kmid = inp.k[:, cfg.n_sink:cfg.n_sink + cfg.L_mid]
 
@@ -206,13 +212,18 @@ class PathRunner:
                                         ctypes.byref(wk._c), cfg.m, wk.P, self.p(self.phi_k), self.pdt, st)
         assert r == 0, r
 
-    def build(self, st):
+    def summaries(self, st):
         cfg, p = self.cfg, self.p
         W, b = (None, None) if self.mlp is not None else (self.W, self.b)   # MLP rows are given
         r = self.L.rma_build_summaries(ctypes.byref(self.kv), ctypes.byref(self.sp_pre), p(W), p(b),
                                        cfg.m, cfg.P, p(self.phi_k), self.pdt, p(self.S), p(self.u),
                                        p(self.kappa), p(self.ws), self.ws.numel(), st)
         assert r == 0, r
+
+    def build(self, st):
+        if self.mlp is not None:
+            self.phik(st)
+        self.summaries(st)
 
     def phi(self, s, st):
         cfg, p = self.cfg, self.p
@@ -242,49 +253,60 @@ class PathRunner:
                                     p(self.u), 0, p(self.y[s]), None, p(self.ws), self.ws.numel(), st)
         assert r == 0, r
 
-    def full(self, s, st):
-        """The full-attention reference for decode step s (no diagnostics)."""
+    def one_call(self, s, st):
+        cfg, p = self.cfg, self.p
+        f, Wq, bq = (None, self.W, self.b) if self.fused_phi else (self.f[s], None, None)
+        r = self.L.rma_decode(p(self.q[s]), p(f), p(Wq), p(bq), cfg.G, ctypes.byref(self.kv),
+                              ctypes.byref(self.sp_dec[s]), p(self.kappa), self.K, p(self.phi_k), self.pdt,
+                              p(self.Wm), p(self.bm), cfg.P, cfg.m, p(self.S), p(self.u), 0, None, None,
+                              p(self.y[s]), None, p(self.ws), self.ws.numel(), st)
+        assert r == 0, r
+
+    def decode_calls(self, s):
+        """The calls of decode step s, in order, as (name, fn(stream))."""
+        calls = [] if self.fused_phi else [("phi", lambda st: self.phi(s, st))]
+        if self.separate:
+            calls += [("topk", lambda st: self.topk(s, st)), ("merge", lambda st: self.merge(s, st))]
+        else:
+            calls += [("decode", lambda st: self.one_call(s, st))]
+        return calls
+
+    def decode(self, st):
+        for s in range(self.cfg.steps):
+            for _, fn in self.decode_calls(s):
+                fn(st)
+
+    def full(self, st):
+        """The full-attention reference for every decode step (no diagnostics)."""
         cfg, p = self.cfg, self.p
         if self.yf is None:
             self.yf = self.t.empty(cfg.steps, cfg.U, cfg.G, cfg.d, dtype=self.t.float32, device=self.k.device)
-        r = self.L.rma_decode_full(p(self.q[s]), cfg.G, ctypes.byref(self.kv), ctypes.byref(self.sp_dec[s]),
-                                   None, 0, None, p(self.yf[s]), None, p(self.ws), self.ws.numel(), st)
-        assert r == 0, r
+        for s in range(cfg.steps):
+            r = self.L.rma_decode_full(p(self.q[s]), cfg.G, ctypes.byref(self.kv), ctypes.byref(self.sp_dec[s]),
+                                       None, 0, None, p(self.yf[s]), None, p(self.ws), self.ws.numel(), st)
+            assert r == 0, r
 
-    def step(self, st):
-        """The whole path: prefill summaries, then every decode step."""
-        if self.mlp is not None:
-            self.phik(st)
-        self.build(st)
-        for s in range(self.cfg.steps):
-            if not self.fused_phi:
-                self.phi(s, st)
-            self.topk(s, st)
-            self.merge(s, st)
-
-    def traced_step(self, st, R):
-        """The whole path, eager, with every kernel timed by a pair of HIP events
-        that its own dispatch stamps at its start and end (rma_trace_arm).
-        Returns one record per call: (call name, [(kernel name, start event,
-        end event), ...])."""
+    def traced(self, R, what, st):
+        """The build or the decode, eager, with every kernel timed by a pair of
+        HIP events that its own dispatch stamps at its start and end
+        (rma_trace_arm).  Returns [(kernel name, start event, end event), ...]."""
         t = self.t
         out = []
 
-        def traced(name, fn):
-            evs = [t.cuda.Event(enable_timing=True) for _ in range(4)]
+        def one(fn):
+            evs = [t.cuda.Event(enable_timing=True) for _ in range(8)]
             R.rma_trace_arm(evs)
-            fn()
-            names = R.rma_trace_kernels()
-            out.append((name, [(n, evs[2 * j], evs[2 * j + 1]) for j, n in enumerate(names)]))
+            fn(st)
+            out.extend((n, evs[2 * j], evs[2 * j + 1]) for j, n in enumerate(R.rma_trace_kernels()))
 
-        if self.mlp is not None:
-            traced("phik", lambda: self.phik(st))
-        traced("build", lambda: self.build(st))
-        for s in range(self.cfg.steps):
-            if not self.fused_phi:
-                traced("phi", lambda: self.phi(s, st))
-            traced("topk", lambda: self.topk(s, st))
-            traced("merge", lambda: self.merge(s, st))
+        if what == "build":
+            if self.mlp is not None:
+                one(self.phik)
+            one(self.summaries)
+        else:
+            for s in range(self.cfg.steps):
+                for _, fn in self.decode_calls(s):
+                    one(fn)
         return out
 
 
@@ -343,42 +365,51 @@ def timed_replays(fn, n_copies, n, stream, use_graphs):
     return e0.elapsed_time(e1) / n * 1e3
 
 
-def decode_timing(args, cfg, runners, n_copies, stream, st, use_graphs, queries, log):
-    """The method's decode steps alone (phi_q, top-K, merge over summaries built
-    earlier) and the full-attention reference (rma_decode_full over every
-    position, no diagnostics) for the same decode steps, both replayed like the
-    whole step: the speed ratio of the method's decode against full attention."""
-    n = max(5, min(args.steps, 200))
+def kernel_stats(recs):
+    """Average duration (ms) and launches per record of each kernel name."""
+    tot, cnt = {}, {}
+    for rec in recs:
+        for kname, a, b in rec:
+            tot[kname] = tot.get(kname, 0.0) + a.elapsed_time(b)
+            cnt[kname] = cnt.get(kname, 0) + 1
+    return {k: tot[k] / cnt[k] for k in tot}, {k: cnt[k] / len(recs) for k in cnt}
 
-    def dec(i):
-        r = runners[i % n_copies]
-        for s in range(cfg.steps):
-            if not r.fused_phi:
-                r.phi(s, st)
-            r.topk(s, st)
-            r.merge(s, st)
 
-    def full(i):
-        r = runners[i % n_copies]
-        for s in range(cfg.steps):
-            r.full(s, st)
-
-    dec_us = timed_replays(dec, n_copies, n, stream, use_graphs)
-    full_us = timed_replays(full, n_copies, n, stream, use_graphs)
-    e = 2 if cfg.kv_dtype == "bf16" else 4
-    nbytes = sum(cfg.U * (cfg.L + cfg.n_gen(s)) * cfg.d * e * 2 + cfg.U * cfg.G * cfg.d * 8
-                 for s in range(cfg.steps))
-    log(f"[bench] method decode {dec_us:.2f} us/step ({queries / dec_us:.3f} M queries/s); full-attention "
-        f"decode {full_us:.2f} us/step, {nbytes / 1e6:.1f} MB -> {nbytes / (full_us / 1e6) / 1e9:.1f} GB/s")
-    return dec_us, {"us_per_step": round(full_us, 2), "queries_per_s": round(queries / (full_us / 1e6), 1),
-                    "algorithmic_MB": round(nbytes / 1e6, 3),
-                    "GBps": round(nbytes / (full_us / 1e6) / 1e9, 1),
-                    "method_decode_speedup": round(full_us / dec_us, 3), "timed_steps": n}
+def ceilings(torch, log, mb=2048):
+    """Measured streaming ceilings on this GPU with torch's own kernels: a read
+    that writes almost nothing (the sum of an fp32 array) and a copy (one read,
+    one write), over arrays well above the 256 MB last-level cache."""
+    n = int(mb * 1e6) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("read", lambda: torch.sum(a, dim=0, out=out), 4 * n),
+                             ("copy", lambda: b.copy_(a), 8 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(nbytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9, 1)
+    del a, b
+    log(f"[bench] streaming ceilings over {4 * n / 1e9:.2f} GB arrays: read {res['read']} GB/s, "
+        f"copy {res['copy']} GB/s (read + write)")
+    return {"read_GBps": res["read"], "copy_GBps": res["copy"], "array_GB": round(4 * n / 1e9, 2),
+            "kernels": "torch.sum (read), Tensor.copy_ (read + write)"}
 
 
 def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
-    """The oracle (numpy fp64) on host cores: prefill + decode of whole units
-    (with mlp_mode, its MLP feature maps on the same seeded weights)."""
+    """The oracle (numpy fp64) on host cores.  Decode queries/s: for each unit of
+    a bounded sample its prefill summaries are built (timed apart, as build
+    tokens/s), then every decode query of the unit is timed (exhaustive Top-K by
+    a full sort with exact rationals near ties, then the merge).  With all the
+    host's BLAS threads, then with one."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     import oracle as O
@@ -395,19 +426,21 @@ def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
         from kv_cache_reads_amd import workload as Wl
         pk, pq = (Wl.generate_phi_mlp(cfg, which, m=cfg.m) for which in "kq")
         hp = lambda par, i: {k: v[i].double().numpy() if v.dim() > 1 else float(v[i]) for k, v in par.items()}
-    with threadpool_limits(limits=ncpu):
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        nq, units, dt = 0, 0, 0.0
-        done = False
-        while not done:
-            for uidx in range(cfg.U):
+
+    def run(limit, budget):
+        with threadpool_limits(limits=limit):
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            nq, units, t_dec, t_build, toks = 0, 0, 0.0, 0.0, 0
+            while t_dec + t_build < budget:
+                uidx = units % cfg.U
                 hu = host(uidx)                      # host copy, not timed
-                t1 = time.perf_counter()
+                t0 = time.perf_counter()
                 if mlp_mode:
                     P = O.phi_mlp(hu["k"][M], hp(pk, uidx % cfg.P))
                     S, uu = O.summaries(P, hu["v"][M])
                 else:
                     P, S, uu = O.prefill_unit(hu["k"][M], hu["v"][M], hu["W"], hu["b"])
+                t1 = time.perf_counter()
                 for s in range(cfg.steps):
                     for g in range(cfg.G):
                         q = hu["q"][s, g]
@@ -418,15 +451,25 @@ def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
                         O.decode_query(q, f, hu["k"], hu["v"], P, S, uu, cfg.L, cfg.n_sink, cfg.n_tail,
                                        cfg.n_gen(s), K)
                         nq += 1
-                dt += time.perf_counter() - t1
+                t2 = time.perf_counter()
+                t_build += t1 - t0
+                t_dec += t2 - t1
+                toks += cfg.L_mid
                 units += 1
-                if dt >= seconds:
-                    done = True
-                    break
-    return dict(value=nq / dt, unit="queries/s", cores=int(threads), kind="oracle",
-                sample=f"{units} units of the same workload (prefill summaries + all {cfg.steps} decode "
-                       f"step(s) x {cfg.G} query heads per unit), {dt:.1f} s, numpy fp64 with "
-                       f"{threads} BLAS threads on {ncpu} visible cores")
+        return dict(q_per_s=nq / t_dec, build_tokens_per_s=toks / t_build, units=units, queries=nq,
+                    t_dec=t_dec, t_build=t_build, threads=int(threads))
+
+    full = run(ncpu, seconds)
+    one = run(1, max(seconds / 3, 3.0))
+    return dict(value=round(full["q_per_s"], 2), unit="queries/s", cores=full["threads"], kind="oracle",
+                sample=(f"{full['units']} units of the workload ({full['queries']} decode queries: exhaustive "
+                        f"Top-K + merge, {full['t_dec']:.1f} s; their prefill summaries timed apart, "
+                        f"{full['t_build']:.1f} s), numpy fp64 with {full['threads']} BLAS threads on {ncpu} "
+                        f"visible cores"),
+                build_tokens_per_s=round(full["build_tokens_per_s"], 1),
+                single_thread={"queries_per_s": round(one["q_per_s"], 2),
+                               "build_tokens_per_s": round(one["build_tokens_per_s"], 1),
+                               "sample": f"{one['units']} units, {one['queries']} queries, 1 BLAS thread"})
 
 
 def main():
@@ -456,6 +499,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: neg over {n * 4} bytes read + {n * 4} bytes written, 3 launches")
         del a, b
+    ceil = None if args.no_ceiling else ceilings(torch, log)
     t0 = time.time()
     inp = Wl.generate(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -474,7 +518,8 @@ def main():
     sp = R.Span(cfg.L, cfg.n_sink, cfg.n_tail, cfg.n_gen(cfg.steps - 1))
     wsb = max(R.rma_workspace_bytes(R.RMA_OP_BUILD_SUMMARIES, inp.k, sp, 1, 0, cfg.m),
               R.rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, inp.k, sp, cfg.G, K, cfg.m),
-              R.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, inp.k, sp, cfg.G, K, cfg.m))
+              R.rma_workspace_bytes(R.RMA_OP_DECODE_MERGE, inp.k, sp, cfg.G, K, cfg.m),
+              R.rma_workspace_bytes(R.RMA_OP_DECODE, inp.k, sp, cfg.G, K, cfg.m))
     if not args.no_full:
         wsb = max(wsb, R.rma_workspace_bytes(R.RMA_OP_DECODE_FULL, inp.k, sp, cfg.G, 0, cfg.m))
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
@@ -483,36 +528,36 @@ def main():
     if mlp_mode:
         store_phi = True
         mlp = tuple(R.PhiMlpWeights(Wl.generate_phi_mlp(cfg, which, m=cfg.m, device="cuda")) for which in "kq")
-    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi, fused_phi, mlp) for c in copies]
+    runners = [PathRunner(R, cfg, c, K, ws, torch, store_phi, fused_phi, mlp, args.separate) for c in copies]
     log(f"[bench] {n_copies} rotating copies of {per_copy / 1e6:.1f} MB; workspace {wsb / 1e6:.1f} MB")
 
     stream = torch.cuda.Stream()
     st = ctypes.c_void_p(stream.cuda_stream)
-    # eager reference outputs (copy 0) for the graph check
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)   # noqa: E731
+    # prefill summaries of every copy (the decode reads them), then the eager
+    # reference of copy 0's decode for the graph check
     with torch.cuda.stream(stream):
-        runners[0].step(st)
+        for r in runners:
+            r.build(st)
+        runners[0].decode(st)
     stream.synchronize()
     y_eager = runners[0].y.clone()
-    idx_eager = runners[0].idx.clone()
 
     # timed steps continue the rotation over the copies where the warm-up left it
     start = args.warmup % n_copies
     graphs = None
     if not args.eager:
         try:
-            rnd, graphs = capture_rounds(
-                torch, lambda i: runners[i].step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)),
-                n_copies, stream, start)
+            rnd, graphs = capture_rounds(torch, lambda i: runners[i].decode(cur()), n_copies, stream, start)
             # replay checks against the eager result, with eager work in between:
             # the single-step graph of copy 0, then a whole round
             for rep in range(4):
                 runners[0].y.zero_()
                 (graphs[0] if rep < 3 else rnd).replay()
                 torch.cuda.synchronize()
-                assert torch.equal(runners[0].y, y_eager) and torch.equal(runners[0].idx, idx_eager), \
-                    "graph replay differs from eager"
+                assert torch.equal(runners[0].y, y_eager), "graph replay differs from eager"
                 with torch.cuda.stream(stream):
-                    runners[0].step(st)
+                    runners[0].decode(st)
                 stream.synchronize()
             log(f"[bench] HIP graph replays match the eager run (single steps and rounds of {n_copies})")
         except Exception as ex:  # fall back to eager launches
@@ -524,10 +569,10 @@ def main():
             if graphs is not None:
                 graphs[i % n_copies].replay()
             else:
-                runners[i % n_copies].step(st)
+                runners[i % n_copies].decode(st)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, synchronised on both sides
+    # ---- timed region: exactly `steps` decode steps, synchronised on both sides
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -537,66 +582,75 @@ def main():
             replay_steps(rnd, graphs, n_copies, args.steps, start)
         else:
             for i in range(args.steps):
-                runners[(start + i) % n_copies].step(st)
+                runners[(start + i) % n_copies].decode(st)
         e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     queries = cfg.U * cfg.G * cfg.steps
     value = queries / (ms_per_step / 1e3)
+    dec_bytes = sum(decode_step_bytes(cfg, K, cfg.n_gen(s), store_phi, fused_phi) for s in range(cfg.steps))
+    dec_gbs = dec_bytes / (ms_per_step / 1e3) / 1e9
+    log(f"[bench] decode {ms_per_step * 1e3:.2f} us/step, {dec_bytes / 1e6:.1f} MB algorithmic -> {dec_gbs:.1f} GB/s "
+        f"({dec_gbs / PEAK_HBM_GBS:.1%} of peak); {value / 1e6:.3f} M queries/s")
 
-    # ---- per-kernel durations: HIP events that each kernel's own dispatch stamps
-    # at its start and end (eager launches on the path's stream, queued ahead)
+    # ---- per-kernel durations (eager launches on the path's stream, queued ahead)
     n_t = int(max(5, min(200, args.steps, 2.0 / max(ms_per_step / 1e3, 1e-6))))
-    recs = []
     with torch.cuda.stream(stream):
-        for i in range(n_t):
-            recs.append(runners[i % n_copies].traced_step(st, R))
+        drecs = [runners[i % n_copies].traced(R, "decode", st) for i in range(n_t)]
+        brecs = [runners[i % n_copies].traced(R, "build", st) for i in range(min(n_t, 50))]
     torch.cuda.synchronize()
-    names = ["build", "topk", "merge"] if fused_phi else ["build", "phi", "topk", "merge"]
-    if mlp_mode:
-        names = ["phik"] + names
-    call_ms = {n: 0.0 for n in names}
-    kern_ms, kern_n = {}, {}
-    for rec in recs:
-        for call, ks in rec:
-            call_ms[call] += ks[0][1].elapsed_time(ks[-1][2])
-            for kname, a, b in ks:
-                kern_ms[kname] = kern_ms.get(kname, 0.0) + a.elapsed_time(b)
-                kern_n[kname] = kern_n.get(kname, 0) + 1
-    dur = {n: call_ms[n] / n_t for n in names}                       # ms per step
-    kavg = {k: kern_ms[k] / kern_n[k] for k in kern_ms}               # ms per launch
-    launches = {k: kern_n[k] / n_t for k in kern_n}                  # launches per step
-    nb = call_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi, mlp_mode)
+    dk_avg, dk_n = kernel_stats(drecs)
+    bk_avg, _ = kernel_stats(brecs)
     kb = kernel_bytes(cfg, K, cfg.n_gen(0), store_phi, fused_phi)
-    step_bytes = nb["build"] + nb["phik"] + sum(call_bytes(cfg, K, cfg.n_gen(s), store_phi, fused_phi, mlp_mode)[c]
-                                   for s in range(cfg.steps) for c in ("phi", "topk", "merge"))
-    prefill_calls = ("build", "phik")
-    gbs = {n: nb[n] * (1 if n in prefill_calls else cfg.steps) / (dur[n] / 1e3) / 1e9 for n in names}
-    kgbs = {k: kb[k] / (kavg[k] / 1e3) / 1e9 for k in kavg}
-    kfl = kernel_flops(cfg)
-    ktf = {k: kfl[k] / (kavg[k] / 1e3) / 1e12 for k in kavg if k in kfl}      # TFLOP/s
-    for n in names:
-        log(f"[bench] {n:6s} {dur[n] * 1e3:9.2f} us/step  {gbs[n]:8.1f} GB/s")
-    for k in kavg:
-        log(f"[bench]   {k:22s} {kavg[k] * 1e3:9.2f} us/launch x{launches[k]:.0f}  "
-            f"{kb[k] / 1e6:8.2f} MB  {kgbs[k]:8.1f} GB/s" + (f"  {ktf[k]:8.1f} TFLOP/s" if k in ktf else ""))
-    log(f"[bench] step {ms_per_step * 1e3:.2f} us, {step_bytes / 1e6:.1f} MB algorithmic "
-        f"-> {step_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; {value / 1e6:.3f} M queries/s")
-    decode_us = sum(dur[n] for n in names if n not in prefill_calls) * 1e3
-    dom = max(kavg, key=lambda k: kavg[k] * launches[k])     # most time per step
-    achieved = kgbs[dom]
+    for k in dk_avg:
+        log(f"[bench]   {k:22s} {dk_avg[k] * 1e3:9.2f} us/launch x{dk_n[k]:.0f}  {kb.get(k, 0) / 1e6:8.2f} MB  "
+            f"{kb.get(k, 0) / (dk_avg[k] / 1e3) / 1e9:8.1f} GB/s")
+    dom = max(dk_avg, key=lambda k: dk_avg[k] * dk_n[k])
+    achieved = kb[dom] / (dk_avg[dom] / 1e3) / 1e9
     traffic = measured_traffic(dom, cfg.name, K)
-    if dom in ktf:   # a matrix-core contraction: its own bf16 peak
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ktf[dom], 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ktf[dom] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": kfl[dom], "algorithmic_bytes_per_launch": kb[dom],
-                "avg_launch_us": round(kavg[dom] * 1e3, 3),
-                "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md"}
-    else:
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(kavg[dom] * 1e3, 3),
-                "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md"}
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(dk_avg[dom] * 1e3, 3),
+            "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md",
+            "decode_step": {"algorithmic_MB": round(dec_bytes / 1e6, 3), "us": round(ms_per_step * 1e3, 2),
+                            "GBps": round(dec_gbs, 1), "frac": round(dec_gbs / PEAK_HBM_GBS, 4)}}
+
+    # ---- the prefill summary build, on its own (graph replays over the copies)
+    use_graphs = graphs is not None
+    build_us = timed_replays(lambda i: runners[i % n_copies].build(cur()), n_copies,
+                             max(5, min(args.steps, 100)), stream, use_graphs)
+    bbytes = build_bytes(cfg, store_phi)
+    bgbs = bbytes / (build_us / 1e6) / 1e9
+    algo_fl, issued_fl = build_flops(cfg)
+    bk = "build_mfma_kernel" if "build_mfma_kernel" in bk_avg else max(bk_avg, key=bk_avg.get)
+    bk_us = bk_avg[bk] * 1e3
+    kb_b = kernel_bytes(cfg, K, 0, store_phi)[bk]
+    build = {"call_us": round(build_us, 2), "algorithmic_MB": round(bbytes / 1e6, 3), "GBps": round(bgbs, 1),
+             "frac_hbm": round(bgbs / PEAK_HBM_GBS, 4),
+             "per_kernel_us": {k: round(v * 1e3, 2) for k, v in bk_avg.items()},
+             "tokens_per_s": round(cfg.U * cfg.L_mid / (build_us / 1e6), 1),
+             "roofline": {"bound": "hbm", "kernel": bk, "achieved": round(kb_b / (bk_us / 1e6) / 1e9, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(kb_b / (bk_us / 1e6) / 1e9 / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes_per_launch": kb_b, "avg_launch_us": round(bk_us, 3),
+                          "traffic": measured_traffic(bk, cfg.name, K)}}
+    if bk == "build_mfma_kernel":
+        build["mfma"] = {"algorithmic_TFLOP": round(algo_fl / 1e12, 4), "issued_TFLOP": round(issued_fl / 1e12, 4),
+                         "algorithmic_TFLOPs": round(algo_fl / (bk_us / 1e6) / 1e12, 1),
+                         "issued_TFLOPs": round(issued_fl / (bk_us / 1e6) / 1e12, 1),
+                         "util_algorithmic": round(algo_fl / (bk_us / 1e6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "util_issued": round(issued_fl / (bk_us / 1e6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "peak_TFLOPs": PEAK_BF16_TFLOPS,
+                         "issued_note": "W is split into bf16 high + low parts: the projection's MFMAs double"}
+    log(f"[bench] build {build_us:.2f} us/call, {bbytes / 1e6:.1f} MB -> {bgbs:.1f} GB/s; kernels {build['per_kernel_us']}")
+
+    # ---- whole path: build + decode per step
+    def whole(i):
+        r = runners[i % n_copies]
+        r.build(cur())
+        r.decode(cur())
+    whole_us = timed_replays(whole, n_copies, max(5, min(args.steps, 200)), stream, use_graphs)
+    log(f"[bench] whole path (build + decode) {whole_us:.2f} us/step ({queries / whole_us:.3f} M queries/s)")
 
     out = {
         "metric": METRIC,
@@ -616,34 +670,43 @@ def main():
             "units": cfg.U, "query_heads_per_unit": cfg.G, "head_dim": cfg.d, "context": cfg.L,
             "anchors": [cfg.n_sink, cfg.n_tail], "K": K, "phi_features": cfg.m,
             "decode_steps": cfg.steps, "queries_per_step": queries,
-            "step": ("prefill MLP phi_k + summaries over those rows + MLP phi_q + top-K + merge" if mlp_mode
-                     else "prefill summaries + top-K + merge (phi_q computed inside the merge)" if fused_phi
-                     else "prefill summaries + phi_q + top-K + merge"),
+            "step": ("one decode pass over the batch: " +
+                     ("rma_decode_topk + rma_decode_merge" if args.separate else
+                      "rma_decode (scan, then the fused selection and merge)") +
+                     (", f = phi_q(q) inside" if fused_phi else ", phi_q by its own kernel") +
+                     "; summaries built beforehand (reported under build)"),
             "phi": ("MLP family: one-block ReZero MLP, width 512, exponentiated output, d_phi 64, random "
                     "weights, bf16 matrix-core operands" if mlp_mode else "elu(Wx+b)+1"),
-            **({"per_kernel_TFLOPs": {k: round(v, 1) for k, v in ktf.items()}} if ktf else {}),
             "phi_k_rows": "stored" if store_phi else "recomputed at decode (not stored)",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
-            "rotating_copies": n_copies, "launch": f"hip_graph, rounds of {n_copies} steps" if graphs is not None else "eager",
-            "step_algorithmic_MB": round(step_bytes / 1e6, 3),
-            "step_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-            "per_call_us": {n: round(dur[n] * 1e3, 2) for n in names},
-            "per_call_GBps": {n: round(gbs[n], 1) for n in names},
-            "per_kernel_us": {k: round(kavg[k] * 1e3, 2) for k in kavg},
-            "per_kernel_GBps": {k: round(kgbs[k], 1) for k in kavg},
-            "decode_only_queries_per_s": round(queries / (decode_us / 1e6), 1),
+            "rotating_copies": n_copies,
+            "launch": f"hip_graph, rounds of {n_copies} steps" if graphs is not None else "eager",
+            "decode_per_kernel_us": {k: round(v * 1e3, 2) for k, v in dk_avg.items()},
+            "decode_per_kernel_GBps": {k: round(kb.get(k, 0) / (v / 1e3) / 1e9, 1) for k, v in dk_avg.items()},
+            "decode_GBps": round(dec_gbs, 1),
+            "build": build,
+            "whole_path": {"us_per_step": round(whole_us, 2), "queries_per_s": round(queries / (whole_us / 1e6), 1),
+                           "step": "rma_build_summaries + the decode step"},
+            "ceilings": ceil,
         },
         "roofline": roof,
     }
+    if mlp_mode:
+        fl = mlp_flops(cfg)
+        out["config"]["mlp_TFLOPs"] = {k: round(fl[k] / (v / 1e3) / 1e12, 1)
+                                       for k, v in {**bk_avg, **dk_avg}.items() if k in fl}
     if not args.no_full:
-        dec_us, out["config"]["full_exact_decode"] = decode_timing(args, cfg, runners, n_copies, stream, st,
-                                                                   graphs is not None, queries, log)
-        out["config"]["decode_only_us_per_step"] = round(dec_us, 2)
-        out["config"]["decode_only_queries_per_s"] = round(queries / (dec_us / 1e6), 1)
-        dbytes = step_bytes - nb["build"] - nb["phik"]
-        out["config"]["decode_only_GBps"] = round(dbytes / (dec_us / 1e6) / 1e9, 1)
+        full_us = timed_replays(lambda i: runners[i % n_copies].full(cur()), n_copies,
+                                max(5, min(args.steps, 200)), stream, use_graphs)
+        fbytes = sum(kernel_bytes(cfg, K, cfg.n_gen(s))["full_partial_kernel"] for s in range(cfg.steps))
+        out["config"]["full_exact_decode"] = {
+            "us_per_step": round(full_us, 2), "queries_per_s": round(queries / (full_us / 1e6), 1),
+            "algorithmic_MB": round(fbytes / 1e6, 3), "GBps": round(fbytes / (full_us / 1e6) / 1e9, 1),
+            "method_decode_speedup": round(full_us / (ms_per_step * 1e3), 3)}
+        log(f"[bench] full-attention decode {full_us:.2f} us/step -> method speedup "
+            f"{full_us / (ms_per_step * 1e3):.3f}")
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s (+ one thread)")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, K, args.cpu_seconds, mlp_mode)
     else:
         out["cpu_baseline"] = None
