@@ -187,12 +187,12 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   TopkPlan p{};
   const int64_t Lm = l_mid(sp);
   const int64_t U = kv.n_units;
-  const int tile = (kv.d == 64) ? 64 : 32;  // tokens per scan block pass
+  const int tile = scan_tile(kv.d);  // tokens per scan block pass
   const int64_t ch_max = std::max<int64_t>(tile, (kScanScoreSlots / G) / tile * tile);
   if (Lm > 0) {
     int64_t lo = ceil_div(Lm, ch_max);
     int64_t hi = std::min<int64_t>(kSelMaxChunks, ceil_div(Lm, tile));
-    int64_t nc = std::max<int64_t>(lo, std::min<int64_t>(ceil_div(512, U), hi));
+    int64_t nc = std::max<int64_t>(lo, std::min<int64_t>(ceil_div(kScanBlocks, U), hi));
     int64_t ch = ceil_div(ceil_div(Lm, nc), tile) * tile;
     p.ch = (int)ch;
     p.n_chunks = (int)ceil_div(Lm, ch);

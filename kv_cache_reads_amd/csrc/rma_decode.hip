@@ -92,6 +92,12 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ float s_uf;
   __shared__ float s_f[M];          // f = phi_q(q) of this head
 
+  // every kernel argument into registers at once: one round trip for all of
+  // them rather than one per branch that first needs some
+  asm volatile("" ::"s"(q), "s"(G), "s"(kb), "s"(vb), "s"(ustride), "s"(L), "s"(n_sink), "s"(n_tail),
+               "s"(n_gen), "s"(L_mid), "s"(ch), "s"(n_chunks), "s"(r_cap), "s"(K), "s"(hpw), "s"(ent),
+               "s"(meta), "s"(idx_out), "s"(sc_out), "s"(phi_q), "s"(Wq), "s"(bq), "s"(P), "s"(phik),
+               "s"(S), "s"(u_), "s"(flags), "s"(y), "s"(stats), "s"(inv_sqrt_d));
   const int ug = blockIdx.x, u = ug / G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;

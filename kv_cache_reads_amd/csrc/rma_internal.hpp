@@ -66,6 +66,9 @@ BuildPlan plan_build(const rma_kv& kv, int64_t tokens, int m, bool computed_phi,
 
 // ------------------------------------------------------------- top-k
 constexpr int kScanThreads = 256;
+// tokens a scan block scores per pass: 64 / (d / 16) tokens per wave
+constexpr int scan_tile(int d) { return (kScanThreads / 64) * (64 / (d / 16)); }
+constexpr int kScanBlocks = 512;        // scan blocks aimed for when the units are few
 constexpr int kScanBins = 512;          // linear score bins per head in the scan
 constexpr int kScanScoreSlots = 8192;   // fp32 LDS score slots per scan block (G * ch <= this)
 constexpr int kSelMaxChunks = 256;

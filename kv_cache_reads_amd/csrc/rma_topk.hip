@@ -39,7 +39,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   constexpr int E = 16;              // key elements per lane
   constexpr int LPT = D / E;         // lanes per token (4 or 8)
   constexpr int TPW = kWave / LPT;   // tokens per wave pass
-  constexpr int TPP = 4 * TPW;       // tokens per block pass
+  constexpr int TPP = scan_tile(D);  // tokens per block pass
+  static_assert(TPP == (kScanThreads / kWave) * TPW, "one token slot per lane group");
   constexpr int EPP = RowPieces<KT>::kElemsPerPiece;
   constexpr int PIECES = E / EPP;    // 16-byte loads per lane per token
   constexpr int UNR = (sizeof(KT) == 2) ? 4 : 2;
@@ -48,9 +49,8 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 
   __shared__ float sc[G * CHMAX];
   __shared__ uint32_t hist[G * NB];
-  __shared__ int s_buf[257];
+  __shared__ float4 s_q[G * D / 4];
   __shared__ HeadParams s_hp[G];
-  __shared__ int s_bc[G], s_nrep[G];
 
   const int u = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
@@ -58,20 +58,10 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   const int t0 = c * ch;
   const int n = min(ch, L_mid - t0);
 
-  // query slices first: global loads complete in issue order, so the head
-  // parameters below only wait for these, not for the key rows
-  float qr[G][E];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float4* qp = reinterpret_cast<const float4*>(q + ((size_t)u * G + g) * D + part * E);
-#pragma unroll
-    for (int i = 0; i < E / 4; ++i) {
-      float4 v = qp[i];
-      qr[g][4 * i] = v.x; qr[g][4 * i + 1] = v.y; qr[g][4 * i + 2] = v.z; qr[g][4 * i + 3] = v.w;
-    }
-  }
-  // histogram bins are filled while scoring
-  for (int i = tid; i < G * NB; i += kScanThreads) hist[i] = 0u;
+  // the unit's queries (G d floats) once per block, first: global loads
+  // complete in issue order, so their wait below does not wait for the keys
+  static_assert(G * D / 4 <= kScanThreads, "one 16-byte query piece per thread");
+  const float4 q4 = reinterpret_cast<const float4*>(q + (size_t)u * G * D)[min(tid, G * D / 4 - 1)];
 
   const KT* kp = kb + (size_t)u * ustride + (size_t)(n_sink + t0) * D + part * E;
   constexpr int STEP = TPP * UNR;
@@ -91,8 +81,22 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   load(ra, 0);
   if (STEP < n) load(rb, STEP);
 
+  // histogram bins are filled while scoring
+  for (int i = tid; i < G * NB; i += kScanThreads) hist[i] = 0u;
+  if (tid < G * D / 4) s_q[tid] = q4;
+  __syncthreads();  // histogram cleared, queries in LDS
+
   // every lane derives the same parameters from its query slices (the LPT lanes
   // of a token hold the whole query; fixed reduction order)
+  float qr[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 v = s_q[(g * D + part * E) / 4 + i];
+      qr[g][4 * i] = v.x; qr[g][4 * i + 1] = v.y; qr[g][4 * i + 2] = v.z; qr[g][4 * i + 3] = v.w;
+    }
+  }
   HeadParams hp[G];
   const float kap_u = kappa[u];
 #pragma unroll
@@ -105,7 +109,6 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 #pragma unroll
   for (int g = 0; g < G; ++g)
     if (tid == g) s_hp[g] = hp[g];
-  __syncthreads();  // histogram cleared
 
   auto score = [&](const uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
@@ -136,25 +139,41 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   }
   __syncthreads();
 
-  // ---- per head: smallest bin threshold that still passes >= min(r_min, n) tokens
-  for (int g = wave; g < G; g += 4) {
+  // ---- per head, one wave: the smallest bin threshold that still passes
+  //      >= min(r_min, n) tokens, then the passing tokens in position order
+  //      (rows of 64 scores, appended by ballot)
+  for (int g = wave; g < G; g += kScanThreads / kWave) {
     const int target = min(r_min, n);
-    const uint32_t* h = hist + g * NB;
+    constexpr int BPL = NB / kWave;   // bins per lane, read once as 16-byte words
+    static_assert(BPL % 4 == 0, "whole 16-byte histogram reads");
+    uint32_t hb_[BPL];
+    {
+      const uint4* h4 = reinterpret_cast<const uint4*>(hist + g * NB + lane * BPL);
+#pragma unroll
+      for (int j = 0; j < BPL / 4; ++j) {
+        const uint4 v = h4[j];
+        hb_[4 * j] = v.x; hb_[4 * j + 1] = v.y; hb_[4 * j + 2] = v.z; hb_[4 * j + 3] = v.w;
+      }
+    }
     int ls = 0;
 #pragma unroll
-    for (int j = 0; j < NB / kWave; ++j) ls += (int)h[lane * (NB / kWave) + j];
+    for (int j = 0; j < BPL; ++j) ls += (int)hb_[j];
     const int incl = wave_incl_scan_dpp(ls);
     const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
     const int suf = total - incl + ls;  // tokens in this lane's bins and above
     const unsigned long long ball = __ballot(suf >= target);
     const int lstar = 63 - __clzll((long long)ball);
-    int bc = 0, run = 0;
-    if (lane == lstar) {
-      run = suf - ls;
-      bc = lane * (NB / kWave);
-      for (int j = NB / kWave - 1; j >= 0; --j) {
-        run += (int)h[lane * (NB / kWave) + j];
-        if (run >= target) { bc = lane * (NB / kWave) + j; break; }
+    // in lane lstar: the highest bin from which the bins at and above it hold
+    // >= target tokens (the other lanes compute the same walk and discard it)
+    int bc = lane * BPL, run = suf - ls;
+    {
+      bool found = false;
+#pragma unroll
+      for (int j = BPL - 1; j >= 0; --j) {
+        if (!found) {
+          run += (int)hb_[j];
+          if (run >= target) { bc = lane * BPL + j; found = true; }
+        }
       }
     }
     bc = __builtin_amdgcn_readlane(bc, lstar);
@@ -163,50 +182,37 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
     // same tokens pass, and the select's completeness test is least strict
     int hb = -1;
 #pragma unroll
-    for (int j = 0; j < NB / kWave; ++j) {
-      const int bin = lane * (NB / kWave) + j;
-      if (bin < bc && h[bin] != 0u) hb = bin;
+    for (int j = 0; j < BPL; ++j) {
+      const int bin = lane * BPL + j;
+      if (bin < bc && hb_[j] != 0u) hb = bin;
     }
     hb = (int)wave_max_dpp((float)hb);
-    if (lane == 0) { s_bc[g] = hb + 1; s_nrep[g] = run; }
-  }
-  __syncthreads();
-
-  // ---- ordered compaction of the passing tokens (position order), all heads
-  //      with one multi-value block scan
-  //      (each thread a contiguous run of at most PMAX tokens; one pass over the
-  //      scores keeps a bit per passing token, the write pass visits those only)
-  constexpr int PMAX = (CHMAX + kScanThreads - 1) / kScanThreads;
-  static_assert(PMAX <= 32, "one 32-bit pass mask per head");
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  int bcs[G], cnt[G], tot[G];
-  uint32_t pm[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) { bcs[g] = s_bc[g]; pm[g] = 0u; }
-#pragma unroll
-  for (int k = 0; k < PMAX; ++k) {
-    if (i0 + k < i1) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        pm[g] |= (lin_bin(sc[g * CHMAX + i0 + k], hp[g]) >= bcs[g]) ? (1u << k) : 0u;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) cnt[g] = __popc(pm[g]);
-  block_excl_scan256_n<G>(cnt, s_buf, tot);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
+    const int bcut = hb + 1;
     float2* dst = ent + ((size_t)(u * G + g) * n_chunks + c) * r_cap;
-    int pos = cnt[g];
-    for (uint32_t mk = pm[g]; mk != 0u; mk &= mk - 1u, ++pos) {
-      const int i = i0 + __ffs(mk) - 1;
-      if (pos < r_cap) dst[pos] = make_float2(sc[g * CHMAX + i], __int_as_float(t0 + i));
+    const HeadParams hg = s_hp[g];
+    constexpr int RB = 8;   // rows of 64 scores per batch: loads first, then ballots, then stores
+    int base = 0;
+    for (int r0 = 0; r0 < n; r0 += RB * kWave) {
+      float x[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int i = r0 + k * kWave + lane;
+        x[k] = sc[g * CHMAX + min(i, n - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int i = r0 + k * kWave + lane;
+        const bool pass = i < n && lin_bin(x[k], hg) >= bcut;
+        const uint64_t bm = __ballot(pass);
+        const int pos = base + lanes_below(bm);
+        if (pass && pos < r_cap) dst[pos] = make_float2(x[k], __int_as_float(t0 + i));
+        base += (int)__popcll(bm);
+      }
     }
-  }
-  if (tid < G) {
-    meta[(size_t)(u * G + tid) * n_chunks + c] = make_int2(s_bc[tid], s_nrep[tid]);
-    if (c == 0) hpw[u * G + tid] = make_float4(s_hp[tid].rg, s_hp[tid].inv_w, s_hp[tid].eps, 0.f);
+    if (lane == 0) {
+      meta[(size_t)(u * G + g) * n_chunks + c] = make_int2(bcut, run);
+      if (c == 0) hpw[u * G + g] = make_float4(hg.rg, hg.inv_w, hg.eps, 0.f);
+    }
   }
 }
 
