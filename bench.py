@@ -70,7 +70,15 @@ def parse():
 # Bytes per launch from rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 # dispatch) of this script, each scaled by what the same counter reads for a plain
 # copy of known size.  A record holds only for the kernel sources it was taken on.
-TRAFFIC = {}
+TRAFFIC = {
+    # (kernel, workload, K): profiles/traffic_c1.md, profiles/traffic_c4.md
+    ("decode_fused_kernel", "c1", 328): {"fetch_bytes": 8658050, "write_bytes": 8192, "csrc": "a58ffcec0992e2ed"},
+    ("topk_scan_kernel", "c1", 328): {"fetch_bytes": 33749204, "write_bytes": 636576, "csrc": "a58ffcec0992e2ed"},
+    ("build_mfma_kernel", "c1", 328): {"fetch_bytes": 69263916, "write_bytes": 84054662, "csrc": "a58ffcec0992e2ed"},
+    ("decode_fused_kernel", "c4", 1310): {"fetch_bytes": 2389589514, "write_bytes": 1376256, "csrc": "a58ffcec0992e2ed"},
+    ("topk_scan_kernel", "c4", 1310): {"fetch_bytes": 30556113958, "write_bytes": 78078333, "csrc": "a58ffcec0992e2ed"},
+    ("build_mfma_kernel", "c4", 1310): {"fetch_bytes": 60215018728, "write_bytes": 30167614227, "csrc": "a58ffcec0992e2ed"},
+}
 
 
 def csrc_digest():
