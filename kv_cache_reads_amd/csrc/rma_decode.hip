@@ -87,6 +87,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ int s_buf[kSelThreads / kWave + 1];
   __shared__ int s_wcnt[NW];
   __shared__ float s_wm[NW];
+  __shared__ float s_amax[NW];
   __shared__ float s_fin[NV];
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
@@ -292,16 +293,36 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       if (lane == 0) s_uf = t;
     }
   }
+  // the exactly scored rows' scores q.k / sqrt(d) (eight lanes, q from LDS) and
+  // their maximum; the group's first row stays loaded for its term
+  auto ex_score = [&](const RawPiece<KT, CPL>& rk) {
+    float kv[CPL];
+    rk.unpack(kv);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) a = __fmaf_rn(s_qf[part * CPL + i], kv[i], a);
+    return lane_group_sum<LPE>(a) * inv_sqrt_d;
+  };
+  float a0 = -INFINITY;
+  {
+    float am = -INFINITY;
+    if (grp < n_ex) am = a0 = ex_score(xk);
+    for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
+      RawPiece<KT, CPL> rk;
+      rk.load(kunit + (size_t)ex_pos(j) * D + part * CPL);
+      am = fmaxf(am, ex_score(rk));
+    }
+    am = wave_max_dpp(am);
+    if (lane == 0) s_amax[wave] = am;
+  }
   __syncthreads();
 
-  // ---- 4. the selection, the whole block (the exact fallback when it fails)
-  SelOut out;
-  out.lpos = lpos;
-  out.lsc = lsc;
-  if (idx_out != nullptr) {
-    out.io = idx_out + (size_t)ug * K;
-    out.so = sc_out + (size_t)ug * K;
-  }
+  // ---- 4. the selection, the whole block (the exact fallback when it fails):
+  //      the K selected into the LDS list (and to idx / sel when asked).  The
+  //      reference for the exponentials: no score of the exact support exceeds
+  //      the larger of the exact rows' maximum and the union's top score (the
+  //      top mid score, the fallback's scores aside, which may pass it by an ulp)
+  float mref = -INFINITY;
   {
     const HeadParams hp{hp_in[0], hp_in[1], hp_in[2]};
     float lo = INFINITY, hi = -INFINITY;
@@ -309,47 +330,42 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     for (int w = 0; w < NW; ++w) {
       lo = fminf(lo, s_rlo[w]);
       hi = fmaxf(hi, s_rhi[w]);
+      mref = fmaxf(mref, s_amax[w]);
+    }
+    mref = fmaxf(mref, hi * inv_sqrt_d);
+    SelOut io;
+    if (idx_out != nullptr) {
+      io.io = idx_out + (size_t)ug * K;
+      io.so = sc_out + (size_t)ug * K;
     }
     const bool ok = block_select<KT, D, NT>(es, ep, s_nE, lo, hi, s_bcs, s_nrep, n_chunks, ch, L_mid,
-                                            n_sink, K, s_trunc != 0, hp, s_qf, kunit, inv_sqrt_d, wl, out);
+                                            n_sink, K, s_trunc != 0, hp, s_qf, kunit, inv_sqrt_d, wl,
+                                            lpos, lsc, io);
     if (!ok) {   // uniform: a chunk withheld tokens or the band was too wide
       __syncthreads();
+      SelOut out = io;
+      out.lpos = lpos;
+      out.lsc = lsc;
       exact_fallback<KT, D, NT>(s_qf, kunit, n_sink, L_mid, K, out, inv_sqrt_d, s_hist, s_misc, s_buf);
     }
   }
   __syncthreads();   // the list
 
-  // the group's running sums: N = sum e^{s - m} v, Z = sum e^{s - m} over the
-  // exact support; NK = sum w v, ZK = sum w over the retrieved entries
+  // the group's sums: N = sum e^{s - mref} v, Z = sum e^{s - mref} over the
+  // exact support; NK = sum w v, ZK = sum w over the retrieved entries; mx =
+  // the largest score added
   float N[CPL], NK[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) { N[c] = 0.f; NK[c] = 0.f; }
-  float Z = 0.f, ZK = 0.f, mrun = -INFINITY;
-  auto add_exp = [&](float s, const float (&vv)[CPL]) {
-    if (s > mrun) {
-      const float r = __expf(mrun - s);  // 0 while nothing is accumulated
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) N[c] *= r;
-      Z *= r;
-      mrun = s;
-    }
-    const float ew = __expf(s - mrun);
+  float Z = 0.f, ZK = 0.f, mx = -INFINITY;
+  auto add_exp = [&](float sc, const float (&vv)[CPL]) {
+    const float ew = __expf(sc - mref);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) N[c] = __fmaf_rn(ew, vv[c], N[c]);
     Z += ew;
+    mx = fmaxf(mx, sc);
   };
-  // an exactly scored row: its score q.k / sqrt(d) and its term
-  auto add_exact = [&](const RawPiece<KT, CPL>& rk, const RawPiece<KT, CPL>& rv) {
-    float kv[CPL], vv[CPL];
-    rk.unpack(kv);
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) a = __fmaf_rn(s_qf[part * CPL + i], kv[i], a);   // q from LDS
-    a = lane_group_sum<LPE>(a);
-    rv.unpack(vv);
-    add_exp(a * inv_sqrt_d, vv);
-  };
-  bool ex_due = grp < n_ex;   // the group's first exact row, loaded at the start
+  bool ex_due = grp < n_ex;   // the group's first exact row (score a0, value row xv)
 
   // ---- 5. retrieved entries from the list
   float fr[FPL];
@@ -370,8 +386,10 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       else pr[e].zero();
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
-    if (ex_due) {   // uniform within the group; scored while the batch loads
-      add_exact(xk, xv);
+    if (ex_due) {   // uniform within the group; added while the batch loads
+      float vv[CPL];
+      xv.unpack(vv);
+      add_exp(a0, vv);
       ex_due = false;
     }
 #pragma unroll
@@ -391,36 +409,35 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       }
     }
   }
-  if (ex_due) add_exact(xk, xv);
+  if (ex_due) {
+    float vv[CPL];
+    xv.unpack(vv);
+    add_exp(a0, vv);
+  }
   for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
     const int pos = ex_pos(j);
     xv.load(vunit + (size_t)pos * D + part * CPL);
     xk.load(kunit + (size_t)pos * D + part * CPL);
-    add_exact(xk, xv);
+    const float sc = ex_score(xk);
+    float vv[CPL];
+    xv.unpack(vv);
+    add_exp(sc, vv);
   }
 
-  // ---- 6. combine.  The block's largest running max; every group rescales to
-  //      it; the two groups of a 16-lane row add (row rotation by 8); the pair
-  //      sums go through LDS and are added in pair order (deterministic).
+  // ---- 6. combine: the two groups of a 16-lane row add (row rotation by 8);
+  //      the pair sums go through LDS and are added in pair order
+  //      (deterministic); the largest score added, per wave
   {
-    const float wm = wave_max_dpp(mrun);
-    if (lane == 0) s_wm[wave] = wm;
-  }
-  __syncthreads();   // also: every gather has read the list, so its LDS is free
-  float ms = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
-  {
-    const float r = mrun == -INFINITY ? 0.f : __expf(mrun - ms);
+    const float wm = wave_max_dpp(mx);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      N[c] *= r;
       N[c] += dpp_f<0x128>(N[c]);      // row_ror:8: the other group of the row
       NK[c] += dpp_f<0x128>(NK[c]);
     }
-    Z *= r;
     Z += dpp_f<0x128>(Z);
     ZK += dpp_f<0x128>(ZK);
+    __syncthreads();   // every gather has read the list: its LDS is free
+    if (lane == 0) s_wm[wave] = wm;
     if ((lane & 15) < LPE) {
       float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NV;
 #pragma unroll
@@ -445,15 +462,19 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     if (sl == 0 && j < NV) s_fin[j] = acc;
   }
   __syncthreads();
+  float ms = -INFINITY;   // m*: the largest score of the exact support
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
   const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
   const float uf = rs ? s_uf : 0.f;
   float zr = 0.f;
   if (rs) zr = fmaxf(uf - (sub ? ZKt : 0.f), 0.f);
-  // y = (N_E + e^{-m*} nu) / (Z_E + e^{-m*} Z_R), scaled by e^{m* - Mx} with
-  // Mx = max(m*, log Z_R) so that neither term overflows
+  // y = (N_E + e^{-mref} nu) / (Z_E + e^{-mref} Z_R) with N_E, Z_E taken
+  // relative to mref, scaled by e^{mref - Mx} with Mx = max(mref, log Z_R) so
+  // that neither term overflows
   const float lz = zr > 0.f ? __logf(zr) : -INFINITY;
-  const float Mx = fmaxf(ms, lz);
-  const float a = __expf(ms - Mx);
+  const float Mx = fmaxf(mref, lz);
+  const float a = __expf(mref - Mx);
   const float bres = __expf(-Mx);
   const float den = a * ZE + bres * zr;
   for (int col = tid; col < D; col += NT) {
@@ -468,7 +489,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   }
   if (stats != nullptr && tid == 0) {
     stats[(size_t)ug * 4 + 0] = ms;
-    stats[(size_t)ug * 4 + 1] = ZE;
+    stats[(size_t)ug * 4 + 1] = ZE * __expf(mref - ms);   // relative to m*
     stats[(size_t)ug * 4 + 2] = zr;
     stats[(size_t)ug * 4 + 3] = ZKt;
   }

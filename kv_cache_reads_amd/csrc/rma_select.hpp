@@ -554,13 +554,18 @@ struct HeadSelect {
 //   histogram over [lo, hi] | the bin bK of the K-th largest score, its members
 //   and extent | t = the K-th largest fp32 score (rank among the members), the
 //   completeness certificate of every chunk for t - 2.5 eps, the count above
-//   t + 2.5 eps and the band [t - 2.5 eps, t + 2.5 eps] | the band's
+//   t + 2.5 eps per wave (wave w owns a contiguous range of rows) and the band
+//   [t - 2.5 eps, t + 2.5 eps] | the entries above the band into the list (wave
+//   w's at the sum of the lower waves' counts, position order), the band's
 //   double-double scores (one lane group per member) when it must be split |
-//   rank and mark | the ordered output: wave w owns a contiguous range of rows,
-//   counts its entries | and writes them at the sum of the lower waves' counts.
+//   rank and mark | the band's winners appended in position order.
+// The list (lpos: positions, lsc: scaled scores; K entries) feeds the gather;
+// its order is fixed by the data, so the sums over it are deterministic.  With
+// out.io set the K indices and kept scores are also written in position order
+// (one more count and barrier).
 // Returns false (the same on every thread) when the block must run the exact
-// fallback (a chunk withheld tokens, too few entries, band too wide); `out`
-// is untouched then.  The caller puts a barrier before any use of `out`.
+// fallback (a chunk withheld tokens, too few entries, band too wide).  The
+// caller puts a barrier before reading the list.
 struct BlockSelLds {
   uint32_t* hist;   // kSelBins
   float* cand;      // kSelBandMax: scores of the K-th bin's members
@@ -580,7 +585,8 @@ template <typename KT, int D, int NT>
 __device__ bool block_select(const float* es, int* ep, int nE, float lo, float hi, const int* s_bcs,
                              const int* s_nrep, int n_chunks, int ch, int L_mid, int n_sink, int K,
                              bool trunc, const HeadParams& hp, const float* qf, const KT* kunit,
-                             float inv_sqrt_d, const BlockSelLds& w, const SelOut& out) {
+                             float inv_sqrt_d, const BlockSelLds& w, int* lpos, float* lsc,
+                             const SelOut& out) {
   constexpr int NBS = kSelBins;
   constexpr int NW = NT / kWave;
   constexpr int BPL = NBS / kWave;             // histogram bins per lane (each wave reads them all)
@@ -589,9 +595,12 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (trunc || nE < K) return false;
   const int rows = (nE + kWave - 1) / kWave;
+  const int RW = (rows + NW - 1) / NW;   // wave w's rows [r0, r1) for the ordered steps
+  const int r0 = min(rows, wave * RW), r1 = min(rows, r0 + RW);
 
   const bool whole = K == L_mid;   // every mid token is selected (the chunks reported all)
   float th_lo = -INFINITY, th_hi = -INFINITY;
+  int nb = 0, kp = 0;
   if (!whole) {
     const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
     auto ubin = [&](float x) {
@@ -705,10 +714,11 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
       }
       if (__ballot(bad) != 0ull) return false;
     }
-    // ---- the count above th_hi and the band, appended (order free)
+    // ---- the count above th_hi (per wave, over its row range) and the band,
+    //      appended (order free)
     {
       int nin = 0;
-      for (int r = wave; r < rows; r += NW) {
+      for (int r = r0; r < r1; ++r) {
         const float x = es[r * kWave + lane];
         nin += (int)__popcll(__ballot(x > th_hi));
         const bool inb = x > -INFINITY && x <= th_hi && x >= th_lo;
@@ -721,11 +731,30 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
           if (inb && o < kSelBandMax) w.bslot[o] = r * kWave + lane;
         }
       }
-      if (lane == 0 && nin > 0) atomicAdd(&w.misc[3], nin);
+      if (lane == 0) w.wcnt[wave] = nin;
     }
     __syncthreads();
-    const int nb = w.misc[4], kp = K - w.misc[3];
+    nb = w.misc[4];
+    int nin = 0, o = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int c = w.wcnt[v];
+      o += v < wave ? c : 0;
+      nin += c;
+    }
+    kp = K - nin;
     if (nb > kSelBandMax || kp < 1 || nb < kp) return false;
+    // ---- the list, first part: the entries above th_hi in position order
+    for (int r = r0; r < r1; ++r) {
+      const float x = es[r * kWave + lane];
+      const bool a = x > th_hi;
+      const uint64_t bm = __ballot(a);
+      if (a) {
+        lpos[o + lanes_below(bm)] = n_sink + ep[r * kWave + lane];
+        lsc[o + lanes_below(bm)] = x * inv_sqrt_d;
+      }
+      o += (int)__popcll(bm);
+    }
     if (nb > kp) {
       // ---- the band's double-double scores, one lane group per member
       constexpr int P = DDGroup<KT, D>::P;
@@ -747,31 +776,64 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
       for (int b = tid; b < nb; b += NT) ep[w.bslot[b]] |= SELF;
     }
     __syncthreads();
-  }
-  // ---- the ordered output: wave w owns rows [w RW, (w + 1) RW)
-  const int RW = (rows + NW - 1) / NW;
-  const int r0 = min(rows, wave * RW), r1 = min(rows, r0 + RW);
-  auto taken = [&](float x, int e) { return x > -INFINITY && (whole || x > th_hi || (e & SELF) != 0); };
-  int cnt = 0;
-  for (int r = r0; r < r1; ++r)
-    cnt += (int)__popcll(__ballot(taken(es[r * kWave + lane], ep[r * kWave + lane])));
-  if (lane == 0) w.wcnt[wave] = cnt;
-  __syncthreads();
-  int o = 0, total = 0;
+    // ---- the list, second part: the band's winners in position order
+    for (int b = tid; b < nb; b += NT) {
+      const int e = ep[w.bslot[b]];
+      if ((e & SELF) == 0) continue;
+      const int mp = e & ~SELF;
+      int before = 0;
+      for (int b2 = 0; b2 < nb; ++b2) {
+        const int e2 = ep[w.bslot[b2]];
+        before += (e2 & SELF) != 0 && (e2 & ~SELF) < mp;
+      }
+      lpos[nin + before] = n_sink + mp;
+      lsc[nin + before] = es[w.bslot[b]] * inv_sqrt_d;
+    }
+  } else {
+    // every entry is selected: the list in position order (wave w's rows at the
+    // sum of the lower waves' counts)
+    int cnt = 0;
+    for (int r = r0; r < r1; ++r) cnt += (int)__popcll(__ballot(es[r * kWave + lane] > -INFINITY));
+    if (lane == 0) w.wcnt[wave] = cnt;
+    __syncthreads();
+    int o = 0;
 #pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const int c = w.wcnt[v];
-    o += v < wave ? c : 0;
-    total += c;
+    for (int v = 0; v < NW; ++v) o += v < wave ? w.wcnt[v] : 0;
+    for (int r = r0; r < r1; ++r) {
+      const float x = es[r * kWave + lane];
+      const bool a = x > -INFINITY;
+      const uint64_t bm = __ballot(a);
+      if (a) {
+        lpos[o + lanes_below(bm)] = n_sink + ep[r * kWave + lane];
+        lsc[o + lanes_below(bm)] = x * inv_sqrt_d;
+      }
+      o += (int)__popcll(bm);
+    }
   }
-  if (total != K) return false;
-  for (int r = r0; r < r1; ++r) {
-    const float x = es[r * kWave + lane];
-    const int e = ep[r * kWave + lane];
-    const bool tk = taken(x, e);
-    const uint64_t bm = __ballot(tk);
-    if (tk) out.put(o + lanes_below(bm), n_sink + (e & ~SELF), x * inv_sqrt_d);
-    o += (int)__popcll(bm);
+  // ---- the indices and kept scores in position order, when asked: wave w's
+  //      taken entries at the sum of the lower waves' counts
+  if (out.io != nullptr) {
+    auto taken = [&](float x, int e) { return x > -INFINITY && (whole || x > th_hi || (e & SELF) != 0); };
+    int cnt = 0;
+    for (int r = r0; r < r1; ++r)
+      cnt += (int)__popcll(__ballot(taken(es[r * kWave + lane], ep[r * kWave + lane])));
+    __syncthreads();   // the counts above are read
+    if (lane == 0) w.wcnt[wave] = cnt;
+    __syncthreads();
+    int o = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) o += v < wave ? w.wcnt[v] : 0;
+    for (int r = r0; r < r1; ++r) {
+      const float x = es[r * kWave + lane];
+      const int e = ep[r * kWave + lane];
+      const bool tk = taken(x, e);
+      const uint64_t bm = __ballot(tk);
+      if (tk && o + lanes_below(bm) < K) {
+        out.io[o + lanes_below(bm)] = n_sink + (e & ~SELF);
+        out.so[o + lanes_below(bm)] = x * inv_sqrt_d;
+      }
+      o += (int)__popcll(bm);
+    }
   }
   return true;
 }
