@@ -13,19 +13,20 @@
 //   1. wave 0: each chunk's offset in the union (a wave scan of the counts);
 //      everyone: f = phi_q(q) into LDS;
 //   2. the reports into the union (compacted, position order) and its score
-//      range; phi(q)^T S per feature block and u^T f;
+//      range; phi(q)^T S per feature block and u^T f; the exactly scored rows'
+//      scores and their maximum;
 //   3. the selection (block_select in rma_select.hpp, the exact fallback if it
-//      fails): the K positions, ascending, and their scaled fp32 scores into
-//      an LDS list (and to idx / sel when asked);
+//      fails): the K positions and their scaled fp32 scores into an LDS list
+//      (and, when asked, to idx / sel in ascending order);
 //   4. the retrieved tokens from that list: their V and phi_k rows are
 //      gathered with every load of a batch issued before the first is used;
-//      e^{s - m} v, w = f.phi_k and w v accumulate per 8-lane group with a
-//      running max; the anchors' and generated tokens' exact terms are added
-//      while the first batch loads;
-//   5. the combine: the block's largest running max, one rescale per group,
-//      the two groups of a 16-lane row added by DPP, the pair sums added in
-//      pair order through LDS (deterministic); then the subtraction, the clamp
-//      and one normalisation.
+//      e^{s - mref} v, w = f.phi_k and w v accumulate per 8-lane group, where
+//      mref, the larger of the exact rows' maximum and the union's top score,
+//      bounds every score of the exact support (no running-max rescale); the
+//      exact rows' terms are added while the first batch loads;
+//   5. the combine: the two groups of a 16-lane row added by DPP, the pair sums
+//      added in pair order through LDS (deterministic), m* = the largest score
+//      added; then the subtraction, the clamp and one normalisation.
 // The arithmetic of a term is the merge kernel's; the order of the sums
 // differs (the fused kernel spreads a head's entries over more groups).
 #include "rma_select.hpp"
