@@ -287,8 +287,24 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
             device_info().lds_per_block;
   }
   p.fused = fused;
+  // With few heads and a large budget the fused kernel's gather, one block per
+  // head, is bound by the loads one CU keeps in flight: then each head's list
+  // is split over several blocks (each selects, gathers a slice of about one
+  // round and writes a partial) and merge_combine_kernel combines the slices:
+  // from four rounds on (with three the second kernel costs about what the
+  // split saves).  At most 16 slices, one block per CU in all, none empty.
+  const int64_t per_round = (int64_t)(p.fused_threads / 8) *
+                            (kv.dtype == RMA_BF16 ? (kv.d == 64 ? 4 : 2) : 1);
+  const int64_t rounds = K > 0 ? ceil_div(K, per_round) : 0;
+  const int64_t split_cap = heads <= 128 ? std::min<int64_t>(rounds, 16) : 1;
+  p.fused_split = 1;
+  if (fused && p.fused_threads == 1024 && rounds >= 4) {
+    const int64_t ns = std::max<int64_t>(1, std::min<int64_t>(split_cap, (int64_t)device_cus() / heads));
+    const int64_t sl = ceil_div(K, ns);
+    p.fused_split = (int)ceil_div(K, sl);
+  }
   // the separate path's regions are always reserved, so the size does not
-  // depend on the device
+  // depend on the device (the split partials are sized for the most slices)
   size_t off = align_up(p.topk.total);
   p.off_idx = off;
   off = align_up(off + (size_t)heads * K * 4);
@@ -296,6 +312,8 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
   off = align_up(off + (size_t)heads * K * 4);
   p.off_merge = off;
   off = align_up(off + p.merge.total);
+  p.off_fpart = off;
+  if (split_cap > 1) off = align_up(off + (size_t)heads * split_cap * (4 + 3 * kv.d) * 4);
   p.total = std::max(off, kAlign);
   return p;
 }

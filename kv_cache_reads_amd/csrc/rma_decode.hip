@@ -48,7 +48,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
                     const float* __restrict__ Wq, const float* __restrict__ bq, int P,
                     const PT* __restrict__ phik, const float* __restrict__ S,
                     const float* __restrict__ u_, uint32_t flags, float* __restrict__ y,
-                    float* __restrict__ stats, float inv_sqrt_d) {
+                    float* __restrict__ stats, float inv_sqrt_d, int n_split,
+                    float* __restrict__ sparts) {
   constexpr int NW = NT / kWave;
   constexpr int LPE = 8;            // lanes per entry
   constexpr int NGR = NT / LPE;     // entry groups
@@ -100,7 +101,12 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
                "s"(n_gen), "s"(L_mid), "s"(ch), "s"(n_chunks), "s"(r_cap), "s"(K), "s"(hpw), "s"(ent),
                "s"(meta), "s"(idx_out), "s"(sc_out), "s"(phi_q), "s"(Wq), "s"(bq), "s"(P), "s"(phik),
                "s"(S), "s"(u_), "s"(flags), "s"(y), "s"(stats), "s"(inv_sqrt_d));
-  const int ug = blockIdx.x, u = ug / G, tid = threadIdx.x;
+  // block (head ug, slice rs_) of n_split: every slice's block selects, slice
+  // rs_ gathers the list entries [rs_ sl, (rs_ + 1) sl) (slice 0 also the exact
+  // rows) and writes a partial that merge_combine_kernel combines
+  const int heads = gridDim.x / n_split;
+  const int rsl = blockIdx.x / heads;
+  const int ug = blockIdx.x - rsl * heads, u = ug / G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
   const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
@@ -335,7 +341,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     }
     mref = fmaxf(mref, hi * inv_sqrt_d);
     SelOut io;
-    if (idx_out != nullptr) {
+    if (idx_out != nullptr && rsl == 0) {
       io.io = idx_out + (size_t)ug * K;
       io.so = sc_out + (size_t)ug * K;
     }
@@ -366,20 +372,23 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     Z += ew;
     mx = fmaxf(mx, sc);
   };
-  bool ex_due = grp < n_ex;   // the group's first exact row (score a0, value row xv)
+  bool ex_due = grp < n_ex && rsl == 0;   // the group's first exact row (score a0, value row xv)
+  // this block's slice of the list
+  const int sl = (K + n_split - 1) / n_split;
+  const int j_lo = min(K, rsl * sl), j_hi = min(K, j_lo + sl);
 
   // ---- 5. retrieved entries from the list
   float fr[FPL];
 #pragma unroll
   for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
-  for (int jb = grp; jb < K; jb += NGR * B) {
+  for (int jb = j_lo + grp; jb < j_hi; jb += NGR * B) {
     RawPiece<KT, CPL> vr[B];
     RawPiece<PT, FPL> pr[B];
     float scs[B];
 #pragma unroll
     for (int e = 0; e < B; ++e) {
       const int jj = jb + e * NGR;
-      const int jc = jj < K ? jj : jb;
+      const int jc = jj < j_hi ? jj : jb;
       const int pos = min(max(lpos[jc], n_sink), n_sink + max(L_mid, 1) - 1);
       scs[e] = lsc[jc];
       vr[e].load(vunit + (size_t)pos * D + part * CPL);
@@ -401,7 +410,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
       for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
       w = lane_group_sum<LPE>(w);
-      if (jb + e * NGR < K) {  // uniform within the group
+      if (jb + e * NGR < j_hi) {  // uniform within the group
         vr[e].unpack(vv);
         add_exp(scs[e], vv);
 #pragma unroll
@@ -415,7 +424,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     xv.unpack(vv);
     add_exp(a0, vv);
   }
-  for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
+  for (int j = grp + NGR; rsl == 0 && j < n_ex; j += NGR) {   // more exact rows than groups
     const int pos = ex_pos(j);
     xv.load(vunit + (size_t)pos * D + part * CPL);
     xk.load(kunit + (size_t)pos * D + part * CPL);
@@ -468,6 +477,31 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
   const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
   const float uf = rs ? s_uf : 0.f;
+  if (n_split > 1) {
+    // this slice's partial in merge_kernel's layout (m, Z_E, sum w, u^T f, N_E,
+    // sum w v, phi(q)^T S), Z_E and N_E taken relative to m = the largest score
+    // this block added
+    constexpr int PFL = 4 + 3 * D;
+    float* pp = sparts + ((size_t)ug * n_split + rsl) * PFL;
+    const float sc = ms == -INFINITY ? 0.f : __expf(mref - ms);
+    if (tid == 0) {
+      pp[0] = ms;
+      pp[1] = ZE * sc;
+      pp[2] = ZKt;
+      pp[3] = uf;
+    }
+    for (int col = tid; col < D; col += NT) {
+      float fs = 0.f;
+      if (rs) {
+#pragma unroll
+        for (int k = 0; k < FB; ++k) fs += s_part[k][col];
+      }
+      pp[4 + col] = s_fin[col] * sc;
+      pp[4 + D + col] = s_fin[D + col];
+      pp[4 + 2 * D + col] = fs;
+    }
+    return;
+  }
   float zr = 0.f;
   if (rs) zr = fmaxf(uf - (sub ? ZKt : 0.f), 0.f);
   // y = (N_E + e^{-mref} nu) / (Z_E + e^{-mref} Z_R) with N_E, Z_E taken
@@ -512,13 +546,18 @@ hipError_t launch_fused_nt(const DecodePlan& pl, const float* q, int G, const rm
   // the plan checked the fit; a launch that would not fit is refused here too
   if (lds + kernel_static_lds<&decode_fused_kernel<KT, PT, D, M, NT>>() > device_info().lds_per_block)
     return hipErrorInvalidConfiguration;
-  return launch_kernel("decode_fused_kernel", kern, dim3(kv.n_units * G), dim3(NT), (uint32_t)lds, st, q,
-                       G, static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride,
-                       (int)sp.L, sp.n_sink, sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, tp.n_chunks,
-                       tp.r_cap, K, reinterpret_cast<const float4*>(ws + tp.off_hp),
-                       reinterpret_cast<const float2*>(ws + tp.off_ent),
-                       reinterpret_cast<const int2*>(ws + tp.off_meta), idx, sel, phi_q, Wq, bq, P,
-                       static_cast<const PT*>(phi_k), S, u, flags, y, stats, 1.0f / sqrtf((float)D));
+  const int ns = pl.fused_split;
+  float* parts = reinterpret_cast<float*>(ws + pl.off_fpart);
+  const int heads = (int)(kv.n_units * G);
+  hipError_t e = launch_kernel(
+      "decode_fused_kernel", kern, dim3(heads * ns), dim3(NT), (uint32_t)lds, st, q, G,
+      static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
+      sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, tp.n_chunks, tp.r_cap, K,
+      reinterpret_cast<const float4*>(ws + tp.off_hp), reinterpret_cast<const float2*>(ws + tp.off_ent),
+      reinterpret_cast<const int2*>(ws + tp.off_meta), idx, sel, phi_q, Wq, bq, P,
+      static_cast<const PT*>(phi_k), S, u, flags, y, stats, 1.0f / sqrtf((float)D), ns, parts);
+  if (e != hipSuccess || ns == 1) return e;
+  return launch_merge_combine(parts, ns, heads, D, flags, K, L_mid, y, stats, st);
 }
 
 template <typename KT, typename PT, int D>

@@ -106,8 +106,9 @@ struct DecodePlan {
   TopkPlan topk;       // the scan's chunks and reports (workspace offset 0)
   bool fused;
   int fused_threads;   // 256, 512 or 1024
+  int fused_split;     // blocks per head of the fused kernel (> 1: partials + combine)
   MergePlan merge;     // the separate path
-  size_t off_idx, off_sel, off_merge, total;
+  size_t off_idx, off_sel, off_merge, off_fpart, total;
 };
 DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m, int phi_dtype,
                        bool recompute);
@@ -200,6 +201,9 @@ hipError_t launch_topk(const TopkPlan& pl, const float* q, int G, const rma_kv& 
                        const rma_span& sp, const float* kappa, int K, int32_t* idx,
                        float* sel_scores, uint8_t* ws, hipStream_t st);
 
+// combines per-slice partials (merge_kernel's layout) of `heads` query heads
+hipError_t launch_merge_combine(const float* parts, int n_slices, int heads, int d, uint32_t flags,
+                                int K, int L_mid, float* y, float* stats, hipStream_t st);
 hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q, const float* Wq,
                         const float* bq, int G,
                         const rma_kv& kv, const rma_span& sp, const int32_t* idx,

@@ -589,4 +589,13 @@ hipError_t launch_merge(const MergePlan& pl, const float* q, const float* phi_q,
 #undef RMA_MERGE_DISPATCH
 }
 
+hipError_t launch_merge_combine(const float* parts, int n_slices, int heads, int d, uint32_t flags,
+                                int K, int L_mid, float* y, float* stats, hipStream_t st) {
+  if (d == 64)
+    return launch_kernel("merge_combine_kernel", merge_combine_kernel<64>, dim3(heads),
+                         dim3(kMergeCombineThreads), 0, st, parts, n_slices, flags, K, L_mid, y, stats);
+  return launch_kernel("merge_combine_kernel", merge_combine_kernel<128>, dim3(heads),
+                       dim3(kMergeCombineThreads), 0, st, parts, n_slices, flags, K, L_mid, y, stats);
+}
+
 }  // namespace rma
