@@ -72,12 +72,12 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # (kernel, workload, K): profiles/traffic_c1.md, profiles/traffic_c4.md
-    ("decode_fused_kernel", "c1", 328): {"fetch_bytes": 8667261, "write_bytes": 8192, "csrc": "80d79ef82bc08e48"},
-    ("topk_scan_kernel", "c1", 328): {"fetch_bytes": 33749245, "write_bytes": 636576, "csrc": "80d79ef82bc08e48"},
-    ("build_mfma_kernel", "c1", 328): {"fetch_bytes": 69263911, "write_bytes": 84052827, "csrc": "80d79ef82bc08e48"},
-    ("decode_fused_kernel", "c4", 1310): {"fetch_bytes": 2395478987, "write_bytes": 1376256, "csrc": "80d79ef82bc08e48"},
-    ("topk_scan_kernel", "c4", 1310): {"fetch_bytes": 30548098464, "write_bytes": 78078701, "csrc": "80d79ef82bc08e48"},
-    ("build_mfma_kernel", "c4", 1310): {"fetch_bytes": 60214982131, "write_bytes": 30167611285, "csrc": "80d79ef82bc08e48"},
+    ("decode_fused_kernel", "c1", 328): {"fetch_bytes": 8688762, "write_bytes": 8192, "csrc": "84684ba5cd0deaee"},
+    ("topk_scan_kernel", "c1", 328): {"fetch_bytes": 33749165, "write_bytes": 636576, "csrc": "84684ba5cd0deaee"},
+    ("build_mfma_kernel", "c1", 328): {"fetch_bytes": 69263932, "write_bytes": 84052635, "csrc": "84684ba5cd0deaee"},
+    ("decode_fused_kernel", "c4", 1310): {"fetch_bytes": 2395496516, "write_bytes": 1376256, "csrc": "84684ba5cd0deaee"},
+    ("topk_scan_kernel", "c4", 1310): {"fetch_bytes": 30555932274, "write_bytes": 78080694, "csrc": "84684ba5cd0deaee"},
+    ("build_mfma_kernel", "c4", 1310): {"fetch_bytes": 60214996201, "write_bytes": 30167612013, "csrc": "84684ba5cd0deaee"},
 }
 
 
