@@ -64,11 +64,11 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   constexpr int NV = 2 * D + 2;     // combined values: N[D], sum w v [D], Z, sum w
   constexpr int NP = NT / 16;       // group pairs (two groups per 16-lane row)
   // dynamic LDS: the union of the chunk reports (scores, positions; room for
-  // n_chunks r_cap entries rounded up to whole batches of the selection's rows),
+  // n_chunks r_cap entries rounded up to whole rows of 64),
   // then the list of the K selected (positions, scaled scores); after the
   // gathers the combine reuses it from the start
   extern __shared__ __align__(16) float dyn[];
-  constexpr int UB = kWaveSelRows * kWave;
+  constexpr int UB = kWave;   // the union is padded to whole rows of 64 entries
   const int PS = (n_chunks * r_cap + UB - 1) / UB * UB;
   float* es = dyn;
   int* ep = reinterpret_cast<int*>(dyn + PS);
@@ -207,7 +207,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 
   // ---- 2. wave 0: each chunk's offset in the union (a wave scan of the counts
   //      it reported, at most r_cap each), the chunk table, empty entries after
-  //      the union up to a whole batch of rows.  Everyone: q for the band
+  //      the union up to a whole row of 64.  Everyone: q for the band
   //      rescoring, f = phi_q(q).
   if (wave == 0) {
     int wc4[4], ls = 0;

@@ -76,7 +76,6 @@ constexpr int kSelBandMax = 512;        // band members resolved in LDS
 constexpr int kSelMaxEntries = 16384;   // union entries held in LDS by a select block
 constexpr int kSelBins = 1024;          // linear bins over the union's score range
 constexpr int kSelThreads = 1024;       // select block size
-constexpr int kWaveSelRows = 8;         // rows of 64 entries per load batch of the one-wave selection
 
 struct TopkPlan {
   int n_chunks, ch, r_min, r_cap;
@@ -119,7 +118,7 @@ inline bool fused_slots_fit(int n_chunks, int nt) { return n_chunks >= 1 && n_ch
 // dynamic LDS of the fused kernel: the union of the chunk reports and the
 // selected list, or (reusing it) the combine's group-pair sums
 inline size_t fused_dyn_bytes(int n_chunks, int r_cap, int K, int d, int nt) {
-  const size_t ub = (size_t)kWaveSelRows * 64;   // whole load batches of the one-wave selection
+  const size_t ub = 64;   // the union padded to whole rows of 64 entries
   const size_t a = 2 * (((size_t)n_chunks * r_cap + ub - 1) / ub * ub) + 2 * (size_t)K;
   const size_t b = (size_t)(nt / 16) * (2 * d + 2);
   return (a > b ? a : b) * 4 + 16;
