@@ -95,18 +95,22 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ float s_uf;
   __shared__ float s_f[M];          // f = phi_q(q) of this head
 
+  // block (head g of unit u, slice rsl) of the (G, units, n_split) grid: every
+  // slice's block selects, slice rsl gathers the list entries [rsl sl, (rsl + 1)
+  // sl) (slice 0 also the exact rows) and writes a partial that
+  // merge_combine_kernel combines.  The grid's shape gives u and rsl without a
+  // division (the workgroups still start in head-major order, slice by slice)
+  const int rsl = blockIdx.z, u = blockIdx.y;
+  const int ug = u * G + blockIdx.x, tid = threadIdx.x;
+  // the head's binning parameters: a uniform load issued first, while no
+  // statement with side effects precedes it (so it goes through the scalar cache)
+  const f32x4 hp_in = *reinterpret_cast<const f32x4*>(hpw + ug);
   // every kernel argument into registers at once: one round trip for all of
   // them rather than one per branch that first needs some
   asm volatile("" ::"s"(q), "s"(G), "s"(kb), "s"(vb), "s"(ustride), "s"(L), "s"(n_sink), "s"(n_tail),
                "s"(n_gen), "s"(L_mid), "s"(ch), "s"(n_chunks), "s"(r_cap), "s"(K), "s"(hpw), "s"(ent),
                "s"(meta), "s"(idx_out), "s"(sc_out), "s"(phi_q), "s"(Wq), "s"(bq), "s"(P), "s"(phik),
                "s"(S), "s"(u_), "s"(flags), "s"(y), "s"(stats), "s"(inv_sqrt_d));
-  // block (head ug, slice rs_) of n_split: every slice's block selects, slice
-  // rs_ gathers the list entries [rs_ sl, (rs_ + 1) sl) (slice 0 also the exact
-  // rows) and writes a partial that merge_combine_kernel combines
-  const int heads = gridDim.x / n_split;
-  const int rsl = blockIdx.x / heads;
-  const int ug = blockIdx.x - rsl * heads, u = ug / G, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
   const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
@@ -122,12 +126,11 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const int2* mt = meta + (size_t)ug * n_chunks;
   const float2* en = ent + (size_t)ug * n_chunks * r_cap;
 
-  // ---- 1. loads.  The selection's: the head's parameters, the chunk table, and
-  //      the report slots (a power-of-two group of tpc threads per chunk; thread
-  //      t serves chunk t >> lg_t, its slots my_s + k tpc, so no slot index needs
-  //      a division); the first SPEC tpc slots of each chunk now, the rest (only
-  //      where r_cap exceeds them) in later rounds
-  const f32x4 hp_in = *reinterpret_cast<const f32x4*>(hpw + ug);
+  // ---- 1. loads.  The selection's: the chunk table and the report slots (a
+  //      power-of-two group of tpc threads per chunk; thread t serves chunk
+  //      t >> lg_t, its slots my_s + k tpc, so no slot index needs a division);
+  //      the first SPEC tpc slots of each chunk now, the rest (only where r_cap
+  //      exceeds them) in later rounds
   const int lg_c = n_chunks > 1 ? 32 - __clz(n_chunks - 1) : 0;
   const int lg_t = __builtin_ctz(NT) - lg_c, tpc = 1 << lg_t;
   const int my_c = tid >> lg_t, my_s = tid & (tpc - 1);
@@ -155,7 +158,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   }
   float wq[EPT], xq[EPT], fb0;
   {
-    const int pset = u % P;
+    const int pset = P > 1 ? u % P : 0;
     const float* wr = fcomp ? Wq + ((size_t)pset * M + fi) * D + fpart * EPT : qg;
     const float* qs = qg + fpart * EPT;
 #pragma unroll
@@ -332,6 +335,9 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   float mref = -INFINITY;
   {
     const HeadParams hp{hp_in[0], hp_in[1], hp_in[2]};
+    // the load's unused fourth word stays allocated until here, so no register
+    // of the load is reused (which would make the prologue wait for it)
+    asm volatile("" ::"s"(hp_in[3]));
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -374,7 +380,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   };
   bool ex_due = grp < n_ex && rsl == 0;   // the group's first exact row (score a0, value row xv)
   // this block's slice of the list
-  const int sl = (K + n_split - 1) / n_split;
+  const int sl = n_split > 1 ? (K + n_split - 1) / n_split : K;
   const int j_lo = min(K, rsl * sl), j_hi = min(K, j_lo + sl);
 
   // ---- 5. retrieved entries from the list
@@ -404,13 +410,13 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     }
 #pragma unroll
     for (int e = 0; e < B; ++e) {
-      float ph[FPL], vv[CPL];
-      pr[e].unpack(ph);
-      float w = 0.f;
+      if (jb + e * NGR < j_hi) {  // uniform within the group; a wave skips its empty slots
+        float ph[FPL], vv[CPL];
+        pr[e].unpack(ph);
+        float w = 0.f;
 #pragma unroll
-      for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
-      w = lane_group_sum<LPE>(w);
-      if (jb + e * NGR < j_hi) {  // uniform within the group
+        for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+        w = lane_group_sum<LPE>(w);
         vr[e].unpack(vv);
         add_exp(scs[e], vv);
 #pragma unroll
@@ -550,7 +556,7 @@ hipError_t launch_fused_nt(const DecodePlan& pl, const float* q, int G, const rm
   float* parts = reinterpret_cast<float*>(ws + pl.off_fpart);
   const int heads = (int)(kv.n_units * G);
   hipError_t e = launch_kernel(
-      "decode_fused_kernel", kern, dim3(heads * ns), dim3(NT), (uint32_t)lds, st, q, G,
+      "decode_fused_kernel", kern, dim3(G, kv.n_units, ns), dim3(NT), (uint32_t)lds, st, q, G,
       static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
       sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, tp.n_chunks, tp.r_cap, K,
       reinterpret_cast<const float4*>(ws + tp.off_hp), reinterpret_cast<const float2*>(ws + tp.off_ent),

@@ -610,38 +610,33 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
     // ---- histogram over [lo, hi]
     for (int i = tid; i < nE; i += NT) atomicAdd(&w.hist[ubin(es[i])], 1u);
     __syncthreads();
-    // ---- every wave: the bin of the K-th largest (lane l owns the 16 bins
-    //      NBS-16(l+1) .. NBS-16l-1, read as four 16-byte words) ...
-    int cb[BPL], ls = 0;
+    // ---- every wave: the bin of the K-th largest.  Lane l owns the 16 bins
+    //      NBS-16(l+1) .. NBS-16l-1 (read as four 16-byte words); a scan of the
+    //      lanes' sums names the lane holding it, whose 16 bins the first 16
+    //      lanes then take one each (descending) and scan again
+    int bK = 0, above = 0;
     {
+      static_assert(BPL == 16, "the second scan covers one 16-lane row");
       const uint4* h4 = reinterpret_cast<const uint4*>(w.hist + NBS - BPL * (lane + 1));
+      int ls = 0;
 #pragma unroll
       for (int j = 0; j < BPL / 4; ++j) {
         const uint4 v = h4[j];
-        cb[4 * j] = (int)v.x; cb[4 * j + 1] = (int)v.y; cb[4 * j + 2] = (int)v.z; cb[4 * j + 3] = (int)v.w;
+        ls += (int)(v.x + v.y + v.z + v.w);
       }
-#pragma unroll
-      for (int j = 0; j < BPL; ++j) ls += cb[j];
-    }
-    const int incl = wave_incl_scan_dpp(ls);
-    const int owner = __ffsll((long long)__ballot(incl >= K)) - 1;
-    int bK = 0, above = 0;
-    {
-      // descending within the lane: bin NBS-BPL*lane-1-j is cb[BPL-1-j]
-      int run = incl - ls, b = 0, a = 0;
-      bool found = false;
-#pragma unroll
-      for (int j = 0; j < BPL; ++j) {
-        const int c = cb[BPL - 1 - j];
-        if (!found && run + c >= K) {
-          b = NBS - 1 - BPL * lane - j;
-          a = run;
-          found = true;
-        }
-        run += c;
-      }
-      bK = __builtin_amdgcn_readlane(b, owner);
-      above = __builtin_amdgcn_readlane(a, owner);
+      const int incl = wave_incl_scan_dpp(ls);
+      const int owner = __ffsll((long long)__ballot(incl >= K)) - 1;
+      const int run0 = __builtin_amdgcn_readlane(incl - ls, owner);   // entries above its bins
+      const int bo = NBS - 1 - BPL * owner;
+      const int c = lane < BPL ? (int)w.hist[bo - lane] : 0;
+      int cum = c;                        // inclusive scan inside each 16-lane row
+      cum += dpp_i<0x111>(cum);           // row_shr:1
+      cum += dpp_i<0x112>(cum);           // row_shr:2
+      cum += dpp_i<0x114>(cum);           // row_shr:4
+      cum += dpp_i<0x118>(cum);           // row_shr:8
+      const int jf = __ffsll((long long)__ballot(lane < BPL && run0 + cum >= K)) - 1;
+      bK = bo - jf;
+      above = __builtin_amdgcn_readlane(run0 + cum - c, jf);
     }
     const int rK = K - above;   // the K-th score is the rK-th largest member of bin bK
     // ... and its members: scores appended (order free), extent
