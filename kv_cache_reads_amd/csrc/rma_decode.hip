@@ -271,8 +271,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
           if (j < wc) {
             es[o0 + j] = sv2[k].x;
             ep[o0 + j] = __float_as_int(sv2[k].y);
-            rlo = fminf(rlo, sv2[k].x);
-            rhi = fmaxf(rhi, sv2[k].x);
+            rlo = fmin_m3(rlo, sv2[k].x);
+            rhi = fmax_m3(rhi, sv2[k].x);
           }
         }
         j0 += SPEC * tpc;
@@ -320,7 +320,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
       RawPiece<KT, CPL> rk;
       rk.load(kunit + (size_t)ex_pos(j) * D + part * CPL);
-      am = fmaxf(am, ex_score(rk));
+      am = fmax_m3(am, ex_score(rk));
     }
     am = wave_max_dpp(am);
     if (lane == 0) s_amax[wave] = am;
@@ -341,11 +341,11 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      lo = fminf(lo, s_rlo[w]);
-      hi = fmaxf(hi, s_rhi[w]);
-      mref = fmaxf(mref, s_amax[w]);
+      lo = fmin_m3(lo, s_rlo[w]);
+      hi = fmax_m3(hi, s_rhi[w]);
+      mref = fmax_m3(mref, s_amax[w]);
     }
-    mref = fmaxf(mref, hi * inv_sqrt_d);
+    mref = fmax_m3(mref, hi * inv_sqrt_d);
     SelOut io;
     if (idx_out != nullptr && rsl == 0) {
       io.io = idx_out + (size_t)ug * K;
@@ -376,7 +376,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
     for (int c = 0; c < CPL; ++c) N[c] = __fmaf_rn(ew, vv[c], N[c]);
     Z += ew;
-    mx = fmaxf(mx, sc);
+    mx = fmax_m3(mx, sc);
   };
   bool ex_due = grp < n_ex && rsl == 0;   // the group's first exact row (score a0, value row xv)
   // this block's slice of the list
@@ -480,7 +480,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __syncthreads();
   float ms = -INFINITY;   // m*: the largest score of the exact support
 #pragma unroll
-  for (int w = 0; w < NW; ++w) ms = fmaxf(ms, s_wm[w]);
+  for (int w = 0; w < NW; ++w) ms = fmax_m3(ms, s_wm[w]);
   const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
   const float uf = rs ? s_uf : 0.f;
   if (n_split > 1) {

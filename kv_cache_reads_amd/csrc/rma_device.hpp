@@ -173,17 +173,27 @@ __device__ __forceinline__ float dpp_f(float v) {
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+// minimum / maximum as one v_med3_f32 against -inf / +inf: fminf / fmaxf would
+// first quiet each operand (a NaN-canonicalising instruction apiece)
+__device__ __forceinline__ float fmin_m3(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -3.4028235e38f); }
+__device__ __forceinline__ float fmax_m3(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.4028235e38f); }
 // max within each row of 16 lanes, in every lane of the row
 __device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
+  v = fmax_m3(v, dpp_f<0xB1>(v));
+  v = fmax_m3(v, dpp_f<0x4E>(v));
+  v = fmax_m3(v, dpp_f<0x141>(v));
+  v = fmax_m3(v, dpp_f<0x140>(v));
   return v;
 }
+// the wave's maximum: rows combined by row broadcasts (row 0 into 1, 2 into 3,
+// then 1 into 2 and 3), read from lane 63
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = row_max16(v);
-  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+  const int b = __float_as_int(v);
+  v = fmax_m3(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x142, 0xA, 0xF, false)));
+  const int c = __float_as_int(v);
+  v = fmax_m3(v, __int_as_float(__builtin_amdgcn_update_dpp(c, c, 0x143, 0xC, 0xF, false)));
+  return readlane_f(v, kWave - 1);
 }
 __device__ __forceinline__ float wave_min_dpp(float v) { return -wave_max_dpp(-v); }
 __device__ __forceinline__ float wave_sum_dpp(float v) {

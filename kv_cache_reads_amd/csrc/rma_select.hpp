@@ -47,7 +47,8 @@ __device__ __forceinline__ HeadParams head_params(float n2, float kappa) {
 
 __device__ __forceinline__ int lin_bin(float x, const HeadParams& h) {
   const float t = __fmul_rn(__fadd_rn(x, h.rg), h.inv_w);
-  return (t >= 0.f) ? (int)fminf(t, (float)(kScanBins - 1)) : 0;  // monotone in x; NaN -> 0
+  // clamped to [0, kScanBins - 1] in one v_med3_f32 and truncated: monotone in x
+  return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(kScanBins - 1));
 }
 
 // Block-wide exclusive scan of one int per thread (NT threads); returns the
@@ -605,7 +606,7 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
     const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
     auto ubin = [&](float x) {
       const float t = __fmul_rn(__fsub_rn(x, lo), inv);
-      return (t >= 0.f) ? (int)fminf(t, (float)(NBS - 1)) : 0;  // monotone in x
+      return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(NBS - 1));  // clamped: monotone in x
     };
     // ---- histogram over [lo, hi]
     for (int i = tid; i < nE; i += NT) atomicAdd(&w.hist[ubin(es[i])], 1u);
@@ -653,8 +654,8 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
           const int o = base + lanes_below(bm);
           if (m && o < kSelBandMax) w.cand[o] = x;
         }
-        xlo = m ? fminf(xlo, x) : xlo;
-        xhi = m ? fmaxf(xhi, x) : xhi;
+        xlo = m ? fmin_m3(xlo, x) : xlo;
+        xhi = m ? fmax_m3(xhi, x) : xhi;
       }
       xlo = wave_min_dpp(xlo);
       xhi = wave_max_dpp(xhi);

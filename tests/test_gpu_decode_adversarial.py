@@ -25,6 +25,7 @@ import torch
 
 import oracle as O
 from kv_cache_reads_amd import rma as R
+from parity_util import check_scan_error
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -82,6 +83,7 @@ def _decode_case(k, q, L, ns, nt, K, units=(0,), m=64, seed=0):
                 f"d={d} {k.dtype} K={K} unit {uu} head {gg}: {np.setdiff1d(got, ref)[:8]} vs {np.setdiff1d(ref, got)[:8]}"
             s_ref = kf[got] @ q[uu, gg].double().numpy() / math.sqrt(d)
             assert np.allclose(sel[uu, gg].numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
+            check_scan_error(sel[uu, gg].numpy(), s_ref, q[uu, gg], kf, d, f"d={d} {k.dtype} K={K} u{uu} g{gg}")
     return fused
 
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from parity_util import (R, W, check_prefill, check_summaries, check_y, hip_decode, hip_prefill,
+from parity_util import (R, W, check_prefill, check_scan_error, check_summaries, check_y, hip_decode, hip_prefill,
                          host_unit, log, oracle_decode, oracle_prefill, prefill_span, decode_span)
 
 pytestmark = pytest.mark.gpu
@@ -347,6 +347,7 @@ def _topk_case(k, q, L, ns, nt, K, units=(0,)):
             # selected scores are the fp32 scores of the selected tokens
             s_ref = kf[got] @ q[u, g].double().numpy() / math.sqrt(d)
             assert np.allclose(sel[u, g].cpu().numpy(), s_ref, rtol=1e-5, atol=1e-5 * np.abs(s_ref).max())
+            check_scan_error(sel[u, g].cpu().numpy(), s_ref, q[u, g], kf, d, f"d={d} {k.dtype} K={K} u{u} g{g}")
     return idx
 
 
