@@ -279,7 +279,12 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
   // block leaves each lane)
   p.fused_threads = heads < 1024 && !(kv.dtype == RMA_F32 && kv.d == 128) ? 1024
                     : (kv.d == 64 ? 256 : 512);
-  bool fused = K > 0 && !recompute && p.topk.n_chunks <= kSelMaxChunks &&
+  // the fused kernel addresses a unit's K/V rows and phi_k rows through 32-bit
+  // byte offsets: larger units take the two kernels (64-bit addressing)
+  const int64_t kv_bytes = (sp.L + sp.n_gen) * kv.d * (kv.dtype == RMA_BF16 ? 2 : 4);
+  const int64_t phi_bytes = l_mid(sp) * m * (phi_dtype == RMA_BF16 ? 2 : 4);
+  const bool off32_fits = kv_bytes < ((int64_t)1 << 32) && phi_bytes < ((int64_t)1 << 32);
+  bool fused = K > 0 && !recompute && off32_fits && p.topk.n_chunks <= kSelMaxChunks &&
                fused_slots_fit(p.topk.n_chunks, p.fused_threads);
   if (fused) {
     const size_t dyn = fused_dyn_bytes(p.topk.n_chunks, p.topk.r_cap, K, kv.d, p.fused_threads);

@@ -79,7 +79,9 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   static_assert(kSelMaxChunks == 4 * kWave, "four chunks per lane of wave 0");
   __shared__ int s_off[kSelMaxChunks], s_bcs[kSelMaxChunks], s_nrep[kSelMaxChunks];
   __shared__ int s_nE, s_trunc;
-  __shared__ float s_rlo[NW], s_rhi[NW];
+  // ordered-integer keys (ord_f32) reduced by LDS atomics: the union's lowest and
+  // highest score, the exact rows' highest score, the largest score added
+  __shared__ uint32_t s_rng[4];
   __shared__ float s_qf[D];
   __shared__ uint32_t s_hist[kSelBins];
   __shared__ float s_cand[kSelBandMax];
@@ -88,8 +90,6 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ int s_misc[8];
   __shared__ int s_buf[kSelThreads / kWave + 1];
   __shared__ int s_wcnt[NW];
-  __shared__ float s_wm[NW];
-  __shared__ float s_amax[NW];
   __shared__ float s_fin[NV];
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
@@ -125,6 +125,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const float* qg = q + (size_t)ug * D;
   const int2* mt = meta + (size_t)ug * n_chunks;
   const float2* en = ent + (size_t)ug * n_chunks * r_cap;
+  const PT* phiu = phik + (size_t)u * L_mid * M;   // this unit's phi_k rows
 
   // ---- 1. loads.  The selection's: the chunk table and the report slots (a
   //      power-of-two group of tpc threads per chunk; thread t serves chunk
@@ -135,17 +136,17 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const int lg_t = __builtin_ctz(NT) - lg_c, tpc = 1 << lg_t;
   const int my_c = tid >> lg_t, my_s = tid & (tpc - 1);
   const int cc = min(my_c, n_chunks - 1);
-  const int2 m_mine = mt[cc];
+  const int2 m_mine = *off32(mt, cc);
   float2 sv2[SPEC];
 #pragma unroll
-  for (int k = 0; k < SPEC; ++k) sv2[k] = en[(size_t)cc * r_cap + min(my_s + k * tpc, r_cap - 1)];
+  for (int k = 0; k < SPEC; ++k) sv2[k] = *off32(en, cc * r_cap + min(my_s + k * tpc, r_cap - 1));
   // the chunk table: four chunks per lane of wave 0, which computes the offsets
   int2 mc[4];
   if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) mc[k] = mt[min(lane * 4 + k, n_chunks - 1)];
+    for (int k = 0; k < 4; ++k) mc[k] = *off32(mt, min(lane * 4 + k, n_chunks - 1));
   }
-  const float q_in = qg[min(tid, D - 1)];
+  const float q_in = *off32(qg, min(tid, D - 1));
   // the merge's: f's operands (or the given features), q, S, u
   constexpr int TPF = NT / M, EPT = D / TPF;     // threads per feature, elements each
   const int fi = tid / TPF, fpart = tid % TPF;
@@ -153,20 +154,21 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   float qr[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; i += 4) {
-    const float4 t = *reinterpret_cast<const float4*>(qg + part * CPL + i);
+    const float4 t = *reinterpret_cast<const float4*>(off32(qg, part * CPL + i));
     qr[i] = t.x; qr[i + 1] = t.y; qr[i + 2] = t.z; qr[i + 3] = t.w;
   }
   float wq[EPT], xq[EPT], fb0;
   {
     const int pset = P > 1 ? u % P : 0;
-    const float* wr = fcomp ? Wq + ((size_t)pset * M + fi) * D + fpart * EPT : qg;
-    const float* qs = qg + fpart * EPT;
+    const float* wb = fcomp ? Wq + (size_t)pset * M * D : qg;   // W of this unit's set
+    const uint32_t wo = fcomp ? fi * D + fpart * EPT : 0u;
+    const uint32_t qo = fpart * EPT;
 #pragma unroll
     for (int i = 0; i < EPT; i += 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(wr + i);
+      const float4 w4 = *reinterpret_cast<const float4*>(off32(wb, wo + i));
       wq[i] = w4.x; wq[i + 1] = w4.y; wq[i + 2] = w4.z; wq[i + 3] = w4.w;
       if constexpr (TPF != LPE) {
-        const float4 x4 = *reinterpret_cast<const float4*>(qs + i);
+        const float4 x4 = *reinterpret_cast<const float4*>(off32(qg, qo + i));
         xq[i] = x4.x; xq[i + 1] = x4.y; xq[i + 2] = x4.z; xq[i + 3] = x4.w;
       }
     }
@@ -174,8 +176,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
       for (int i = 0; i < EPT; ++i) xq[i] = qr[i];
     }
-    fb0 = fcomp ? bq[(size_t)pset * M + fi]
-                : (resid && phi_q != nullptr ? phi_q[(size_t)ug * M + (tid % M)] : 0.f);
+    fb0 = fcomp ? *off32(bq + (size_t)pset * M, fi)
+                : (resid && phi_q != nullptr ? *off32(phi_q + (size_t)ug * M, tid % M) : 0.f);
   }
   // phi(q)^T S: thread (column scol, feature block fb) holds its FPB elements of
   // S (coalesced along the columns); without a residual the loads read q
@@ -185,15 +187,16 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const int scol = tid % D, fb = tid / D;
   float sv[FPB];
   {
-    const float* Sp = rs ? S + (size_t)u * M * D + (size_t)fb * FPB * D + scol : qg;
-    const size_t sst = rs ? D : 0;
+    const float* Sb = rs ? S + (size_t)u * M * D : qg;   // this unit's S
+    const uint32_t so = rs ? fb * FPB * D + scol : 0u;
+    const uint32_t sst = rs ? D : 0u;
 #pragma unroll
-    for (int i = 0; i < FPB; ++i) sv[i] = Sp[sst * i];
+    for (int i = 0; i < FPB; ++i) sv[i] = *off32(Sb, so + sst * i);
   }
   constexpr int UPL = (M + kWave - 1) / kWave;   // u^T f terms per lane (last wave)
   float uu[UPL];
 #pragma unroll
-  for (int i = 0; i < UPL; ++i) uu[i] = rs ? u_[(size_t)u * M + min(lane + kWave * i, M - 1)] : 0.f;
+  for (int i = 0; i < UPL; ++i) uu[i] = rs ? *off32(u_ + (size_t)u * M, min(lane + kWave * i, M - 1)) : 0.f;
   // the exactly scored rows (sinks, tail, generated tokens): group g takes rows
   // g, g + NGR, ...; the first now, scored while the retrieved rows load
   auto ex_pos = [&](int j) {
@@ -202,11 +205,12 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   RawPiece<KT, CPL> xv, xk;
   {
     const int pos = ex_pos(grp < n_ex ? grp : 0);
-    xv.load(vunit + (size_t)pos * D + part * CPL);
-    xk.load(kunit + (size_t)pos * D + part * CPL);
+    xv.load(off32(vunit, pos * D + part * CPL));
+    xk.load(off32(kunit, pos * D + part * CPL));
   }
   const BlockSelLds wl{s_hist, s_cand, s_bslot, s_bdd, s_misc, s_wcnt};
   init_block_select<NT>(wl);
+  if (tid < 4) s_rng[tid] = tid == 0 ? 0xffffffffu : 0u;   // the identities of min / max
 
   // ---- 2. wave 0: each chunk's offset in the union (a wave scan of the counts
   //      it reported, at most r_cap each), the chunk table, empty entries after
@@ -279,14 +283,14 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
         if (j0 >= wc) break;
 #pragma unroll
         for (int k = 0; k < SPEC; ++k)
-          sv2[k] = en[(size_t)cc * r_cap + min(j0 + my_s + k * tpc, r_cap - 1)];
+          sv2[k] = *off32(en, cc * r_cap + min(j0 + my_s + k * tpc, r_cap - 1));
       }
     }
     rlo = wave_min_dpp(rlo);
     rhi = wave_max_dpp(rhi);
     if (lane == 0) {
-      s_rlo[wave] = rlo;
-      s_rhi[wave] = rhi;
+      atomicMin(&s_rng[0], ord_f32(rlo));
+      atomicMax(&s_rng[1], ord_f32(rhi));
     }
   }
   if (rs) {
@@ -319,11 +323,11 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     if (grp < n_ex) am = a0 = ex_score(xk);
     for (int j = grp + NGR; j < n_ex; j += NGR) {   // more exact rows than groups
       RawPiece<KT, CPL> rk;
-      rk.load(kunit + (size_t)ex_pos(j) * D + part * CPL);
+      rk.load(off32(kunit, ex_pos(j) * D + part * CPL));
       am = fmax_m3(am, ex_score(rk));
     }
     am = wave_max_dpp(am);
-    if (lane == 0) s_amax[wave] = am;
+    if (lane == 0) atomicMax(&s_rng[2], ord_f32(am));
   }
   __syncthreads();
 
@@ -338,14 +342,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     // the load's unused fourth word stays allocated until here, so no register
     // of the load is reused (which would make the prologue wait for it)
     asm volatile("" ::"s"(hp_in[3]));
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lo = fmin_m3(lo, s_rlo[w]);
-      hi = fmax_m3(hi, s_rhi[w]);
-      mref = fmax_m3(mref, s_amax[w]);
-    }
-    mref = fmax_m3(mref, hi * inv_sqrt_d);
+    const float lo = unord_f32(s_rng[0]), hi = unord_f32(s_rng[1]);
+    mref = fmax_m3(unord_f32(s_rng[2]), hi * inv_sqrt_d);
     SelOut io;
     if (idx_out != nullptr && rsl == 0) {
       io.io = idx_out + (size_t)ug * K;
@@ -397,8 +395,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       const int jc = jj < j_hi ? jj : jb;
       const int pos = min(max(lpos[jc], n_sink), n_sink + max(L_mid, 1) - 1);
       scs[e] = lsc[jc];
-      vr[e].load(vunit + (size_t)pos * D + part * CPL);
-      if (sub) pr[e].load(phik + ((size_t)u * L_mid + (pos - n_sink)) * M + part * FPL);
+      vr[e].load(off32(vunit, pos * D + part * CPL));
+      if (sub) pr[e].load(off32(phiu, (pos - n_sink) * M + part * FPL));
       else pr[e].zero();
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
@@ -432,8 +430,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   }
   for (int j = grp + NGR; rsl == 0 && j < n_ex; j += NGR) {   // more exact rows than groups
     const int pos = ex_pos(j);
-    xv.load(vunit + (size_t)pos * D + part * CPL);
-    xk.load(kunit + (size_t)pos * D + part * CPL);
+    xv.load(off32(vunit, pos * D + part * CPL));
+    xk.load(off32(kunit, pos * D + part * CPL));
     const float sc = ex_score(xk);
     float vv[CPL];
     xv.unpack(vv);
@@ -453,7 +451,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     Z += dpp_f<0x128>(Z);
     ZK += dpp_f<0x128>(ZK);
     __syncthreads();   // every gather has read the list: its LDS is free
-    if (lane == 0) s_wm[wave] = wm;
+    if (lane == 0) atomicMax(&s_rng[3], ord_f32(wm));
     if ((lane & 15) < LPE) {
       float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NV;
 #pragma unroll
@@ -478,9 +476,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     if (sl == 0 && j < NV) s_fin[j] = acc;
   }
   __syncthreads();
-  float ms = -INFINITY;   // m*: the largest score of the exact support
-#pragma unroll
-  for (int w = 0; w < NW; ++w) ms = fmax_m3(ms, s_wm[w]);
+  const float ms = unord_f32(s_rng[3]);   // m*: the largest score of the exact support
   const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
   const float uf = rs ? s_uf : 0.f;
   if (n_split > 1) {

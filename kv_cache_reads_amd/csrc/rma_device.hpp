@@ -243,6 +243,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// base[i] as a wave-uniform 64-bit base plus a 32-bit unsigned byte offset: the
+// global loads' SGPR-base + VGPR-offset form, one 32-bit address operation per
+// load rather than a 64-bit add.  The caller guarantees i * sizeof(T) < 2^32.
+template <typename T>
+__device__ __forceinline__ const T* off32(const T* base, uint32_t i) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * (uint32_t)sizeof(T));
+}
+
 // ---------------------------------------------------------------- keys
 // Monotone map fp32 -> uint32 (a < b  =>  key(a) <= key(b); -0 < +0).
 __device__ __forceinline__ uint32_t ord_f32(float x) {

@@ -598,6 +598,18 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
   const int rows = (nE + kWave - 1) / kWave;
   const int RW = (rows + NW - 1) / NW;   // wave w's rows [r0, r1) for the ordered steps
   const int r0 = min(rows, wave * RW), r1 = min(rows, r0 + RW);
+  // the per-wave counts in w.wcnt: their sum over the lower waves and over all
+  // (the first NW lanes take one each and scan inside their 16-lane row)
+  auto wave_counts_prefix = [&](int& below, int& total) {
+    static_assert(NW <= 16, "the counts fit one 16-lane row");
+    int c = lane < NW ? w.wcnt[lane] : 0;
+    c += dpp_i<0x111>(c);   // row_shr:1
+    c += dpp_i<0x112>(c);   // row_shr:2
+    c += dpp_i<0x114>(c);   // row_shr:4
+    c += dpp_i<0x118>(c);   // row_shr:8
+    total = __builtin_amdgcn_readlane(c, NW - 1);
+    below = wave > 0 ? __builtin_amdgcn_readlane(c, wave - 1) : 0;
+  };
 
   const bool whole = K == L_mid;   // every mid token is selected (the chunks reported all)
   float th_lo = -INFINITY, th_hi = -INFINITY;
@@ -732,12 +744,7 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
     __syncthreads();
     nb = w.misc[4];
     int nin = 0, o = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int c = w.wcnt[v];
-      o += v < wave ? c : 0;
-      nin += c;
-    }
+    wave_counts_prefix(o, nin);
     kp = K - nin;
     if (nb > kSelBandMax || kp < 1 || nb < kp) return false;
     // ---- the list, first part: the entries above th_hi in position order
@@ -792,9 +799,8 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
     for (int r = r0; r < r1; ++r) cnt += (int)__popcll(__ballot(es[r * kWave + lane] > -INFINITY));
     if (lane == 0) w.wcnt[wave] = cnt;
     __syncthreads();
-    int o = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) o += v < wave ? w.wcnt[v] : 0;
+    int o = 0, tot = 0;
+    wave_counts_prefix(o, tot);
     for (int r = r0; r < r1; ++r) {
       const float x = es[r * kWave + lane];
       const bool a = x > -INFINITY;
@@ -816,9 +822,8 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
     __syncthreads();   // the counts above are read
     if (lane == 0) w.wcnt[wave] = cnt;
     __syncthreads();
-    int o = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) o += v < wave ? w.wcnt[v] : 0;
+    int o = 0, tot = 0;
+    wave_counts_prefix(o, tot);
     for (int r = r0; r < r1; ++r) {
       const float x = es[r * kWave + lane];
       const int e = ep[r * kWave + lane];
