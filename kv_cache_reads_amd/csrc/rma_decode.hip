@@ -84,6 +84,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ uint32_t s_rng[4];
   __shared__ float s_qf[D];
   __shared__ uint32_t s_hist[kSelBins];
+  __shared__ uint32_t s_coarse[kSelBins / 16];
   __shared__ float s_cand[kSelBandMax];
   __shared__ int s_bslot[kSelBandMax];
   __shared__ DD s_bdd[kSelBandMax];
@@ -208,7 +209,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     xv.load(off32(vunit, pos * D + part * CPL));
     xk.load(off32(kunit, pos * D + part * CPL));
   }
-  const BlockSelLds wl{s_hist, s_cand, s_bslot, s_bdd, s_misc, s_wcnt};
+  const BlockSelLds wl{s_hist, s_coarse, s_cand, s_bslot, s_bdd, s_misc, s_wcnt};
   init_block_select<NT>(wl);
   if (tid < 4) s_rng[tid] = tid == 0 ? 0xffffffffu : 0u;   // the identities of min / max
 
@@ -286,11 +287,10 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
           sv2[k] = *off32(en, cc * r_cap + min(j0 + my_s + k * tpc, r_cap - 1));
       }
     }
-    rlo = wave_min_dpp(rlo);
-    rhi = wave_max_dpp(rhi);
+    const uint32_t klo = ~wave_max_u32(~ord_f32(rlo)), khi = wave_max_u32(ord_f32(rhi));
     if (lane == 0) {
-      atomicMin(&s_rng[0], ord_f32(rlo));
-      atomicMax(&s_rng[1], ord_f32(rhi));
+      atomicMin(&s_rng[0], klo);
+      atomicMax(&s_rng[1], khi);
     }
   }
   if (rs) {
@@ -326,8 +326,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       rk.load(off32(kunit, ex_pos(j) * D + part * CPL));
       am = fmax_m3(am, ex_score(rk));
     }
-    am = wave_max_dpp(am);
-    if (lane == 0) atomicMax(&s_rng[2], ord_f32(am));
+    const uint32_t ka = wave_max_u32(ord_f32(am));
+    if (lane == 0) atomicMax(&s_rng[2], ka);
   }
   __syncthreads();
 
@@ -442,7 +442,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   //      the pair sums go through LDS and are added in pair order
   //      (deterministic); the largest score added, per wave
   {
-    const float wm = wave_max_dpp(mx);
+    const uint32_t km = wave_max_u32(ord_f32(mx));
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       N[c] += dpp_f<0x128>(N[c]);      // row_ror:8: the other group of the row
@@ -451,7 +451,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     Z += dpp_f<0x128>(Z);
     ZK += dpp_f<0x128>(ZK);
     __syncthreads();   // every gather has read the list: its LDS is free
-    if (lane == 0) atomicMax(&s_rng[3], ord_f32(wm));
+    if (lane == 0) atomicMax(&s_rng[3], km);
     if ((lane & 15) < LPE) {
       float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NV;
 #pragma unroll

@@ -177,25 +177,19 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // first quiet each operand (a NaN-canonicalising instruction apiece)
 __device__ __forceinline__ float fmin_m3(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -3.4028235e38f); }
 __device__ __forceinline__ float fmax_m3(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.4028235e38f); }
-// max within each row of 16 lanes, in every lane of the row
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmax_m3(v, dpp_f<0xB1>(v));
-  v = fmax_m3(v, dpp_f<0x4E>(v));
-  v = fmax_m3(v, dpp_f<0x141>(v));
-  v = fmax_m3(v, dpp_f<0x140>(v));
-  return v;
+// the wave's maximum of unsigned keys: butterflies inside each 16-lane row, then
+// row 0 into 1 and 2 into 3, then 1 into 2 and 3 (row broadcasts), read from
+// lane 63.  Every DPP source that is absent or masked reads 0, the identity of
+// the unsigned maximum, so each step is one v_max_u32 with the DPP modifier
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));    // quad xor 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));    // quad xor 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));   // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));   // row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
-// the wave's maximum: rows combined by row broadcasts (row 0 into 1, 2 into 3,
-// then 1 into 2 and 3), read from lane 63
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = row_max16(v);
-  const int b = __float_as_int(v);
-  v = fmax_m3(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x142, 0xA, 0xF, false)));
-  const int c = __float_as_int(v);
-  v = fmax_m3(v, __int_as_float(__builtin_amdgcn_update_dpp(c, c, 0x143, 0xC, 0xF, false)));
-  return readlane_f(v, kWave - 1);
-}
-__device__ __forceinline__ float wave_min_dpp(float v) { return -wave_max_dpp(-v); }
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v = lane_group_sum<16>(v);
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
@@ -261,6 +255,9 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(u);
 }
+// the wave's maximum / minimum of fp32 values through their ordered keys
+__device__ __forceinline__ float wave_max_dpp(float v) { return unord_f32(wave_max_u32(ord_f32(v))); }
+__device__ __forceinline__ float wave_min_dpp(float v) { return unord_f32(~wave_max_u32(~ord_f32(v))); }
 __device__ __forceinline__ uint64_t ord_f64(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);

@@ -569,6 +569,7 @@ struct HeadSelect {
 // caller puts a barrier before reading the list.
 struct BlockSelLds {
   uint32_t* hist;   // kSelBins
+  uint32_t* coarse; // kSelBins / 16: the sums of 16 consecutive bins
   float* cand;      // kSelBandMax: scores of the K-th bin's members
   int* bslot;       // kSelBandMax: band members' entries
   DD* bdd;          // kSelBandMax: their double-double scores
@@ -579,6 +580,7 @@ struct BlockSelLds {
 template <int NT>
 __device__ __forceinline__ void init_block_select(const BlockSelLds& w) {
   for (int b = threadIdx.x; b < kSelBins; b += NT) w.hist[b] = 0u;
+  for (int b = threadIdx.x; b < kSelBins / 16; b += NT) w.coarse[b] = 0u;
   if (threadIdx.x < 8) w.misc[threadIdx.x] = threadIdx.x == 1 ? (int)0xffffffffu : 0;
 }
 
@@ -620,23 +622,21 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
       const float t = __fmul_rn(__fsub_rn(x, lo), inv);
       return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(NBS - 1));  // clamped: monotone in x
     };
-    // ---- histogram over [lo, hi]
-    for (int i = tid; i < nE; i += NT) atomicAdd(&w.hist[ubin(es[i])], 1u);
+    // ---- histogram over [lo, hi], with the sums of 16 bins beside it
+    for (int i = tid; i < nE; i += NT) {
+      const int b = ubin(es[i]);
+      atomicAdd(&w.hist[b], 1u);
+      atomicAdd(&w.coarse[b >> 4], 1u);
+    }
     __syncthreads();
     // ---- every wave: the bin of the K-th largest.  Lane l owns the 16 bins
-    //      NBS-16(l+1) .. NBS-16l-1 (read as four 16-byte words); a scan of the
-    //      lanes' sums names the lane holding it, whose 16 bins the first 16
+    //      NBS-16(l+1) .. NBS-16l-1 (their sum is one coarse count); a scan of
+    //      the lanes' sums names the lane holding it, whose 16 bins the first 16
     //      lanes then take one each (descending) and scan again
     int bK = 0, above = 0;
     {
-      static_assert(BPL == 16, "the second scan covers one 16-lane row");
-      const uint4* h4 = reinterpret_cast<const uint4*>(w.hist + NBS - BPL * (lane + 1));
-      int ls = 0;
-#pragma unroll
-      for (int j = 0; j < BPL / 4; ++j) {
-        const uint4 v = h4[j];
-        ls += (int)(v.x + v.y + v.z + v.w);
-      }
+      static_assert(BPL == 16, "one coarse count per lane; the second scan covers one 16-lane row");
+      const int ls = (int)w.coarse[NBS / BPL - 1 - lane];
       const int incl = wave_incl_scan_dpp(ls);
       const int owner = __ffsll((long long)__ballot(incl >= K)) - 1;
       const int run0 = __builtin_amdgcn_readlane(incl - ls, owner);   // entries above its bins
@@ -669,11 +669,10 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
         xlo = m ? fmin_m3(xlo, x) : xlo;
         xhi = m ? fmax_m3(xhi, x) : xhi;
       }
-      xlo = wave_min_dpp(xlo);
-      xhi = wave_max_dpp(xhi);
-      if (lane == 0 && xlo <= xhi) {
-        atomicMin(reinterpret_cast<uint32_t*>(&w.misc[1]), ord_f32(xlo));
-        atomicMax(reinterpret_cast<uint32_t*>(&w.misc[2]), ord_f32(xhi));
+      const uint32_t klo = ~wave_max_u32(~ord_f32(xlo)), khi = wave_max_u32(ord_f32(xhi));
+      if (lane == 0 && klo <= khi) {
+        atomicMin(reinterpret_cast<uint32_t*>(&w.misc[1]), klo);
+        atomicMax(reinterpret_cast<uint32_t*>(&w.misc[2]), khi);
       }
     }
     __syncthreads();
