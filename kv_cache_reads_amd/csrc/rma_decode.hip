@@ -79,9 +79,10 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   static_assert(kSelMaxChunks == 4 * kWave, "four chunks per lane of wave 0");
   __shared__ int s_off[kSelMaxChunks], s_bcs[kSelMaxChunks], s_nrep[kSelMaxChunks];
   __shared__ int s_nE, s_trunc;
-  // ordered-integer keys (ord_f32) reduced by LDS atomics: the union's lowest and
-  // highest score, the exact rows' highest score, the largest score added
+  // ordered-integer keys (ord_f32) reduced by LDS atomics: [2] the exact rows'
+  // highest score, [3] the largest score added ([0], [1] unused)
   __shared__ uint32_t s_rng[4];
+  __shared__ int s_bin_lo, s_bin_hi;   // the union's scan-bin range: lowest cut, highest top
   __shared__ float s_qf[D];
   __shared__ uint32_t s_hist[kSelBins];
   __shared__ uint32_t s_coarse[kSelBins / 16];
@@ -214,11 +215,13 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   if (tid < 4) s_rng[tid] = tid == 0 ? 0xffffffffu : 0u;   // the identities of min / max
 
   // ---- 2. wave 0: each chunk's offset in the union (a wave scan of the counts
-  //      it reported, at most r_cap each), the chunk table, empty entries after
-  //      the union up to a whole row of 64.  Everyone: q for the band
-  //      rescoring, f = phi_q(q).
+  //      it reported, at most r_cap each), the chunk table, the scan-bin range
+  //      of the union (every report lies between its chunk's cut and top bins),
+  //      empty entries after the union up to a whole row of 64.  Everyone: q
+  //      for the band rescoring, f = phi_q(q).
   if (wave == 0) {
     int wc4[4], ls = 0;
+    uint32_t blo = 0u, bhi = 0u;   // max of ~cut (the lowest cut) and of top + 1
     bool tr = false;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -226,7 +229,13 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       wc4[k] = c < n_chunks ? min(mc[k].y, r_cap) : 0;
       tr |= c < n_chunks && mc[k].y > r_cap;   // the chunk withheld tokens
       ls += wc4[k];
+      if (c < n_chunks) {
+        blo = max(blo, ~(uint32_t)(mc[k].x & 0xffff));
+        bhi = max(bhi, (uint32_t)(mc[k].x >> 16) + 1u);
+      }
     }
+    blo = ~wave_max_u32(blo);
+    bhi = wave_max_u32(bhi);
     const int incl = wave_incl_scan_dpp(ls);
     int o = incl - ls;
 #pragma unroll
@@ -234,7 +243,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
       const int c = lane * 4 + k;
       if (c < n_chunks) {
         s_off[c] = o;
-        s_bcs[c] = mc[k].x;
+        s_bcs[c] = mc[k].x & 0xffff;
         s_nrep[c] = mc[k].y;
       }
       o += wc4[k];
@@ -249,6 +258,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     if (lane == 0) {
       s_nE = nE;
       s_trunc = trunc;
+      s_bin_lo = (int)blo;
+      s_bin_hi = (int)bhi;   // one past the highest top bin
     }
   }
   if (tid < D) s_qf[tid] = q_in;
@@ -263,10 +274,15 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   }
   __syncthreads();
 
-  // ---- 3. the reports into the union (chunk c's j-th at s_off[c] + j) and its
-  //      score range; phi(q)^T S per feature block and u^T f
+  // ---- 3. the reports into the union (chunk c's j-th at s_off[c] + j) and the
+  //      histogram of their selection bins (with 16-bin sums); phi(q)^T S per
+  //      feature block and u^T f
+  const HeadParams hp{hp_in[0], hp_in[1], hp_in[2]};
+  // the load's unused fourth word stays allocated until here, so no register of
+  // the load is reused (which would make the prologue wait for it)
+  asm volatile("" ::"s"(hp_in[3]));
+  const SelBins sbin = sel_bins(hp, s_bin_lo, s_bin_hi);
   {
-    float rlo = INFINITY, rhi = -INFINITY;
     if (my_c < n_chunks) {
       const int wc = min(m_mine.y, r_cap), o0 = s_off[my_c];
       for (int j0 = 0;;) {
@@ -276,8 +292,9 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
           if (j < wc) {
             es[o0 + j] = sv2[k].x;
             ep[o0 + j] = __float_as_int(sv2[k].y);
-            rlo = fmin_m3(rlo, sv2[k].x);
-            rhi = fmax_m3(rhi, sv2[k].x);
+            const int b = sbin(sv2[k].x);
+            atomicAdd(&s_hist[b], 1u);
+            atomicAdd(&s_coarse[b >> 4], 1u);
           }
         }
         j0 += SPEC * tpc;
@@ -286,11 +303,6 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
         for (int k = 0; k < SPEC; ++k)
           sv2[k] = *off32(en, cc * r_cap + min(j0 + my_s + k * tpc, r_cap - 1));
       }
-    }
-    const uint32_t klo = ~wave_max_u32(~ord_f32(rlo)), khi = wave_max_u32(ord_f32(rhi));
-    if (lane == 0) {
-      atomicMin(&s_rng[0], klo);
-      atomicMax(&s_rng[1], khi);
     }
   }
   if (rs) {
@@ -334,22 +346,19 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   // ---- 4. the selection, the whole block (the exact fallback when it fails):
   //      the K selected into the LDS list (and to idx / sel when asked).  The
   //      reference for the exponentials: no score of the exact support exceeds
-  //      the larger of the exact rows' maximum and the union's top score (the
-  //      top mid score, the fallback's scores aside, which may pass it by an ulp)
+  //      the larger of the exact rows' maximum and the upper edge of the union's
+  //      highest scan bin (the fallback's scores aside, which may pass it by an
+  //      ulp)
   float mref = -INFINITY;
   {
-    const HeadParams hp{hp_in[0], hp_in[1], hp_in[2]};
-    // the load's unused fourth word stays allocated until here, so no register
-    // of the load is reused (which would make the prologue wait for it)
-    asm volatile("" ::"s"(hp_in[3]));
-    const float lo = unord_f32(s_rng[0]), hi = unord_f32(s_rng[1]);
-    mref = fmax_m3(unord_f32(s_rng[2]), hi * inv_sqrt_d);
+    const float hi_edge = __fsub_rn(__fdiv_rn((float)s_bin_hi, hp.inv_w), hp.rg);
+    mref = fmax_m3(unord_f32(s_rng[2]), hi_edge * inv_sqrt_d);
     SelOut io;
     if (idx_out != nullptr && rsl == 0) {
       io.io = idx_out + (size_t)ug * K;
       io.so = sc_out + (size_t)ug * K;
     }
-    const bool ok = block_select<KT, D, NT>(es, ep, s_nE, lo, hi, s_bcs, s_nrep, n_chunks, ch, L_mid,
+    const bool ok = block_select<KT, D, NT>(es, ep, s_nE, sbin, s_bcs, s_nrep, n_chunks, ch, L_mid,
                                             n_sink, K, s_trunc != 0, hp, s_qf, kunit, inv_sqrt_d, wl,
                                             lpos, lsc, io);
     if (!ok) {   // uniform: a chunk withheld tokens or the band was too wide

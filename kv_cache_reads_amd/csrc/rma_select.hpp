@@ -302,7 +302,7 @@ struct HeadSelect {
     if (tid < n_chunks) {
       trunc = mm.y > r_cap;
       w_c = min(mm.y, r_cap);
-      s_bcs[tid] = mm.x;
+      s_bcs[tid] = mm.x & 0xffff;   // the cut bin (the chunk's top bin above it)
       s_nrep[tid] = mm.y;
     }
     int nE;
@@ -567,6 +567,21 @@ struct HeadSelect {
 // Returns false (the same on every thread) when the block must run the exact
 // fallback (a chunk withheld tokens, too few entries, band too wide).  The
 // caller puts a barrier before reading the list.
+// The block selection's bins: kSelBins linear bins over the scan-bin interval
+// [b_lo, b_hi) that holds every report, on the scan's bin coordinate
+// (x + rg) inv_w (the same two roundings as lin_bin), shifted and scaled;
+// monotone in x and clamped, so any score maps to a bin
+struct SelBins {
+  float rg, inv_w, b_lo, scale;
+  __device__ __forceinline__ int operator()(float x) const {
+    const float t = __fmul_rn(__fsub_rn(__fmul_rn(__fadd_rn(x, rg), inv_w), b_lo), scale);
+    return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(kSelBins - 1));
+  }
+};
+__device__ __forceinline__ SelBins sel_bins(const HeadParams& hp, int b_lo, int b_hi) {
+  return SelBins{hp.rg, hp.inv_w, (float)b_lo, __fdiv_rn((float)kSelBins, (float)max(b_hi - b_lo, 1))};
+}
+
 struct BlockSelLds {
   uint32_t* hist;   // kSelBins
   uint32_t* coarse; // kSelBins / 16: the sums of 16 consecutive bins
@@ -585,7 +600,7 @@ __device__ __forceinline__ void init_block_select(const BlockSelLds& w) {
 }
 
 template <typename KT, int D, int NT>
-__device__ bool block_select(const float* es, int* ep, int nE, float lo, float hi, const int* s_bcs,
+__device__ bool block_select(const float* es, int* ep, int nE, const SelBins& ubin, const int* s_bcs,
                              const int* s_nrep, int n_chunks, int ch, int L_mid, int n_sink, int K,
                              bool trunc, const HeadParams& hp, const float* qf, const KT* kunit,
                              float inv_sqrt_d, const BlockSelLds& w, int* lpos, float* lsc,
@@ -617,18 +632,8 @@ __device__ bool block_select(const float* es, int* ep, int nE, float lo, float h
   float th_lo = -INFINITY, th_hi = -INFINITY;
   int nb = 0, kp = 0;
   if (!whole) {
-    const float inv = hi > lo ? (float)NBS / (hi - lo) : 0.f;
-    auto ubin = [&](float x) {
-      const float t = __fmul_rn(__fsub_rn(x, lo), inv);
-      return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(NBS - 1));  // clamped: monotone in x
-    };
-    // ---- histogram over [lo, hi], with the sums of 16 bins beside it
-    for (int i = tid; i < nE; i += NT) {
-      const int b = ubin(es[i]);
-      atomicAdd(&w.hist[b], 1u);
-      atomicAdd(&w.coarse[b >> 4], 1u);
-    }
-    __syncthreads();
+    // (the caller built the histogram of the union's scores on these bins,
+    // with the sums of 16 bins beside it, while placing the reports)
     // ---- every wave: the bin of the K-th largest.  Lane l owns the 16 bins
     //      NBS-16(l+1) .. NBS-16l-1 (their sum is one coarse count); a scan of
     //      the lanes' sums names the lane holding it, whose 16 bins the first 16

@@ -9,7 +9,9 @@
 //         query heads (fp32 FMA on bf16/fp32 keys, d split over 4-8 lanes and
 //         summed with DPP).  Scores stay in LDS; a linear-bin histogram per head
 //         picks a per-chunk threshold so that at least r_min tokens pass, and
-//         the passing tokens (score, position) are written in position order.
+//         the passing tokens (score, position) are written in position order;
+//         the chunk's entry of the table: (cut bin | top non-empty bin << 16,
+//         tokens at or above the cut).
 //  select grid (units * G).  Gathers the chunk reports, radix-selects the K-th
 //         largest fp32 score t, proves that no chunk withheld a token within
 //         the error band, keeps every token above t + 2.5*eps, resolves the
@@ -180,14 +182,18 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
     run = __builtin_amdgcn_readlane(run, lstar);
     // lower the threshold to just above the highest non-empty bin below it: the
     // same tokens pass, and the select's completeness test is least strict
-    int hb = -1;
+    // (and the chunk's highest non-empty bin: its reports lie in [bcut, top])
+    int hb = -1, tb = -1;
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const int bin = lane * BPL + j;
-      if (bin < bc && hb_[j] != 0u) hb = bin;
+      if (hb_[j] != 0u) {
+        tb = bin;
+        if (bin < bc) hb = bin;
+      }
     }
-    hb = (int)wave_max_dpp((float)hb);
-    const int bcut = hb + 1;
+    const int bcut = (int)wave_max_u32((uint32_t)(hb + 1));
+    const int top = (int)wave_max_u32((uint32_t)(tb + 1)) - 1;
     float2* dst = ent + ((size_t)(u * G + g) * n_chunks + c) * r_cap;
     const HeadParams hg = s_hp[g];
     constexpr int RB = 8;   // rows of 64 scores per batch: loads first, then ballots, then stores
@@ -210,7 +216,7 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       }
     }
     if (lane == 0) {
-      meta[(size_t)(u * G + g) * n_chunks + c] = make_int2(bcut, run);
+      meta[(size_t)(u * G + g) * n_chunks + c] = make_int2(bcut | (top << 16), run);
       if (c == 0) hpw[u * G + g] = make_float4(hg.rg, hg.inv_w, hg.eps, 0.f);
     }
   }
