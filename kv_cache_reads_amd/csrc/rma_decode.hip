@@ -61,19 +61,23 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   // groups x 4 entries already keep 512 entries in flight)
   constexpr int B0 = sizeof(KT) == 4 ? 2 : sizeof(PT) == 4 ? (D == 128 ? 2 : 4) : D == 128 ? 4 : 8;
   constexpr int B = NT == 1024 ? (B0 > 1 ? B0 / 2 : 1) : B0;
-  constexpr int NV = 2 * D + 2;     // combined values: N[D], sum w v [D], Z, sum w
+  constexpr int NV = 2 * D;         // combined vectors: N[D], sum w v [D] (Z, sum w apart)
   constexpr int NP = NT / 16;       // group pairs (two groups per 16-lane row)
+  // row stride of the pair sums: = 8 (mod 64 banks), so the 8 x 8 lanes of a
+  // wave that read pair pp0 + sl, value j0 + jj hit 64 different banks
+  constexpr int NVS = NV + 8;
   // dynamic LDS: the union of the chunk reports (scores, positions; room for
-  // n_chunks r_cap entries rounded up to whole rows of 64),
-  // then the list of the K selected (positions, scaled scores); after the
-  // gathers the combine reuses it from the start
+  // n_chunks r_cap entries rounded up to whole rows of 64), at least as large as
+  // the combine's pair sums, which reuse it once the list is complete; then the
+  // list of the K selected (positions, scaled scores)
   extern __shared__ __align__(16) float dyn[];
   constexpr int UB = kWave;   // the union is padded to whole rows of 64 entries
   const int PS = (n_chunks * r_cap + UB - 1) / UB * UB;
+  const int UR = max(2 * PS, NP * NVS);
   float* es = dyn;
   int* ep = reinterpret_cast<int*>(dyn + PS);
-  int* lpos = reinterpret_cast<int*>(dyn + 2 * PS);
-  float* lsc = dyn + 2 * PS + K;
+  int* lpos = reinterpret_cast<int*>(dyn + UR);
+  float* lsc = dyn + UR + K;
   float* red = dyn;
 
   static_assert(kSelMaxChunks == 4 * kWave, "four chunks per lane of wave 0");
@@ -86,13 +90,14 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ float s_qf[D];
   __shared__ uint32_t s_hist[kSelBins];
   __shared__ uint32_t s_coarse[kSelBins / 16];
-  __shared__ float s_cand[kSelBandMax];
+  __shared__ __align__(16) float s_cand[kSelBandMax];
   __shared__ int s_bslot[kSelBandMax];
   __shared__ DD s_bdd[kSelBandMax];
   __shared__ int s_misc[8];
   __shared__ int s_buf[kSelThreads / kWave + 1];
   __shared__ int s_wcnt[NW];
-  __shared__ float s_fin[NV];
+  __shared__ float s_fin[NV + 2];   // the sums: N, sum w v, Z, sum w
+  __shared__ float s_zw[NW][2];     // per wave: Z, sum w
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
   __shared__ float s_f[M];          // f = phi_q(q) of this head
@@ -448,8 +453,10 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   }
 
   // ---- 6. combine: the two groups of a 16-lane row add (row rotation by 8);
-  //      the pair sums go through LDS and are added in pair order
-  //      (deterministic); the largest score added, per wave
+  //      the pair sums go to the union's LDS (no longer read once the list is
+  //      complete, so no wait for the other waves) and are added in pair order
+  //      (deterministic); Z and sum w per wave (its four rows in order); the
+  //      largest score added, per wave
   {
     const uint32_t km = wave_max_u32(ord_f32(mx));
 #pragma unroll
@@ -459,18 +466,21 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     }
     Z += dpp_f<0x128>(Z);
     ZK += dpp_f<0x128>(ZK);
-    __syncthreads();   // every gather has read the list: its LDS is free
-    if (lane == 0) atomicMax(&s_rng[3], km);
+    // read out of lanes 0, 16, 32, 48 by the whole wave (inside a lane-0 branch
+    // the compiler could leave the row additions above to lane 0 alone)
+    const float zw = (readlane_f(Z, 0) + readlane_f(Z, 16)) + (readlane_f(Z, 32) + readlane_f(Z, 48));
+    const float zkw = (readlane_f(ZK, 0) + readlane_f(ZK, 16)) + (readlane_f(ZK, 32) + readlane_f(ZK, 48));
+    if (lane == 0) {
+      atomicMax(&s_rng[3], km);
+      s_zw[wave][0] = zw;
+      s_zw[wave][1] = zkw;
+    }
     if ((lane & 15) < LPE) {
-      float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NV;
+      float* rp = red + (size_t)(wave * 4 + (lane >> 4)) * NVS;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         rp[part * CPL + c] = N[c];
         rp[D + part * CPL + c] = NK[c];
-      }
-      if (part == 0) {
-        rp[2 * D] = Z;
-        rp[2 * D + 1] = ZK;
       }
     }
   }
@@ -479,14 +489,22 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
     const int j = j0 + tid / 8, sl = tid % 8;
     float acc = 0.f;
     if (j < NV) {
-      for (int pp = sl; pp < NP; pp += 8) acc += red[(size_t)pp * NV + j];
+      for (int pp = sl; pp < NP; pp += 8) acc += red[(size_t)pp * NVS + j];
     }
     acc = lane_group_sum<8>(acc);
     if (sl == 0 && j < NV) s_fin[j] = acc;
   }
+  if (wave == NW - 1) {   // Z and sum w over the waves: lanes 0.. and 16.. in a fixed butterfly
+    static_assert(NW <= 16, "one wave's sums per lane of a 16-lane row");
+    const int wv = lane & 15, which = lane >> 4;
+    float z = (which < 2 && wv < NW) ? s_zw[wv][which] : 0.f;
+    z = lane_group_sum<16>(z);
+    if (lane == 0) s_fin[NV] = z;
+    if (lane == 16) s_fin[NV + 1] = z;
+  }
   __syncthreads();
   const float ms = unord_f32(s_rng[3]);   // m*: the largest score of the exact support
-  const float ZE = s_fin[2 * D], ZKt = s_fin[2 * D + 1];
+  const float ZE = s_fin[NV], ZKt = s_fin[NV + 1];
   const float uf = rs ? s_uf : 0.f;
   if (n_split > 1) {
     // this slice's partial in merge_kernel's layout (m, Z_E, sum w, u^T f, N_E,

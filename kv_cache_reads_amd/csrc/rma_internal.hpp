@@ -119,9 +119,9 @@ inline bool fused_slots_fit(int n_chunks, int nt) { return n_chunks >= 1 && n_ch
 // selected list, or (reusing it) the combine's group-pair sums
 inline size_t fused_dyn_bytes(int n_chunks, int r_cap, int K, int d, int nt) {
   const size_t ub = 64;   // the union padded to whole rows of 64 entries
-  const size_t a = 2 * (((size_t)n_chunks * r_cap + ub - 1) / ub * ub) + 2 * (size_t)K;
-  const size_t b = (size_t)(nt / 16) * (2 * d + 2);
-  return (a > b ? a : b) * 4 + 16;
+  const size_t a = 2 * (((size_t)n_chunks * r_cap + ub - 1) / ub * ub);
+  const size_t b = (size_t)(nt / 16) * (2 * d + 8);   // the combine's pair sums reuse the union
+  return ((a > b ? a : b) + 2 * (size_t)K) * 4 + 16;
 }
 // static LDS of the fused kernel instantiation a plan would launch
 size_t fused_static_lds(int kv_dtype, int phi_dtype, int d, int m, int nt);

@@ -585,7 +585,7 @@ __device__ __forceinline__ SelBins sel_bins(const HeadParams& hp, int b_lo, int 
 struct BlockSelLds {
   uint32_t* hist;   // kSelBins
   uint32_t* coarse; // kSelBins / 16: the sums of 16 consecutive bins
-  float* cand;      // kSelBandMax: scores of the K-th bin's members
+  float* cand;      // kSelBandMax: scores of the K-th bin's members (16-byte aligned)
   int* bslot;       // kSelBandMax: band members' entries
   DD* bdd;          // kSelBandMax: their double-double scores
   int* misc;        // 8: [0] members, [1] / [2] ordered min / max member, [3] count above, [4] band, [5] t
@@ -686,14 +686,19 @@ __device__ bool block_select(const float* es, int* ep, int nE, const SelBins& ub
     if (nm <= kSelBandMax) {
       // t = the rK-th largest member (every member holding that value agrees)
       float t = -INFINITY;
-      if (nm <= kWave) {     // every wave ranks them
+      if (nm <= kWave) {     // every wave ranks them (four members per 16-byte read)
         if (lane < nm) {
           const float x = w.cand[lane];
           int gt = 0, ge = 0;
-          for (int k2 = 0; k2 < nm; ++k2) {
-            const float y = w.cand[k2];
-            gt += y > x;
-            ge += y >= x;
+          for (int k4 = 0; k4 < nm; k4 += 4) {
+            const float4 y4 = *reinterpret_cast<const float4*>(w.cand + k4);
+            const float y[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool in = k4 + i < nm;
+              gt += in && y[i] > x;
+              ge += in && y[i] >= x;
+            }
           }
           if (gt < rK && rK <= ge) t = x;
         }
