@@ -5,28 +5,36 @@
 // subtraction; §4.3 Eq. 10 for the single normalisation; App. C.1 for the
 // clamp of the residual denominator).
 //
-// rma_decode runs the scan of rma_decode_topk, then this kernel, grid U * G.
-// A block first issues every load it needs before the selection's result: its
-// head's chunk reports and chunk table, the query, the feature map's operands
-// (or the given features), S and u, and one exactly scored row per 8-lane
-// group.  Then, in order (each step behind one barrier):
-//   1. wave 0: each chunk's offset in the union (a wave scan of the counts);
-//      everyone: f = phi_q(q) into LDS;
-//   2. the reports into the union (compacted, position order) and its score
-//      range; phi(q)^T S per feature block and u^T f; the exactly scored rows'
-//      scores and their maximum;
+// rma_decode runs the scan of rma_decode_topk, then this kernel, grid (G, U,
+// slices).  A block first issues every load it needs before the selection's
+// result: its head's chunk reports and chunk table, the query, the feature
+// map's operands (or the given features), S and u, and one exactly scored row
+// per 8-lane group.  Then, in order (each step behind one barrier):
+//   1. wave 0: each chunk's offset in the union (a wave scan of the counts)
+//      and the union's scan-bin range (lowest cut, highest top bin of the
+//      chunk table); everyone: f = phi_q(q) into LDS;
+//   2. the reports into the union (compacted, position order), each counted
+//      in the selection histogram as it is placed; phi(q)^T S per feature
+//      block and u^T f; the exactly scored rows' scores and their maximum;
 //   3. the selection (block_select in rma_select.hpp, the exact fallback if it
 //      fails): the K positions and their scaled fp32 scores into an LDS list
 //      (and, when asked, to idx / sel in ascending order);
 //   4. the retrieved tokens from that list: their V and phi_k rows are
 //      gathered with every load of a batch issued before the first is used;
 //      e^{s - mref} v, w = f.phi_k and w v accumulate per 8-lane group, where
-//      mref, the larger of the exact rows' maximum and the union's top score,
-//      bounds every score of the exact support (no running-max rescale); the
-//      exact rows' terms are added while the first batch loads;
+//      mref, the larger of the exact rows' maximum and the upper edge of the
+//      union's highest scan bin, bounds every score of the exact support (no
+//      running-max rescale); the exact rows' terms are added while the first
+//      batch loads;
 //   5. the combine: the two groups of a 16-lane row added by DPP, the pair sums
-//      added in pair order through LDS (deterministic), m* = the largest score
-//      added; then the subtraction, the clamp and one normalisation.
+//      written into the union's LDS (free once the list is complete) and added
+//      in pair order, Z and sum w per wave in row order (deterministic), m* =
+//      the largest score added; then the subtraction, the clamp and one
+//      normalisation.
+// Every wave executes most of these steps, four waves to a SIMD: the vector
+// instructions per wave, not memory, bound a block, so work each wave would
+// repeat for itself is kept out of the waves (LDS atomics on order-preserving
+// keys, DPP scans, 16-lane row scans in place of per-wave loops).
 // The arithmetic of a term is the merge kernel's; the order of the sums
 // differs (the fused kernel spreads a head's entries over more groups).
 #include "rma_select.hpp"
