@@ -15,9 +15,13 @@ OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["rma_api.hip", "rma_build.hip", "rma_topk.hip", "rma_merge.hip", "rma_decode.hip",
            "rma_full.hip", "rma_phi_mlp.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# packed fp32 ops stay disabled: ordinary float code is compiled to unpacked VALU ops
+# packed fp32 ops stay disabled: ordinary float code is compiled to unpacked VALU ops.
+# The first kernel arguments are preloaded into SGPRs at wave launch (gfx950's
+# kernarg preload; the code keeps a fallback that loads them when the launch
+# does not), so a kernel's first loads need not wait for the argument segment.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
