@@ -109,6 +109,7 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   __shared__ float s_part[NT / D][D];
   __shared__ float s_uf;
   __shared__ float s_f[M];          // f = phi_q(q) of this head
+  __shared__ uint32_t s_fhl[2][M / 2];   // f as packed bf16 hi / lo pairs (bf16 phi rows)
 
   // block (head g of unit u, slice rsl) of the (G, units, n_split) grid: every
   // slice's block selects, slice rsl gathers the list entries [rsl sl, (rsl + 1)
@@ -295,6 +296,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   // the load is reused (which would make the prologue wait for it)
   asm volatile("" ::"s"(hp_in[3]));
   const SelBins sbin = sel_bins(hp, s_bin_lo, s_bin_hi);
+  if (sizeof(PT) == 2 && sub && tid < M / 2)   // f as bf16 hi / lo pairs for the gather
+    split_f_bf16x2(s_f[2 * tid], s_f[2 * tid + 1], s_fhl[0][tid], s_fhl[1][tid]);
   {
     if (my_c < n_chunks) {
       const int wc = min(m_mine.y, r_cap), o0 = s_off[my_c];
@@ -404,9 +407,19 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   const int j_lo = min(K, rsl * sl), j_hi = min(K, j_lo + sl);
 
   // ---- 5. retrieved entries from the list
-  float fr[FPL];
+  constexpr bool DOT2 = sizeof(PT) == 2;   // bf16 phi rows: w on the bf16 dot instruction
+  float fr[DOT2 ? 1 : FPL];
+  uint32_t fh[FPL / 2], fl[FPL / 2];
+  if constexpr (DOT2) {
 #pragma unroll
-  for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
+    for (int j = 0; j < FPL / 2; ++j) {
+      fh[j] = sub ? s_fhl[0][part * (FPL / 2) + j] : 0u;
+      fl[j] = sub ? s_fhl[1][part * (FPL / 2) + j] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
+  }
   for (int jb = j_lo + grp; jb < j_hi; jb += NGR * B) {
     RawPiece<KT, CPL> vr[B];
     RawPiece<PT, FPL> pr[B];
@@ -431,11 +444,16 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
     for (int e = 0; e < B; ++e) {
       if (jb + e * NGR < j_hi) {  // uniform within the group; a wave skips its empty slots
-        float ph[FPL], vv[CPL];
-        pr[e].unpack(ph);
+        float vv[CPL];
         float w = 0.f;
+        if constexpr (DOT2) {
+          w = dot_phi_bf16<FPL>(pr[e], fh, fl);
+        } else {
+          float ph[FPL];
+          pr[e].unpack(ph);
 #pragma unroll
-        for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+          for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+        }
         w = lane_group_sum<LPE>(w);
         vr[e].unpack(vv);
         add_exp(scs[e], vv);

@@ -405,6 +405,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// ---- w = f . phi over bf16 phi rows on the bf16 dot instruction.  f (fp32) is
+// split into two packed bf16 pairs, hi = f rounded to bf16 and lo = the
+// remainder rounded to bf16, so hi + lo = f within 2^-17 |f|; each product of
+// bf16 values is exact, and v_dot2_f32_bf16 adds two of them to the fp32 sum.
+// Per feature pair one instruction for hi and one for lo, where unpacking the
+// row and multiplying in fp32 takes four.
+__device__ __forceinline__ void split_f_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+template <int N>
+__device__ __forceinline__ float dot_phi_bf16(const RawPiece<uint16_t, N>& p, const uint32_t (&fh)[N / 2],
+                                              const uint32_t (&fl)[N / 2]) {
+  float w = 0.f;
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    const uint32_t x[4] = {p.w[i].x, p.w[i].y, p.w[i].z, p.w[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2_t v = __builtin_bit_cast(bf16x2_t, x[k]);
+      w = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2_t, fh[4 * i + k]), w, false);
+      w = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2_t, fl[4 * i + k]), w, false);
+    }
+  }
+  return w;
+}
+
 // ---- the phi projection on the MFMA, shared by the summary builder and the
 // decode recompute of retrieved phi_k rows (same operands, same instruction
 // order, so both produce the same bits)

@@ -206,6 +206,16 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
+  // bf16 phi rows: w on the bf16 dot instruction, f as packed bf16 hi / lo pairs
+  // (the fused decode kernel splits the same values the same way)
+  constexpr bool DOT2 = sizeof(PT) == 2 && !RECOMP;
+  uint32_t fh[FPL / 2], fl[FPL / 2];
+#pragma unroll
+  for (int j = 0; j < FPL / 2; ++j) {
+    fh[j] = 0u;
+    fl[j] = 0u;
+    if (DOT2 && sub) split_f_bf16x2(fr[2 * j], fr[2 * j + 1], fh[j], fl[j]);
+  }
   if constexpr (RECOMP) {
     if (sub) rfq = s_f[(wave % NFT) * 16 + (lane & 15)];
   }
@@ -306,14 +316,19 @@ merge_kernel(const float* __restrict__ q, const float* __restrict__ phi_q,
         for (int e = 0; e < B; ++e) {
           // both dots on every lane (zeros where unused), so the 8-lane sums
           // never run under divergent control flow
-          float kv[CPL], ph[FPL], vv[CPL];
+          float kv[CPL], vv[CPL];
           kr[e].unpack(kv);
-          pr[e].unpack(ph);
           float a = 0.f, w = 0.f;
 #pragma unroll
           for (int i = 0; i < CPL; ++i) a = __fmaf_rn(qr[i], kv[i], a);
+          if constexpr (DOT2) {
+            w = dot_phi_bf16<FPL>(pr[e], fh, fl);
+          } else {
+            float ph[FPL];
+            pr[e].unpack(ph);
 #pragma unroll
-          for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+            for (int i = 0; i < FPL; ++i) w = __fmaf_rn(fr[i], ph[i], w);
+          }
           a = lane_group_sum<LPE>(a);
           w = lane_group_sum<LPE>(w);
           if constexpr (RECOMP) w = (!EX && sub) ? s_w[jcs[e]] : 0.f;
