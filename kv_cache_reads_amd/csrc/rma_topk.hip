@@ -165,21 +165,21 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
     const int suf = total - incl + ls;  // tokens in this lane's bins and above
     const unsigned long long ball = __ballot(suf >= target);
     const int lstar = 63 - __clzll((long long)ball);
-    // in lane lstar: the highest bin from which the bins at and above it hold
-    // >= target tokens (the other lanes compute the same walk and discard it)
-    int bc = lane * BPL, run = suf - ls;
-    {
-      bool found = false;
-#pragma unroll
-      for (int j = BPL - 1; j >= 0; --j) {
-        if (!found) {
-          run += (int)hb_[j];
-          if (run >= target) { bc = lane * BPL + j; found = true; }
-        }
-      }
-    }
-    bc = __builtin_amdgcn_readlane(bc, lstar);
-    run = __builtin_amdgcn_readlane(run, lstar);
+    // the highest bin from which the bins at and above it hold >= target
+    // tokens: lane lstar's BPL bins, one per lane of the first BPL (descending),
+    // scanned inside the first 16-lane row on top of the tokens above them
+    static_assert(BPL <= 16, "lane lstar's bins fit one 16-lane row");
+    const int above = __builtin_amdgcn_readlane(suf - ls, lstar);
+    const int bt = lstar * BPL + BPL - 1;   // lane lstar's top bin
+    const int cl = lane < BPL ? (int)hist[g * NB + bt - lane] : 0;
+    int cum = cl;
+    cum += dpp_i<0x111>(cum);   // row_shr:1
+    cum += dpp_i<0x112>(cum);   // row_shr:2
+    cum += dpp_i<0x114>(cum);   // row_shr:4
+    cum += dpp_i<0x118>(cum);   // row_shr:8
+    const int jf = __ffsll((long long)__ballot(lane < BPL && above + cum >= target)) - 1;
+    const int bc = bt - jf;
+    const int run = __builtin_amdgcn_readlane(above + cum, jf);
     // lower the threshold to just above the highest non-empty bin below it: the
     // same tokens pass, and the select's completeness test is least strict
     // (and the chunk's highest non-empty bin: its reports lie in [bcut, top])
@@ -211,7 +211,9 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
         const bool pass = i < n && lin_bin(x[k], hg) >= bcut;
         const uint64_t bm = __ballot(pass);
         const int pos = base + lanes_below(bm);
-        if (pass && pos < r_cap) dst[pos] = make_float2(x[k], __int_as_float(t0 + i));
+        if (pass && pos < r_cap)   // a 32-bit byte offset from the uniform base (one address operation)
+          *reinterpret_cast<float2*>(reinterpret_cast<char*>(dst) + (uint32_t)pos * 8u) =
+              make_float2(x[k], __int_as_float(t0 + i));
         base += (int)__popcll(bm);
       }
     }
