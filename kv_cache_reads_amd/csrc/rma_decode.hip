@@ -47,17 +47,19 @@ namespace rma {
 
 template <typename KT, typename PT, int D, int M, int NT>
 __global__ void __launch_bounds__(NT)
-decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ kb,
-                    const KT* __restrict__ vb, int64_t ustride, int L, int n_sink, int n_tail,
-                    int n_gen, int L_mid, int ch, int n_chunks, int r_cap, int K,
-                    const float4* __restrict__ hpw, const float2* __restrict__ ent,
-                    const int2* __restrict__ meta, int32_t* __restrict__ idx_out,
-                    float* __restrict__ sc_out, const float* __restrict__ phi_q,
-                    const float* __restrict__ Wq, const float* __restrict__ bq, int P,
+decode_fused_kernel(const float4* __restrict__ hpw, const int2* __restrict__ meta,
+                    const float2* __restrict__ ent, const float* __restrict__ q,
+                    const float* __restrict__ Wq, int G, int n_chunks, int r_cap, int P,
+                    const KT* __restrict__ kb, const KT* __restrict__ vb, int64_t ustride, int L,
+                    int n_sink, int n_tail, int n_gen, int L_mid, int ch, int K,
+                    int32_t* __restrict__ idx_out, float* __restrict__ sc_out,
+                    const float* __restrict__ phi_q, const float* __restrict__ bq,
                     const PT* __restrict__ phik, const float* __restrict__ S,
                     const float* __restrict__ u_, uint32_t flags, float* __restrict__ y,
                     float* __restrict__ stats, float inv_sqrt_d, int n_split,
                     float* __restrict__ sparts) {
+  // (the first 14 argument words, hpw .. P, arrive preloaded in registers: the
+  // loads of the reports, the chunk table, q and W below need no other argument)
   constexpr int NW = NT / kWave;
   constexpr int LPE = 8;            // lanes per entry
   constexpr int NGR = NT / LPE;     // entry groups
@@ -121,27 +123,11 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   // the head's binning parameters: a uniform load issued first, while no
   // statement with side effects precedes it (so it goes through the scalar cache)
   const f32x4 hp_in = *reinterpret_cast<const f32x4*>(hpw + ug);
-  // every kernel argument into registers at once: one round trip for all of
-  // them rather than one per branch that first needs some
-  asm volatile("" ::"s"(q), "s"(G), "s"(kb), "s"(vb), "s"(ustride), "s"(L), "s"(n_sink), "s"(n_tail),
-               "s"(n_gen), "s"(L_mid), "s"(ch), "s"(n_chunks), "s"(r_cap), "s"(K), "s"(hpw), "s"(ent),
-               "s"(meta), "s"(idx_out), "s"(sc_out), "s"(phi_q), "s"(Wq), "s"(bq), "s"(P), "s"(phik),
-               "s"(S), "s"(u_), "s"(flags), "s"(y), "s"(stats), "s"(inv_sqrt_d));
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int part = lane & (LPE - 1), grp = tid / LPE;
-  const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
-  // the subtraction runs only when part of the mid-region stays unretrieved
-  const bool sub = (flags == RMA_MERGE_SUB) && K > 0 && K < L_mid;
-  const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
-  const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
-  const bool rs = resid && !whole_mid;   // phi(q)^T S and u^T f are needed
-
-  const KT* kunit = kb + (size_t)u * ustride;
-  const KT* vunit = vb + (size_t)u * ustride;
   const float* qg = q + (size_t)ug * D;
   const int2* mt = meta + (size_t)ug * n_chunks;
   const float2* en = ent + (size_t)ug * n_chunks * r_cap;
-  const PT* phiu = phik + (size_t)u * L_mid * M;   // this unit's phi_k rows
 
   // ---- 1. loads.  The selection's: the chunk table and the report slots (a
   //      power-of-two group of tpc threads per chunk; thread t serves chunk
@@ -166,7 +152,6 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   // the merge's: f's operands (or the given features), q, S, u
   constexpr int TPF = NT / M, EPT = D / TPF;     // threads per feature, elements each
   const int fi = tid / TPF, fpart = tid % TPF;
-  const bool fcomp = resid && Wq != nullptr;
   float qr[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; i += 4) {
@@ -176,8 +161,8 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
   float wq[EPT], xq[EPT], fb0;
   {
     const int pset = P > 1 ? u % P : 0;
-    const float* wb = fcomp ? Wq + (size_t)pset * M * D : qg;   // W of this unit's set
-    const uint32_t wo = fcomp ? fi * D + fpart * EPT : 0u;
+    const float* wb = Wq != nullptr ? Wq + (size_t)pset * M * D : qg;   // W of this unit's set
+    const uint32_t wo = Wq != nullptr ? fi * D + fpart * EPT : 0u;
     const uint32_t qo = fpart * EPT;
 #pragma unroll
     for (int i = 0; i < EPT; i += 4) {
@@ -192,6 +177,27 @@ decode_fused_kernel(const float* __restrict__ q, int G, const KT* __restrict__ k
 #pragma unroll
       for (int i = 0; i < EPT; ++i) xq[i] = qr[i];
     }
+  }
+  // every other kernel argument into registers at once (one round trip, now
+  // that the first loads are in flight) rather than one per branch that needs some
+  asm volatile("" ::"s"(q), "s"(G), "s"(kb), "s"(vb), "s"(ustride), "s"(L), "s"(n_sink), "s"(n_tail),
+               "s"(n_gen), "s"(L_mid), "s"(ch), "s"(n_chunks), "s"(r_cap), "s"(K), "s"(hpw), "s"(ent),
+               "s"(meta), "s"(idx_out), "s"(sc_out), "s"(phi_q), "s"(Wq), "s"(bq), "s"(P), "s"(phik),
+               "s"(S), "s"(u_), "s"(flags), "s"(y), "s"(stats), "s"(inv_sqrt_d));
+  const int n_a = n_sink + n_tail, n_ex = n_a + n_gen;
+  // the subtraction runs only when part of the mid-region stays unretrieved
+  const bool sub = (flags == RMA_MERGE_SUB) && K > 0 && K < L_mid;
+  const bool resid = flags != RMA_MERGE_NO_RESIDUAL;
+  const bool whole_mid = (flags == RMA_MERGE_SUB) && K == L_mid;
+  const bool rs = resid && !whole_mid;   // phi(q)^T S and u^T f are needed
+
+  const KT* kunit = kb + (size_t)u * ustride;
+  const KT* vunit = vb + (size_t)u * ustride;
+  const PT* phiu = phik + (size_t)u * L_mid * M;   // this unit's phi_k rows
+
+  const bool fcomp = resid && Wq != nullptr;
+  {
+    const int pset = P > 1 ? u % P : 0;
     fb0 = fcomp ? *off32(bq + (size_t)pset * M, fi)
                 : (resid && phi_q != nullptr ? *off32(phi_q + (size_t)ug * M, tid % M) : 0.f);
   }
@@ -605,11 +611,11 @@ hipError_t launch_fused_nt(const DecodePlan& pl, const float* q, int G, const rm
   float* parts = reinterpret_cast<float*>(ws + pl.off_fpart);
   const int heads = (int)(kv.n_units * G);
   hipError_t e = launch_kernel(
-      "decode_fused_kernel", kern, dim3(G, kv.n_units, ns), dim3(NT), (uint32_t)lds, st, q, G,
+      "decode_fused_kernel", kern, dim3(G, kv.n_units, ns), dim3(NT), (uint32_t)lds, st,
+      reinterpret_cast<const float4*>(ws + tp.off_hp), reinterpret_cast<const int2*>(ws + tp.off_meta),
+      reinterpret_cast<const float2*>(ws + tp.off_ent), q, Wq, G, tp.n_chunks, tp.r_cap, P,
       static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
-      sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, tp.n_chunks, tp.r_cap, K,
-      reinterpret_cast<const float4*>(ws + tp.off_hp), reinterpret_cast<const float2*>(ws + tp.off_ent),
-      reinterpret_cast<const int2*>(ws + tp.off_meta), idx, sel, phi_q, Wq, bq, P,
+      sp.n_tail, (int)sp.n_gen, L_mid, tp.ch, K, idx, sel, phi_q, bq,
       static_cast<const PT*>(phi_k), S, u, flags, y, stats, 1.0f / sqrtf((float)D), ns, parts);
   if (e != hipSuccess || ns == 1) return e;
   return launch_merge_combine(parts, ns, heads, D, flags, K, L_mid, y, stats, st);
