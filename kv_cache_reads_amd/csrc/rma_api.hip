@@ -299,7 +299,8 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
   // from four rounds on (with three the second kernel costs about what the
   // split saves).  At most 16 slices, one block per CU in all, none empty.
   const int64_t per_round = (int64_t)(p.fused_threads / 8) *
-                            (kv.dtype == RMA_BF16 ? (kv.d == 64 ? 4 : 2) : 1);
+                            fused_gather_batch(kv.dtype == RMA_BF16 ? 2 : 4, phi_dtype == RMA_BF16 ? 2 : 4,
+                                               kv.d, p.fused_threads);
   const int64_t rounds = K > 0 ? ceil_div(K, per_round) : 0;
   const int64_t split_cap = heads <= 128 ? std::min<int64_t>(rounds, 16) : 1;
   p.fused_split = 1;

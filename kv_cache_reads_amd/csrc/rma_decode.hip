@@ -66,11 +66,10 @@ decode_fused_kernel(const float4* __restrict__ hpw, const int2* __restrict__ met
   constexpr int CPL = D / LPE;      // value columns per lane
   constexpr int FPL = M / LPE;      // phi features per lane
   constexpr int SPEC = kFusedSpec<NT>;     // report slots per thread
-  // retrieved entries per group whose row loads are in flight together: as in
-  // the merge kernel, halved in 1024-thread blocks (128 VGPRs per lane; 128
-  // groups x 4 entries already keep 512 entries in flight)
-  constexpr int B0 = sizeof(KT) == 4 ? 2 : sizeof(PT) == 4 ? (D == 128 ? 2 : 4) : D == 128 ? 4 : 8;
-  constexpr int B = NT == 1024 ? (B0 > 1 ? B0 / 2 : 1) : B0;
+  // retrieved entries per group whose row loads are in flight together (the
+  // merge kernel's batch, fewer in 1024-thread blocks, whose lanes have 128
+  // registers: 128 groups x 4 rows at d = 64, x 3 at d = 128 with bf16 rows)
+  constexpr int B = fused_gather_batch((int)sizeof(KT), (int)sizeof(PT), D, NT);
   constexpr int NV = 2 * D;         // combined vectors: N[D], sum w v [D] (Z, sum w apart)
   constexpr int NP = NT / 16;       // group pairs (two groups per 16-lane row)
   // row stride of the pair sums: = 8 (mod 64 banks), so the 8 x 8 lanes of a

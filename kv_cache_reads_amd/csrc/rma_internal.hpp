@@ -114,6 +114,15 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
 // report slots each thread of the fused kernel loads per round (a chunk's slots
 // are spread over the 2^(log2 NT - ceil(log2 n_chunks)) threads it gets)
 template <int NT> constexpr int kFusedSpec = 8;
+// Retrieved entries each 8-lane group of the fused kernel gathers per round
+// (every load of a round in flight together): as many as its registers allow
+// (128 per lane in 1024-thread blocks) without spilling
+constexpr int fused_gather_batch(int kt_bytes, int pt_bytes, int d, int nt) {
+  const int b0 = kt_bytes == 4 ? 2 : pt_bytes == 4 ? (d == 128 ? 2 : 4) : d == 128 ? 4 : 8;
+  if (nt != 1024) return b0;
+  if (kt_bytes == 2 && pt_bytes == 2 && d == 128) return 3;
+  return b0 > 1 ? b0 / 2 : 1;
+}
 inline bool fused_slots_fit(int n_chunks, int nt) { return n_chunks >= 1 && n_chunks <= nt; }
 // dynamic LDS of the fused kernel: the union of the chunk reports and the
 // selected list, or (reusing it) the combine's group-pair sums
