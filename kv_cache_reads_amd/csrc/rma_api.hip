@@ -294,15 +294,15 @@ DecodePlan plan_decode(const rma_kv& kv, const rma_span& sp, int G, int K, int m
   p.fused = fused;
   // With few heads and a large budget the fused kernel's gather, one block per
   // head, is bound by the loads one CU keeps in flight: then each head's list
-  // is split over several blocks (each selects, gathers a slice of about one
-  // round and writes a partial) and merge_combine_kernel combines the slices:
-  // from four rounds on (with three the second kernel costs about what the
-  // split saves).  At most 16 slices, one block per CU in all, none empty.
+  // is split over several blocks (each selects, gathers a slice and writes a
+  // partial) and merge_combine_kernel combines the slices: from four rounds on
+  // (with three the second kernel costs about what the split saves), over as
+  // many blocks as there are CUs, at most 16 slices per head, none empty.
   const int64_t per_round = (int64_t)(p.fused_threads / 8) *
                             fused_gather_batch(kv.dtype == RMA_BF16 ? 2 : 4, phi_dtype == RMA_BF16 ? 2 : 4,
                                                kv.d, p.fused_threads);
   const int64_t rounds = K > 0 ? ceil_div(K, per_round) : 0;
-  const int64_t split_cap = heads <= 128 ? std::min<int64_t>(rounds, 16) : 1;
+  const int64_t split_cap = heads <= 128 ? 16 : 1;
   p.fused_split = 1;
   if (fused && p.fused_threads == 1024 && rounds >= 4) {
     const int64_t ns = std::max<int64_t>(1, std::min<int64_t>(split_cap, (int64_t)device_cus() / heads));
