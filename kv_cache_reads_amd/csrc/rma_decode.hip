@@ -425,13 +425,17 @@ decode_fused_kernel(const float4* __restrict__ hpw, const int2* __restrict__ met
 #pragma unroll
     for (int i = 0; i < FPL; ++i) fr[i] = sub ? s_f[part * FPL + i] : 0.f;
   }
-  for (int jb = j_lo + grp; jb < j_hi; jb += NGR * B) {
+  // the first ng groups gather, entry jb + e ng in slot e, so that every slot
+  // but a few of the last round holds an entry (an empty slot would still
+  // issue its loads: the batch's load count is fixed)
+  const int ng = min(NGR, (j_hi - j_lo + B - 1) / B);
+  for (int jb = j_lo + grp; grp < ng && jb < j_hi; jb += ng * B) {
     RawPiece<KT, CPL> vr[B];
     RawPiece<PT, FPL> pr[B];
     float scs[B];
 #pragma unroll
     for (int e = 0; e < B; ++e) {
-      const int jj = jb + e * NGR;
+      const int jj = jb + e * ng;
       const int jc = jj < j_hi ? jj : jb;
       const int pos = min(max(lpos[jc], n_sink), n_sink + max(L_mid, 1) - 1);
       scs[e] = lsc[jc];
@@ -448,7 +452,7 @@ decode_fused_kernel(const float4* __restrict__ hpw, const int2* __restrict__ met
     }
 #pragma unroll
     for (int e = 0; e < B; ++e) {
-      if (jb + e * NGR < j_hi) {  // uniform within the group; a wave skips its empty slots
+      if (jb + e * ng < j_hi) {  // uniform within the group; a wave skips its empty slots
         float vv[CPL];
         float w = 0.f;
         if constexpr (DOT2) {
