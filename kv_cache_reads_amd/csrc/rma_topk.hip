@@ -47,9 +47,13 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   constexpr int PIECES = E / EPP;    // 16-byte loads per lane per token
   constexpr int UNR = (sizeof(KT) == 2) ? 4 : 2;
   constexpr int CHMAX = (kScanScoreSlots / G) / TPP * TPP;
+  // score rows of the G heads 8 words apart modulo the 32 banks: one store
+  // instruction writes a token group's scores of every head without conflicts
+  constexpr int SCS = CHMAX + 8;
   constexpr int NB = kScanBins;
+  constexpr int GJ = (G + LPT - 1) / LPT;   // heads whose score a lane stores
 
-  __shared__ float sc[G * CHMAX];
+  __shared__ float sc[G * SCS];
   __shared__ uint32_t hist[G * NB];
   __shared__ float4 s_q[G * D / 4];
   __shared__ HeadParams s_hp[G];
@@ -111,6 +115,15 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 #pragma unroll
   for (int g = 0; g < G; ++g)
     if (tid == g) s_hp[g] = hp[g];
+  // lane `part` of a token's lane group stores heads part, part + LPT, ...
+  HeadParams hm[GJ];
+#pragma unroll
+  for (int j = 0; j < GJ; ++j) {
+    hm[j] = hp[j * LPT];
+#pragma unroll
+    for (int g = j * LPT + 1; g < G && g < (j + 1) * LPT; ++g)
+      if (part == g - j * LPT) hm[j] = hp[g];
+  }
 
   auto score = [&](const uint4 (&raw)[UNR][PIECES], int p0) {
 #pragma unroll
@@ -119,15 +132,24 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
       float kv[E];
 #pragma unroll
       for (int pc = 0; pc < PIECES; ++pc) unpack_piece(raw[i][pc], (const KT*)nullptr, kv + pc * EPP);
+      float a[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float a = 0.f;
+        a[g] = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) a = __fmaf_rn(qr[g][e], kv[e], a);
-        a = lane_group_sum<LPT>(a);
-        if (t < n && (g % LPT) == part) {
-          sc[g * CHMAX + t] = a;
-          atomicAdd(&hist[g * NB + lin_bin(a, hp[g])], 1u);
+        for (int e = 0; e < E; ++e) a[g] = __fmaf_rn(qr[g][e], kv[e], a[g]);
+        a[g] = lane_group_sum<LPT>(a[g]);   // the same bits in every lane of the group
+      }
+      // one score store and one histogram count per lane and owned head
+#pragma unroll
+      for (int j = 0; j < GJ; ++j) {
+        float mine = a[j * LPT];
+#pragma unroll
+        for (int g = j * LPT + 1; g < G && g < (j + 1) * LPT; ++g) mine = part == g - j * LPT ? a[g] : mine;
+        const int gg = j * LPT + part;
+        if (t < n && gg < G) {
+          sc[gg * SCS + t] = mine;
+          atomicAdd(&hist[gg * NB + lin_bin(mine, hm[j])], 1u);
         }
       }
     }
@@ -203,7 +225,7 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
         const int i = r0 + k * kWave + lane;
-        x[k] = sc[g * CHMAX + min(i, n - 1)];
+        x[k] = sc[g * SCS + min(i, n - 1)];
       }
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
