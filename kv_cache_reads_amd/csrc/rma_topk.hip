@@ -146,6 +146,9 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
         float mine = a[j * LPT];
 #pragma unroll
         for (int g = j * LPT + 1; g < G && g < (j + 1) * LPT; ++g) mine = part == g - j * LPT ? a[g] : mine;
+        // materialised before the branch: the sums' last DPP steps then fold
+        // into single v_add_f32_dpp instructions instead of a move and an add
+        asm volatile("" : "+v"(mine));
         const int gg = j * LPT + part;
         if (t < n && gg < G) {
           sc[gg * SCS + t] = mine;
