@@ -188,7 +188,7 @@ TopkPlan plan_topk(const rma_kv& kv, const rma_span& sp, int G, int K) {
   const int64_t Lm = l_mid(sp);
   const int64_t U = kv.n_units;
   const int tile = scan_tile(kv.d);  // tokens per scan block pass
-  const int64_t ch_max = std::max<int64_t>(tile, (kScanScoreSlots / G) / tile * tile);
+  const int64_t ch_max = std::max<int64_t>(tile, scan_chmax(kv.d, G));
   if (Lm > 0) {
     int64_t lo = ceil_div(Lm, ch_max);
     int64_t hi = std::min<int64_t>(kSelMaxChunks, ceil_div(Lm, tile));

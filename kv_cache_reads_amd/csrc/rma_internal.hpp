@@ -70,7 +70,12 @@ constexpr int kScanThreads = 256;
 constexpr int scan_tile(int d) { return (kScanThreads / 64) * (64 / (d / 16)); }
 constexpr int kScanBlocks = 512;        // scan blocks aimed for when the units are few
 constexpr int kScanBins = 512;          // linear score bins per head in the scan
-constexpr int kScanScoreSlots = 8192;   // fp32 LDS score slots per scan block (G * ch <= this)
+constexpr int kScanLdsBudget = 54272;   // LDS bytes per scan block: three fit the 160 KB of a CU
+// tokens per scan chunk that fit the budget: G rows of fp32 scores (8 words of
+// padding each) beside the G histograms and the G queries, whole block passes
+constexpr int scan_chmax(int d, int G) {
+  return ((kScanLdsBudget - G * (kScanBins * 4 + d * 4) - 64) / (4 * G) - 8) / scan_tile(d) * scan_tile(d);
+}
 constexpr int kSelMaxChunks = 256;
 constexpr int kSelBandMax = 512;        // band members resolved in LDS
 constexpr int kSelMaxEntries = 16384;   // union entries held in LDS by a select block

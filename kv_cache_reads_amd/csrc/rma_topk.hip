@@ -46,7 +46,7 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   constexpr int EPP = RowPieces<KT>::kElemsPerPiece;
   constexpr int PIECES = E / EPP;    // 16-byte loads per lane per token
   constexpr int UNR = (sizeof(KT) == 2) ? 4 : 2;
-  constexpr int CHMAX = (kScanScoreSlots / G) / TPP * TPP;
+  constexpr int CHMAX = scan_chmax(D, G);
   // score rows of the G heads 8 words apart modulo the 32 banks: one store
   // instruction writes a token group's scores of every head without conflicts
   constexpr int SCS = CHMAX + 8;

@@ -431,7 +431,9 @@ def _select_layout(L, ns, nt, U, G, K, d=64):
     per thread of that group the wide-union path runs instead."""
     Lm = L - ns - nt
     tile = 64 if d == 64 else 32
-    ch_max = max(tile, (8192 // G) // tile * tile)
+    # tokens per chunk whose fp32 scores fit the scan block's LDS budget (54272
+    # bytes: G score rows of ch + 8 words beside G 512-bin histograms and queries)
+    ch_max = max(tile, ((54272 - G * (512 * 4 + d * 4) - 64) // (4 * G) - 8) // tile * tile)
     lo, hi = -(-Lm // ch_max), min(256, -(-Lm // tile))
     nc = max(lo, min(-(-512 // U), hi))
     ch = -(-(-(-Lm // nc)) // tile) * tile
