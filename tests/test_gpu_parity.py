@@ -442,7 +442,7 @@ def _select_layout(L, ns, nt, U, G, K, d=64):
         r_cap = ch
     else:
         mu = K / chunks
-        rmin = max(16, (math.ceil(mu + 5 * math.sqrt(mu) + 8) + 7) // 8 * 8)
+        rmin = max(16, (math.ceil(mu + 4 * math.sqrt(mu) + 4) + 7) // 8 * 8)
         r_cap = min(ch, 2 * min(ch, rmin) + 32)
     tpc = 1024 >> ((chunks - 1).bit_length() if chunks > 1 else 0)
     return chunks, r_cap, r_cap <= 8 * tpc
