@@ -40,8 +40,11 @@ __device__ __forceinline__ HeadParams head_params(float n2, float kappa) {
   HeadParams h;
   h.rg = fmaxf(__fmul_rn(qn, kap), 1e-30f);
   h.inv_w = __fdiv_rn((float)kScanBins, __fmul_rn(2.f, h.rg));
-  // gamma_19 < 1.14e-6; 5e-6 leaves room for the roundings of |q| and kappa
-  h.eps = __fmul_rn(5e-6f, __fmul_rn(qn, kap));
+  // the fp32 dot's error is at most gamma_19 sum|q_j k_j| <= gamma_19 |q| kappa,
+  // gamma_19 < 1.134e-6; |q| here is within 7e-7 of the exact norm (a fp32 sum
+  // of squares and a rounded root), kappa is an upper bound and the products
+  // below add two roundings, so 2e-6 covers the bound with 75% to spare
+  h.eps = __fmul_rn(2e-6f, __fmul_rn(qn, kap));
   return h;
 }
 

@@ -140,12 +140,12 @@ def hip_decode_one_call(inp, pre, K, step, flags=R.RMA_MERGE_SUB, ws=None, fused
 
 def check_scan_error(sel, s_ref, q, kf, d, what):
     """The selection's certificate assumes every fp32 score of the scan lies within
-    eps = 5e-6 |q| kappa of the exact q.k (kappa >= the largest key norm); the
+    eps = 2e-6 |q| kappa of the exact q.k (kappa >= the largest key norm); the
     kept scores are those scan scores times fp32(1/sqrt(d)), which adds at most
     two roundings (3e-7 relative)."""
     qn = float(np.linalg.norm(q.double().numpy()))
     kap = float(np.linalg.norm(kf, axis=1).max())
     raw = np.abs(s_ref) * math.sqrt(d)
-    bound = (5e-6 * qn * kap + 3e-7 * raw) / math.sqrt(d)
+    bound = (2e-6 * qn * kap + 3e-7 * raw) / math.sqrt(d)
     err = np.abs(sel.astype(np.float64) - s_ref)
     assert np.all(err <= bound), f"{what}: scan score error {float((err / bound).max()):.2f}x the eps bound"
