@@ -240,3 +240,49 @@ def test_static_topk_refuses_oversized_calls_before_any_hip_call():
     assert r == R.RMA_ERR_WORKSPACE
     assert b"static" in L.rma_last_error()
     assert L.rma_decode_topk_static(0x2000, 4, ctypes.byref(kv), ctypes.byref(sp), 0x3000, 0, 0, 0, None) == R.RMA_OK
+
+
+def _topk_plan_bytes(L, ns, nt, U, G, K, d):
+    """The Top-K workspace by the planner's rule, written out: chunks of whole
+    scan-block passes, as many as give ~512 blocks but no longer than the fp32
+    scores a scan block keeps in its LDS budget (54272 bytes: G score rows of
+    ch + 8 words beside G 512-bin histograms and the G queries), and per chunk
+    room for 2 r_min + 32 reports, r_min = mu + 4 sqrt(mu) + 4 rounded up to 8
+    (at least 16), mu = K / chunks."""
+    import math
+
+    Lm = L - ns - nt
+    tile = 64 if d == 64 else 32
+    ch_max = max(tile, ((54272 - G * (512 * 4 + d * 4) - 64) // (4 * G) - 8) // tile * tile)
+    lo, hi = -(-Lm // ch_max), min(256, -(-Lm // tile))
+    nc = max(lo, min(-(-512 // U), hi))
+    ch = -(-(-(-Lm // nc)) // tile) * tile
+    chunks = -(-Lm // ch)
+    if K >= Lm:
+        r_cap = ch
+    else:
+        mu = K / chunks
+        rmin = max(16, (math.ceil(mu + 4 * math.sqrt(mu) + 4) + 7) // 8 * 8)
+        r_cap = min(ch, 2 * min(ch, rmin) + 32)
+    up = lambda x: -(-x // 256) * 256
+    return up(U * G * chunks * r_cap * 8) + up(U * G * chunks * 8) + up(U * G * 16), chunks, ch
+
+
+@pytest.mark.parametrize("shape", [
+    (1024, 4, 32, 1, 2, 10, 64),          # the tiny workload: 16 chunks
+    (32768, 4, 64, 8, 4, 328, 64),        # 32K layer: 64 chunks of 512
+    (65536, 4, 64, 8, 3, 2621, 128),      # 64K layer, 4 % budget
+    (16384, 4, 64, 2048, 4, 163, 64),     # many units: chunks bounded by the LDS score store (2752)
+    (131072, 4, 64, 896, 3, 1310, 128),   # 128K, d = 128: 35 chunks (at most 3840 tokens)
+    (40000, 4, 64, 300, 8, 400, 64),      # eight heads per unit
+])
+def test_topk_workspace_follows_the_chunk_and_report_rule(shape):
+    L_, ns, nt, U, G, K, d = shape
+    kv = _kv(d=d, U=U, T=L_)
+    got = R.lib().rma_workspace_bytes(R.RMA_OP_DECODE_TOPK, ctypes.byref(kv), ctypes.byref(_sp(L_, ns, nt)), G, K, 0)
+    want, chunks, ch = _topk_plan_bytes(L_, ns, nt, U, G, K, d)
+    assert got == want, (got, want, chunks, ch)
+    if U == 2048:
+        assert (chunks, ch) == (6, 2752)
+    if U == 896:
+        assert (chunks, ch) == (35, 3744)   # under the 3840-token bound
