@@ -383,16 +383,20 @@ def kernel_stats(recs):
     return {k: tot[k] / cnt[k] for k in tot}, {k: cnt[k] / len(recs) for k in cnt}
 
 
-def ceilings(torch, log, mb=2048):
-    """Measured streaming ceilings on this GPU with torch's own kernels: a read
-    that writes almost nothing (the sum of an fp32 array) and a copy (one read,
-    one write), over arrays well above the 256 MB last-level cache."""
+def ceilings(torch, log, R, mb=2048):
+    """Measured streaming ceilings on this GPU, over arrays well above the 256 MB
+    last-level cache: the library's streaming read (rma_stream_read: 1024
+    workgroups, each a contiguous piece, the scan's load form), and torch's own
+    kernels, a read that writes almost nothing (the sum of an fp32 array) and a
+    copy (one read, one write)."""
     n = int(mb * 1e6) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     out = torch.empty((), dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
     res = {}
-    for name, fn, nbytes in (("read", lambda: torch.sum(a, dim=0, out=out), 4 * n),
+    for name, fn, nbytes in (("stream_read", lambda: R.rma_stream_read(a, 1024, sink), 4 * n),
+                             ("read", lambda: torch.sum(a, dim=0, out=out), 4 * n),
                              ("copy", lambda: b.copy_(a), 8 * n)):
         for _ in range(3):
             fn()
@@ -406,10 +410,46 @@ def ceilings(torch, log, mb=2048):
         torch.cuda.synchronize()
         res[name] = round(nbytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9, 1)
     del a, b
-    log(f"[bench] streaming ceilings over {4 * n / 1e9:.2f} GB arrays: read {res['read']} GB/s, "
-        f"copy {res['copy']} GB/s (read + write)")
-    return {"read_GBps": res["read"], "copy_GBps": res["copy"], "array_GB": round(4 * n / 1e9, 2),
-            "kernels": "torch.sum (read), Tensor.copy_ (read + write)"}
+    log(f"[bench] streaming ceilings over {4 * n / 1e9:.2f} GB arrays: library streaming read "
+        f"{res['stream_read']} GB/s, torch read {res['read']} GB/s, copy {res['copy']} GB/s (read + write)")
+    return {"stream_read_GBps": res["stream_read"], "read_GBps": res["read"], "copy_GBps": res["copy"],
+            "array_GB": round(4 * n / 1e9, 2),
+            "kernels": "rma_stream_read with 1024 workgroups (stream_read), torch.sum (read), "
+                       "Tensor.copy_ (read + write)"}
+
+
+def scan_blocks(cfg):
+    """The Top-K scan's grid (chunks per unit x units) by the library's planning
+    rule: chunks of whole 256-thread block passes (64 tokens at d = 64, 32 at
+    d = 128), about 512 blocks when the units are few (at most 256 chunks per
+    unit), none longer than the fp32 scores a scan block keeps in its 54272
+    bytes of LDS (G rows of ch + 8 words beside G 512-bin histograms and the
+    queries)."""
+    Lm, U, G, d = cfg.L_mid, cfg.U, cfg.G, cfg.d
+    tile = 64 if d == 64 else 32
+    ch_max = max(tile, ((54272 - G * (512 * 4 + d * 4) - 64) // (4 * G) - 8) // tile * tile)
+    lo, hi = -(-Lm // ch_max), min(256, -(-Lm // tile))
+    nc = max(lo, min(-(-512 // U), hi))
+    ch = -(-(-(-Lm // nc)) // tile) * tile
+    return -(-Lm // ch) * U
+
+
+def same_shape_read(R, torch, runners, n_copies, blocks, reps):
+    """The library's streaming read over each rotating copy's key cache with the
+    scan's grid, timed by dispatch-stamped event pairs: what reading the scan's
+    bytes with the scan's grid costs when nothing else is done.  Returns (bytes
+    per launch, average microseconds)."""
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    evs = []
+    for i in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        R.rma_trace_arm(e)
+        R.rma_stream_read(runners[i % n_copies].k, blocks, sink)
+        evs.append(e)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs[1:]) / (len(evs) - 1) * 1e3
+    k = runners[0].k
+    return k.numel() * k.element_size(), us
 
 
 def cpu_baseline(cfg, inp, K, seconds, mlp_mode=False):
@@ -507,7 +547,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: neg over {n * 4} bytes read + {n * 4} bytes written, 3 launches")
         del a, b
-    ceil = None if args.no_ceiling else ceilings(torch, log)
+    ceil = None if args.no_ceiling else ceilings(torch, log, R)
     t0 = time.time()
     inp = Wl.generate(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -626,11 +666,19 @@ def main():
         per_kernel[k] = {"algorithmic_bytes_per_launch": kb.get(k, 0), "avg_launch_us": round(dk_avg[k] * 1e3, 3),
                          "launches_per_step": round(dk_n[k], 3),
                          "achieved": round(a_k, 1), "frac": round(a_k / PEAK_HBM_GBS, 4), "traffic": t_k}
+    ss_bytes, ss_us = same_shape_read(R, torch, runners, n_copies, scan_blocks(cfg), max(6, min(n_t, 60)))
+    ss_gbs = ss_bytes / (ss_us / 1e6) / 1e9
+    log(f"[bench] streaming read of the keys with the scan's grid ({scan_blocks(cfg)} blocks): "
+        f"{ss_us:.2f} us, {ss_gbs:.1f} GB/s")
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(dk_avg[dom] * 1e3, 3),
             "traffic_source": None if traffic is None else f"profiles/traffic_{cfg.name}.md",
             "dominant_by": "algorithmic bytes per decode step",
+            "same_shape_read": {"kernel": "rma_stream_read over the key cache with the scan's grid",
+                                "blocks": scan_blocks(cfg), "bytes": ss_bytes, "us": round(ss_us, 3),
+                                "GBps": round(ss_gbs, 1), "frac": round(ss_gbs / PEAK_HBM_GBS, 4),
+                                "scan_over_read": round(achieved / ss_gbs, 4) if dom == "topk_scan_kernel" else None},
             "decode_kernels": per_kernel,
             "decode_step": {"algorithmic_MB": round(dec_bytes / 1e6, 3), "us": round(ms_per_step * 1e3, 2),
                             "GBps": round(dec_gbs, 1), "frac": round(dec_gbs / PEAK_HBM_GBS, 4)}}

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RMA_ABI_VERSION 8
+#define RMA_ABI_VERSION 9
 
 /* Most events one kernel trace can hold (rma_trace_arm). */
 #define RMA_TRACE_MAX_EVENTS 16
@@ -394,6 +394,21 @@ int32_t rma_trace_count(void);
 
 /* Name of the j-th timed kernel of that call (0-based), or NULL. */
 const char* rma_trace_name(int32_t j);
+
+/* Streaming-read ceiling, for benchmarks only (not part of the method): reads
+ * the device range [p, p + bytes) once with `blocks` workgroups of 256 threads,
+ * block b taking the b-th of `blocks` contiguous pieces, with the load form of
+ * the Top-K scan (nontemporal 16-byte loads, two batches of eight per thread in
+ * flight), and writes to sink[b] the XOR of the 32-bit words of block b's
+ * piece (the XOR of all `blocks` words is that of the whole range).  Its time
+ * is what the device allows for reading those bytes with that grid: the
+ * reference the scan's own rate is compared with.  p (device, 16-byte aligned,
+ * `bytes` a positive multiple of 16) and sink (device, `blocks` uint32,
+ * overwritten) belong to the caller.  Enqueues one kernel on `stream` (a trace
+ * armed by rma_trace_arm times it); never synchronizes.
+ * Errors: RMA_ERR_INVALID_ARG (NULL pointer, misalignment, bytes not a
+ * positive multiple of 16, blocks outside 1..2^20); RMA_ERR_HIP. */
+rma_status rma_stream_read(const void* p, int64_t bytes, int32_t blocks, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librma.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["rma_api.hip", "rma_build.hip", "rma_topk.hip", "rma_merge.hip", "rma_decode.hip",
-           "rma_full.hip", "rma_phi_mlp.hip"]
+           "rma_full.hip", "rma_phi_mlp.hip", "rma_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 ops stay disabled: ordinary float code is compiled to unpacked VALU ops.
 # The first kernel arguments are preloaded into SGPRs at wave launch (gfx950's

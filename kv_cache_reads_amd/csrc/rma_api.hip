@@ -373,6 +373,18 @@ const char* rma_trace_name(int32_t j) {
   return (j >= 0 && j < t.count) ? t.name[j] : nullptr;
 }
 
+rma_status rma_stream_read(const void* p, int64_t bytes, int32_t blocks, uint32_t* sink, void* stream) {
+  g_last_error[0] = 0;
+  RMA_CHECK(p != nullptr && sink != nullptr, RMA_ERR_INVALID_ARG, "NULL pointer argument");
+  RMA_CHECK(aligned16(p), RMA_ERR_INVALID_ARG, "p must be 16-byte aligned");
+  RMA_CHECK(bytes > 0 && bytes % 16 == 0, RMA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  RMA_CHECK(blocks >= 1 && blocks <= (1 << 20), RMA_ERR_INVALID_ARG, "blocks %d outside 1..2^20", blocks);
+  TraceScope ts((hipStream_t)stream);
+  const hipError_t e = launch_stream_read(p, bytes, blocks, sink, (hipStream_t)stream);
+  RMA_CHECK(e == hipSuccess, RMA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return RMA_OK;
+}
+
 size_t rma_workspace_bytes(int32_t op, const rma_kv* kv, const rma_span* sp, int32_t G, int32_t K,
                            int32_t m) {
   if (kv == nullptr || sp == nullptr || kv->n_units < 1 || (kv->d != 64 && kv->d != 128))

@@ -200,6 +200,8 @@ hipError_t launch_phi(const void* x, int x_dtype, int n_units, int64_t rows, int
                       int d, const float* W, const float* b, int m, int P, void* phi,
                       int phi_dtype, hipStream_t st);
 
+hipError_t launch_stream_read(const void* p, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st);
+
 hipError_t launch_build(const BuildPlan& pl, const rma_kv& kv, const rma_span& sp, int m0, int len,
                         bool acc, const float* W, const float* b, int m, int P, void* phi_k,
                         int phi_dtype, float* S, float* u, float* kappa, uint8_t* ws,

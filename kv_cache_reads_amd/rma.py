@@ -103,6 +103,8 @@ def lib():
     L.rma_trace_count.restype = _I32
     L.rma_trace_name.argtypes = [_I32]
     L.rma_trace_name.restype = ctypes.c_char_p
+    L.rma_stream_read.argtypes = [_VP, _I64, _I32, _VP, _VP]
+    L.rma_stream_read.restype = _I32
     for f in ("rma_phi_features", "rma_phi_mlp_features", "rma_build_summaries", "rma_build_summaries_range", "rma_decode_topk",
               "rma_decode_topk_static", "rma_decode_merge", "rma_decode", "rma_decode_full"):
         getattr(L, f).restype = _I32
@@ -422,6 +424,17 @@ def rma_trace_arm(events) -> None:
         handles.append(e.cuda_event)
     arr = (_VP * max(len(handles), 1))(*handles)
     _check(L.rma_trace_arm(arr, len(handles)))
+
+
+def rma_stream_read(x: torch.Tensor, blocks: int, sink: torch.Tensor) -> None:
+    """Streaming-read ceiling (benchmark instrumentation): reads the bytes of the
+    contiguous device tensor `x` once with `blocks` workgroups, each a contiguous
+    piece; block b writes the XOR of its piece's 32-bit words to sink[b]
+    (`sink`: a contiguous device int32 tensor of at least `blocks` words)."""
+    if not (x.is_cuda and x.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+            and sink.is_contiguous() and sink.numel() >= int(blocks)):
+        raise ValueError("x must be a contiguous device tensor and sink a device int32 tensor of >= blocks words")
+    _check(lib().rma_stream_read(_p(x), x.numel() * x.element_size(), int(blocks), _p(sink), _stream()))
 
 
 def rma_trace_kernels():

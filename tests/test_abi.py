@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rma_abi_version() == 8
+    assert L.rma_abi_version() == 9
     assert L.rma_status_string(-3) == b"RMA_ERR_WORKSPACE"
     assert L.rma_status_string(7) == b"RMA_ERR_UNKNOWN"
 
@@ -286,3 +286,15 @@ def test_topk_workspace_follows_the_chunk_and_report_rule(shape):
         assert (chunks, ch) == (6, 2752)
     if U == 896:
         assert (chunks, ch) == (35, 3744)   # under the 3840-token bound
+
+
+def test_stream_read_validation():
+    L = R.lib()
+    sink = 0x9000
+    assert L.rma_stream_read(None, 1024, 4, sink, None) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_stream_read(0x10000, 1024, 4, None, None) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_stream_read(0x10008, 1024, 4, sink, None) == R.RMA_ERR_INVALID_ARG    # misaligned
+    assert L.rma_stream_read(0x10000, 1000, 4, sink, None) == R.RMA_ERR_INVALID_ARG    # not 16-byte multiple
+    assert L.rma_stream_read(0x10000, 0, 4, sink, None) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_stream_read(0x10000, 1024, 0, sink, None) == R.RMA_ERR_INVALID_ARG
+    assert L.rma_stream_read(0x10000, 1024, (1 << 20) + 1, sink, None) == R.RMA_ERR_INVALID_ARG
