@@ -5,7 +5,7 @@
 // subtraction; §4.3 Eq. 10 for the single normalisation; App. C.1 for the
 // clamp of the residual denominator).
 //
-// rma_decode runs the scan of rma_decode_topk, then this kernel, grid (G, U,
+// rma_decode runs the scan of rma_decode_topk, then this kernel, grid (U, G,
 // slices).  A block first issues every load it needs before the selection's
 // result: its head's chunk reports and chunk table, the query, the feature
 // map's operands (or the given features), S and u, and one exactly scored row
@@ -112,13 +112,15 @@ decode_fused_kernel(const float4* __restrict__ hpw, const int2* __restrict__ met
   __shared__ float s_f[M];          // f = phi_q(q) of this head
   __shared__ uint32_t s_fhl[2][M / 2];   // f as packed bf16 hi / lo pairs (bf16 phi rows)
 
-  // block (head g of unit u, slice rsl) of the (G, units, n_split) grid: every
+  // block (unit u, head g, slice rsl) of the (units, G, n_split) grid: every
   // slice's block selects, slice rsl gathers the list entries [rsl sl, (rsl + 1)
   // sl) (slice 0 also the exact rows) and writes a partial that
-  // merge_combine_kernel combines.  The grid's shape gives u and rsl without a
-  // division (the workgroups still start in head-major order, slice by slice)
-  const int rsl = blockIdx.z, u = blockIdx.y;
-  const int ug = u * G + blockIdx.x, tid = threadIdx.x;
+  // merge_combine_kernel combines.  The grid's shape gives u, g and rsl without
+  // a division.  Consecutive workgroups take consecutive units and go to the 8
+  // XCDs in turn, so when the unit count is a multiple of 8 a unit's heads run on
+  // one XCD and share its L2 copy of S, u and the feature map's weights.
+  const int rsl = blockIdx.z, u = blockIdx.x;
+  const int ug = u * G + blockIdx.y, tid = threadIdx.x;
   // the head's binning parameters: a uniform load issued first, while no
   // statement with side effects precedes it (so it goes through the scalar cache)
   const f32x4 hp_in = *reinterpret_cast<const f32x4*>(hpw + ug);
@@ -614,7 +616,7 @@ hipError_t launch_fused_nt(const DecodePlan& pl, const float* q, int G, const rm
   float* parts = reinterpret_cast<float*>(ws + pl.off_fpart);
   const int heads = (int)(kv.n_units * G);
   hipError_t e = launch_kernel(
-      "decode_fused_kernel", kern, dim3(G, kv.n_units, ns), dim3(NT), (uint32_t)lds, st,
+      "decode_fused_kernel", kern, dim3(kv.n_units, G, ns), dim3(NT), (uint32_t)lds, st,
       reinterpret_cast<const float4*>(ws + tp.off_hp), reinterpret_cast<const int2*>(ws + tp.off_meta),
       reinterpret_cast<const float2*>(ws + tp.off_ent), q, Wq, G, tp.n_chunks, tp.r_cap, P,
       static_cast<const KT*>(kv.k), static_cast<const KT*>(kv.v), kv.unit_stride, (int)sp.L, sp.n_sink,
