@@ -5,7 +5,7 @@
 // Ranking is by the exact real value of q.k_i, ties to the lower position.
 //
 // Two kernels:
-//  scan   grid (chunks, units).  Streams each unit's K_mid rows once for all G
+//  scan   grid (units, chunks).  Streams each unit's K_mid rows once for all G
 //         query heads (fp32 FMA on bf16/fp32 keys, d split over 4-8 lanes and
 //         summed with DPP).  Scores stay in LDS; a linear-bin histogram per head
 //         picks a per-chunk threshold so that at least r_min tokens pass, and
@@ -58,7 +58,10 @@ topk_scan_kernel(const float* __restrict__ q, const KT* __restrict__ kb, int64_t
   __shared__ float4 s_q[G * D / 4];
   __shared__ HeadParams s_hp[G];
 
-  const int u = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  // grid (units, chunks): consecutive workgroups take consecutive units and go
+  // to the 8 XCDs in turn, so with a unit count that is a multiple of 8 a
+  // unit's chunks, and the fused kernel's blocks that read their reports, share an XCD
+  const int u = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
   const int part = lane % LPT, slot = lane / LPT;
   const int t0 = c * ch;
@@ -338,7 +341,7 @@ template <typename KT, int D>
 hipError_t launch_scan_t(const TopkPlan& pl, const float* q, int G, const rma_kv& kv,
                          const rma_span& sp, const float* kappa, uint8_t* ws, hipStream_t st) {
   const int L_mid = (int)(sp.L - sp.n_sink - sp.n_tail);
-  return launch_scan_g<KT, D>(G, dim3(pl.n_chunks, kv.n_units), st, q, static_cast<const KT*>(kv.k),
+  return launch_scan_g<KT, D>(G, dim3(kv.n_units, pl.n_chunks), st, q, static_cast<const KT*>(kv.k),
                               kv.unit_stride, sp.n_sink, L_mid, pl, kappa,
                               reinterpret_cast<float2*>(ws + pl.off_ent),
                               reinterpret_cast<int2*>(ws + pl.off_meta),
