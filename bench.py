@@ -72,12 +72,12 @@ def parse():
 # copy of known size.  A record holds only for the kernel sources it was taken on.
 TRAFFIC = {
     # (kernel, workload, K): profiles/traffic_c1.md, profiles/traffic_c4.md
-    ("decode_fused_kernel", "c1", 328): {"fetch_bytes": 6298379, "write_bytes": 8192, "csrc": "a6dca0a094536f8f"},
-    ("topk_scan_kernel", "c1", 328): {"fetch_bytes": 33717192, "write_bytes": 500320, "csrc": "a6dca0a094536f8f"},
-    ("build_mfma_kernel", "c1", 328): {"fetch_bytes": 69255919, "write_bytes": 84054640, "csrc": "a6dca0a094536f8f"},
-    ("decode_fused_kernel", "c4", 1310): {"fetch_bytes": 2352836449, "write_bytes": 1376256, "csrc": "a6dca0a094536f8f"},
-    ("topk_scan_kernel", "c4", 1310): {"fetch_bytes": 30250619355, "write_bytes": 62364523, "csrc": "a6dca0a094536f8f"},
-    ("build_mfma_kernel", "c4", 1310): {"fetch_bytes": 60212716604, "write_bytes": 30167612291, "csrc": "a6dca0a094536f8f"},
+    ("decode_fused_kernel", "c1", 328): {"fetch_bytes": 6298366, "write_bytes": 8192, "csrc": "4346d9d15ab6b371"},
+    ("topk_scan_kernel", "c1", 328): {"fetch_bytes": 33659714, "write_bytes": 451168, "csrc": "4346d9d15ab6b371"},
+    ("build_mfma_kernel", "c1", 328): {"fetch_bytes": 69255656, "write_bytes": 84056022, "csrc": "4346d9d15ab6b371"},
+    ("decode_fused_kernel", "c4", 1310): {"fetch_bytes": 2352763431, "write_bytes": 1376256, "csrc": "4346d9d15ab6b371"},
+    ("topk_scan_kernel", "c4", 1310): {"fetch_bytes": 30241179891, "write_bytes": 62556054, "csrc": "4346d9d15ab6b371"},
+    ("build_mfma_kernel", "c4", 1310): {"fetch_bytes": 60212594223, "write_bytes": 30167620968, "csrc": "4346d9d15ab6b371"},
 }
 
 
